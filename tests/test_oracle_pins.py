@@ -1,0 +1,436 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+Each test ties one oracle function to something independent of its code: a
+value printed on the pages, the byte order of memory, a library routine
+(numpy integer/fp64 matmul, numpy/torch dtype converters), a closed form, an
+invariant, or a special case that reduces to a textbook computation.  They are
+chosen so that a plausible slip (a dropped term, a wrong shift or group index,
+a transposed operand, a sign error, round-half-up instead of half-even) fails
+at least one of them.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth_inputs as si
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- converters
+
+def test_bf16_widen_matches_torch():
+    r = np.random.default_rng(1)
+    bits = r.integers(0, 2**16, size=4096, dtype=np.uint32).astype(np.uint16)
+    bits = bits[((bits >> 7) & 0xFF) != 0xFF]          # finite values only
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.to_f64(bits, "bf16"), ref)
+
+
+def test_f16_widen_matches_numpy_including_subnormals():
+    bits = np.arange(0, 2**16, dtype=np.uint32).astype(np.uint16)
+    bits = bits[((bits >> 10) & 0x1F) != 0x1F]
+    ref = bits.view(np.float16).astype(np.float64)
+    np.testing.assert_array_equal(oracle.to_f64(bits, "f16"), ref)
+
+
+def test_f64_to_f16_rounding_matches_numpy():
+    r = np.random.default_rng(2)
+    v = np.concatenate([
+        r.standard_normal(20000) * 10.0 ** r.integers(-9, 5, 20000),
+        [0.0, -0.0, 65504.0, 65519.99, 65520.0, -65520.0, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26,
+         2.0 ** -14, 2.0 ** -14 - 2.0 ** -25, 1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 1e9],
+    ])
+    # ties-to-even cases at several binades
+    for e in range(-20, 15):
+        v = np.append(v, [(1024 + 0.5) * 2.0 ** (e - 10), (1025 + 0.5) * 2.0 ** (e - 10)])
+    with np.errstate(over="ignore"):
+        ref = v.astype(np.float16).view(np.uint16)
+    np.testing.assert_array_equal(oracle.f64_to_f16(v), ref)
+
+
+def test_f32_to_bf16_rounding_matches_torch():
+    r = np.random.default_rng(3)
+    u = r.integers(0, 2**32, size=50000, dtype=np.uint64).astype(np.uint32)
+    u = u[((u >> 23) & 0xFF) != 0xFF]
+    # exact ties: low 16 bits = 0x8000 with both parities of the kept part
+    ties = (np.arange(1, 200, dtype=np.uint32) << 16) | np.uint32(0x8000)
+    v = np.concatenate([u, ties]).view(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.f32_to_bf16(v), ref)
+
+
+# ---------------------------------------------------------------- O1 unpack
+
+def test_unpack_8bit_low_byte_is_lowest_column():
+    # mlx_int8.rs "Layout": four unsigned bytes per word, low byte = lowest column.
+    # Little-endian memory puts byte j of the stream in bits [8j, 8j+8) of the word.
+    stream = np.array([1, 2, 3, 4, 250, 0, 17, 255], dtype=np.uint8)
+    words = stream.view(np.uint32)
+    assert words[0] == 0x04030201
+    np.testing.assert_array_equal(oracle.unpack_affine(words[None, :], 1, 8, 8)[0], stream)
+
+
+def test_unpack_4bit_and_2bit_closed_forms():
+    np.testing.assert_array_equal(
+        oracle.unpack_affine(np.array([[0x76543210]], dtype=np.uint32), 1, 8, 4)[0], np.arange(8))
+    np.testing.assert_array_equal(
+        oracle.unpack_affine(np.array([[0xFEDCBA98]], dtype=np.uint32), 1, 8, 4)[0], np.arange(8, 16))
+    # 2-bit codes 0,1,2,3 repeating: byte = 0b11100100 = 0xE4
+    np.testing.assert_array_equal(
+        oracle.unpack_affine(np.array([[0xE4E4E4E4]], dtype=np.uint32), 1, 16, 2)[0], np.tile(np.arange(4), 4))
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_unpack_every_code_at_every_position(bits):
+    per = 32 // bits
+    vals = np.arange(2 ** bits, dtype=np.uint32)
+    for pos in range(per):
+        words = (vals << np.uint32(bits * pos)).astype(np.uint32)[:, None]
+        codes = oracle.unpack_affine(words, len(vals), per, bits)
+        expect = np.zeros((len(vals), per), dtype=np.uint8)
+        expect[:, pos] = vals
+        np.testing.assert_array_equal(codes, expect)
+
+
+def _codes_by_memory_order(packed: np.ndarray, bits: int) -> np.ndarray:
+    """Independent decode: walk the bytes of the words in memory order and split
+    each byte low bits first."""
+    by = np.ascontiguousarray(packed).view(np.uint8)
+    per_byte = 8 // bits
+    parts = [(by >> np.uint8(bits * j)) & np.uint8(2 ** bits - 1) for j in range(per_byte)]
+    return np.stack(parts, axis=-1).reshape(packed.shape[0], -1)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_unpack_random_words_matches_memory_order(bits):
+    r = np.random.default_rng(bits)
+    packed = r.integers(0, 2**32, size=(5, 12), dtype=np.uint64).astype(np.uint32)
+    K = 12 * 32 // bits
+    np.testing.assert_array_equal(oracle.unpack_affine(packed, 5, K, bits), _codes_by_memory_order(packed, bits))
+
+
+# ---------------------------------------------------------------- O2/O3 affine
+
+def _const(shape, value, dtype="bf16"):
+    return si.store(np.full(shape, value, dtype=np.float32), dtype)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_affine_unit_scale_zero_bias_is_integer_matmul(bits):
+    # scale 1, bias 0, integer x: y = x . Q^T exactly (numpy int64 matmul on codes
+    # decoded by memory order).  Catches a transposed operand or a wrong row stride.
+    M, N, K, G = 3, 7, 128, 32
+    r = np.random.default_rng(10 + bits)
+    packed = r.integers(0, 2**32, size=(N, K * bits // 32), dtype=np.uint64).astype(np.uint32)
+    xi = r.integers(-20, 21, size=(M, K))
+    x = si.bf16_bits(xi.astype(np.float32))
+    y = oracle.qmm_affine(x, "bf16", packed, _const((N, K // G), 1.0), _const((N, K // G), 0.0), "bf16",
+                          M, N, K, G, bits)
+    Q = _codes_by_memory_order(packed, bits).astype(np.int64)
+    np.testing.assert_array_equal(y, (xi @ Q.T).astype(np.float64))
+
+
+@pytest.mark.parametrize("sb", ["bf16", "f16", "f32"])
+def test_affine_zero_codes_leave_only_group_bias(sb):
+    # codes 0 => w[n,k] = bias[n, k/G]; y = x . repeat(bias)^T (numpy fp64 matmul).
+    M, N, K, G = 4, 6, 256, 64
+    r = np.random.default_rng(20)
+    b = si.store(r.standard_normal((N, K // G)).astype(np.float32), sb)
+    s = si.store(r.uniform(0.1, 1, (N, K // G)).astype(np.float32), sb)
+    x = si.activations(M, K, seed=(21,))
+    y = oracle.qmm_affine(x, "bf16", np.zeros((N, K * 4 // 32), np.uint32), s, b, sb, M, N, K, G, 4)
+    W = np.repeat(oracle.to_f64(b, sb), G, axis=1)
+    ref = oracle.to_f64(x, "bf16") @ W.T
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_affine_constant_codes_scale_by_group(G):
+    # all codes = c, bias 0: w[n,k] = c*scale[n, k/G]; checks the group index k/G.
+    M, N, K, c = 2, 5, 512, 11
+    r = np.random.default_rng(G)
+    s = si.bf16_bits(r.uniform(0.01, 0.1, (N, K // G)).astype(np.float32))
+    word = np.uint32(sum(c << (4 * j) for j in range(8)))
+    packed = np.full((N, K // 8), word, dtype=np.uint32)
+    x = si.activations(M, K, seed=(G, 1))
+    y = oracle.qmm_affine(x, "bf16", packed, s, _const((N, K // G), 0.0), "bf16", M, N, K, G, 4)
+    W = c * np.repeat(oracle.to_f64(s, "bf16"), G, axis=1)
+    np.testing.assert_allclose(y, oracle.to_f64(x, "bf16") @ W.T, rtol=1e-12, atol=1e-12)
+
+
+def test_affine_linear_in_x_and_in_scale_bias():
+    M, N, K, G = 3, 9, 256, 64
+    case = si.affine_case(M, N, K, G, 4, seed=(30,))
+    r = np.random.default_rng(31)
+    x1, x2 = r.integers(-8, 9, (M, K)), r.integers(-8, 9, (M, K))
+    f = lambda xi: oracle.qmm_affine(si.bf16_bits(xi.astype(np.float32)), "bf16", case.packed, case.scales,
+                                     case.biases, "bf16", M, N, K, G, 4)
+    np.testing.assert_allclose(f(x1 + x2), f(x1) + f(x2), rtol=1e-13, atol=1e-12)
+    # doubling scale and bias doubles y (exact: powers of two)
+    s2 = si.bf16_bits(2 * si.bits_to_f32(case.scales, "bf16"))
+    b2 = si.bf16_bits(2 * si.bits_to_f32(case.biases, "bf16"))
+    y1 = oracle.qmm_affine(case.x, "bf16", case.packed, case.scales, case.biases, "bf16", M, N, K, G, 4)
+    y2 = oracle.qmm_affine(case.x, "bf16", case.packed, s2, b2, "bf16", M, N, K, G, 4)
+    np.testing.assert_array_equal(y2, 2 * y1)
+
+
+def test_affine_group_permutation_invariance():
+    # Moving whole groups (x columns, code words, scale/bias columns together) leaves y.
+    M, N, K, G, bits = 2, 6, 512, 64, 4
+    case = si.affine_case(M, N, K, G, bits, seed=(40,))
+    r = np.random.default_rng(41)
+    pg = r.permutation(K // G)
+    kcols = (pg[:, None] * G + np.arange(G)).ravel()
+    wpg = G * bits // 32
+    wcols = (pg[:, None] * wpg + np.arange(wpg)).ravel()
+    y = oracle.qmm_affine_case(case)
+    y2 = oracle.qmm_affine(case.x[:, kcols], "bf16", case.packed[:, wcols], case.scales[:, pg], case.biases[:, pg],
+                           "bf16", M, N, K, G, bits)
+    np.testing.assert_allclose(y2, y, rtol=1e-12, atol=1e-12)
+
+
+def test_affine_k_perm_reads_x_through_permutation():
+    M, N, K, G = 2, 5, 256, 64
+    case = si.affine_case(M, N, K, G, 4, seed=(50,))
+    kp = np.random.default_rng(51).permutation(K).astype(np.int32)
+    y_perm = oracle.qmm_affine(case.x, "bf16", case.packed, case.scales, case.biases, "bf16", M, N, K, G, 4, k_perm=kp)
+    y_ref = oracle.qmm_affine(case.x[:, kp], "bf16", case.packed, case.scales, case.biases, "bf16", M, N, K, G, 4)
+    np.testing.assert_array_equal(y_perm, y_ref)
+    with pytest.raises(ValueError):
+        bad = kp.copy()
+        bad[3] = K
+        oracle.qmm_affine(case.x, "bf16", case.packed, case.scales, case.biases, "bf16", M, N, K, G, 4, k_perm=bad)
+
+
+def test_affine_rejects_bad_arguments():
+    with pytest.raises(ValueError):
+        oracle.qmm_affine(np.zeros((1, 96), np.uint16), "bf16", np.zeros((1, 12), np.uint32),
+                          np.zeros((1, 2), np.uint16), np.zeros((1, 2), np.uint16), "bf16", 1, 1, 96, 64, 4)
+    with pytest.raises(ValueError):
+        oracle.qmm_affine(np.zeros((1, 64), np.uint16), "bf16", np.zeros((1, 8), np.uint32),
+                          np.zeros((1, 1), np.uint16), np.zeros((1, 1), np.uint16), "bf16", 1, 1, 64, 64, 3)
+
+
+# ---------------------------------------------------------------- G1/G2 GPTQ
+
+def _golden_values(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return np.array([float(l) for l in f if l.strip() and not l.startswith("#")])
+
+
+def test_gptq_worked_example_row0():
+    # TinyGPT "GPTQReader" smoke test: codes 0..15, scale 1, stored zero 0 -> [-1 .. 14]
+    K, N, G = 16, 8, 16
+    codes = np.zeros((K, N), dtype=np.uint32)
+    codes[:, 0] = np.arange(16)
+    qweight = np.zeros((K // 8, N), dtype=np.uint32)
+    for i in range(K):                      # nibble i%8 of word (i/8) along IN
+        qweight[i // 8] |= codes[i] << np.uint32(4 * (i % 8))
+    assert qweight[0, 0] == 0x76543210 and qweight[1, 0] == 0xFEDCBA98
+    scales = si.f16_bits(np.ones((1, N), np.float32))
+    qzeros = np.zeros((1, N // 8), dtype=np.int32)
+    W = oracle.dequant_gptq(qweight.view(np.int32), qzeros, scales, None, K, N, G)
+    np.testing.assert_array_equal(W[0], _golden_values("gptq_row0.txt"))
+
+
+def test_gptq_zero_nibble_along_out_axis():
+    # qzeros packs 8 zero points along OUT: column o uses nibble o%8 of word o/8.
+    K, N, G = 8, 16, 8
+    qweight = np.zeros((1, N), dtype=np.int32)           # codes 0
+    zs = np.arange(N, dtype=np.uint32) % 16               # stored zero per column
+    qzeros = si.pack_nibbles_along_last(zs[None, :]).view(np.int32)
+    scales = si.f16_bits(np.ones((1, N), np.float32))
+    W = oracle.dequant_gptq(qweight, qzeros, scales, None, K, N, G)
+    np.testing.assert_array_equal(W[:, 0], -(zs.astype(np.float64) + 1))
+
+
+def test_gptq_top_nibble_is_unsigned():
+    # an int32 word with the sign bit set still holds code 15 in its top nibble
+    K, N, G = 8, 8, 8
+    qweight = np.full((1, N), 0xF0000000, dtype=np.uint32).view(np.int32)
+    assert qweight[0, 0] < 0
+    W = oracle.dequant_gptq(qweight, np.zeros((1, 1), np.int32), si.f16_bits(np.ones((1, N), np.float32)),
+                            None, K, N, G)
+    np.testing.assert_array_equal(W[0], [-1.0] * 7 + [14.0])
+
+
+def _gptq_codes_by_memory_order(qweight: np.ndarray) -> np.ndarray:
+    """[K/8, N] words -> [K, N] codes: code i sits in nibble i%8 of word i/8."""
+    w = np.ascontiguousarray(qweight).view(np.uint32)
+    parts = [(w >> np.uint32(4 * j)) & np.uint32(0xF) for j in range(8)]
+    return np.stack(parts, axis=1).reshape(-1, w.shape[1])
+
+
+@pytest.mark.parametrize("bias_dtype", ["f32", "f16"])
+def test_gptq_repack_equals_gptq_dequant(bias_dtype):
+    # bias_aff = -scale*(zero+1):  code*scale + bias == scale*(code - zero) term by term.
+    case = si.gptq_case(2, 512, 64, 128, seed=(60,))
+    packed, s_aff, b_aff, kp = oracle.gptq_to_affine_repack(case.qweight, case.qzeros, case.scales, case.g_idx,
+                                                            case.K, case.N, case.G, bias_dtype)
+    assert sorted(kp.tolist()) == list(range(case.K))
+    assert np.all(np.diff(case.g_idx[kp]) >= 0)                      # grouped
+    for g in range(case.K // case.G):                                 # stable inside a group
+        assert np.all(np.diff(kp[g * case.G:(g + 1) * case.G]) > 0)
+    W_aff = oracle.dequant_affine(packed, s_aff, b_aff, "f16", case.N, case.K, case.G, 4, bias_dtype=bias_dtype)
+    W_g = oracle.dequant_gptq(case.qweight, case.qzeros, case.scales, case.g_idx, case.K, case.N, case.G)
+    if bias_dtype == "f32":
+        np.testing.assert_array_equal(W_aff, W_g[:, kp])               # bit-exact
+    else:
+        assert np.max(np.abs(W_aff - W_g[:, kp])) <= 2.0 ** -11 * np.max(np.abs(W_g)) + 1e-12
+    # and the repacked layer computes the same y through k_perm
+    y_g = oracle.qmm_gptq(case.x, case.qweight, case.qzeros, case.scales, case.g_idx, 2, case.K, case.N, case.G)
+    y_a = oracle.qmm_affine(case.x, "f16", packed, s_aff, b_aff, "f16", 2, case.N, case.K, case.G, 4, k_perm=kp,
+                            bias_dtype=bias_dtype)
+    if bias_dtype == "f32":
+        np.testing.assert_allclose(y_a, y_g, rtol=1e-12, atol=1e-12)
+    else:                                    # f16 bias is rounded: within the float bar
+        assert oracle.affine_tolerance_report(y_a, y_g)["ok"]
+
+
+def test_gptq_gidx_permutation_invariance():
+    # Permuting K consistently in x, qweight codes and g_idx leaves y unchanged.
+    case = si.gptq_case(3, 256, 16, 64, seed=(70,))
+    r = np.random.default_rng(71)
+    p = r.permutation(case.K)
+    codes = _gptq_codes_by_memory_order(case.qweight)[p]              # [K, N]
+    qw2 = np.zeros_like(case.qweight.view(np.uint32))
+    for i in range(case.K):
+        qw2[i // 8] |= codes[i].astype(np.uint32) << np.uint32(4 * (i % 8))
+    y1 = oracle.qmm_gptq(case.x, case.qweight, case.qzeros, case.scales, case.g_idx, 3, case.K, case.N, case.G)
+    y2 = oracle.qmm_gptq(case.x[:, p], qw2.view(np.int32), case.qzeros, case.scales, case.g_idx[p], 3,
+                         case.K, case.N, case.G)
+    np.testing.assert_allclose(y2, y1, rtol=1e-12, atol=1e-12)
+
+
+def test_gptq_trivial_gidx_equals_affine_on_transposed_packing():
+    case = si.gptq_case(2, 256, 16, 64, seed=(80,), act_order=False)
+    y_none = oracle.qmm_gptq(case.x, case.qweight, case.qzeros, case.scales, None, 2, case.K, case.N, case.G)
+    y_expl = oracle.qmm_gptq(case.x, case.qweight, case.qzeros, case.scales, case.g_idx, 2, case.K, case.N, case.G)
+    np.testing.assert_array_equal(y_none, y_expl)
+    # same layer in the affine format, built with numpy only
+    codes = _gptq_codes_by_memory_order(case.qweight).T                # [N, K]
+    packed = si.pack_nibbles_along_last(codes)
+    s = case.scales.T.copy()                                           # [N, K/G] f16 patterns
+    zeros = case.zeros.T.astype(np.float64)                            # drawn zero points (z_stored+1)
+    b = (-oracle.to_f64(s, "f16") * zeros).astype(np.float32)
+    W = codes.astype(np.float64) * np.repeat(oracle.to_f64(s, "f16"), case.G, 1) + np.repeat(b.astype(np.float64), case.G, 1)
+    y_aff = oracle.to_f64(case.x, "f16") @ W.T
+    np.testing.assert_allclose(y_none, y_aff, rtol=1e-12, atol=1e-12)
+
+
+def test_gptq_repack_rejects_uneven_groups():
+    case = si.gptq_case(1, 256, 8, 64, seed=(90,))
+    g = case.g_idx.copy()
+    i0 = int(np.flatnonzero(case.g_idx == 0)[0])
+    g[i0] = 1                                   # group 0 now has G-1 members, group 1 has G+1
+    with pytest.raises(ValueError):
+        oracle.gptq_to_affine_repack(case.qweight, case.qzeros, case.scales, g, case.K, case.N, case.G)
+
+
+# ---------------------------------------------------------------- W4A8
+
+def _s4_by_memory_order(w_q4: np.ndarray) -> np.ndarray:
+    by = np.ascontiguousarray(w_q4).view(np.uint8)
+    lo = (by << np.uint8(4)).view(np.int8) >> 4     # arithmetic shift sign-extends
+    hi = by.view(np.int8) >> 4
+    return np.stack([lo, hi], axis=-1).reshape(w_q4.shape[0], -1).astype(np.int64)
+
+
+def test_w4a8_acc_matches_integer_matmul_all_nibbles():
+    # every nibble value -8..7 present in every row; numpy int64 matmul is the reference
+    M, N, K = 8, 8, 64
+    r = np.random.default_rng(100)
+    codes = np.stack([r.permutation(np.tile(np.arange(-8, 8), K // 16)) for _ in range(N)])
+    w_q4 = si.pack_nibbles_along_last(codes & 0xF)
+    np.testing.assert_array_equal(_s4_by_memory_order(w_q4), codes)
+    q = r.integers(-127, 128, size=(M, K)).astype(np.int8)
+    acc = oracle.w4a8_acc(q, w_q4, M, N, K)
+    np.testing.assert_array_equal(acc, q.astype(np.int64) @ codes.T)
+
+
+def test_w4a8_quantize_ties_and_extremes():
+    # amax = 127 * 2^-3 makes s_x = 2^-3 exactly, so x = (j + 1/2) * 2^-3 is an exact tie
+    e = 2.0 ** -3
+    row = [127 * e, 0.5 * e, 1.5 * e, 2.5 * e, 3.5 * e, -0.5 * e, -1.5 * e, -2.5 * e, 126.5 * e, -127 * e,
+           0.0, 10 * e, 10.25 * e, 10.75 * e, 64.5 * e, 65.5 * e]
+    x = si.f16_bits(np.array([row], dtype=np.float32))
+    assert np.array_equal(si.bits_to_f32(x, "f16")[0], np.array(row, dtype=np.float32))   # all exact in f16
+    q, s = oracle.w4a8_quantize_act(x, 1, len(row))
+    assert s[0] == np.float32(e)
+    expect = [127, 0, 2, 2, 4, 0, -2, -2, 126, -127, 0, 10, 10, 11, 64, 66]   # half to even
+    np.testing.assert_array_equal(q[0], expect)
+
+
+def test_w4a8_quantize_properties_and_zero_row():
+    case = si.w4a8_case(6, 8, 256, seed=(110,))
+    x = case.x.copy()
+    x[3] = 0                                                  # an all-zero row
+    q, s = oracle.w4a8_quantize_act(x, 6, 256)
+    xf = si.bits_to_f32(x, "f16")
+    assert s[3] == 0 and not q[3].any()
+    for m in (0, 1, 2, 4, 5):
+        assert s[m] == np.float32(np.abs(xf[m]).max()) / np.float32(127)
+        k = int(np.abs(xf[m]).argmax())
+        assert abs(int(q[m, k])) == 127 and np.sign(q[m, k]) == np.sign(xf[m, k])
+        # each code is within half a step of x/s (plus float slack)
+        assert np.all(np.abs(q[m].astype(np.float64) - xf[m] / s[m]) <= 0.5 + 1e-5)
+    assert np.abs(q.astype(int)).max() <= 127
+    _, _, acc, y = oracle.w4a8(x, case.w_q4, case.s_w, 6, 8, 256)
+    assert not y[3].any() and not acc[3].any()
+
+
+def test_w4a8_y_is_acc_times_scales():
+    case = si.w4a8_case(4, 16, 128, seed=(120,))
+    q, s, acc, y = oracle.w4a8(case.x, case.w_q4, case.s_w, 4, 16, 128)
+    np.testing.assert_array_equal(acc, q.astype(np.int64) @ _s4_by_memory_order(case.w_q4).T)
+    ref = acc.astype(np.float64) * s.astype(np.float64)[:, None] * oracle.to_f64(case.s_w, "f16")[None, :]
+    np.testing.assert_array_equal(y, ref)
+
+
+# ---------------------------------------------------------------- quantize_pack
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("sb", ["bf16", "f16", "f32"])
+def test_quantize_pack_recovers_grid_aligned_weights(bits, sb):
+    # w = q*s + b with s = 2^-6, b = -0.25 (exact everywhere) and both 0 and
+    # 2^bits-1 present in each group must come back unchanged.
+    N, K, G = 4, 256, 64
+    r = np.random.default_rng(bits)
+    qmax = 2 ** bits - 1
+    q = r.integers(0, qmax + 1, size=(N, K))
+    q[:, ::G] = 0
+    q[:, 1::G] = qmax
+    s, b = 2.0 ** -6, -0.25
+    w = (q * s + b).astype(np.float32)
+    packed, S, B = oracle.quantize_pack_affine(w, "f32", N, K, G, bits, sb)
+    np.testing.assert_array_equal(_codes_by_memory_order(packed, bits), q)
+    np.testing.assert_array_equal(oracle.to_f64(S, sb), np.full((N, K // G), s))
+    np.testing.assert_array_equal(oracle.to_f64(B, sb), np.full((N, K // G), b))
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_quantize_pack_reconstruction_error_bound(bits):
+    N, K, G = 8, 512, 64
+    w = si.dense_weights(N, K, seed=(130, bits), dtype="bf16")
+    packed, S, B = oracle.quantize_pack_affine(w, "bf16", N, K, G, bits, "bf16")
+    Wd = oracle.dequant_affine(packed, S, B, "bf16", N, K, G, bits)
+    wf = oracle.to_f64(w, "bf16")
+    s = np.repeat(oracle.to_f64(S, "bf16"), G, axis=1)
+    # half a step, plus the bf16 rounding of scale and bias stretched over 2^bits steps
+    slack = 0.5 * s + (2 ** bits) * s * 2.0 ** -8 + np.abs(np.repeat(oracle.to_f64(B, "bf16"), G, 1)) * 2.0 ** -8
+    assert np.all(np.abs(Wd - wf) <= slack + 1e-12)
+    codes = _codes_by_memory_order(packed, bits)
+    assert codes.min() == 0 and codes.max() <= 2 ** bits - 1
+
+
+def test_quantize_pack_constant_group_gives_zero_scale():
+    N, K, G = 2, 64, 32
+    w = np.full((N, K), 0.375, dtype=np.float32)
+    packed, S, B = oracle.quantize_pack_affine(w, "f32", N, K, G, 4, "bf16")
+    assert not packed.any()
+    np.testing.assert_array_equal(oracle.to_f64(S, "bf16"), 0.0)
+    np.testing.assert_array_equal(oracle.to_f64(B, "bf16"), 0.375)
