@@ -1,0 +1,180 @@
+"""Python binding of libqaff (group-wise affine quantized matmul, MI355X / gfx950).
+
+Argument marshalling only: every computation runs in the HIP kernels of
+libqaff.so, reached through its C ABI (include/qaff.h).  PyTorch supplies
+device memory and the current HIP stream; nothing here computes.  There is no
+CPU fallback: if the library is missing this module raises on first use.
+
+Functions mirror the C entry points:
+    qmm_affine, qgemv_affine, qmm_gptq, qgemm_w4a8,
+    gptq_to_affine_repack, quantize_pack_affine
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["QaffError", "qmm_affine", "qgemv_affine", "qmm_gptq", "qgemm_w4a8", "gptq_to_affine_repack",
+           "quantize_pack_affine", "library_path", "lib", "STATUS", "DTYPE"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libqaff.so")
+
+STATUS = {0: "QAFF_OK", 1: "QAFF_E_INVAL", 2: "QAFF_E_UNSUPPORTED", 3: "QAFF_E_ALIGN", 4: "QAFF_E_HIP"}
+DTYPE = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2}
+
+_I64, _I32, _VP = C.c_int64, C.c_int32, C.c_void_p
+
+# argument type lists of the exported symbols (include/qaff.h)
+_SIGS = {
+    "qmm_affine": [_VP] * 6 + [_I64] * 3 + [_I32] * 5 + [_VP],
+    "qgemv_affine": [_VP] * 6 + [_I64] * 3 + [_I32] * 5 + [_VP],
+    "qmm_gptq": [_VP] * 6 + [_I64] * 3 + [_I32, _VP],
+    "qgemm_w4a8": [_VP] * 7 + [_I64] * 3 + [_VP],
+    "gptq_to_affine_repack": [_VP] * 7 + [_I32, _VP] + [_I64] * 2 + [_I32, _VP],
+    "quantize_pack_affine": [_VP, _I32, _VP, _VP, _VP, _I32, _I64, _I64, _I32, _I32, _VP],
+}
+
+
+class QaffError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded libqaff.so (ctypes), with argument types declared."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+        L = C.CDLL(_LIB_PATH)
+        for name, argtypes in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = argtypes
+            f.restype = C.c_int
+        L.qaff_last_error.restype = C.c_char_p
+        L.qaff_last_error.argtypes = []
+        L.qaff_version.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise QaffError(status, where, lib().qaff_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in DTYPE:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    return DTYPE[t.dtype]
+
+
+def _u32(t: torch.Tensor) -> torch.Tensor:
+    # packed words travel as int32 or uint32 tensors; only the bits matter
+    if t.dtype not in (torch.int32, torch.uint32):
+        raise ValueError("packed words must be an int32/uint32 tensor")
+    return t
+
+
+def _affine(fn: str, x, w_packed, scales, biases, group_size, bits, k_perm, out):
+    M, K = x.shape
+    N = w_packed.shape[0]
+    y = out if out is not None else torch.empty((M, N), dtype=x.dtype, device=x.device)
+    st = getattr(lib(), fn)(_ptr(x), _ptr(_u32(w_packed)), _ptr(scales), _ptr(biases), _ptr(k_perm), _ptr(y), M, N, K,
+                            group_size, bits, _dt(x), _dt(scales), _dt(biases), _stream(x.device))
+    _check(st, fn)
+    return y
+
+
+def qmm_affine(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor,
+               group_size: int, bits: int, k_perm: Optional[torch.Tensor] = None,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y[M,N] = x[M,K] . W^T, W[n,k] = code*scale[n,k/G] + bias[n,k/G]."""
+    return _affine("qmm_affine", x, w_packed, scales, biases, group_size, bits, k_perm, out)
+
+
+def qgemv_affine(x, w_packed, scales, biases, group_size: int, bits: int, k_perm=None, out=None) -> torch.Tensor:
+    """As qmm_affine, always on the GEMV kernel (M <= 16)."""
+    return _affine("qgemv_affine", x, w_packed, scales, biases, group_size, bits, k_perm, out)
+
+
+def qmm_gptq(x: torch.Tensor, qweight: torch.Tensor, qzeros: torch.Tensor, scales: torch.Tensor,
+             g_idx: Optional[torch.Tensor], group_size: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = x . W^T for a GPTQ layer (qweight [K/8,N], qzeros [K/G,N/8], scales f16 [K/G,N])."""
+    M, K = x.shape
+    N = qweight.shape[1]
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=x.device)
+    st = lib().qmm_gptq(_ptr(x), _ptr(qweight), _ptr(qzeros), _ptr(scales), _ptr(g_idx), _ptr(y), M, N, K,
+                        group_size, _stream(x.device))
+    _check(st, "qmm_gptq")
+    return y
+
+
+def qgemm_w4a8(x: torch.Tensor, w_q4: torch.Tensor, s_w: torch.Tensor, want_acc: bool = False):
+    """Returns (y f16 [M,N], x_q int8 [M,K], s_x f32 [M], acc int32 [M,N] or None)."""
+    M, K = x.shape
+    N = w_q4.shape[0]
+    dev = x.device
+    y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    x_q = torch.empty((M, K), dtype=torch.int8, device=dev)
+    s_x = torch.empty((M,), dtype=torch.float32, device=dev)
+    acc = torch.empty((M, N), dtype=torch.int32, device=dev) if want_acc else None
+    st = lib().qgemm_w4a8(_ptr(x), _ptr(_u32(w_q4)), _ptr(s_w), _ptr(y), _ptr(x_q), _ptr(s_x), _ptr(acc), M, N, K,
+                          _stream(dev))
+    _check(st, "qgemm_w4a8")
+    return y, x_q, s_x, acc
+
+
+def gptq_to_affine_repack(qweight: torch.Tensor, qzeros: torch.Tensor, scales: torch.Tensor,
+                          g_idx: Optional[torch.Tensor], group_size: int, bias_dtype=torch.float32):
+    """Returns (w_packed [N,K/8] int32, scales [N,K/G] f16, biases [N,K/G] bias_dtype, k_perm [K] int32)."""
+    K = qweight.shape[0] * 8
+    N = qweight.shape[1]
+    dev = qweight.device
+    w = torch.empty((N, K // 8), dtype=torch.int32, device=dev)
+    s = torch.empty((N, K // group_size), dtype=torch.float16, device=dev)
+    b = torch.empty((N, K // group_size), dtype=bias_dtype, device=dev)
+    kp = torch.empty((K,), dtype=torch.int32, device=dev)
+    st = lib().gptq_to_affine_repack(_ptr(qweight), _ptr(qzeros), _ptr(scales), _ptr(g_idx), _ptr(w), _ptr(s),
+                                     _ptr(b), DTYPE[bias_dtype], _ptr(kp), K, N, group_size, _stream(dev))
+    _check(st, "gptq_to_affine_repack")
+    return w, s, b, kp
+
+
+def quantize_pack_affine(w: torch.Tensor, group_size: int, bits: int, sb_dtype=torch.bfloat16):
+    """Returns (w_packed [N, K*bits/32] int32, scales [N,K/G], biases [N,K/G])."""
+    N, K = w.shape
+    dev = w.device
+    packed = torch.empty((N, K * bits // 32), dtype=torch.int32, device=dev)
+    s = torch.empty((N, K // group_size), dtype=sb_dtype, device=dev)
+    b = torch.empty((N, K // group_size), dtype=sb_dtype, device=dev)
+    st = lib().quantize_pack_affine(_ptr(w), _dt(w), _ptr(packed), _ptr(s), _ptr(b), DTYPE[sb_dtype], N, K,
+                                    group_size, bits, _stream(dev))
+    _check(st, "quantize_pack_affine")
+    return packed, s, b

@@ -1,0 +1,116 @@
+// Shared device helpers and launcher declarations of libqaff (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qaff {
+
+enum Dtype : int { BF16 = 0, F16 = 1, F32 = 2 };
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+typedef __attribute__((ext_vector_type(16))) int i32x16_t;
+
+// ---- scalar storage formats -------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// element i of a bf16 / f16 / f32 array as float (exact)
+__device__ __forceinline__ float load_as_f32(const void* base, long i, int dt) {
+  if (dt == BF16) return bf16_bits_to_f32(((const uint16_t*)base)[i]);
+  if (dt == F16) return f16_bits_to_f32(((const uint16_t*)base)[i]);
+  return ((const float*)base)[i];
+}
+
+// float -> 16-bit storage, round to nearest even (v_cvt_pk_bf16_f32 / v_cvt_f16_f32)
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
+  return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
+  return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+__device__ __forceinline__ uint16_t f32_to_act_bits(float v, bool f16) {
+  return f16 ? f32_to_f16_bits(v) : f32_to_bf16_bits(v);
+}
+
+// ---- wave reduction -----------------------------------------------------
+// Sum over the 64 lanes of a wave: rotates inside each row of 16 lanes with
+// DPP (every lane of the row ends with the row sum), then two swaps across
+// rows.  Every lane returns the full sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_mov<0x128>(v);  // row_ror:8
+  v += dpp_mov<0x124>(v);  // row_ror:4
+  v += dpp_mov<0x122>(v);  // row_ror:2
+  v += dpp_mov<0x121>(v);  // row_ror:1
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+}  // namespace qaff
+
+// ---- launchers (host side; each returns a hipError_t) ---------------------
+
+namespace qaff {
+
+struct AffineArgs {
+  const void* x;
+  const uint32_t* w;
+  const void* scales;
+  const void* biases;
+  const int32_t* k_perm;
+  void* y;
+  int64_t M, N, K;
+  int G, bits;
+  int act_dt, s_dt, b_dt;
+};
+
+hipError_t launch_gemv_affine(const AffineArgs& a, hipStream_t s);
+hipError_t launch_gemm_affine(const AffineArgs& a, hipStream_t s);
+
+struct GptqArgs {
+  const void* x;
+  const int32_t* qweight;
+  const int32_t* qzeros;
+  const void* scales;
+  const int32_t* g_idx;
+  void* y;
+  int64_t M, N, K;
+  int G;
+};
+hipError_t launch_gptq_direct(const GptqArgs& a, hipStream_t s);
+hipError_t launch_gptq_repack(const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                              const int32_t* k_perm_dev, uint32_t* w_out, void* s_out, void* b_out, int bias_dt,
+                              int64_t K, int64_t N, int G, hipStream_t s);
+
+struct W4A8Args {
+  const void* x;
+  const uint32_t* w;
+  const void* s_w;
+  void* y;
+  int8_t* x_q;
+  float* s_x;
+  int32_t* acc;
+  int64_t M, N, K;
+};
+hipError_t launch_w4a8(const W4A8Args& a, hipStream_t s);
+
+hipError_t launch_quantize_pack(const void* w, int w_dt, uint32_t* packed, void* scales, void* biases, int sb_dt,
+                                int64_t N, int64_t K, int G, int bits, hipStream_t s);
+
+}  // namespace qaff

@@ -1,0 +1,521 @@
+// Prefill GEMM for group-wise affine weights (M > 16): y = x . W^T with
+// W[n,k] = q(n,k) * scale[n, k/G] + bias[n, k/G] (mlx_int8.rs "Layout";
+// Transformers "Metal" page: 2/4/8-bit codes, per-group scale and bias).
+//
+// Exactness.  Rounding the dequantized weight to bf16 or fp16 is not accurate
+// enough for the elementwise bound (8-bit codes especially), so the kernel
+// never rounds a weight.  It writes
+//     q = sum_a c_a * p_a + OFF            (code pieces p_a in [-8, 7], c_a a power of 2)
+//     scale * 2^-e_n = sum_j s_j            (pieces s_j with <= 8 significant bits)
+//     W = 2^e_n * sum_{a,j} c_a p_a s_j + (OFF*scale + bias)
+// Every c_a p_a s_j has at most 3 + 8 = 11 significant bits, so it is EXACT in
+// fp16.  x is scaled per row by a power of two (2^-e_m) into fp16, exact in
+// fp16's normal range.  Then
+//     y[m,n] = 2^(e_m+e_n) * ( sum_k xh[m,k] * sum_{a,j} c_a p_a s_j
+//                            + sum_g xs[m,g] * cb[n,g] )
+// with xs the group sums of xh and cb = (OFF*scale + bias) * 2^-e_n.  The
+// first sum runs on v_mfma_f32_32x32x16_f16 (one pass per (a, j) pair: 1 for
+// 4-bit codes with bf16 scales, 2 for 8-bit codes or f16 scales); the second
+// is a short tail of v_mfma_f32_32x32x16_bf16 over 3*K/G columns carrying
+// hi/lo bf16 splits of xs and cb.  Everything accumulates in one fp32 tile.
+//
+// Kernels:
+//   prep_x  : per row of x: e_m, xh (fp16, permuted to the code decode order,
+//             read through k_perm when given), tail A = [xs_hi, xs_hi, xs_lo]
+//   prep_w  : per row of W: e_n, scale pieces s_j (fp16), tail B = [cb_hi, cb_lo, cb_hi]
+//   gemm    : 256 threads, tile BM x 256 (4 waves side by side along N, each
+//             BM x 64); x tile double-buffered in LDS; packed codes go from
+//             global memory straight to registers, are decoded with the
+//             exponent-bias trick (code | 0x6400 = 1024 + code in fp16) and
+//             scaled with packed fp16 math; XCD-aware tile order.
+#include <mutex>
+
+#include "common.h"
+
+namespace qaff {
+
+hipError_t launch_gemv_affine(const AffineArgs& a, hipStream_t s);
+
+namespace {
+
+constexpr int BN = 256;       // tile width along N (4 waves x 64)
+constexpr int BK = 64;        // codes per K tile
+constexpr int LDS_ROW = 144;  // bytes per x row in LDS: 64 fp16 + 16 bytes of padding (no bank conflicts)
+
+__device__ __forceinline__ uint32_t f32_bits(float v) { return __float_as_uint(v); }
+__device__ __forceinline__ float trunc_bf16(float v) { return __uint_as_float(f32_bits(v) & 0xffff0000u); }
+
+// Position, within its block, of the source column of permuted column j.
+// It matches the order in which the kernel decodes codes from a word:
+//   4-bit: (c0,c4),(c1,c5),(c2,c6),(c3,c7)            block of 8
+//   8-bit: (c0,c2),(c1,c3) per word, two words          block of 8
+//   2-bit: (c0,c8),(c1,c9),...,(c7,c15)                 block of 16
+template <int BITS>
+struct Perm {
+  static constexpr int BLK = BITS == 2 ? 16 : 8;
+  static __device__ __forceinline__ int src(int j) {
+    if (BITS == 4) return (j >> 1) + ((j & 1) << 2);
+    if (BITS == 8) return (j & 4) + (j >> 1 & 1) + ((j & 1) << 1);
+    return (j >> 1) + ((j & 1) << 3);
+  }
+};
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// exponent e with |v| * 2^-e in [1, 2) (0 for v == 0)
+__device__ __forceinline__ int exp_of(float v) {
+  if (!(v > 0.f)) return 0;
+  int e;
+  (void)frexpf(v, &e);
+  return e - 1;
+}
+
+// ---------------------------------------------------------------------------
+// prep_x: one block (256 threads) per padded row m.
+template <int BITS>
+__global__ __launch_bounds__(256) void prep_x_kernel(const void* __restrict__ x, int act_dt,
+                                                     const int32_t* __restrict__ k_perm, int M, int K, int G,
+                                                     int Kt, _Float16* __restrict__ xh, uint16_t* __restrict__ tA,
+                                                     int* __restrict__ em) {
+  constexpr int BLK = Perm<BITS>::BLK;
+  const int m = blockIdx.x, t = threadIdx.x;
+  const int ng = K / G;
+  _Float16* xrow = xh + (long)m * K;
+  uint16_t* trow = tA + (long)m * Kt;
+  if (m >= M) {  // padding rows of the tile grid are zero
+    for (int k = t; k < K; k += 256) xrow[k] = (_Float16)0.f;
+    for (int k = t; k < Kt; k += 256) trow[k] = 0;
+    if (t == 0) em[m] = 0;
+    return;
+  }
+  const long base = (long)m * K;
+  __shared__ float red[4];
+  float amax = 0.f;
+  for (int k = t; k < K; k += 256) amax = fmaxf(amax, fabsf(load_as_f32(x, base + k, act_dt)));
+  amax = wave_max(amax);
+  if ((t & 63) == 0) red[t >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const int e = exp_of(amax);
+  if (t == 0) em[m] = e;
+  const float sc = ldexpf(1.f, -e);
+
+  // blocks of BLK permuted columns; the lanes that share a group are
+  // consecutive and aligned, so the group sum is a butterfly over them
+  const int nblk = K / BLK;
+  const int bpg = G / BLK;  // blocks per group: 2..16, a power of two
+  for (int b0 = 0; b0 < nblk; b0 += 256) {
+    const int bi = b0 + t;
+    float part = 0.f;
+    if (bi < nblk) {
+      _Float16 out[BLK];
+#pragma unroll
+      for (int j = 0; j < BLK; ++j) {
+        const int k = bi * BLK + Perm<BITS>::src(j);
+        const float v = load_as_f32(x, base + (k_perm ? k_perm[k] : k), act_dt) * sc;
+        out[j] = (_Float16)v;
+        part += v;
+      }
+#pragma unroll
+      for (int j = 0; j < BLK; j += 8) *reinterpret_cast<f16x8_t*>(xrow + bi * BLK + j) =
+          f16x8_t{out[j], out[j + 1], out[j + 2], out[j + 3], out[j + 4], out[j + 5], out[j + 6], out[j + 7]};
+    }
+    for (int o = 1; o < bpg; o <<= 1) part += __shfl_xor(part, o);
+    if (bi < nblk && (bi % bpg) == 0) {
+      const int g = bi / bpg;
+      const uint16_t hi = f32_to_bf16_bits(part);
+      const uint16_t lo = f32_to_bf16_bits(part - bf16_bits_to_f32(hi));
+      trow[3 * g] = hi;
+      trow[3 * g + 1] = hi;
+      trow[3 * g + 2] = lo;
+    }
+  }
+  for (int k = 3 * ng + t; k < Kt; k += 256) trow[k] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// prep_w: one wave per padded row n.  PS = number of scale pieces.
+template <int PS>
+__global__ __launch_bounds__(256) void prep_w_kernel(const void* __restrict__ scales, int s_dt,
+                                                     const void* __restrict__ biases, int b_dt, float off, int N,
+                                                     int ng, int Kt, _Float16* __restrict__ sh,
+                                                     uint16_t* __restrict__ tB, int* __restrict__ en) {
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  _Float16* srow = sh + (long)n * ng * PS;
+  uint16_t* trow = tB + (long)n * Kt;
+  if (n >= N) {
+    for (int i = lane; i < ng * PS; i += 64) srow[i] = (_Float16)0.f;
+    for (int k = lane; k < Kt; k += 64) trow[k] = 0;
+    if (lane == 0) en[n] = 0;
+    return;
+  }
+  const long base = (long)n * ng;
+  float smax = 0.f;
+  for (int g = lane; g < ng; g += 64) smax = fmaxf(smax, fabsf(load_as_f32(scales, base + g, s_dt)));
+  smax = wave_max(smax);
+  const int e = exp_of(smax);
+  if (lane == 0) en[n] = e;
+  const float sc = ldexpf(1.f, -e);
+  for (int g = lane; g < ng; g += 64) {
+    const float s = load_as_f32(scales, base + g, s_dt);
+    const float b = load_as_f32(biases, base + g, b_dt);
+    float r = s * sc;  // exact: a power-of-two scaling
+#pragma unroll
+    for (int j = 0; j < PS; ++j) {
+      const float p = (j == PS - 1) ? r : trunc_bf16(r);
+      srow[g * PS + j] = (_Float16)p;
+      r -= p;
+    }
+    const float cb = fmaf(off, s, b) * sc;
+    const uint16_t hi = f32_to_bf16_bits(cb);
+    const uint16_t lo = f32_to_bf16_bits(cb - bf16_bits_to_f32(hi));
+    trow[3 * g] = hi;
+    trow[3 * g + 1] = lo;
+    trow[3 * g + 2] = hi;
+  }
+  for (int k = 3 * ng + lane; k < Kt; k += 64) trow[k] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// main GEMM
+
+struct GemmParams {
+  const _Float16* xh;
+  const uint16_t* tA;
+  const int* em;
+  const uint32_t* w;
+  const _Float16* sh;
+  const uint16_t* tB;
+  const int* en;
+  uint16_t* y;
+  int M, N, K, ng, Kt, G;
+  int Tm, Tn, per_xcd;
+  int out_f16;
+};
+
+__device__ __forceinline__ f16x2_t h2(uint32_t v) { return __builtin_bit_cast(f16x2_t, v); }
+__device__ __forceinline__ uint32_t u32(f16x2_t v) { return __builtin_bit_cast(uint32_t, v); }
+
+// B fragment (8 fp16 = 4 dwords) for one 32x32x16 step, one code piece, one
+// scale piece.  `wd` holds the lane's words for this step (1 for 4-bit, 2 for
+// 8-bit, 1 (half used) for 2-bit).
+template <int BITS>
+struct Decode {
+  // integer pieces as exact fp16 pairs, in the kernel's decode order
+  static constexpr int NPIECE = BITS == 8 ? 2 : 1;
+  static constexpr float OFFQ = BITS == 4 ? 8.f : (BITS == 8 ? 136.f : 0.f);
+  static __device__ __forceinline__ void pieces(const uint32_t* wd, int half, f16x2_t (&v)[NPIECE][4]) {
+    const f16x2_t k1032 = {(_Float16)-1032.f, (_Float16)-1032.f};
+    const f16x2_t k1024 = {(_Float16)-1024.f, (_Float16)-1024.f};
+    if constexpr (BITS == 4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[0][i] = h2(((wd[0] >> (4 * i)) & 0x000F000Fu) | 0x64006400u) + k1032;
+    } else if constexpr (BITS == 8) {
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        v[0][2 * w] = h2(((wd[w] >> 4) & 0x000F000Fu) | 0x64006400u) + k1032;       // hi nibbles (c0,c2)
+        v[0][2 * w + 1] = h2(((wd[w] >> 12) & 0x000F000Fu) | 0x64006400u) + k1032;  // (c1,c3)
+        v[1][2 * w] = h2((wd[w] & 0x000F000Fu) | 0x64006400u) + k1032;              // lo nibbles
+        v[1][2 * w + 1] = h2(((wd[w] >> 8) & 0x000F000Fu) | 0x64006400u) + k1032;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[0][i] = h2(((wd[0] >> (2 * (i + 4 * half))) & 0x00030003u) | 0x64006400u) + k1024;
+    }
+  }
+  // multiplier of piece a
+  static constexpr float piece_mult(int a) { return (BITS == 8 && a == 0) ? 16.f : 1.f; }
+};
+
+template <int BITS, int PS, int MB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_affine_kernel(GemmParams p) {
+  using D = Decode<BITS>;
+  constexpr int BM = MB * 32;
+  constexpr int WPL = BITS;             // words per lane per K tile (32 codes)
+  constexpr int WPR = 2 * BITS;         // words per row per K tile
+  constexpr int A_CHUNKS = BM * 8 / 256;  // 16-byte chunks of the x tile per thread
+
+  // XCD-aware tile order: consecutive blocks go round-robin over the 8 XCDs,
+  // so block b runs on XCD b%8; give each XCD a contiguous range of tiles
+  // (m-major) so the x rows of a tile row stay in that XCD's L2.
+  const int b = blockIdx.x;
+  const int v = (b & 7) * p.per_xcd + (b >> 3);
+  if (v >= p.Tm * p.Tn) return;
+  const int tm = v / p.Tn, tn = v % p.Tn;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2][BM * LDS_ROW];
+
+  f32x16_t acc[MB][2];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // rows of W this lane decodes (clamped into range; results past N are dropped)
+  int nrow[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int n = n0 + wave * 64 + nb * 32 + l32;
+    nrow[nb] = n < p.N ? n : p.N - 1;
+  }
+
+  // ---- tail: sum_g xs * cb on bf16 MFMA, operands straight from global
+  for (int kt = 0; kt < p.Kt; kt += 16) {
+    bf16x8_t bt[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      bt[nb] = *reinterpret_cast<const bf16x8_t*>(p.tB + (long)(n0 + wave * 64 + nb * 32 + l32) * p.Kt + kt + 8 * half);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const bf16x8_t at = *reinterpret_cast<const bf16x8_t*>(p.tA + (long)(m0 + mb * 32 + l32) * p.Kt + kt + 8 * half);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, bt[nb], acc[mb][nb], 0, 0, 0);
+    }
+  }
+
+  // ---- main loop over K tiles of 64 codes
+  const int nkt = p.K / BK;
+  const long wrow = (long)p.K * BITS / 32;  // words per row of W
+  uint32_t wcur[2][WPL], wnxt[2][WPL];
+  f16x2_t scur[2][PS], snxt[2][PS];
+  uint4 areg[A_CHUNKS];
+
+  auto load_w = [&](int kt, uint32_t (&wd)[2][WPL], f16x2_t (&sd)[2][PS]) {
+    const int g = (kt * BK + 32 * half) / p.G;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const uint32_t* src = p.w + nrow[nb] * wrow + kt * WPR + half * WPL;
+      if constexpr (WPL == 1) {
+        wd[nb][0] = src[0];
+      } else if constexpr (WPL == 2) {
+        const uint2 u = *reinterpret_cast<const uint2*>(src);
+        wd[nb][0] = u.x;
+        wd[nb][1] = u.y;
+      } else {
+#pragma unroll
+        for (int q = 0; q < WPL / 4; ++q) {
+          const uint4 u = reinterpret_cast<const uint4*>(src)[q];
+          wd[nb][4 * q] = u.x;
+          wd[nb][4 * q + 1] = u.y;
+          wd[nb][4 * q + 2] = u.z;
+          wd[nb][4 * q + 3] = u.w;
+        }
+      }
+      const _Float16* sp = p.sh + ((long)nrow[nb] * p.ng + g) * PS;
+#pragma unroll
+      for (int j = 0; j < PS; ++j) sd[nb][j] = f16x2_t{sp[j], sp[j]};
+    }
+  };
+  auto load_a = [&](int kt) {
+#pragma unroll
+    for (int c = 0; c < A_CHUNKS; ++c) {
+      const int ch = t + 256 * c, row = ch >> 3, col = ch & 7;
+      areg[c] = *reinterpret_cast<const uint4*>(p.xh + (long)(m0 + row) * p.K + kt * BK + col * 8);
+    }
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < A_CHUNKS; ++c) {
+      const int ch = t + 256 * c, row = ch >> 3, col = ch & 7;
+      *reinterpret_cast<uint4*>(&lds[buf][row * LDS_ROW + col * 16]) = areg[c];
+    }
+  };
+
+  load_a(0);
+  load_w(0, wcur, scur);
+  store_a(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int buf = kt & 1;
+    const bool more = kt + 1 < nkt;
+    if (more) {
+      load_a(kt + 1);
+      load_w(kt + 1, wnxt, snxt);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      // x fragments of this step for all m blocks
+      f16x8_t af[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        af[mb] = *reinterpret_cast<const f16x8_t*>(&lds[buf][(mb * 32 + l32) * LDS_ROW + (32 * half + 8 * s) * 2]);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        uint32_t wd[2];
+        if constexpr (BITS == 4) {
+          wd[0] = wcur[nb][s];
+        } else if constexpr (BITS == 8) {
+          wd[0] = wcur[nb][2 * s];
+          wd[1] = wcur[nb][2 * s + 1];
+        } else {
+          wd[0] = wcur[nb][s >> 1];
+        }
+        f16x2_t v[D::NPIECE][4];
+        D::pieces(wd, s & 1, v);
+#pragma unroll
+        for (int a = 0; a < D::NPIECE; ++a)
+#pragma unroll
+          for (int j = 0; j < PS; ++j) {
+            f16x2_t sj = scur[nb][j];
+            if (D::piece_mult(a) != 1.f) sj = sj * f16x2_t{(_Float16)16.f, (_Float16)16.f};
+            f16x8_t bfr;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const f16x2_t q = v[a][i] * sj;
+              bfr[2 * i] = q[0];
+              bfr[2 * i + 1] = q[1];
+            }
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mb], bfr, acc[mb][nb], 0, 0, 0);
+          }
+      }
+    }
+    if (more) {
+      store_a(buf ^ 1);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+        for (int q = 0; q < WPL; ++q) wcur[nb][q] = wnxt[nb][q];
+#pragma unroll
+        for (int j = 0; j < PS; ++j) scur[nb][j] = snxt[nb][j];
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: y = 2^(e_m + e_n) * acc, rounded to the activation dtype.
+  // 32x32 accumulator layout: lane -> column l32; register r -> row
+  // 8*(r/4) + 4*half + r%4.
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int n = n0 + wave * 64 + nb * 32 + l32;
+    if (n >= p.N) continue;
+    const int e_n = p.en[n];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (m < p.M) {
+          const float val = ldexpf(acc[mb][nb][r], p.em[m] + e_n);
+          p.y[(long)m * p.N + n] = p.out_f16 ? f32_to_f16_bits(val) : f32_to_bf16_bits(val);
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+
+std::once_flag g_pool_once[64];
+
+void keep_pool_memory(hipStream_t s) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return;
+  std::call_once(g_pool_once[dev], [dev] {
+    hipMemPool_t pool;
+    if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+      uint64_t thr = UINT64_MAX;  // keep freed scratch in the pool instead of returning it
+      (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+    }
+  });
+  (void)s;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+template <int BITS, int PS>
+hipError_t run(const AffineArgs& a, hipStream_t s) {
+  const int M = (int)a.M, N = (int)a.N, K = (int)a.K, G = a.G;
+  const int ng = K / G;
+  const int Kt = (3 * ng + 15) / 16 * 16;
+  const int MB = M <= 64 ? 2 : 8;
+  const int BM = MB * 32;
+  const int Mp = (M + BM - 1) / BM * BM, Np = (N + BN - 1) / BN * BN;
+
+  const size_t o_xh = 0, s_xh = align256((size_t)Mp * K * 2);
+  const size_t o_ta = o_xh + s_xh, s_ta = align256((size_t)Mp * Kt * 2);
+  const size_t o_em = o_ta + s_ta, s_em = align256((size_t)Mp * 4);
+  const size_t o_sh = o_em + s_em, s_sh = align256((size_t)Np * ng * PS * 2);
+  const size_t o_tb = o_sh + s_sh, s_tb = align256((size_t)Np * Kt * 2);
+  const size_t o_en = o_tb + s_tb, s_en = align256((size_t)Np * 4);
+  const size_t total = o_en + s_en;
+
+  keep_pool_memory(s);
+  char* scratch = nullptr;
+  hipError_t e = hipMallocAsync((void**)&scratch, total, s);
+  if (e != hipSuccess) return e;
+
+  _Float16* xh = (_Float16*)(scratch + o_xh);
+  uint16_t* tA = (uint16_t*)(scratch + o_ta);
+  int* em = (int*)(scratch + o_em);
+  _Float16* sh = (_Float16*)(scratch + o_sh);
+  uint16_t* tB = (uint16_t*)(scratch + o_tb);
+  int* en = (int*)(scratch + o_en);
+
+  hipLaunchKernelGGL((prep_x_kernel<BITS>), dim3(Mp), dim3(256), 0, s, a.x, a.act_dt, a.k_perm, M, K, G, Kt, xh, tA, em);
+  hipLaunchKernelGGL((prep_w_kernel<PS>), dim3(Np / 4), dim3(256), 0, s, a.scales, a.s_dt, a.biases, a.b_dt,
+                     Decode<BITS>::OFFQ, N, ng, Kt, sh, tB, en);
+
+  GemmParams p;
+  p.xh = xh;
+  p.tA = tA;
+  p.em = em;
+  p.w = a.w;
+  p.sh = sh;
+  p.tB = tB;
+  p.en = en;
+  p.y = (uint16_t*)a.y;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.ng = ng;
+  p.Kt = Kt;
+  p.G = G;
+  p.Tm = Mp / BM;
+  p.Tn = Np / BN;
+  p.per_xcd = (p.Tm * p.Tn + 7) / 8;
+  p.out_f16 = a.act_dt == F16;
+  const dim3 grid(8 * p.per_xcd);
+  if (MB == 2)
+    hipLaunchKernelGGL((gemm_affine_kernel<BITS, PS, 2>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((gemm_affine_kernel<BITS, PS, 8>), grid, dim3(256), 0, s, p);
+  e = hipGetLastError();
+  hipError_t f = hipFreeAsync(scratch, s);
+  return e != hipSuccess ? e : f;
+}
+
+template <int BITS>
+hipError_t run_bits(const AffineArgs& a, hipStream_t s) {
+  switch (a.s_dt) {
+    case BF16: return run<BITS, 1>(a, s);
+    case F16: return run<BITS, 2>(a, s);
+    default: return run<BITS, 3>(a, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_affine(const AffineArgs& a, hipStream_t s) {
+  // whole 64-code K tiles only; otherwise the GEMV kernel (chunks of 4 rows) is used
+  if (a.K % BK != 0) return launch_gemv_affine(a, s);
+  switch (a.bits) {
+    case 2: return run_bits<2>(a, s);
+    case 4: return run_bits<4>(a, s);
+    default: return run_bits<8>(a, s);
+  }
+}
+
+}  // namespace qaff

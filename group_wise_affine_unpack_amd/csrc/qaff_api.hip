@@ -1,0 +1,235 @@
+// C ABI of libqaff: argument checks, dispatch, error reporting.
+// The declarations and their contracts are in include/qaff.h.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/qaff.h"
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return QAFF_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(QAFF_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool act_dtype_ok(int d) { return d == QAFF_BF16 || d == QAFF_F16; }
+bool sb_dtype_ok(int d) { return d == QAFF_BF16 || d == QAFF_F16 || d == QAFF_F32; }
+bool group_ok(int g) { return g == 32 || g == 64 || g == 128; }
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;  // int32 index arithmetic inside the kernels
+
+int check_affine(const void* x, const uint32_t* w, const void* s, const void* b, const void* y, int64_t M,
+                 int64_t N, int64_t K, int G, int bits, int act_dt, int s_dt, int b_dt) {
+  if (M < 0 || N < 0 || K <= 0) return fail(QAFF_E_INVAL, "sizes must satisfy M >= 0, N >= 0, K > 0 (got %lld, %lld, %lld)", (long long)M, (long long)N, (long long)K);
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return fail(QAFF_E_UNSUPPORTED, "dimension above 2^30");
+  if (!(bits == 2 || bits == 4 || bits == 8)) return fail(QAFF_E_INVAL, "bits must be 2, 4 or 8 (got %d)", bits);
+  if (!group_ok(G)) return fail(QAFF_E_INVAL, "group_size must be 32, 64 or 128 (got %d)", G);
+  if (K % G != 0) return fail(QAFF_E_INVAL, "K=%lld is not a multiple of group_size=%d", (long long)K, G);
+  if ((K * bits) % 128 != 0) return fail(QAFF_E_UNSUPPORTED, "K*bits must be a multiple of 128 (whole 16-byte row loads)");
+  if (!act_dtype_ok(act_dt)) return fail(QAFF_E_INVAL, "act_dtype must be QAFF_BF16 or QAFF_F16 (got %d)", act_dt);
+  if (!sb_dtype_ok(s_dt) || !sb_dtype_ok(b_dt)) return fail(QAFF_E_INVAL, "scale/bias dtype must be BF16, F16 or F32");
+  if (M == 0 || N == 0) return QAFF_OK;
+  if (!x || !w || !s || !b || !y) return fail(QAFF_E_INVAL, "null tensor pointer");
+  if (!aligned16(x) || !aligned16(w)) return fail(QAFF_E_ALIGN, "x and w_packed must be 16-byte aligned");
+  return QAFF_OK;
+}
+
+qaff::AffineArgs affine_args(const void* x, const uint32_t* w, const void* s, const void* b, const int32_t* kp,
+                             void* y, int64_t M, int64_t N, int64_t K, int G, int bits, int act_dt, int s_dt,
+                             int b_dt) {
+  qaff::AffineArgs a;
+  a.x = x;
+  a.w = w;
+  a.scales = s;
+  a.biases = b;
+  a.k_perm = kp;
+  a.y = y;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.G = G;
+  a.bits = bits;
+  a.act_dt = act_dt;
+  a.s_dt = s_dt;
+  a.b_dt = b_dt;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qaff_last_error(void) { return g_last_error.c_str(); }
+
+int qaff_version(void) { return 100; }
+
+int qgemv_affine(const void* x, const uint32_t* w_packed, const void* scales, const void* biases,
+                 const int32_t* k_perm, void* y, int64_t M, int64_t N, int64_t K, int32_t group_size,
+                 int32_t bits, int32_t act_dtype, int32_t scale_dtype, int32_t bias_dtype, void* stream) {
+  int rc = check_affine(x, w_packed, scales, biases, y, M, N, K, group_size, bits, act_dtype, scale_dtype, bias_dtype);
+  if (rc != QAFF_OK) return rc;
+  if (M > 16) return fail(QAFF_E_INVAL, "qgemv_affine takes M <= 16 (got %lld)", (long long)M);
+  if (M == 0 || N == 0) return ok();
+  (void)hipGetLastError();
+  hipError_t e = qaff::launch_gemv_affine(
+      affine_args(x, w_packed, scales, biases, k_perm, y, M, N, K, group_size, bits, act_dtype, scale_dtype, bias_dtype),
+      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gemv launch");
+  return ok();
+}
+
+int qmm_affine(const void* x, const uint32_t* w_packed, const void* scales, const void* biases,
+               const int32_t* k_perm, void* y, int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t bits,
+               int32_t act_dtype, int32_t scale_dtype, int32_t bias_dtype, void* stream) {
+  int rc = check_affine(x, w_packed, scales, biases, y, M, N, K, group_size, bits, act_dtype, scale_dtype, bias_dtype);
+  if (rc != QAFF_OK) return rc;
+  if (M == 0 || N == 0) return ok();
+  const qaff::AffineArgs a =
+      affine_args(x, w_packed, scales, biases, k_perm, y, M, N, K, group_size, bits, act_dtype, scale_dtype, bias_dtype);
+  (void)hipGetLastError();
+  hipError_t e = (M <= 16) ? qaff::launch_gemv_affine(a, static_cast<hipStream_t>(stream))
+                           : qaff::launch_gemm_affine(a, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return fail(QAFF_E_UNSUPPORTED, "this shape/dtype combination has no kernel");
+  if (e != hipSuccess) return hip_fail(e, M <= 16 ? "gemv launch" : "gemm launch");
+  return ok();
+}
+
+int qmm_gptq(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales, const int32_t* g_idx,
+             void* y, int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream) {
+  if (M < 0 || N <= 0 || K <= 0) return fail(QAFF_E_INVAL, "sizes must satisfy M >= 0, N > 0, K > 0");
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return fail(QAFF_E_UNSUPPORTED, "dimension above 2^30");
+  if (!group_ok(group_size)) return fail(QAFF_E_INVAL, "group_size must be 32, 64 or 128 (got %d)", group_size);
+  if (K % group_size || K % 8 || N % 8) return fail(QAFF_E_INVAL, "need K %% G == 0, K %% 8 == 0, N %% 8 == 0");
+  if (M == 0) return ok();
+  if (!x || !qweight || !qzeros || !scales || !y) return fail(QAFF_E_INVAL, "null tensor pointer");
+  if (!aligned16(x) || !aligned16(qweight)) return fail(QAFF_E_ALIGN, "x and qweight must be 16-byte aligned");
+  qaff::GptqArgs a;
+  a.x = x;
+  a.qweight = qweight;
+  a.qzeros = qzeros;
+  a.scales = scales;
+  a.g_idx = g_idx;
+  a.y = y;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.G = group_size;
+  (void)hipGetLastError();
+  hipError_t e = qaff::launch_gptq_direct(a, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return fail(QAFF_E_UNSUPPORTED, "this shape has no kernel");
+  if (e != hipSuccess) return hip_fail(e, "gptq launch");
+  return ok();
+}
+
+int qgemm_w4a8(const void* x, const uint32_t* w_q4, const void* s_w, void* y, int8_t* x_q, float* s_x,
+               int32_t* acc_out, int64_t M, int64_t N, int64_t K, void* stream) {
+  if (M < 0 || N <= 0 || K <= 0) return fail(QAFF_E_INVAL, "sizes must satisfy M >= 0, N > 0, K > 0");
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return fail(QAFF_E_UNSUPPORTED, "dimension above 2^30");
+  if (K % 32) return fail(QAFF_E_INVAL, "K must be a multiple of 32 (got %lld)", (long long)K);
+  // |acc| <= K * 127 * 8 must fit int32 (also after the x16 nibble placement used on the device)
+  if (K > (int64_t(1) << 17)) return fail(QAFF_E_UNSUPPORTED, "K above 131072 could overflow the int32 accumulator");
+  if (M == 0) return ok();
+  if (!x || !w_q4 || !s_w || !y || !x_q || !s_x) return fail(QAFF_E_INVAL, "null tensor pointer");
+  if (!aligned16(x) || !aligned16(w_q4) || !aligned16(x_q)) return fail(QAFF_E_ALIGN, "x, w_q4 and x_q must be 16-byte aligned");
+  qaff::W4A8Args a;
+  a.x = x;
+  a.w = w_q4;
+  a.s_w = s_w;
+  a.y = y;
+  a.x_q = x_q;
+  a.s_x = s_x;
+  a.acc = acc_out;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  (void)hipGetLastError();
+  hipError_t e = qaff::launch_w4a8(a, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return fail(QAFF_E_UNSUPPORTED, "this shape has no kernel");
+  if (e != hipSuccess) return hip_fail(e, "w4a8 launch");
+  return ok();
+}
+
+int gptq_to_affine_repack(const int32_t* qweight, const int32_t* qzeros, const void* scales, const int32_t* g_idx,
+                          uint32_t* w_packed_out, void* scales_out, void* biases_out, int32_t bias_dtype,
+                          int32_t* k_perm_out, int64_t K, int64_t N, int32_t group_size, void* stream) {
+  if (N <= 0 || K <= 0) return fail(QAFF_E_INVAL, "sizes must satisfy N > 0, K > 0");
+  if (N > kMaxDim || K > kMaxDim) return fail(QAFF_E_UNSUPPORTED, "dimension above 2^30");
+  if (!group_ok(group_size)) return fail(QAFF_E_INVAL, "group_size must be 32, 64 or 128 (got %d)", group_size);
+  if (K % group_size || K % 8 || N % 8) return fail(QAFF_E_INVAL, "need K %% G == 0, K %% 8 == 0, N %% 8 == 0");
+  if (!(bias_dtype == QAFF_F16 || bias_dtype == QAFF_F32)) return fail(QAFF_E_INVAL, "bias_dtype must be F16 or F32");
+  if (!qweight || !qzeros || !scales || !w_packed_out || !scales_out || !biases_out || !k_perm_out)
+    return fail(QAFF_E_INVAL, "null tensor pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t ng = K / group_size;
+  // The permutation is built on the host: stable counting sort of 0..K-1 by
+  // group, with a check that every group holds exactly G columns.
+  std::vector<int32_t> perm(K);
+  if (g_idx == nullptr) {
+    for (int64_t i = 0; i < K; ++i) perm[i] = (int32_t)i;
+  } else {
+    std::vector<int32_t> gi(K);
+    hipError_t e = hipMemcpyAsync(gi.data(), g_idx, sizeof(int32_t) * K, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "reading g_idx");
+    std::vector<int64_t> count(ng + 1, 0);
+    for (int64_t i = 0; i < K; ++i) {
+      if (gi[i] < 0 || gi[i] >= ng) return fail(QAFF_E_INVAL, "g_idx[%lld]=%d is outside [0, %lld)", (long long)i, gi[i], (long long)ng);
+      ++count[gi[i] + 1];
+    }
+    for (int64_t g = 0; g < ng; ++g)
+      if (count[g + 1] != group_size)
+        return fail(QAFF_E_INVAL, "group %lld holds %lld columns, not group_size=%d", (long long)g, (long long)count[g + 1], group_size);
+    for (int64_t g = 0; g < ng; ++g) count[g + 1] += count[g];
+    for (int64_t i = 0; i < K; ++i) perm[count[gi[i]]++] = (int32_t)i;
+  }
+  (void)hipGetLastError();
+  hipError_t e = hipMemcpyAsync(k_perm_out, perm.data(), sizeof(int32_t) * K, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "writing k_perm");
+  e = qaff::launch_gptq_repack(qweight, qzeros, scales, k_perm_out, w_packed_out, scales_out, biases_out, bias_dtype,
+                               K, N, group_size, s);
+  if (e != hipSuccess) return hip_fail(e, "repack launch");
+  // perm lives on this host stack frame: the copy must finish before returning
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "repack");
+  return ok();
+}
+
+int quantize_pack_affine(const void* w, int32_t w_dtype, uint32_t* w_packed_out, void* scales_out, void* biases_out,
+                         int32_t sb_dtype, int64_t N, int64_t K, int32_t group_size, int32_t bits, void* stream) {
+  if (N < 0 || K <= 0) return fail(QAFF_E_INVAL, "sizes must satisfy N >= 0, K > 0");
+  if (N > kMaxDim || K > kMaxDim) return fail(QAFF_E_UNSUPPORTED, "dimension above 2^30");
+  if (!(bits == 2 || bits == 4 || bits == 8)) return fail(QAFF_E_INVAL, "bits must be 2, 4 or 8 (got %d)", bits);
+  if (!group_ok(group_size)) return fail(QAFF_E_INVAL, "group_size must be 32, 64 or 128 (got %d)", group_size);
+  if (K % group_size) return fail(QAFF_E_INVAL, "K is not a multiple of group_size");
+  if (!sb_dtype_ok(w_dtype) || !sb_dtype_ok(sb_dtype)) return fail(QAFF_E_INVAL, "dtypes must be BF16, F16 or F32");
+  if (N == 0) return ok();
+  if (!w || !w_packed_out || !scales_out || !biases_out) return fail(QAFF_E_INVAL, "null tensor pointer");
+  (void)hipGetLastError();
+  hipError_t e = qaff::launch_quantize_pack(w, w_dtype, w_packed_out, scales_out, biases_out, sb_dtype, N, K,
+                                            group_size, bits, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "quantize_pack launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,110 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load on a machine without a GPU, export every function that
+include/qaff.h declares, and reject bad arguments before touching the HIP
+runtime: argument checks run first, so these calls (with fake pointer values)
+never launch anything.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import group_wise_affine_unpack_amd as qa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVAL, UNSUP, ALIGN = 0, 1, 2, 3
+A = 0x10000          # a fake, 16-byte aligned "device" address; never dereferenced
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "qaff.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)) - {"if"})
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert {"qmm_affine", "qgemv_affine", "qmm_gptq", "qgemm_w4a8", "gptq_to_affine_repack",
+            "quantize_pack_affine", "qaff_last_error", "qaff_version"} <= set(names)
+    lib = qa.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.qaff_version() >= 100
+
+
+def _affine(fn="qmm_affine", x=A, w=A, s=A, b=A, kp=None, y=A, M=1, N=64, K=256, G=64, bits=4, adt=0, sdt=0, bdt=0):
+    return getattr(qa.lib(), fn)(x, w, s, b, kp, y, M, N, K, G, bits, adt, sdt, bdt, None)
+
+
+def _msg():
+    return qa.lib().qaff_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bits=3), INVAL), (dict(bits=16), INVAL), (dict(G=48), INVAL), (dict(G=256), INVAL),
+    (dict(K=96, G=64), INVAL), (dict(M=-1), INVAL), (dict(N=-5), INVAL), (dict(K=0), INVAL),
+    (dict(adt=2), INVAL), (dict(adt=7), INVAL), (dict(sdt=3), INVAL), (dict(bdt=-1), INVAL),
+    (dict(x=None), INVAL), (dict(w=None), INVAL), (dict(s=None), INVAL), (dict(b=None), INVAL),
+    (dict(y=None), INVAL), (dict(x=A + 2), ALIGN), (dict(w=A + 4), ALIGN),
+    (dict(K=96, G=32, bits=2), UNSUP), (dict(K=(1 << 30) + 64), UNSUP),
+])
+@pytest.mark.parametrize("fn", ["qmm_affine", "qgemv_affine"])
+def test_affine_argument_errors(fn, kw, code):
+    assert _affine(fn, **kw) == code
+    assert _msg() != ""
+
+
+def test_affine_empty_batch_is_ok_without_launch():
+    assert _affine(M=0, x=None, y=None) == OK
+    assert _affine(N=0, w=None, s=None, b=None, y=None) == OK
+    assert _msg() == ""
+
+
+def test_gemv_rejects_large_m():
+    assert _affine("qgemv_affine", M=17) == INVAL
+    assert "M <= 16" in _msg()
+
+
+def test_gptq_argument_errors():
+    f = qa.lib().qmm_gptq
+    assert f(A, A, A, A, None, A, 1, 64, 256, 100, None) == INVAL      # bad G
+    assert f(A, A, A, A, None, A, 1, 60, 256, 64, None) == INVAL       # N % 8
+    assert f(A, A, A, A, None, A, 1, 64, 200, 64, None) == INVAL       # K % G
+    assert f(None, A, A, A, None, A, 1, 64, 256, 64, None) == INVAL
+    assert f(A + 8, A, A, A, None, A, 1, 64, 256, 64, None) == ALIGN
+    assert f(None, None, None, None, None, None, 0, 64, 256, 64, None) == OK
+
+
+def test_w4a8_argument_errors():
+    f = qa.lib().qgemm_w4a8
+    assert f(A, A, A, A, A, A, None, 8, 64, 100, None) == INVAL        # K % 32
+    assert f(A, A, A, None, A, A, None, 8, 64, 128, None) == INVAL
+    assert f(A, A + 4, A, A, A, A, None, 8, 64, 128, None) == ALIGN
+    assert f(A, A, A, A, A, A, None, 8, 64, 1 << 18, None) == UNSUP    # int32 overflow guard
+    assert f(None, None, None, None, None, None, None, 0, 64, 128, None) == OK
+
+
+def test_repack_argument_errors():
+    f = qa.lib().gptq_to_affine_repack
+    assert f(A, A, A, None, A, A, A, 0, A, 256, 64, 64, None) == INVAL  # bias dtype bf16 refused
+    assert f(A, A, A, None, A, A, A, 2, A, 256, 60, 64, None) == INVAL  # N % 8
+    assert f(A, A, A, None, A, None, A, 2, A, 256, 64, 64, None) == INVAL
+
+
+def test_quantize_pack_argument_errors():
+    f = qa.lib().quantize_pack_affine
+    assert f(A, 0, A, A, A, 0, 4, 256, 64, 5, None) == INVAL
+    assert f(A, 0, A, A, A, 0, 4, 250, 64, 4, None) == INVAL
+    assert f(A, 9, A, A, A, 0, 4, 256, 64, 4, None) == INVAL
+    assert f(None, 0, None, None, None, 0, 0, 256, 64, 4, None) == OK
+
+
+def test_binding_has_no_cpu_path():
+    import torch
+    x = torch.zeros((1, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        qa.qmm_affine(x, torch.zeros((8, 32), dtype=torch.int32), torch.zeros((8, 4), dtype=torch.bfloat16),
+                      torch.zeros((8, 4), dtype=torch.bfloat16), 64, 4)
