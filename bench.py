@@ -186,6 +186,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--skip-gemv", action="store_true", help="time only the prefill GEMM (for profiling)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -201,6 +202,10 @@ def main():
     device = torch.device("cuda:0")
     qa.lib()
 
+    if args.skip_gemv:
+        for bits in (4, 8):
+            print(json.dumps({"gemm_m2048": time_gemm(torch, qa, si, device, bits)}), flush=True)
+        return
     res = time_gemv_stack(args, torch, qa, si, device)
     print(f"[bench] gemv stack: {res['ms_per_step']*1e3:.1f} us/step, {res['gbs']:.0f} GB/s, "
           f"{res['avg_launch_us']:.2f} us/launch avg", file=sys.stderr, flush=True)

@@ -1,0 +1,106 @@
+"""GPU parity of the GPTQ paths: the direct kernel, the repack (bit-exact
+against the oracle's repack) and repack followed by qmm_affine with k_perm."""
+import numpy as np
+import pytest
+import torch
+
+import group_wise_affine_unpack_amd as qa
+import oracle
+import synth_inputs as si
+from gpu_util import assert_float_bar, dev16, dev32, host_f64, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(case, dev):
+    x = dev16(case.x, "f16", dev)
+    qw = torch.from_numpy(np.ascontiguousarray(case.qweight)).to(dev)
+    qz = torch.from_numpy(np.ascontiguousarray(case.qzeros)).to(dev)
+    s = dev16(case.scales, "f16", dev)
+    gi = None if case.g_idx is None else torch.from_numpy(np.ascontiguousarray(case.g_idx)).to(dev)
+    return x, qw, qz, s, gi
+
+
+def _log(case, what):
+    print(f"[case] {what} {case.name} M={case.M} K={case.K} N={case.N} G={case.G} act_order={case.g_idx is not None}",
+          flush=True)
+
+
+@pytest.mark.parametrize("M", si.CFG3_M)
+def test_cfg3_direct(M):
+    dev = require_gpu()
+    case = si.cfg3_case(M)
+    _log(case, "direct")
+    x, qw, qz, s, gi = _dev(case, dev)
+    y = qa.qmm_gptq(x, qw, qz, s, gi, case.G)
+    torch.cuda.synchronize()
+    cols = si.sample_indices(case.N, 1024 if M > 1 else case.N, seed=(3, 5, M))
+    ref = oracle.qmm_gptq(case.x, case.qweight, case.qzeros, case.scales, case.g_idx, M, case.K, case.N, case.G)
+    assert_float_bar(host_f64(y)[:, cols], ref[:, cols], case.name)
+
+
+@pytest.mark.parametrize("bias_dtype", ["f32", "f16"])
+def test_cfg3_repack_bit_exact(bias_dtype):
+    dev = require_gpu()
+    case = si.cfg3_case(1)
+    _log(case, "repack")
+    x, qw, qz, s, gi = _dev(case, dev)
+    tdt = torch.float32 if bias_dtype == "f32" else torch.float16
+    w, s_aff, b_aff, kp = qa.gptq_to_affine_repack(qw, qz, s, gi, case.G, bias_dtype=tdt)
+    torch.cuda.synchronize()
+    rp, rs, rb, rk = oracle.gptq_to_affine_repack(case.qweight, case.qzeros, case.scales, case.g_idx, case.K, case.N,
+                                                  case.G, bias_dtype)
+    np.testing.assert_array_equal(kp.cpu().numpy(), rk)
+    np.testing.assert_array_equal(w.cpu().numpy().view(np.uint32), rp)
+    np.testing.assert_array_equal(s_aff.cpu().view(torch.int16).numpy().view(np.uint16), rs)
+    if bias_dtype == "f32":
+        np.testing.assert_array_equal(b_aff.cpu().numpy(), rb)
+    else:
+        np.testing.assert_array_equal(b_aff.cpu().view(torch.int16).numpy().view(np.uint16), rb)
+
+
+@pytest.mark.parametrize("M", si.CFG3_M)
+@pytest.mark.parametrize("bias_dtype", ["f32", "f16"])
+def test_cfg3_repack_then_qmm_affine(M, bias_dtype):
+    dev = require_gpu()
+    case = si.cfg3_case(M)
+    _log(case, f"repack+affine bias={bias_dtype}")
+    x, qw, qz, s, gi = _dev(case, dev)
+    tdt = torch.float32 if bias_dtype == "f32" else torch.float16
+    w, s_aff, b_aff, kp = qa.gptq_to_affine_repack(qw, qz, s, gi, case.G, bias_dtype=tdt)
+    y = qa.qmm_affine(x, w, s_aff, b_aff, case.G, 4, k_perm=kp)
+    torch.cuda.synchronize()
+    cols = si.sample_indices(case.N, 1024 if M > 1 else case.N, seed=(3, 6, M))
+    ref = oracle.qmm_gptq(case.x, case.qweight, case.qzeros, case.scales, case.g_idx, M, case.K, case.N, case.G)
+    assert_float_bar(host_f64(y)[:, cols], ref[:, cols], case.name)
+
+
+@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("act_order", [True, False])
+@pytest.mark.parametrize("M", [1, 3, 20])
+def test_small_direct_and_repack(G, act_order, M):
+    dev = require_gpu()
+    case = si.gptq_case(M, 1024, 200, G, seed=(31, G, M), act_order=act_order, name=f"gptq_small_G{G}")
+    if not act_order:
+        case.g_idx = None
+    _log(case, "small")
+    x, qw, qz, s, gi = _dev(case, dev)
+    ref = oracle.qmm_gptq(case.x, case.qweight, case.qzeros, case.scales, case.g_idx, M, case.K, case.N, case.G)
+    y = qa.qmm_gptq(x, qw, qz, s, gi, G)
+    w, sa, ba, kp = qa.gptq_to_affine_repack(qw, qz, s, gi, G)
+    y2 = qa.qmm_affine(x, w, sa, ba, G, 4, k_perm=kp)
+    torch.cuda.synchronize()
+    assert_float_bar(host_f64(y), ref, case.name + " direct")
+    assert_float_bar(host_f64(y2), ref, case.name + " repack")
+
+
+def test_repack_rejects_uneven_groups():
+    dev = require_gpu()
+    case = si.gptq_case(1, 256, 16, 64, seed=(32,))
+    g = case.g_idx.copy()
+    g[int(np.flatnonzero(g == 0)[0])] = 1
+    case.g_idx = g
+    x, qw, qz, s, gi = _dev(case, dev)
+    with pytest.raises(qa.QaffError) as ei:
+        qa.gptq_to_affine_repack(qw, qz, s, gi, 64)
+    assert ei.value.status == 1

@@ -1,0 +1,66 @@
+"""GPU parity of the W4A8 path: int8 codes, per-token scales and int32
+accumulators bit-exact against the oracle; y within the float bar."""
+import numpy as np
+import pytest
+import torch
+
+import group_wise_affine_unpack_amd as qa
+import oracle
+import synth_inputs as si
+from gpu_util import assert_float_bar, dev16, host_f64, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(case):
+    dev = require_gpu()
+    print(f"[case] {case.name} M={case.M} N={case.N} K={case.K}", flush=True)
+    x = dev16(case.x, "f16", dev)
+    w = torch.from_numpy(np.ascontiguousarray(case.w_q4).view(np.int32)).to(dev)
+    sw = dev16(case.s_w, "f16", dev)
+    y, xq, sx, acc = qa.qgemm_w4a8(x, w, sw, want_acc=True)
+    torch.cuda.synchronize()
+    return y, xq.cpu().numpy(), sx.cpu().numpy(), acc
+
+
+def _check(case, rows=None):
+    y, xq, sx, acc = _run(case)
+    q_ref, s_ref = oracle.w4a8_quantize_act(case.x, case.M, case.K)
+    np.testing.assert_array_equal(xq, q_ref)
+    np.testing.assert_array_equal(sx.view(np.uint32), s_ref.view(np.uint32))
+    rows = np.arange(case.M) if rows is None else rows
+    acc_ref = oracle.w4a8_acc(q_ref[rows], case.w_q4, len(rows), case.N, case.K)
+    acc_gpu = acc.cpu().numpy()[rows].astype(np.int64)
+    np.testing.assert_array_equal(acc_gpu, acc_ref)
+    y_ref = acc_ref.astype(np.float64) * s_ref[rows].astype(np.float64)[:, None] * \
+        oracle.to_f64(case.s_w, "f16")[None, :]
+    assert_float_bar(host_f64(y)[rows], y_ref, case.name)
+
+
+@pytest.mark.parametrize("M", si.CFG4_M)
+@pytest.mark.parametrize("N,K", si.CFG4_SHAPES)
+def test_cfg4(N, K, M):
+    case = si.cfg4_case(N, K, M, seed=(4, N, K, M))
+    rows = None if M <= 128 else si.sample_indices(M, 48, seed=(4, 9, M))
+    _check(case, rows)
+
+
+def test_every_nibble_and_ragged_shapes():
+    case = si.w4a8_case(13, 200, 192, seed=(40,), name="w4a8_ragged")
+    r = np.random.default_rng(41)
+    codes = np.stack([r.permutation(np.tile(np.arange(-8, 8), 192 // 16)) for _ in range(200)])
+    case.w_q4 = si.pack_nibbles_along_last(codes & 0xF)
+    _check(case)
+
+
+def test_ties_zero_rows_and_extremes():
+    case = si.w4a8_case(8, 64, 128, seed=(42,), name="w4a8_ties")
+    xf = si.bits_to_f32(case.x, "f16").copy()
+    e = 2.0 ** -3
+    xf[0, :] = 0.0
+    xf[1, :] = (np.arange(128) % 40 - 20 + 0.5) * e       # exact ties after scaling
+    xf[1, 0] = 127 * e                                    # amax = 127 * 2^-3 -> s_x = 2^-3
+    xf[2, :] = 65504.0 * np.sign(np.random.default_rng(43).standard_normal(128))
+    xf[3, :] = 2.0 ** -24                                  # smallest subnormal everywhere
+    case.x = si.f16_bits(xf)
+    _check(case)
