@@ -23,8 +23,8 @@
 //   prep_x  : per row of x: e_m, xh (fp16, permuted to the code decode order,
 //             read through k_perm when given), tail A = [xs_hi, xs_hi, xs_lo]
 //   prep_w  : per row of W: e_n, scale pieces s_j (fp16), tail B = [cb_hi, cb_lo, cb_hi]
-//   gemm    : 256 threads, tile BM x 256 (4 waves side by side along N, each
-//             BM x 64); x tile double-buffered in LDS; packed codes go from
+//   gemm    : 256 threads, tile BM x 256 (4 waves along N, each BM x 64);
+//             x tiles DMA'd global->LDS into a 3-stage ring; packed codes go from
 //             global memory straight to registers, are decoded with the
 //             exponent-bias trick (code | 0x6400 = 1024 + code in fp16) and
 //             scaled with packed fp16 math; XCD-aware tile order.
@@ -40,7 +40,6 @@ namespace {
 
 constexpr int BN = 256;       // tile width along N (4 waves x 64)
 constexpr int BK = 64;        // codes per K tile
-constexpr int LDS_ROW = 144;  // bytes per x row in LDS: 64 fp16 + 16 bytes of padding (no bank conflicts)
 
 __device__ __forceinline__ uint32_t f32_bits(float v) { return __float_as_uint(v); }
 __device__ __forceinline__ float trunc_bf16(float v) { return __uint_as_float(f32_bits(v) & 0xffff0000u); }
@@ -75,7 +74,9 @@ __device__ __forceinline__ int exp_of(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// prep_x: one block (256 threads) per padded row m.
+// prep_x: one block (256 threads) per padded row m.  Pass 1 reads the row
+// with 16-byte loads for its max |x| (a permutation does not change it);
+// pass 2 (an L2 hit) writes blocks of BLK permuted, scaled fp16 values.
 template <int BITS>
 __global__ __launch_bounds__(256) void prep_x_kernel(const void* __restrict__ x, int act_dt,
                                                      const int32_t* __restrict__ k_perm, int M, int K, int G,
@@ -87,15 +88,24 @@ __global__ __launch_bounds__(256) void prep_x_kernel(const void* __restrict__ x,
   _Float16* xrow = xh + (long)m * K;
   uint16_t* trow = tA + (long)m * Kt;
   if (m >= M) {  // padding rows of the tile grid are zero
-    for (int k = t; k < K; k += 256) xrow[k] = (_Float16)0.f;
+    for (int c = t; c < K / 8; c += 256) reinterpret_cast<u32x4_t*>(xrow)[c] = u32x4_t{0, 0, 0, 0};
     for (int k = t; k < Kt; k += 256) trow[k] = 0;
     if (t == 0) em[m] = 0;
     return;
   }
-  const long base = (long)m * K;
+  const bool f16 = act_dt == F16;
+  const uint16_t* xr = static_cast<const uint16_t*>(x) + (long)m * K;
   __shared__ float red[4];
   float amax = 0.f;
-  for (int k = t; k < K; k += 256) amax = fmaxf(amax, fabsf(load_as_f32(x, base + k, act_dt)));
+  for (int c = t; c < K / 8; c += 256) {
+    const u32x4_t v = reinterpret_cast<const u32x4_t*>(xr)[c];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = f16 ? f16_bits_to_f32(v[i] & 0xffffu) : bf16_bits_to_f32(v[i] & 0xffffu);
+      const float hi = f16 ? f16_bits_to_f32(v[i] >> 16) : bf16_bits_to_f32(v[i] >> 16);
+      amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
+    }
+  }
   amax = wave_max(amax);
   if ((t & 63) == 0) red[t >> 6] = amax;
   __syncthreads();
@@ -112,11 +122,28 @@ __global__ __launch_bounds__(256) void prep_x_kernel(const void* __restrict__ x,
     const int bi = b0 + t;
     float part = 0.f;
     if (bi < nblk) {
+      float src[BLK];
+      if (k_perm == nullptr) {
+#pragma unroll
+        for (int q = 0; q < BLK / 8; ++q) {
+          const u32x4_t v = reinterpret_cast<const u32x4_t*>(xr + bi * BLK)[q];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            src[8 * q + 2 * i] = f16 ? f16_bits_to_f32(v[i] & 0xffffu) : bf16_bits_to_f32(v[i] & 0xffffu);
+            src[8 * q + 2 * i + 1] = f16 ? f16_bits_to_f32(v[i] >> 16) : bf16_bits_to_f32(v[i] >> 16);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < BLK; ++j) {
+          const uint32_t h = xr[k_perm[bi * BLK + j]];
+          src[j] = f16 ? f16_bits_to_f32(h) : bf16_bits_to_f32(h);
+        }
+      }
       _Float16 out[BLK];
 #pragma unroll
       for (int j = 0; j < BLK; ++j) {
-        const int k = bi * BLK + Perm<BITS>::src(j);
-        const float v = load_as_f32(x, base + (k_perm ? k_perm[k] : k), act_dt) * sc;
+        const float v = src[Perm<BITS>::src(j)] * sc;
         out[j] = (_Float16)v;
         part += v;
       }
@@ -193,6 +220,7 @@ struct GemmParams {
   const int* en;
   uint16_t* y;
   int M, N, K, ng, Kt, G;
+  int Np, gsh;  // padded row count of the W-side scratch; log2(G) - 5
   int Tm, Tn, per_xcd;
   int out_f16;
 };
@@ -231,148 +259,129 @@ struct Decode {
   static constexpr float piece_mult(int a) { return (BITS == 8 && a == 0) ? 16.f : 1.f; }
 };
 
+// Main GEMM.  256 threads = 4 waves, one per SIMD, side by side along N:
+// wave w computes rows [0, BM) x columns [64w, 64w+64) of the BM x 256 tile,
+// so every weight word is decoded once per BM rows.
+//
+// Pipeline (two K tiles in flight):
+//   * x tiles go global -> LDS by buffer_load_dwordx4 ... lds (no staging
+//     registers) into a 3-stage ring, 16-byte chunks XOR-swizzled by row
+//     ((r ^ r>>1) & 7) so the MFMA operand reads are bank-conflict free;
+//   * weight words and scale pieces go through buffer loads with the K
+//     offset in an SGPR, into a 3-deep register ring;
+//   * the loop is unrolled by 3 so every ring index is a constant.
+// Buffer loads past a buffer's end return 0, so the last row tile of W needs
+// no clamping.
+
+constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // raw buffer, 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)RSRC_WORD3);
+}
+
+// Workgroup barrier for the x ring: first wait until at most N vector-memory
+// operations of this wave are outstanding (its older LDS DMA has landed) and
+// its LDS reads have returned, then s_barrier.  No release/acquire fence: a
+// fence would also wait for the DMA still in flight for a later tile.
+template <int N>
+__device__ __forceinline__ void ring_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] bits 3:0, expcnt bits 6:4, lgkmcnt bits 11:8, vmcnt[5:4] bits 15:14
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+}
+
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 1)) & 7; }
+
 template <int BITS, int PS, int MB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_affine_kernel(GemmParams p) {
+struct Stage {
+  static constexpr int WPL = BITS;  // words per lane per K tile
+  uint32_t w[2][WPL];
+  uint32_t s[2][PS];  // raw fp16 bits of the scale pieces (paired at use, not at load)
+};
+
+template <int BITS, int PS, int MB>
+struct Pipe {
   using D = Decode<BITS>;
-  constexpr int BM = MB * 32;
-  constexpr int WPL = BITS;             // words per lane per K tile (32 codes)
-  constexpr int WPR = 2 * BITS;         // words per row per K tile
-  constexpr int A_CHUNKS = BM * 8 / 256;  // 16-byte chunks of the x tile per thread
+  using St = Stage<BITS, PS, MB>;
+  static constexpr int WPL = BITS;
+  static constexpr int WPR = 2 * BITS;
+  static constexpr int A_DMA = MB;
+  // vector-memory instructions issue() emits for one tile: weight words
+  // (one dwordx2, or WPL/4 dwordx4, per n block), PS ushort scale loads per
+  // n block, and A_DMA x chunks
+  static constexpr int N_ISSUE = 2 * (WPL == 2 ? 1 : WPL / 4) + 2 * PS + A_DMA;
 
-  // XCD-aware tile order: consecutive blocks go round-robin over the 8 XCDs,
-  // so block b runs on XCD b%8; give each XCD a contiguous range of tiles
-  // (m-major) so the x rows of a tile row stay in that XCD's L2.
-  const int b = blockIdx.x;
-  const int v = (b & 7) * p.per_xcd + (b >> 3);
-  if (v >= p.Tm * p.Tn) return;
-  const int tm = v / p.Tn, tn = v % p.Tn;
-  const int m0 = tm * BM, n0 = tn * BN;
+  __amdgpu_buffer_rsrc_t rw, rs, rx;
+  uint32_t w_off[2], s_off[2], x_off;
+  int half, l32, wave, gsh;
+  int x_row_step;  // bytes between the rows of consecutive DMA instructions (32 rows)
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int l32 = lane & 31, half = lane >> 5;
-
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2][BM * LDS_ROW];
-
-  f32x16_t acc[MB][2];
-#pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  // rows of W this lane decodes (clamped into range; results past N are dropped)
-  int nrow[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int n = n0 + wave * 64 + nb * 32 + l32;
-    nrow[nb] = n < p.N ? n : p.N - 1;
-  }
-
-  // ---- tail: sum_g xs * cb on bf16 MFMA, operands straight from global
-  for (int kt = 0; kt < p.Kt; kt += 16) {
-    bf16x8_t bt[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-      bt[nb] = *reinterpret_cast<const bf16x8_t*>(p.tB + (long)(n0 + wave * 64 + nb * 32 + l32) * p.Kt + kt + 8 * half);
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const bf16x8_t at = *reinterpret_cast<const bf16x8_t*>(p.tA + (long)(m0 + mb * 32 + l32) * p.Kt + kt + 8 * half);
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, bt[nb], acc[mb][nb], 0, 0, 0);
-    }
-  }
-
-  // ---- main loop over K tiles of 64 codes
-  const int nkt = p.K / BK;
-  const long wrow = (long)p.K * BITS / 32;  // words per row of W
-  uint32_t wcur[2][WPL], wnxt[2][WPL];
-  f16x2_t scur[2][PS], snxt[2][PS];
-  uint4 areg[A_CHUNKS];
-
-  auto load_w = [&](int kt, uint32_t (&wd)[2][WPL], f16x2_t (&sd)[2][PS]) {
-    const int g = (kt * BK + 32 * half) / p.G;
+  // Loads of K tile kt: weights and scales first, the x DMA last (the wait
+  // before a tile is consumed leaves only the newest tile's DMA in flight).
+  __device__ __forceinline__ void issue(int kt, St& st, unsigned char* __restrict__ sA) const {
+    const int g = (2 * kt + half) >> gsh;
+    const int so = kt * WPR * 4;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const uint32_t* src = p.w + nrow[nb] * wrow + kt * WPR + half * WPL;
-      if constexpr (WPL == 1) {
-        wd[nb][0] = src[0];
-      } else if constexpr (WPL == 2) {
-        const uint2 u = *reinterpret_cast<const uint2*>(src);
-        wd[nb][0] = u.x;
-        wd[nb][1] = u.y;
+      if constexpr (WPL == 2) {
+        const u32x2_t u = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rw, w_off[nb], so, 0));
+        st.w[nb][0] = u.x;
+        st.w[nb][1] = u.y;
       } else {
 #pragma unroll
         for (int q = 0; q < WPL / 4; ++q) {
-          const uint4 u = reinterpret_cast<const uint4*>(src)[q];
-          wd[nb][4 * q] = u.x;
-          wd[nb][4 * q + 1] = u.y;
-          wd[nb][4 * q + 2] = u.z;
-          wd[nb][4 * q + 3] = u.w;
+          const u32x4_t u = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[nb] + q * 16, so, 0));
+          st.w[nb][4 * q] = u.x;
+          st.w[nb][4 * q + 1] = u.y;
+          st.w[nb][4 * q + 2] = u.z;
+          st.w[nb][4 * q + 3] = u.w;
         }
       }
-      const _Float16* sp = p.sh + ((long)nrow[nb] * p.ng + g) * PS;
 #pragma unroll
-      for (int j = 0; j < PS; ++j) sd[nb][j] = f16x2_t{sp[j], sp[j]};
+      for (int j = 0; j < PS; ++j) st.s[nb][j] = __builtin_amdgcn_raw_buffer_load_b16(rs, s_off[nb] + (g * PS + j) * 2, 0, 0);
     }
-  };
-  auto load_a = [&](int kt) {
 #pragma unroll
-    for (int c = 0; c < A_CHUNKS; ++c) {
-      const int ch = t + 256 * c, row = ch >> 3, col = ch & 7;
-      areg[c] = *reinterpret_cast<const uint4*>(p.xh + (long)(m0 + row) * p.K + kt * BK + col * 8);
-    }
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < A_CHUNKS; ++c) {
-      const int ch = t + 256 * c, row = ch >> 3, col = ch & 7;
-      *reinterpret_cast<uint4*>(&lds[buf][row * LDS_ROW + col * 16]) = areg[c];
-    }
-  };
+    for (int i = 0; i < A_DMA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (void __attribute__((address_space(3)))*)(sA + i * 4096 + wave * 1024),
+                                               16, x_off, kt * 128 + i * x_row_step, 0, 0);
+    // keep these loads at the top of the step: the barrier of the next step
+    // counts on them having had a whole step of MFMAs to land
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
-  load_a(0);
-  load_w(0, wcur, scur);
-  store_a(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < nkt;
-    if (more) {
-      load_a(kt + 1);
-      load_w(kt + 1, wnxt, snxt);
-    }
+  __device__ __forceinline__ void compute(const St& st, const unsigned char* __restrict__ sA, f32x16_t (&acc)[MB][2]) const {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      // x fragments of this step for all m blocks
       f16x8_t af[MB];
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        af[mb] = *reinterpret_cast<const f16x8_t*>(&lds[buf][(mb * 32 + l32) * LDS_ROW + (32 * half + 8 * s) * 2]);
+      for (int mb = 0; mb < MB; ++mb) {
+        const int r = mb * 32 + l32;
+        af[mb] = *reinterpret_cast<const f16x8_t*>(sA + r * 128 + (((4 * half + s) ^ swz(r)) << 4));
+      }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         uint32_t wd[2];
         if constexpr (BITS == 4) {
-          wd[0] = wcur[nb][s];
+          wd[0] = st.w[nb][s];
         } else if constexpr (BITS == 8) {
-          wd[0] = wcur[nb][2 * s];
-          wd[1] = wcur[nb][2 * s + 1];
+          wd[0] = st.w[nb][2 * s];
+          wd[1] = st.w[nb][2 * s + 1];
         } else {
-          wd[0] = wcur[nb][s >> 1];
+          wd[0] = st.w[nb][s >> 1];
         }
-        f16x2_t v[D::NPIECE][4];
-        D::pieces(wd, s & 1, v);
+        f16x2_t vv[D::NPIECE][4];
+        D::pieces(wd, s & 1, vv);
 #pragma unroll
         for (int a = 0; a < D::NPIECE; ++a)
 #pragma unroll
           for (int j = 0; j < PS; ++j) {
-            f16x2_t sj = scur[nb][j];
+            f16x2_t sj = h2(st.s[nb][j] * 0x00010001u);  // (s, s)
             if (D::piece_mult(a) != 1.f) sj = sj * f16x2_t{(_Float16)16.f, (_Float16)16.f};
             f16x8_t bfr;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const f16x2_t q = v[a][i] * sj;
+              const f16x2_t q = vv[a][i] * sj;
               bfr[2 * i] = q[0];
               bfr[2 * i + 1] = q[1];
             }
@@ -382,18 +391,115 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           }
       }
     }
-    if (more) {
-      store_a(buf ^ 1);
+  }
+
+  // One K tile: barrier (tile kt landed everywhere, tile kt-1's stage free),
+  // loads of tile kt+2 into the freed stage, MFMAs on tile kt.  The loads are
+  // issued even past the last tile: buffer loads beyond a buffer's end read
+  // 0 and such a tile only lands in a free stage, so the step has no branch
+  // and the wait count is the same every time.  The stages are distinct
+  // objects passed as restrict pointers, so the compiler knows the DMA in
+  // flight does not alias the stage being read.
+  __device__ __forceinline__ void step(int kt, const St& cur, const unsigned char* __restrict__ sa_cur, St& nxt,
+                                       unsigned char* __restrict__ sa_nxt, f32x16_t (&acc)[MB][2]) const {
+    // everything but the previous step's issue group (tile kt+1) has landed
+    ring_barrier<N_ISSUE>();
+    issue(kt + 2, nxt, sa_nxt);
+    compute(cur, sa_cur, acc);
+  }
+};
+
+template <int BITS, int PS, int MB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_affine_kernel(GemmParams p) {
+  using St = Stage<BITS, PS, MB>;
+  constexpr int BM = MB * 32;
+  constexpr int WPL = BITS;
+  constexpr int STAGE_BYTES = BM * 128; // one x tile, 64 fp16 per row, no padding
+
+  const int b = blockIdx.x;
+  const int v = (b & 7) * p.per_xcd + (b >> 3);
+  if (v >= p.Tm * p.Tn) return;
+  const int tm = v / p.Tn, tn = v % p.Tn;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l32 = lane & 31, half = lane >> 5;
+
+  __shared__ __attribute__((aligned(1024))) unsigned char sA0[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char sA1[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char sA2[STAGE_BYTES];
+  __shared__ int em_s[BM];
+  for (int i = t; i < BM; i += 256) em_s[i] = p.em[m0 + i];
+
+  f32x16_t acc[MB][2];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int q = 0; q < WPL; ++q) wcur[nb][q] = wnxt[nb][q];
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int j = 0; j < PS; ++j) scur[nb][j] = snxt[nb][j];
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // ---- buffer resources and per-lane offsets
+  Pipe<BITS, PS, MB> P;
+  const uint32_t row_bytes = (uint32_t)p.K * BITS / 8;
+  P.rw = make_rsrc(p.w, (uint32_t)p.N * row_bytes);
+  P.rs = make_rsrc(p.sh, (uint32_t)p.Np * p.ng * PS * 2);
+  P.rx = make_rsrc(p.xh + (long)m0 * p.K, (uint32_t)BM * p.K * 2);
+  P.half = half;
+  P.l32 = l32;
+  P.wave = wave;
+  P.gsh = p.gsh;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const uint32_t n = n0 + wave * 64 + nb * 32 + l32;
+    P.w_off[nb] = n * row_bytes + half * WPL * 4;
+    P.s_off[nb] = n * (uint32_t)p.ng * PS * 2;
+  }
+  // x DMA: instruction i of this wave fills LDS bytes [i*4096 + wave*1024, +1024):
+  // chunk q = i*256 + t -> row q/8 = 32i + t/8, position q%8 = t%8, holding
+  // source chunk pos^swz(row); swz(32i + t/8) does not depend on i.
+  {
+    const int r = t >> 3, pos = t & 7;
+    P.x_off = (uint32_t)r * p.K * 2 + ((pos ^ swz(r)) << 4);
+    P.x_row_step = 32 * p.K * 2;
+  }
+
+  const int nkt = p.K / BK;
+  St st0, st1, st2;
+  P.issue(0, st0, sA0);
+  P.issue(1, st1, sA1);
+
+  // ---- tail: sum_g xs * cb on bf16 MFMA, operands straight from global
+  // (L2-resident), overlapping the first x tiles' DMA
+  {
+    const uint16_t* tb_row[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) tb_row[nb] = p.tB + (long)(n0 + wave * 64 + nb * 32 + l32) * p.Kt + 8 * half;
+    const uint16_t* ta_row = p.tA + (long)(m0 + l32) * p.Kt + 8 * half;
+    const long ta_mb = (long)32 * p.Kt;
+    for (int kt = 0; kt < p.Kt; kt += 16) {
+      bf16x8_t bt[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) bt[nb] = *reinterpret_cast<const bf16x8_t*>(tb_row[nb] + kt);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const bf16x8_t at = *reinterpret_cast<const bf16x8_t*>(ta_row + mb * ta_mb + kt);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, bt[nb], acc[mb][nb], 0, 0, 0);
       }
     }
-    __syncthreads();
   }
+
+  // ---- main loop, unrolled by 3 over the ring
+  // Before tile K is read, only the newest issue group (tile K+1's) may still
+  // be in flight; vector memory operations complete in order.
+  for (int kt = 0; kt < nkt; kt += 3) {
+    P.step(kt, st0, sA0, st2, sA2, acc);
+    if (kt + 1 < nkt) P.step(kt + 1, st1, sA1, st0, sA0, acc);
+    if (kt + 2 < nkt) P.step(kt + 2, st2, sA2, st1, sA1, acc);
+  }
+  // the loads issued past the last tile must land before this workgroup's
+  // LDS can be handed to another one
+  __builtin_amdgcn_s_waitcnt(0);
 
   // ---- epilogue: y = 2^(e_m + e_n) * acc, rounded to the activation dtype.
   // 32x32 accumulator layout: lane -> column l32; register r -> row
@@ -407,9 +513,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        const int mt = mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        const int m = m0 + mt;
         if (m < p.M) {
-          const float val = ldexpf(acc[mb][nb][r], p.em[m] + e_n);
+          const float val = ldexpf(acc[mb][nb][r], em_s[mt] + e_n);
           p.y[(long)m * p.N + n] = p.out_f16 ? f32_to_f16_bits(val) : f32_to_bf16_bits(val);
         }
       }
@@ -437,6 +544,8 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 template <int BITS, int PS>
 hipError_t run(const AffineArgs& a, hipStream_t s) {
+  // buffer resources address W, the scale pieces and one x tile with 32-bit offsets
+  if (a.N * a.K * BITS / 8 >= (int64_t(1) << 31) || a.K * 2 * 256 >= (int64_t(1) << 31)) return hipErrorNotSupported;
   const int M = (int)a.M, N = (int)a.N, K = (int)a.K, G = a.G;
   const int ng = K / G;
   const int Kt = (3 * ng + 15) / 16 * 16;
@@ -483,6 +592,8 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
   p.ng = ng;
   p.Kt = Kt;
   p.G = G;
+  p.Np = Np;
+  p.gsh = G == 32 ? 0 : (G == 64 ? 1 : 2);
   p.Tm = Mp / BM;
   p.Tn = Np / BN;
   p.per_xcd = (p.Tm * p.Tn + 7) / 8;

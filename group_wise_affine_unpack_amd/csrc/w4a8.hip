@@ -98,23 +98,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   const long wrow = p.K / 8;
   const int nkt = p.K / BK;
-  uint4 wcur[2], wnxt[2];
-  uint4 areg[A_CHUNKS];
+  u32x4_t wcur[2], wnxt[2];
+  u32x4_t areg[A_CHUNKS];
 
   // x_q rows past M are read clamped to M-1; their results are not stored
   auto a_src = [&](int kt, int c) {
     const int ch = t + 256 * c, row = ch >> 2, col = ch & 3;
     const int m = m0 + row < p.M ? m0 + row : p.M - 1;
-    return reinterpret_cast<const uint4*>(p.xq + (long)m * p.K + kt * BK) + col;
+    return reinterpret_cast<const u32x4_t*>(p.xq + (long)m * p.K + kt * BK) + col;
   };
 #pragma unroll
   for (int c = 0; c < A_CHUNKS; ++c) areg[c] = *a_src(0, c);
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) wcur[nb] = *reinterpret_cast<const uint4*>(p.w + nrow[nb] * wrow + half * 4);
+  for (int nb = 0; nb < 2; ++nb) wcur[nb] = *reinterpret_cast<const u32x4_t*>(p.w + nrow[nb] * wrow + half * 4);
 #pragma unroll
   for (int c = 0; c < A_CHUNKS; ++c) {
     const int ch = t + 256 * c;
-    *reinterpret_cast<uint4*>(&lds[0][(ch >> 2) * LDS_ROW + (ch & 3) * 16]) = areg[c];
+    *reinterpret_cast<u32x4_t*>(&lds[0][(ch >> 2) * LDS_ROW + (ch & 3) * 16]) = areg[c];
   }
   __syncthreads();
 
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int c = 0; c < A_CHUNKS; ++c) areg[c] = *a_src(kt + 1, c);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
-        wnxt[nb] = *reinterpret_cast<const uint4*>(p.w + nrow[nb] * wrow + (kt + 1) * 8 + half * 4);
+        wnxt[nb] = *reinterpret_cast<const u32x4_t*>(p.w + nrow[nb] * wrow + (kt + 1) * 8 + half * 4);
     }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int c = 0; c < A_CHUNKS; ++c) {
         const int ch = t + 256 * c;
-        *reinterpret_cast<uint4*>(&lds[buf ^ 1][(ch >> 2) * LDS_ROW + (ch & 3) * 16]) = areg[c];
+        *reinterpret_cast<u32x4_t*>(&lds[buf ^ 1][(ch >> 2) * LDS_ROW + (ch & 3) * 16]) = areg[c];
       }
       wcur[0] = wnxt[0];
       wcur[1] = wnxt[1];
