@@ -24,7 +24,7 @@
 //             read through k_perm when given), tail A = [xs_hi, xs_hi, xs_lo]
 //   prep_w  : per row of W: e_n, scale pieces s_j (fp16), tail B = [cb_hi, cb_lo, cb_hi]
 //   gemm    : 256 threads, tile BM x 256 (4 waves along N, each BM x 64);
-//             x tiles DMA'd global->LDS into a 3-stage ring; packed codes go from
+//             x tiles double-buffered in LDS, stored one step ahead; packed codes go from
 //             global memory straight to registers, are decoded with the
 //             exponent-bias trick (code | 0x6400 = 1024 + code in fp16) and
 //             scaled with packed fp16 math; XCD-aware tile order.
@@ -77,18 +77,25 @@ __device__ __forceinline__ int exp_of(float v) {
 // prep_x: one block (256 threads) per padded row m.  Pass 1 reads the row
 // with 16-byte loads for its max |x| (a permutation does not change it);
 // pass 2 (an L2 hit) writes blocks of BLK permuted, scaled fp16 values.
+// xh is tile-blocked: the BM x 64 block of K tile kt of row tile mt is one
+// contiguous 16 KiB..32 KiB piece, row r of it at r*64 elements, so a GEMM
+// step reads a single contiguous block.
 template <int BITS>
 __global__ __launch_bounds__(256) void prep_x_kernel(const void* __restrict__ x, int act_dt,
                                                      const int32_t* __restrict__ k_perm, int M, int K, int G,
-                                                     int Kt, _Float16* __restrict__ xh, uint16_t* __restrict__ tA,
-                                                     int* __restrict__ em) {
+                                                     int Kt, int BM, _Float16* __restrict__ xh,
+                                                     uint16_t* __restrict__ tA, int* __restrict__ em) {
   constexpr int BLK = Perm<BITS>::BLK;
   const int m = blockIdx.x, t = threadIdx.x;
   const int ng = K / G;
-  _Float16* xrow = xh + (long)m * K;
+  const int nkt = K / 64;
+  // element (m, k) of xh sits at xrow[(k/64)*BM*64 + k%64]
+  _Float16* xrow = xh + ((long)(m / BM) * nkt * BM + (m % BM)) * 64;
+  const long kt_stride = (long)BM * 64;
   uint16_t* trow = tA + (long)m * Kt;
   if (m >= M) {  // padding rows of the tile grid are zero
-    for (int c = t; c < K / 8; c += 256) reinterpret_cast<u32x4_t*>(xrow)[c] = u32x4_t{0, 0, 0, 0};
+    for (int c = t; c < K / 8; c += 256)
+      reinterpret_cast<u32x4_t*>(xrow + (c >> 3) * kt_stride)[c & 7] = u32x4_t{0, 0, 0, 0};
     for (int k = t; k < Kt; k += 256) trow[k] = 0;
     if (t == 0) em[m] = 0;
     return;
@@ -148,8 +155,11 @@ __global__ __launch_bounds__(256) void prep_x_kernel(const void* __restrict__ x,
         part += v;
       }
 #pragma unroll
-      for (int j = 0; j < BLK; j += 8) *reinterpret_cast<f16x8_t*>(xrow + bi * BLK + j) =
-          f16x8_t{out[j], out[j + 1], out[j + 2], out[j + 3], out[j + 4], out[j + 5], out[j + 6], out[j + 7]};
+      for (int j = 0; j < BLK; j += 8) {
+        const int k = bi * BLK + j;
+        *reinterpret_cast<f16x8_t*>(xrow + (k >> 6) * kt_stride + (k & 63)) =
+            f16x8_t{out[j], out[j + 1], out[j + 2], out[j + 3], out[j + 4], out[j + 5], out[j + 6], out[j + 7]};
+      }
     }
     for (int o = 1; o < bpg; o <<= 1) part += __shfl_xor(part, o);
     if (bi < nblk && (bi % bpg) == 0) {
@@ -263,12 +273,13 @@ struct Decode {
 // wave w computes rows [0, BM) x columns [64w, 64w+64) of the BM x 256 tile,
 // so every weight word is decoded once per BM rows.
 //
-// Pipeline (two K tiles in flight):
-//   * x tiles go global -> LDS by buffer_load_dwordx4 ... lds (no staging
-//     registers) into a 3-stage ring, 16-byte chunks XOR-swizzled by row
-//     ((r ^ r>>1) & 7) so the MFMA operand reads are bank-conflict free;
+// Pipeline:
+//   * x tiles go global -> registers (loaded two steps before use) -> LDS
+//     (stored one step before use) into two stages; 16-byte chunks are
+//     XOR-swizzled by row ((r ^ r>>1) & 7) so the MFMA operand reads are
+//     bank-conflict free;
 //   * weight words and scale pieces go through buffer loads with the K
-//     offset in an SGPR, into a 3-deep register ring;
+//     offset in an SGPR, into a 3-deep register ring (two steps ahead);
 //   * the loop is unrolled by 3 so every ring index is a constant.
 // Buffer loads past a buffer's end return 0, so the last row tile of W needs
 // no clamping.
@@ -277,18 +288,6 @@ constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // raw buffer, 32-bit data format
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)RSRC_WORD3);
-}
-
-// Workgroup barrier for the x ring: first wait until at most N vector-memory
-// operations of this wave are outstanding (its older LDS DMA has landed) and
-// its LDS reads have returned, then s_barrier.  No release/acquire fence: a
-// fence would also wait for the DMA still in flight for a later tile.
-template <int N>
-__device__ __forceinline__ void ring_barrier() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  // gfx9 s_waitcnt: vmcnt[3:0] bits 3:0, expcnt bits 6:4, lgkmcnt bits 11:8, vmcnt[5:4] bits 15:14
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
-  __builtin_amdgcn_s_barrier();
 }
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 1)) & 7; }
@@ -307,19 +306,19 @@ struct Pipe {
   static constexpr int WPL = BITS;
   static constexpr int WPR = 2 * BITS;
   static constexpr int A_DMA = MB;
-  // vector-memory instructions issue() emits for one tile: weight words
-  // (one dwordx2, or WPL/4 dwordx4, per n block), PS ushort scale loads per
-  // n block, and A_DMA x chunks
-  static constexpr int N_ISSUE = 2 * (WPL == 2 ? 1 : WPL / 4) + 2 * PS + A_DMA;
 
   __amdgpu_buffer_rsrc_t rw, rs, rx;
   uint32_t w_off[2], s_off[2], x_off;
-  int half, l32, wave, gsh;
-  int x_row_step;  // bytes between the rows of consecutive DMA instructions (32 rows)
+  int half, l32, gsh;
+  int a_dst;       // this thread's first LDS chunk in a stage
 
-  // Loads of K tile kt: weights and scales first, the x DMA last (the wait
-  // before a tile is consumed leaves only the newest tile's DMA in flight).
-  __device__ __forceinline__ void issue(int kt, St& st, unsigned char* __restrict__ sA) const {
+  // Loads for K tile kt: the x chunks (into registers; written to LDS one
+  // step later), then the weight words and scale pieces (into a ring entry
+  // used two steps later).
+  __device__ __forceinline__ void issue(int kt, St& st, u32x4_t (&xr)[A_DMA]) const {
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i)
+      xr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, x_off, kt * (MB * 32 * 128) + i * 4096, 0));
     const int g = (2 * kt + half) >> gsh;
     const int so = kt * WPR * 4;
 #pragma unroll
@@ -341,71 +340,89 @@ struct Pipe {
 #pragma unroll
       for (int j = 0; j < PS; ++j) st.s[nb][j] = __builtin_amdgcn_raw_buffer_load_b16(rs, s_off[nb] + (g * PS + j) * 2, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < A_DMA; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (void __attribute__((address_space(3)))*)(sA + i * 4096 + wave * 1024),
-                                               16, x_off, kt * 128 + i * x_row_step, 0, 0);
-    // keep these loads at the top of the step: the barrier of the next step
-    // counts on them having had a whole step of MFMAs to land
-    __builtin_amdgcn_sched_barrier(0);
   }
 
-  __device__ __forceinline__ void compute(const St& st, const unsigned char* __restrict__ sA, f32x16_t (&acc)[MB][2]) const {
+  // x chunk i of this thread lands at LDS byte a_dst + i*4096 of a stage:
+  // row 32i + t/8, position t%8 (already swizzled on the global side)
+  __device__ __forceinline__ void store_x(unsigned char* sA, const u32x4_t (&xr)[A_DMA]) const {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      f16x8_t af[MB];
+    for (int i = 0; i < A_DMA; ++i) *reinterpret_cast<u32x4_t*>(sA + a_dst + i * 4096) = xr[i];
+  }
+
+  __device__ __forceinline__ void read_a(const unsigned char* __restrict__ sA, int s, f16x8_t (&af)[MB]) const {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int r = mb * 32 + l32;
-        af[mb] = *reinterpret_cast<const f16x8_t*>(sA + r * 128 + (((4 * half + s) ^ swz(r)) << 4));
-      }
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        uint32_t wd[2];
-        if constexpr (BITS == 4) {
-          wd[0] = st.w[nb][s];
-        } else if constexpr (BITS == 8) {
-          wd[0] = st.w[nb][2 * s];
-          wd[1] = st.w[nb][2 * s + 1];
-        } else {
-          wd[0] = st.w[nb][s >> 1];
-        }
-        f16x2_t vv[D::NPIECE][4];
-        D::pieces(wd, s & 1, vv);
-#pragma unroll
-        for (int a = 0; a < D::NPIECE; ++a)
-#pragma unroll
-          for (int j = 0; j < PS; ++j) {
-            f16x2_t sj = h2(st.s[nb][j] * 0x00010001u);  // (s, s)
-            if (D::piece_mult(a) != 1.f) sj = sj * f16x2_t{(_Float16)16.f, (_Float16)16.f};
-            f16x8_t bfr;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const f16x2_t q = vv[a][i] * sj;
-              bfr[2 * i] = q[0];
-              bfr[2 * i + 1] = q[1];
-            }
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mb], bfr, acc[mb][nb], 0, 0, 0);
-          }
-      }
+    for (int mb = 0; mb < MB; ++mb) {
+      const int r = mb * 32 + l32;
+      af[mb] = *reinterpret_cast<const f16x8_t*>(sA + r * 128 + (((4 * half + s) ^ swz(r)) << 4));
     }
   }
 
-  // One K tile: barrier (tile kt landed everywhere, tile kt-1's stage free),
-  // loads of tile kt+2 into the freed stage, MFMAs on tile kt.  The loads are
-  // issued even past the last tile: buffer loads beyond a buffer's end read
-  // 0 and such a tile only lands in a free stage, so the step has no branch
-  // and the wait count is the same every time.  The stages are distinct
-  // objects passed as restrict pointers, so the compiler knows the DMA in
-  // flight does not alias the stage being read.
-  __device__ __forceinline__ void step(int kt, const St& cur, const unsigned char* __restrict__ sa_cur, St& nxt,
-                                       unsigned char* __restrict__ sa_nxt, f32x16_t (&acc)[MB][2]) const {
-    // everything but the previous step's issue group (tile kt+1) has landed
-    ring_barrier<N_ISSUE>();
-    issue(kt + 2, nxt, sa_nxt);
-    compute(cur, sa_cur, acc);
+  // the 16-column-step s of a tile: decode this lane's words of both n blocks
+  // and run the MFMAs against the x fragments af
+  __device__ __forceinline__ void mma_step(const St& st, int s, const f16x8_t (&af)[MB], f32x16_t (&acc)[MB][2]) const {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      uint32_t wd[2];
+      if constexpr (BITS == 4) {
+        wd[0] = st.w[nb][s];
+      } else if constexpr (BITS == 8) {
+        wd[0] = st.w[nb][2 * s];
+        wd[1] = st.w[nb][2 * s + 1];
+      } else {
+        wd[0] = st.w[nb][s >> 1];
+      }
+      f16x2_t vv[D::NPIECE][4];
+      D::pieces(wd, s & 1, vv);
+#pragma unroll
+      for (int a = 0; a < D::NPIECE; ++a)
+#pragma unroll
+        for (int j = 0; j < PS; ++j) {
+          f16x2_t sj = h2(st.s[nb][j] * 0x00010001u);  // (s, s)
+          if (D::piece_mult(a) != 1.f) sj = sj * f16x2_t{(_Float16)16.f, (_Float16)16.f};
+          f16x8_t bfr;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const f16x2_t q = vv[a][i] * sj;
+            bfr[2 * i] = q[0];
+            bfr[2 * i + 1] = q[1];
+          }
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mb], bfr, acc[mb][nb], 0, 0, 0);
+        }
+    }
+  }
+
+  // the four 16-column steps of a tile; the x fragments of step s+1 are read
+  // from LDS before the MFMAs of step s, so LDS latency hides behind them
+  __device__ __forceinline__ void compute(const St& st, const unsigned char* __restrict__ sA, f32x16_t (&acc)[MB][2]) const {
+    f16x8_t a0[MB], a1[MB];
+    read_a(sA, 0, a0);
+    read_a(sA, 1, a1);
+    mma_step(st, 0, a0, acc);
+    read_a(sA, 2, a0);
+    mma_step(st, 1, a1, acc);
+    read_a(sA, 3, a1);
+    mma_step(st, 2, a0, acc);
+    mma_step(st, 3, a1, acc);
+  }
+
+  // One K tile kt:
+  //   barrier                 tile kt's x (stored last step) visible to all waves,
+  //                           everyone done with stage (kt+1)&1
+  //   store x of tile kt+1    registers loaded last step -> the other stage
+  //   issue tile kt+2         x into registers, weights/scales into the ring
+  //   compute tile kt
+  // Loads past the last tile read 0 (buffer range checks) and land nowhere
+  // that is read, so the step has no branch.
+  __device__ __forceinline__ void step(int kt, const St& cur, St& nxt, unsigned char* lds, u32x4_t (&xr)[A_DMA],
+                                       f32x16_t (&acc)[MB][2]) const {
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0): own LDS writes done
+    __builtin_amdgcn_s_barrier();
+    store_x(lds + ((kt + 1) & 1) * (MB * 32 * 128), xr);
+    issue(kt + 2, nxt, xr);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+    compute(cur, lds + (kt & 1) * (MB * 32 * 128), acc);
   }
 };
 
@@ -423,9 +440,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int m0 = tm * BM, n0 = tn * BN;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l32 = lane & 31, half = lane >> 5;
 
-  __shared__ __attribute__((aligned(1024))) unsigned char sA0[STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char sA1[STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char sA2[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * STAGE_BYTES];
   __shared__ int em_s[BM];
   for (int i = t; i < BM; i += 256) em_s[i] = p.em[m0 + i];
 
@@ -442,10 +457,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const uint32_t row_bytes = (uint32_t)p.K * BITS / 8;
   P.rw = make_rsrc(p.w, (uint32_t)p.N * row_bytes);
   P.rs = make_rsrc(p.sh, (uint32_t)p.Np * p.ng * PS * 2);
-  P.rx = make_rsrc(p.xh + (long)m0 * p.K, (uint32_t)BM * p.K * 2);
+  P.rx = make_rsrc(p.xh + (long)m0 * p.K, (uint32_t)BM * p.K * 2);  // this row tile's blocks
   P.half = half;
   P.l32 = l32;
-  P.wave = wave;
   P.gsh = p.gsh;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
@@ -453,19 +467,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     P.w_off[nb] = n * row_bytes + half * WPL * 4;
     P.s_off[nb] = n * (uint32_t)p.ng * PS * 2;
   }
-  // x DMA: instruction i of this wave fills LDS bytes [i*4096 + wave*1024, +1024):
-  // chunk q = i*256 + t -> row q/8 = 32i + t/8, position q%8 = t%8, holding
-  // source chunk pos^swz(row); swz(32i + t/8) does not depend on i.
+  // x tile chunks: thread t moves chunks q = i*256 + t, i.e. row 32i + t/8,
+  // LDS position t%8, which holds source chunk (t%8)^swz(row); swz(32i + t/8)
+  // does not depend on i.
   {
     const int r = t >> 3, pos = t & 7;
-    P.x_off = (uint32_t)r * p.K * 2 + ((pos ^ swz(r)) << 4);
-    P.x_row_step = 32 * p.K * 2;
+    P.x_off = (uint32_t)r * 128 + ((pos ^ swz(r)) << 4);  // inside the contiguous BM x 64 block
+    P.a_dst = t * 16;
   }
 
   const int nkt = p.K / BK;
   St st0, st1, st2;
-  P.issue(0, st0, sA0);
-  P.issue(1, st1, sA1);
+  u32x4_t xr[MB];
+  P.issue(0, st0, xr);
+  P.store_x(lds, xr);
+  P.issue(1, st1, xr);
 
   // ---- tail: sum_g xs * cb on bf16 MFMA, operands straight from global
   // (L2-resident), overlapping the first x tiles' DMA
@@ -490,16 +506,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 
   // ---- main loop, unrolled by 3 over the ring
-  // Before tile K is read, only the newest issue group (tile K+1's) may still
-  // be in flight; vector memory operations complete in order.
   for (int kt = 0; kt < nkt; kt += 3) {
-    P.step(kt, st0, sA0, st2, sA2, acc);
-    if (kt + 1 < nkt) P.step(kt + 1, st1, sA1, st0, sA0, acc);
-    if (kt + 2 < nkt) P.step(kt + 2, st2, sA2, st1, sA1, acc);
+    P.step(kt, st0, st2, lds, xr, acc);
+    if (kt + 1 < nkt) P.step(kt + 1, st1, st0, lds, xr, acc);
+    if (kt + 2 < nkt) P.step(kt + 2, st2, st1, lds, xr, acc);
   }
-  // the loads issued past the last tile must land before this workgroup's
-  // LDS can be handed to another one
-  __builtin_amdgcn_s_waitcnt(0);
 
   // ---- epilogue: y = 2^(e_m + e_n) * acc, rounded to the activation dtype.
   // 32x32 accumulator layout: lane -> column l32; register r -> row
@@ -573,7 +584,7 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
   uint16_t* tB = (uint16_t*)(scratch + o_tb);
   int* en = (int*)(scratch + o_en);
 
-  hipLaunchKernelGGL((prep_x_kernel<BITS>), dim3(Mp), dim3(256), 0, s, a.x, a.act_dt, a.k_perm, M, K, G, Kt, xh, tA, em);
+  hipLaunchKernelGGL((prep_x_kernel<BITS>), dim3(Mp), dim3(256), 0, s, a.x, a.act_dt, a.k_perm, M, K, G, Kt, BM, xh, tA, em);
   hipLaunchKernelGGL((prep_w_kernel<PS>), dim3(Np / 4), dim3(256), 0, s, a.scales, a.s_dt, a.biases, a.b_dt,
                      Decode<BITS>::OFFQ, N, ng, Kt, sh, tB, en);
 
