@@ -1,20 +1,33 @@
 #!/usr/bin/env python3
 """Benchmark of the fused group-wise affine dequant + matmul on one MI355X.
 
-Headline metric: 4-bit GEMV throughput at M=1 (GB/s and % of HBM peak) on the
-decode GEMV set of a 1B-parameter decoder (hidden 2048, FFN 8192: q 2048x2048,
-k and v 512x2048, o 2048x2048, gate and up 8192x2048, down 2048x8192; 4-bit
-codes, group 64, bf16 scales/biases/activations).  One step = one decode pass
-over a stack of `--layers` copies of those seven linears (16 by default, 523
-MiB of packed weights, twice the 256 MB Infinity Cache, so each weight is read
-cold from HBM).  The step is captured once in a HIP graph and replayed.
+Headline metric: 4-bit GEMV throughput at M=1 (GB/s and fraction of the HBM
+peak) on the decode GEMV set of a 1B-parameter decoder (hidden 2048, FFN 8192:
+q 2048x2048, k and v 512x2048, o 2048x2048, gate and up 8192x2048, down
+2048x8192; 4-bit codes, group 64, bf16 scales/biases/activations), over a
+stack of `--layers` copies of those seven linears (16 by default: 523 MiB of
+packed weights, twice the 256 MB Infinity Cache, so weights stream from HBM).
 
-Also reported, in the same JSON line: the prefill GEMM figure (M=2048,
-K=4096, N=14336, 4-bit and 8-bit, TFLOP/s against the bf16 dense MFMA peak),
-the roofline object of the GEMV kernel, and the CPU oracle timed on a bounded
-sample of the decode workload.
+One step = every linear of the stack once, at M=1, through the grouped GEMV
+entry point (qgemv_affine_grouped: 56 problems per launch, so 2 launches for
+16 layers).  This is the steady-state figure: the kernel streams weights
+with almost no launch gaps.  In the same JSON line:
+  decode_chain   the same linears in decoder dependency order, one grouped
+                 call per dependent step (qkv, o, gate+up, down): 64 launches
+  per_linear     one qmm_affine launch per linear: 112 launches
+  cfg0_hot       the single 2048x2048 linear relaunched on the same weights
+                 (cache-resident: NOT an HBM figure)
+  gemm_m2048     prefill GEMM, M=2048 K=4096 N=14336, 4- and 8-bit, TFLOP/s
+                 against the bf16 dense MFMA peak
+  w4a8_m2048     W4A8 GEMM (quantize + int8 MFMA), M=2048 N=4096 K=1024
+  roofline       the grouped GEMV kernel of the headline step
+  cpu_baseline   the fp64 CPU oracle on a bounded sample of the same workload
+Every GPU figure is timed with HIP events on the stream the kernels run on:
+the headline step is launched directly (two launches, one host call), the
+many-launch figures as replays of a captured HIP graph.
 
     python bench.py [--steps K] [--warmup W] [--layers L] [--no-cpu-baseline]
+    python bench.py --traffic-probe   (short run for rocprofv3 --pmc passes)
 """
 from __future__ import annotations
 
@@ -32,9 +45,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, published
 METRIC = "q4 GEMV GB/s & %HBM peak (M=1); qGEMM TFLOP/s & %MFMA peak (M=2048)"
 G = 64
 BITS = 4
+PER_LAUNCH = 56                # problems per grouped GEMV launch
 
 
 def gemv_bytes(M, N, K, bits=BITS, group=G):
@@ -65,84 +80,107 @@ def load_traffic(kernel_file, key):
 
 
 def build_stack(layers, device, torch, si):
-    """Seeded weights for `layers` copies of the decode set, resident on the GPU.
-    Returns device tensors plus host copies of layer 0 for the CPU baseline."""
-    dev_layers, host0 = [], None
+    """Seeded weights for `layers` copies of the decode set, resident on the GPU."""
+    stack = []
     for l in range(layers):
         lin = []
         for idx, (name, N, K) in enumerate(si.CFG1_LINEARS):
             packed, s, b = si.affine_weights(N, K, G, BITS, seed=(1, 100 + l, idx), scale_range=(0.005, 0.02),
                                              bias_mode="noise")
-            lin.append((name, N, K,
-                        torch.from_numpy(packed.view(np.int32)).to(device),
-                        torch.from_numpy(s.view(np.int16)).view(torch.bfloat16).to(device),
-                        torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(device),
-                        (packed, s, b) if l == 0 else None))
-        dev_layers.append(lin)
-    return dev_layers
+            lin.append(dict(name=name, N=N, K=K,
+                            w=torch.from_numpy(packed.view(np.int32)).to(device),
+                            s=torch.from_numpy(s.view(np.int16)).view(torch.bfloat16).to(device),
+                            b=torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(device),
+                            host=(packed, s, b) if l == 0 else None))
+        stack.append(lin)
+    return stack
 
 
-def time_gemv_stack(args, torch, qa, si, device):
-    stack = build_stack(args.layers, device, torch, si)
-    M = 1
-    xs = {K: torch.from_numpy(si.activations(M, K, seed=(1, 7, K)).view(np.int16)).view(torch.bfloat16).to(device)
-          for K in (2048, 8192)}
-    ys = {N: torch.empty((M, N), dtype=torch.bfloat16, device=device) for N in (512, 2048, 8192)}
-
-    def step():
-        for lin in stack:
-            for name, N, K, w, s, b, _ in lin:
-                qa.qmm_affine(xs[K], w, s, b, G, BITS, out=ys[N])
-
-    launches_per_step = sum(len(l) for l in stack)
-    bytes_per_step = sum(gemv_bytes(M, N, K) for l in stack for _, N, K, *_ in l)
-
-    # capture one step in a HIP graph (our launches go to torch's current stream)
-    stream = torch.cuda.Stream()
-    stream.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(stream):
-        step()                                # first launches outside capture
-    torch.cuda.current_stream().wait_stream(stream)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step()
-    torch.cuda.synchronize()
-
-    for _ in range(args.warmup):
-        graph.replay()
+def eager_time(torch, fn, steps, warmup):
+    """Run fn() on the current stream, timing `steps` calls with events on that
+    stream (for steps whose host work is far shorter than their GPU work)."""
+    for _ in range(warmup):
+        fn()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
-    for _ in range(args.steps):
-        graph.replay()
+    for _ in range(steps):
+        fn()
     end.record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end)
-    ms_per_step = ms / args.steps
-    gbs = bytes_per_step / (ms_per_step * 1e-3) / 1e9
-    avg_launch_us = ms_per_step * 1e3 / launches_per_step
-    host0 = [(N, K, h) for _, N, K, _, _, _, h in stack[0]]
-    return dict(ms_per_step=ms_per_step, gbs=gbs, bytes_per_step=bytes_per_step,
-                launches_per_step=launches_per_step, avg_launch_us=avg_launch_us,
-                bytes_per_launch=bytes_per_step / launches_per_step, host0=host0,
-                x_host={K: si.activations(M, K, seed=(1, 7, K)) for K in (2048, 8192)})
+    return start.elapsed_time(end) / steps
+
+
+def graph_time(torch, fn, steps, warmup):
+    """Capture fn() in a HIP graph, replay it, time the replays with events on
+    the replay stream.  Returns ms per step."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+class Decode:
+    """The decode set on the GPU plus the three ways of running it."""
+
+    def __init__(self, args, torch, qa, si, device):
+        self.stack = build_stack(args.layers, device, torch, si)
+        self.M = 1
+        self.x_host = {K: si.activations(self.M, K, seed=(1, 7, K)) for K in (2048, 8192)}
+        self.x = {K: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).to(device) for K, v in self.x_host.items()}
+        # one output per linear, so grouped launches never share an output
+        self.y = [[torch.empty((self.M, d["N"]), dtype=torch.bfloat16, device=device) for d in lin]
+                  for lin in self.stack]
+        prob = lambda l, i: (self.x[self.stack[l][i]["K"]], self.stack[l][i]["w"], self.stack[l][i]["s"],
+                             self.stack[l][i]["b"])
+        L = len(self.stack)
+        flat = [(l, i) for l in range(L) for i in range(7)]
+        self.set_call = qa.GroupedGemv([prob(l, i) for l, i in flat], G, BITS, outs=[self.y[l][i] for l, i in flat])
+        # decoder order: q/k/v share x; o; gate/up share x; down
+        self.chain = []
+        for l in range(L):
+            for idx in ((0, 1, 2), (3,), (4, 5), (6,)):
+                self.chain.append(qa.GroupedGemv([prob(l, i) for i in idx], G, BITS, outs=[self.y[l][i] for i in idx]))
+        self.qa = qa
+        self.bytes_per_step = sum(gemv_bytes(self.M, d["N"], d["K"]) for lin in self.stack for d in lin)
+        self.n_linears = 7 * L
+
+    def run_set(self):
+        self.set_call()
+
+    def run_chain(self):
+        for c in self.chain:
+            c()
+
+    def run_per_linear(self):
+        for l, lin in enumerate(self.stack):
+            for i, d in enumerate(lin):
+                self.qa.qmm_affine(self.x[d["K"]], d["w"], d["s"], d["b"], G, BITS, out=self.y[l][i])
 
 
 def time_gemm(torch, qa, si, device, bits, N=14336, K=4096, M=2048, iters=20, warmup=5):
-    """Prefill GEMM on the largest cfg shape; returns None when the path is not built."""
     case = si.cfg2_case(N, K, bits, M=M, seed=(2, N, K))
     x = torch.from_numpy(case.x.view(np.int16)).view(torch.bfloat16).to(device)
     w = torch.from_numpy(case.packed.view(np.int32)).to(device)
     s = torch.from_numpy(case.scales.view(np.int16)).view(torch.bfloat16).to(device)
     b = torch.from_numpy(case.biases.view(np.int16)).view(torch.bfloat16).to(device)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=device)
-    try:
-        qa.qmm_affine(x, w, s, b, G, bits, out=y)
-    except qa.QaffError as e:
-        if e.status == 2:
-            return None
-        raise
     for _ in range(warmup):
         qa.qmm_affine(x, w, s, b, G, bits, out=y)
     torch.cuda.synchronize()
@@ -158,16 +196,36 @@ def time_gemm(torch, qa, si, device, bits, N=14336, K=4096, M=2048, iters=20, wa
             "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4)}
 
 
-def cpu_baseline(res, seconds):
-    """The fp64 oracle on the host cores over layer-0 linears of the same decode
-    workload (M=1), repeated until `seconds` of work or one full layer pass."""
+def time_w4a8(torch, qa, si, device, M=2048, N=4096, K=1024, iters=20, warmup=5):
+    case = si.w4a8_case(M, N, K, seed=(4, N, K, M))
+    x = torch.from_numpy(case.x.view(np.int16)).view(torch.float16).to(device)
+    w = torch.from_numpy(case.w_q4.view(np.int32)).to(device)
+    sw = torch.from_numpy(case.s_w.view(np.int16)).view(torch.float16).to(device)
+    for _ in range(warmup):
+        qa.qgemm_w4a8(x, w, sw)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(iters):
+        qa.qgemm_w4a8(x, w, sw)
+    end.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) * 1e3 / iters
+    tops = 2.0 * M * N * K / (us * 1e-6) / 1e12
+    return {"M": M, "N": N, "K": K, "us_per_call": round(us, 2), "tops": round(tops, 1),
+            "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
+
+
+def cpu_baseline(dec, seconds):
+    """The fp64 oracle on the host cores over the layer-0 linears of the same
+    decode workload (M=1), repeated until `seconds` of work."""
     import oracle
     done_bytes, t0, passes = 0, time.perf_counter(), 0
     while True:
-        for N, K, (packed, s, b) in res["host0"]:
-            x = res["x_host"][K]
-            oracle.qmm_affine(x, "bf16", packed, s, b, "bf16", 1, N, K, G, BITS)
-            done_bytes += gemv_bytes(1, N, K)
+        for d in dec.stack[0]:
+            packed, s, b = d["host"]
+            oracle.qmm_affine(dec.x_host[d["K"]], "bf16", packed, s, b, "bf16", 1, d["N"], d["K"], G, BITS)
+            done_bytes += gemv_bytes(1, d["N"], d["K"])
         passes += 1
         if time.perf_counter() - t0 >= seconds or passes >= 1000:
             break
@@ -177,16 +235,35 @@ def cpu_baseline(res, seconds):
                       f"{dt:.1f} s wall"}
 
 
+def traffic_probe(torch, dec):
+    """A short, eager run for rocprofv3 --pmc passes: a plain copy of known size
+    (calibration), then three headline steps."""
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dec.run_set()
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "set_bytes_per_step": dec.bytes_per_step,
+                      "launches_per_step": -(-dec.n_linears // PER_LAUNCH)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--layers", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-gemm", action="store_true")
-    ap.add_argument("--skip-gemv", action="store_true", help="time only the prefill GEMM (for profiling)")
+    ap.add_argument("--skip-gemv", action="store_true", help="time only the prefill GEMMs (for profiling)")
+    ap.add_argument("--traffic-probe", action="store_true", help="short eager run for rocprofv3 --pmc")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -205,49 +282,78 @@ def main():
     if args.skip_gemv:
         for bits in (4, 8):
             print(json.dumps({"gemm_m2048": time_gemm(torch, qa, si, device, bits)}), flush=True)
+        print(json.dumps({"w4a8_m2048": time_w4a8(torch, qa, si, device)}), flush=True)
         return
-    res = time_gemv_stack(args, torch, qa, si, device)
-    print(f"[bench] gemv stack: {res['ms_per_step']*1e3:.1f} us/step, {res['gbs']:.0f} GB/s, "
-          f"{res['avg_launch_us']:.2f} us/launch avg", file=sys.stderr, flush=True)
 
-    gemm = None
+    dec = Decode(args, torch, qa, si, device)
+    if args.traffic_probe:
+        traffic_probe(torch, dec)
+        return
+
+    launches_set = -(-dec.n_linears // PER_LAUNCH)
+    ms_set = eager_time(torch, dec.run_set, args.steps, args.warmup)
+    gbs_set = dec.bytes_per_step / (ms_set * 1e-3) / 1e9
+    print(f"[bench] decode set (grouped, {launches_set} launches): {ms_set*1e3:.1f} us/step, {gbs_set:.0f} GB/s",
+          file=sys.stderr, flush=True)
+    chain_steps = max(args.steps // 4, 10)
+    ms_chain = graph_time(torch, dec.run_chain, chain_steps, args.warmup)
+    ms_lin = graph_time(torch, dec.run_per_linear, chain_steps, args.warmup)
+    print(f"[bench] decode chain (64 launches): {ms_chain*1e3:.1f} us/step; per linear (112 launches): "
+          f"{ms_lin*1e3:.1f} us/step", file=sys.stderr, flush=True)
+
+    # cfg0 shape relaunched on the same weights: cache-resident latency figure
+    d0 = dec.stack[0][0]
+    y0 = torch.empty((1, d0["N"]), dtype=torch.bfloat16, device=device)
+    hot = lambda: [qa.qmm_affine(dec.x[2048], d0["w"], d0["s"], d0["b"], G, BITS, out=y0) for _ in range(20)]
+    us_hot = graph_time(torch, hot, 20, 5) * 1e3 / 20
+
+    gemm = w4a8 = None
     if not args.no_gemm:
-        gemm = [g for g in (time_gemm(torch, qa, si, device, 4), time_gemm(torch, qa, si, device, 8)) if g]
+        gemm = [time_gemm(torch, qa, si, device, 4), time_gemm(torch, qa, si, device, 8)]
+        w4a8 = time_w4a8(torch, qa, si, device)
         for g in gemm:
             print(f"[bench] gemm b{g['bits']}: {g['us_per_call']} us, {g['tflops']} TFLOP/s", file=sys.stderr,
                   flush=True)
+        print(f"[bench] w4a8: {w4a8['us_per_call']} us, {w4a8['tops']} TOPS", file=sys.stderr, flush=True)
 
-    achieved = res["bytes_per_launch"] / (res["avg_launch_us"] * 1e-6) / 1e9
+    bytes_per_launch = dec.bytes_per_step / launches_set
+    avg_launch_us = ms_set * 1e3 / launches_set
+    achieved = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": load_traffic("gemv_affine.hip", "gemv_decode_stack_m1"),
-                "kernel": "gemv_affine_kernel (4-bit, bf16, M=1)",
-                "bytes_per_launch": round(res["bytes_per_launch"]), "avg_launch_us": round(res["avg_launch_us"], 3)}
+                "traffic": load_traffic("gemv_affine.hip", "gemv_decode_set_m1"),
+                "kernel": "gemv_affine_kernel<4, bf16, M=1> (grouped, 56 linears per launch)",
+                "bytes_per_launch": round(bytes_per_launch), "avg_launch_us": round(avg_launch_us, 3)}
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(res, args.cpu_seconds)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(dec, args.cpu_seconds)
 
     out = {
         "metric": METRIC,
-        "value": round(res["gbs"], 1),
+        "value": round(gbs_set, 1),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(res["ms_per_step"], 4),
+        "ms_per_step": round(ms_set, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "decode GEMV set of a 1B decoder (hidden 2048, FFN 8192), M=1, 4-bit codes, G=64, "
-                               f"bf16 scales/biases/activations, {args.layers}-layer stack, HIP-graph replay",
+        "config": {"workload": f"decode GEMV set of a 1B decoder (hidden 2048, FFN 8192) x {args.layers} layers, "
+                               "M=1, 4-bit codes, G=64, bf16 scales/biases/activations; every linear once per step "
+                               f"through the grouped GEMV ({launches_set} launches per step)",
                    "M": 1, "layers": args.layers, "linears_per_layer": 7, "bits": BITS, "group_size": G,
-                   "bytes_per_step": res["bytes_per_step"], "frac_of_hbm_peak": round(res["gbs"] / HBM_PEAK_GBS, 4)},
+                   "bytes_per_step": dec.bytes_per_step, "frac_of_hbm_peak": round(gbs_set / HBM_PEAK_GBS, 4)},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "decode_chain": {"launches_per_step": 4 * args.layers, "us_per_step": round(ms_chain * 1e3, 1),
+                         "gbs": round(dec.bytes_per_step / (ms_chain * 1e-3) / 1e9, 1)},
+        "per_linear": {"launches_per_step": dec.n_linears, "us_per_step": round(ms_lin * 1e3, 1),
+                       "gbs": round(dec.bytes_per_step / (ms_lin * 1e-3) / 1e9, 1)},
+        "cfg0_hot": {"us_per_launch": round(us_hot, 2), "gbs_not_hbm": round(gemv_bytes(1, 2048, 2048) / us_hot / 1e3, 1)},
         "gemm_m2048": gemm,
+        "w4a8_m2048": w4a8,
     }
     print(json.dumps(out), flush=True)
 

@@ -6,7 +6,7 @@ device memory and the current HIP stream; nothing here computes.  There is no
 CPU fallback: if the library is missing this module raises on first use.
 
 Functions mirror the C entry points:
-    qmm_affine, qgemv_affine, qmm_gptq, qgemm_w4a8,
+    qmm_affine, qgemv_affine, qgemv_affine_grouped, qmm_gptq, qgemm_w4a8,
     gptq_to_affine_repack, quantize_pack_affine
 """
 from __future__ import annotations
@@ -17,7 +17,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["QaffError", "qmm_affine", "qgemv_affine", "qmm_gptq", "qgemm_w4a8", "gptq_to_affine_repack",
+__all__ = ["QaffError", "qmm_affine", "qgemv_affine", "qgemv_affine_grouped", "GroupedGemv", "qmm_gptq", "qgemm_w4a8", "gptq_to_affine_repack",
            "quantize_pack_affine", "library_path", "lib", "STATUS", "DTYPE"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,7 +36,14 @@ _SIGS = {
     "qgemm_w4a8": [_VP] * 7 + [_I64] * 3 + [_VP],
     "gptq_to_affine_repack": [_VP] * 7 + [_I32, _VP] + [_I64] * 2 + [_I32, _VP],
     "quantize_pack_affine": [_VP, _I32, _VP, _VP, _VP, _I32, _I64, _I64, _I32, _I32, _VP],
+    "qgemv_affine_grouped": [_VP, _I32, _I64] + [_I32] * 5 + [_VP],
 }
+
+
+class GemvProblem(C.Structure):
+    """qaff_gemv_problem (include/qaff.h)."""
+    _fields_ = [("x", _VP), ("w_packed", _VP), ("scales", _VP), ("biases", _VP), ("k_perm", _VP), ("y", _VP),
+                ("N", _I64), ("K", _I64)]
 
 
 class QaffError(RuntimeError):
@@ -122,6 +129,61 @@ def qmm_affine(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Tensor, bi
 def qgemv_affine(x, w_packed, scales, biases, group_size: int, bits: int, k_perm=None, out=None) -> torch.Tensor:
     """As qmm_affine, always on the GEMV kernel (M <= 16)."""
     return _affine("qgemv_affine", x, w_packed, scales, biases, group_size, bits, k_perm, out)
+
+
+def qgemv_affine_grouped(problems, group_size: int, bits: int, outs=None):
+    """Independent GEMVs in as few launches as possible.
+
+    problems: sequence of (x, w_packed, scales, biases) or (..., k_perm)
+    tuples sharing M, dtypes, group_size and bits; returns the list of y.
+    """
+    n = len(problems)
+    arr = (GemvProblem * max(n, 1))()
+    ys = []
+    for i, p in enumerate(problems):
+        x, w, sc, bi = p[:4]
+        kp = p[4] if len(p) > 4 else None
+        M, K = x.shape
+        N = w.shape[0]
+        y = outs[i] if outs is not None else torch.empty((M, N), dtype=x.dtype, device=x.device)
+        ys.append(y)
+        arr[i] = GemvProblem(_ptr(x), _ptr(_u32(w)), _ptr(sc), _ptr(bi), _ptr(kp), _ptr(y), N, K)
+    if n == 0:
+        return ys
+    x0, w0, s0, b0 = problems[0][:4]
+    st = lib().qgemv_affine_grouped(C.cast(arr, _VP), n, x0.shape[0], group_size, bits, _dt(x0), _dt(s0), _dt(b0),
+                                    _stream(x0.device))
+    _check(st, "qgemv_affine_grouped")
+    return ys
+
+
+class GroupedGemv:
+    """qgemv_affine_grouped with the descriptor array marshalled once.
+
+    Holds references to every tensor it points at; calling it enqueues the
+    GEMVs on the current stream of the device of the first x.
+    """
+
+    def __init__(self, problems, group_size: int, bits: int, outs=None):
+        self.problems = [tuple(p) for p in problems]
+        self.ys = []
+        self.arr = (GemvProblem * max(len(problems), 1))()
+        for i, p in enumerate(self.problems):
+            x, w, sc, bi = p[:4]
+            kp = p[4] if len(p) > 4 else None
+            M, K = x.shape
+            N = w.shape[0]
+            y = outs[i] if outs is not None else torch.empty((M, N), dtype=x.dtype, device=x.device)
+            self.ys.append(y)
+            self.arr[i] = GemvProblem(_ptr(x), _ptr(_u32(w)), _ptr(sc), _ptr(bi), _ptr(kp), _ptr(y), N, K)
+        x0, _, s0, b0 = self.problems[0][:4]
+        self.args = (len(self.problems), x0.shape[0], group_size, bits, _dt(x0), _dt(s0), _dt(b0))
+        self.device = x0.device
+
+    def __call__(self):
+        st = lib().qgemv_affine_grouped(C.cast(self.arr, _VP), *self.args, _stream(self.device))
+        _check(st, "qgemv_affine_grouped")
+        return self.ys
 
 
 def qmm_gptq(x: torch.Tensor, qweight: torch.Tensor, qzeros: torch.Tensor, scales: torch.Tensor,

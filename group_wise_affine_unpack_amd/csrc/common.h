@@ -45,6 +45,14 @@ __device__ __forceinline__ uint16_t f32_to_act_bits(float v, bool f16) {
   return f16 ? f32_to_f16_bits(v) : f32_to_bf16_bits(v);
 }
 
+// ---- buffer resources -----------------------------------------------------
+// Raw buffer descriptor over [base, base + bytes): a load whose offset
+// (VGPR offset plus immediate) is at or past `bytes` returns zeros.
+constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // raw buffer, 32-bit data format
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)RSRC_WORD3);
+}
+
 // ---- wave reduction -----------------------------------------------------
 // Sum over the 64 lanes of a wave: rotates inside each row of 16 lanes with
 // DPP (every lane of the row ends with the row sum), then two swaps across
@@ -83,6 +91,8 @@ struct AffineArgs {
 };
 
 hipError_t launch_gemv_affine(const AffineArgs& a, hipStream_t s);
+// count problems that share M, G, bits and dtypes, in as few launches as possible
+hipError_t launch_gemv_grouped(const AffineArgs* probs, int count, hipStream_t s);
 hipError_t launch_gemm_affine(const AffineArgs& a, hipStream_t s);
 
 struct GptqArgs {

@@ -284,12 +284,6 @@ struct Decode {
 // Buffer loads past a buffer's end return 0, so the last row tile of W needs
 // no clamping.
 
-constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // raw buffer, 32-bit data format
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)RSRC_WORD3);
-}
-
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 1)) & 7; }
 
 template <int BITS, int PS, int MB>

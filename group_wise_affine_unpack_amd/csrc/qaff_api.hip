@@ -95,7 +95,35 @@ int qgemv_affine(const void* x, const uint32_t* w_packed, const void* scales, co
   hipError_t e = qaff::launch_gemv_affine(
       affine_args(x, w_packed, scales, biases, k_perm, y, M, N, K, group_size, bits, act_dtype, scale_dtype, bias_dtype),
       static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return fail(QAFF_E_UNSUPPORTED, "row or activation too large for 32-bit offsets");
   if (e != hipSuccess) return hip_fail(e, "gemv launch");
+  return ok();
+}
+
+int qgemv_affine_grouped(const qaff_gemv_problem* problems, int32_t count, int64_t M, int32_t group_size,
+                         int32_t bits, int32_t act_dtype, int32_t scale_dtype, int32_t bias_dtype, void* stream) {
+  if (count < 0 || count > 65536) return fail(QAFF_E_INVAL, "count must be in [0, 65536] (got %d)", count);
+  if (count > 0 && problems == nullptr) return fail(QAFF_E_INVAL, "null problem array");
+  if (M > 16) return fail(QAFF_E_INVAL, "qgemv_affine_grouped takes M <= 16 (got %lld)", (long long)M);
+  std::vector<qaff::AffineArgs> args;
+  args.reserve(count);
+  for (int32_t i = 0; i < count; ++i) {
+    const qaff_gemv_problem& p = problems[i];
+    int rc = check_affine(p.x, p.w_packed, p.scales, p.biases, p.y, M, p.N, p.K, group_size, bits, act_dtype,
+                          scale_dtype, bias_dtype);
+    if (rc != QAFF_OK) {
+      const std::string msg = g_last_error;
+      return fail(rc, "problem %d: %s", i, msg.c_str());
+    }
+    if (M > 0 && p.N > 0)
+      args.push_back(affine_args(p.x, p.w_packed, p.scales, p.biases, p.k_perm, p.y, M, p.N, p.K, group_size, bits,
+                                 act_dtype, scale_dtype, bias_dtype));
+  }
+  if (args.empty()) return ok();
+  (void)hipGetLastError();
+  hipError_t e = qaff::launch_gemv_grouped(args.data(), (int)args.size(), static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return fail(QAFF_E_UNSUPPORTED, "a problem is too large for 32-bit offsets");
+  if (e != hipSuccess) return hip_fail(e, "grouped gemv launch");
   return ok();
 }
 

@@ -91,6 +91,40 @@ int qgemv_affine(const void *x, const uint32_t *w_packed, const void *scales, co
                  int32_t bias_dtype, void *stream);
 
 /*
+ * qgemv_affine_grouped - `count` independent GEMVs y_i = x_i . W_i^T of the
+ * qmm_affine form, computed by as few kernel launches as possible (one per
+ * 56 problems).  This is the multi-weight decode GEMV: linears that read the
+ * same input (q/k/v, gate/up) pass the same x, and each problem keeps its own
+ * weights, parameters and output.  It serves decode with M <= 16, where one
+ * launch per small matrix costs more time in launch latency than in reading
+ * the weights (mlx_int8.rs API page, `gemv`: y = W x over the packed layout).
+ *
+ *   problems  HOST array of `count` descriptors (read during the call only);
+ *             every pointer in it is a device pointer with the meaning,
+ *             layout and alignment of the qmm_affine argument of that name
+ *   count     0 <= count <= 65536; 0 returns QAFF_OK
+ *   M, group_size, bits, act_dtype, scale_dtype, bias_dtype
+ *             shared by every problem, with the qmm_affine rules; M <= 16
+ *   Each problem is checked as qgemv_affine would check it; the first bad
+ *   one fails the whole call before anything is launched.  Outputs of
+ *   different problems must not overlap.
+ */
+typedef struct qaff_gemv_problem {
+    const void *x;            /* [M, K] act_dtype */
+    const uint32_t *w_packed; /* [N, K*bits/32] */
+    const void *scales;       /* [N, K/G] */
+    const void *biases;       /* [N, K/G] */
+    const int32_t *k_perm;    /* [K] or NULL */
+    void *y;                  /* [M, N] act_dtype */
+    int64_t N;
+    int64_t K;
+} qaff_gemv_problem;
+
+int qgemv_affine_grouped(const qaff_gemv_problem *problems, int32_t count, int64_t M,
+                         int32_t group_size, int32_t bits, int32_t act_dtype, int32_t scale_dtype,
+                         int32_t bias_dtype, void *stream);
+
+/*
  * qmm_gptq - y[M,N] = x[M,K] . W^T for a GPTQ layer in its own layout
  * (TinyGPT "Quantization Expansion", "GPTQReader" / "Format"):
  *     W[n,i] = scales[g, n] * (q - ((qzeros[g, n/8] >> 4*(n%8)) & 15) - 1),

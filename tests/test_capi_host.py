@@ -108,3 +108,27 @@ def test_binding_has_no_cpu_path():
     with pytest.raises(ValueError):
         qa.qmm_affine(x, torch.zeros((8, 32), dtype=torch.int32), torch.zeros((8, 4), dtype=torch.bfloat16),
                       torch.zeros((8, 4), dtype=torch.bfloat16), 64, 4)
+
+
+def _grouped(probs, M=1, G=64, bits=4, adt=0, sdt=0, bdt=0, count=None):
+    arr = (qa.GemvProblem * max(len(probs), 1))(*[qa.GemvProblem(*p) for p in probs])
+    n = len(probs) if count is None else count
+    return qa.lib().qgemv_affine_grouped(C.cast(arr, C.c_void_p), n, M, G, bits, adt, sdt, bdt, None)
+
+
+def test_grouped_argument_errors():
+    good = (A, A, A, A, None, A, 64, 256)
+    assert _grouped([]) == OK
+    assert qa.lib().qgemv_affine_grouped(None, 0, 1, 64, 4, 0, 0, 0, None) == OK
+    assert qa.lib().qgemv_affine_grouped(None, 2, 1, 64, 4, 0, 0, 0, None) == INVAL
+    assert _grouped([good], count=-1) == INVAL
+    assert _grouped([good], count=65537) == INVAL
+    assert _grouped([good], M=17) == INVAL and "M <= 16" in _msg()
+    assert _grouped([good], bits=3) == INVAL
+    # the first bad problem names itself and nothing is launched
+    assert _grouped([good, (A, A, A, A, None, A, 64, 96)]) == INVAL and "problem 1" in _msg()
+    assert _grouped([good, good, (A + 2, A, A, A, None, A, 64, 256)]) == ALIGN and "problem 2" in _msg()
+    assert _grouped([good, (A, A, A, A, None, None, 64, 256)]) == INVAL
+    # empty problems are skipped without needing pointers; M = 0 launches nothing
+    assert _grouped([(None, None, None, None, None, None, 0, 256)]) == OK
+    assert _grouped([(None, A, A, A, None, None, 64, 256)], M=0) == OK

@@ -101,3 +101,77 @@ def test_output_not_written_past_n():
     qa.qmm_affine(x, w, s, b, 64, 4, out=out[: 2 * 70].view(2, 70))
     torch.cuda.synchronize()
     assert torch.all(out[2 * 70:] == 7.0)
+
+
+def _grouped(cases, share_x=False):
+    dev = require_gpu()
+    probs = []
+    x_shared = None
+    for c in cases:
+        x, w, s, b, kp = affine_to_device(c, dev)
+        if share_x:
+            x_shared = x if x_shared is None else x_shared
+            x = x_shared
+        probs.append((x, w, s, b, kp))
+    c0 = cases[0]
+    print(f"[case] grouped count={len(cases)} M={c0.M} bits={c0.bits} G={c0.G} act={c0.act_dtype} "
+          f"shapes={[(c.N, c.K) for c in cases][:8]}", flush=True)
+    ys = qa.qgemv_affine_grouped(probs, c0.G, c0.bits)
+    torch.cuda.synchronize()
+    return [host_f64(y) for y in ys]
+
+
+@pytest.mark.parametrize("M", si.CFG1_M)
+def test_grouped_decode_layer(M):
+    # the seven linears of one decoder layer in one call, q/k/v and gate/up style sharing of x
+    cases = [si.cfg1_case(N, K, M, seed=(20, i, N, K, M)) for i, (_, N, K) in enumerate(si.CFG1_LINEARS)]
+    ys = _grouped(cases)
+    for c, y in zip(cases, ys):
+        assert_float_bar(y, oracle.qmm_affine_case(c), "grouped_" + c.name)
+
+
+def test_grouped_shared_x():
+    cases = [si.cfg1_case(N, 2048, 1, seed=(21, N)) for N in (2048, 512, 512)]
+    for c in cases[1:]:
+        c.x = cases[0].x
+    ys = _grouped(cases, share_x=True)
+    for c, y in zip(cases, ys):
+        assert_float_bar(y, oracle.qmm_affine_case(c), "shared_x_" + c.name)
+
+
+@pytest.mark.parametrize("bits,act", [(4, "bf16"), (8, "f16"), (2, "bf16")])
+def test_grouped_many_problems_span_launches(bits, act):
+    # more problems than one launch's descriptor table, ragged N, mixed K and one empty problem
+    rng = np.random.default_rng(22)
+    cases = []
+    for i in range(41):
+        N = 0 if i == 17 else int(rng.integers(1, 300))
+        K = int(rng.choice([256, 512, 2048, 4096]))
+        cases.append(si.affine_case(3, N, K, 64, bits, seed=(23, i), act_dtype=act, name=f"g{i}_N{N}_K{K}"))
+    ys = _grouped(cases)
+    for c, y in zip(cases, ys):
+        if c.N == 0:
+            assert y.shape == (3, 0)
+            continue
+        assert_float_bar(y, oracle.qmm_affine_case(c), c.name)
+
+
+def test_grouped_with_k_perm_and_plain_mixed():
+    cases = [si.affine_case(5, 120, 4096, 128, 4, seed=(24, i), act_dtype="f16", name=f"kp{i}") for i in range(3)]
+    cases[1].k_perm = np.random.default_rng(25).permutation(4096).astype(np.int32)
+    ys = _grouped(cases)
+    for c, y in zip(cases, ys):
+        assert_float_bar(y, oracle.qmm_affine_case(c), c.name)
+
+
+@pytest.mark.parametrize("bits,act", [(4, "bf16"), (8, "f16"), (2, "bf16")])
+def test_grouped_large_launch_eight_rows_per_wave(bits, act):
+    # a launch with >= 64 MiB of weights at M = 1 takes the 8-rows-per-wave kernel;
+    # ragged N and a K that splits across waves are mixed in
+    shapes = [(8192, 2048)] * (8 if bits == 4 else (4 if bits == 8 else 16)) + [(1001, 4096), (300, 8192)]
+    cases = [si.affine_case(1, N, K, 64, bits, seed=(26, i, bits), act_dtype=act, name=f"big{i}_N{N}_K{K}")
+             for i, (N, K) in enumerate(shapes)]
+    assert sum(c.N * c.K * bits // 8 for c in cases) >= 64 << 20
+    ys = _grouped(cases)
+    for c, y in zip(cases, ys):
+        assert_float_bar(y, oracle.qmm_affine_case(c), c.name)
