@@ -281,8 +281,8 @@ struct Decode {
 //   * weight words and scale pieces go through buffer loads with the K
 //     offset in an SGPR, into a 3-deep register ring (two steps ahead);
 //   * the loop is unrolled by 3 so every ring index is a constant.
-// Buffer loads past a buffer's end return 0, so the last row tile of W needs
-// no clamping.
+// Rows of W past N are read through per-lane offsets past the buffer's range
+// and come back as zeros, so the last row tile needs no clamping.
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 1)) & 7; }
 
@@ -304,12 +304,17 @@ struct Pipe {
   __amdgpu_buffer_rsrc_t rw, rs, rx;
   uint32_t w_off[2], s_off[2], x_off;
   int half, l32, gsh;
+  int last_kt;     // index of the last K tile
   int a_dst;       // this thread's first LDS chunk in a stage
 
   // Loads for K tile kt: the x chunks (into registers; written to LDS one
   // step later), then the weight words and scale pieces (into a ring entry
   // used two steps later).
+  // A prefetch past the last tile re-reads the last tile: every address stays
+  // inside its buffer, whatever the hardware does with soffset in its range
+  // check; the data is never used.
   __device__ __forceinline__ void issue(int kt, St& st, u32x4_t (&xr)[A_DMA]) const {
+    kt = min(kt, last_kt);
 #pragma unroll
     for (int i = 0; i < A_DMA; ++i)
       xr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, x_off, kt * (MB * 32 * 128) + i * 4096, 0));
@@ -471,6 +476,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 
   const int nkt = p.K / BK;
+  P.last_kt = nkt - 1;
   St st0, st1, st2;
   u32x4_t xr[MB];
   P.issue(0, st0, xr);
@@ -625,8 +631,20 @@ hipError_t run_bits(const AffineArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_affine(const AffineArgs& a, hipStream_t s) {
-  // whole 64-code K tiles only; otherwise the GEMV kernel (chunks of 4 rows) is used
-  if (a.K % BK != 0) return launch_gemv_affine(a, s);
+  // whole 64-code K tiles only; otherwise the GEMV kernel runs on slices of
+  // 16 x rows (each slice reads W once more: a rare shape, not a fast path)
+  if (a.K % BK != 0) {
+    const size_t esz = 2;  // bf16 / f16 activations and outputs
+    for (int64_t m0 = 0; m0 < a.M; m0 += 16) {
+      AffineArgs b = a;
+      b.M = a.M - m0 < 16 ? a.M - m0 : 16;
+      b.x = static_cast<const char*>(a.x) + m0 * a.K * esz;
+      b.y = static_cast<char*>(a.y) + m0 * a.N * esz;
+      const hipError_t e = launch_gemv_affine(b, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   switch (a.bits) {
     case 2: return run_bits<2>(a, s);
     case 4: return run_bits<4>(a, s);
