@@ -253,6 +253,39 @@ def traffic_probe(torch, dec):
                       "launches_per_step": -(-dec.n_linears // PER_LAUNCH)}), flush=True)
 
 
+def record_traffic(fetch_db, write_db):
+    """Turn two rocprofv3 --pmc databases of `bench.py --traffic-probe` (one
+    with FETCH_SIZE, one with WRITE_SIZE) into profiles/traffic.json.  The
+    copy kernel of known size calibrates each counter's unit."""
+    import sqlite3
+
+    def per_kernel(db, counter):
+        rows = sqlite3.connect(db).execute(
+            "select kernel_name, value from counters_collection where counter_name = ?", (counter,)).fetchall()
+        copy = [v for n, v in rows if "copyBuffer" in n or "copy" in n.lower()]
+        gemv = [v for n, v in rows if "gemv_affine_kernel" in n]
+        return max(copy), sum(gemv) / len(gemv)
+
+    copy_bytes = 256 << 20
+    fc, fg = per_kernel(fetch_db, "FETCH_SIZE")
+    wc, wg = per_kernel(write_db, "WRITE_SIZE")
+    f_factor = copy_bytes / (fc * 1024)
+    w_factor = copy_bytes / (wc * 1024)
+    traffic = fg * 1024 * f_factor + wg * 1024 * w_factor
+    rec = {"gemv_decode_set_m1": {
+        "src_hash": src_hash("gemv_affine.hip"),
+        "bytes_per_launch": round(traffic),
+        "fetch_kib_per_launch": round(fg, 1), "write_kib_per_launch": round(wg, 1),
+        "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
+        "calibration": "256 MiB device copy: FETCH_SIZE and WRITE_SIZE of that kernel against 256 MiB",
+        "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -- python3 bench.py --traffic-probe"}}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -264,7 +297,12 @@ def main():
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--skip-gemv", action="store_true", help="time only the prefill GEMMs (for profiling)")
     ap.add_argument("--traffic-probe", action="store_true", help="short eager run for rocprofv3 --pmc")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="write profiles/traffic.json from two --pmc runs of --traffic-probe (no GPU needed)")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
