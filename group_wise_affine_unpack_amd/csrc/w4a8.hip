@@ -10,8 +10,9 @@
 //
 // Kernels:
 //   quant : one block per row; bit-exact codes and scale.
-//   gemm  : v_mfma_i32_32x32x32_i8, tile BM x 256 (4 waves along N), x_q tile
-//           double-buffered in LDS, int4 words decoded in registers.  A nibble
+//   gemm  : v_mfma_i32_32x32x32_i8, tile BM x BN (4 waves along N, each
+//           BM x NB*32), x_q tile double-buffered in LDS, int4 words decoded in
+//           registers; the tile shrinks until the grid covers the chip.  A nibble
 //           is placed in the HIGH half of its byte, which makes the byte the
 //           int8 value 16*v with no sign extension step; the accumulator is
 //           shifted right by 4 at the end (exact: every product is a multiple
@@ -46,7 +47,6 @@ __global__ __launch_bounds__(256) void w4a8_quant_kernel(const uint16_t* __restr
   }
 }
 
-constexpr int BN = 256;
 constexpr int BK = 64;       // int8 codes per K tile
 constexpr int LDS_ROW = 80;  // 64 bytes + 16 bytes padding (conflict-free 16-byte reads)
 
@@ -69,9 +69,10 @@ __device__ __forceinline__ void decode_word(uint32_t w, uint32_t& d0, uint32_t& 
   d1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // (n4, n5, n6, n7)
 }
 
-template <int MB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void w4a8_gemm_kernel(Params p) {
+template <int MB, int NB>
+__global__ __launch_bounds__(256) void w4a8_gemm_kernel(Params p) {
   constexpr int BM = MB * 32;
+  constexpr int BN = NB * 128;
   constexpr int A_CHUNKS = BM * 4 / 256;  // 16-byte chunks of the x_q tile per thread (>= 1)
   const int b = blockIdx.x;
   const int v = (b & 7) * p.per_xcd + (b >> 3);
@@ -82,23 +83,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][BM * LDS_ROW];
 
-  i32x16_t acc[MB][2];
+  i32x16_t acc[MB][NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-  int nrow[2];
+  int nrow[NB];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int n = n0 + wave * 64 + nb * 32 + l32;
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = n0 + wave * NB * 32 + nb * 32 + l32;
     nrow[nb] = n < p.N ? n : p.N - 1;
   }
   const long wrow = p.K / 8;
   const int nkt = p.K / BK;
-  u32x4_t wcur[2], wnxt[2];
+  u32x4_t wcur[NB], wnxt[NB];
   u32x4_t areg[A_CHUNKS];
 
   // x_q rows past M are read clamped to M-1; their results are not stored
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
   for (int c = 0; c < A_CHUNKS; ++c) areg[c] = *a_src(0, c);
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) wcur[nb] = *reinterpret_cast<const u32x4_t*>(p.w + nrow[nb] * wrow + half * 4);
+  for (int nb = 0; nb < NB; ++nb) wcur[nb] = *reinterpret_cast<const u32x4_t*>(p.w + nrow[nb] * wrow + half * 4);
 #pragma unroll
   for (int c = 0; c < A_CHUNKS; ++c) {
     const int ch = t + 256 * c;
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int c = 0; c < A_CHUNKS; ++c) areg[c] = *a_src(kt + 1, c);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
         wnxt[nb] = *reinterpret_cast<const u32x4_t*>(p.w + nrow[nb] * wrow + (kt + 1) * 8 + half * 4);
     }
 #pragma unroll
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int mb = 0; mb < MB; ++mb)
         af[mb] = *reinterpret_cast<const i32x4_t*>(&lds[buf][(mb * 32 + l32) * LDS_ROW + 32 * half + 16 * s]);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < NB; ++nb) {
         const uint32_t w0 = s == 0 ? wcur[nb].x : wcur[nb].z;
         const uint32_t w1 = s == 0 ? wcur[nb].y : wcur[nb].w;
         uint32_t d0, d1, d2, d3;
@@ -153,16 +154,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int ch = t + 256 * c;
         *reinterpret_cast<u32x4_t*>(&lds[buf ^ 1][(ch >> 2) * LDS_ROW + (ch & 3) * 16]) = areg[c];
       }
-      wcur[0] = wnxt[0];
-      wcur[1] = wnxt[1];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) wcur[nb] = wnxt[nb];
     }
     __syncthreads();
   }
 
   // epilogue; 32x32 accumulator layout: lane -> column l32, register r -> row 8*(r/4) + 4*half + r%4
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int n = n0 + wave * 64 + nb * 32 + l32;
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = n0 + wave * NB * 32 + nb * 32 + l32;
     if (n >= p.N) continue;
     const float swn = f16_bits_to_f32(p.sw[n]);
 #pragma unroll
@@ -187,8 +188,15 @@ hipError_t launch_w4a8(const W4A8Args& a, hipStream_t s) {
   hipLaunchKernelGGL(w4a8_quant_kernel, dim3(M), dim3(256), 0, s, (const uint16_t*)a.x, K, a.x_q, a.s_x);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int MB = M <= 64 ? 2 : 8;
-  const int BM = MB * 32;
+  // largest tile whose grid still gives every CU at least two workgroups
+  struct Tile { int mb, nb; };
+  const Tile tiles[] = {{8, 2}, {4, 2}, {4, 1}, {2, 1}};
+  Tile t = tiles[3];
+  for (const Tile& c : tiles) {
+    const long tm = (M + c.mb * 32 - 1) / (c.mb * 32), tn = (N + c.nb * 128 - 1) / (c.nb * 128);
+    if (tm * tn >= 512) { t = c; break; }
+  }
+  if (M <= 64) t = Tile{2, 1};
   Params p;
   p.xq = a.x_q;
   p.sx = a.s_x;
@@ -199,14 +207,18 @@ hipError_t launch_w4a8(const W4A8Args& a, hipStream_t s) {
   p.M = M;
   p.N = N;
   p.K = K;
-  p.Tm = (M + BM - 1) / BM;
-  p.Tn = (N + BN - 1) / BN;
+  p.Tm = (M + t.mb * 32 - 1) / (t.mb * 32);
+  p.Tn = (N + t.nb * 128 - 1) / (t.nb * 128);
   p.per_xcd = (p.Tm * p.Tn + 7) / 8;
   const dim3 grid(8 * p.per_xcd);
-  if (MB == 2)
-    hipLaunchKernelGGL((w4a8_gemm_kernel<2>), grid, dim3(256), 0, s, p);
+  if (t.mb == 8)
+    hipLaunchKernelGGL((w4a8_gemm_kernel<8, 2>), grid, dim3(256), 0, s, p);
+  else if (t.mb == 4 && t.nb == 2)
+    hipLaunchKernelGGL((w4a8_gemm_kernel<4, 2>), grid, dim3(256), 0, s, p);
+  else if (t.mb == 4)
+    hipLaunchKernelGGL((w4a8_gemm_kernel<4, 1>), grid, dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL((w4a8_gemm_kernel<8>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((w4a8_gemm_kernel<2, 1>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
