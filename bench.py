@@ -289,8 +289,8 @@ def record_traffic(fetch_db, write_db):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--layers", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -333,7 +333,7 @@ def main():
     gbs_set = dec.bytes_per_step / (ms_set * 1e-3) / 1e9
     print(f"[bench] decode set (grouped, {launches_set} launches): {ms_set*1e3:.1f} us/step, {gbs_set:.0f} GB/s",
           file=sys.stderr, flush=True)
-    chain_steps = max(args.steps // 4, 10)
+    chain_steps = max(args.steps // 4, 10)  # the GPU clock needs ~100 ms of load to settle
     ms_chain = graph_time(torch, dec.run_chain, chain_steps, args.warmup)
     ms_lin = graph_time(torch, dec.run_per_linear, chain_steps, args.warmup)
     print(f"[bench] decode chain (64 launches): {ms_chain*1e3:.1f} us/step; per linear (112 launches): "

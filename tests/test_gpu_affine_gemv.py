@@ -175,3 +175,22 @@ def test_grouped_large_launch_eight_rows_per_wave(bits, act):
     ys = _grouped(cases)
     for c, y in zip(cases, ys):
         assert_float_bar(y, oracle.qmm_affine_case(c), c.name)
+
+
+@pytest.mark.parametrize("K", [2048, 4096, 8192])
+@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+def test_4bit_m1_rows_split_over_waves(K, G, act):
+    # rows of 1, 2 and 4 KiB: K split over 1, 2 or 4 waves of a workgroup;
+    # ragged N leaves a partly filled last workgroup
+    case = si.affine_case(1, 333, K, G, 4, seed=(27, K, G), act_dtype=act, name=f"m1_K{K}_G{G}_{act}")
+    y = _run(case, qa.qgemv_affine)
+    assert_float_bar(y, oracle.qmm_affine_case(case), case.name)
+
+
+def test_grouped_mixed_k_m1():
+    cases = [si.affine_case(1, N, K, 64, 4, seed=(28, i), name=f"mix{i}_N{N}_K{K}")
+             for i, (N, K) in enumerate([(512, 2048), (77, 8192), (2048, 4096), (5, 2048), (1000, 8192)])]
+    ys = _grouped(cases)
+    for c, y in zip(cases, ys):
+        assert_float_bar(y, oracle.qmm_affine_case(c), c.name)
