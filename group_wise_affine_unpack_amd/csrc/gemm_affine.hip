@@ -246,23 +246,26 @@ struct Decode {
   // integer pieces as exact fp16 pairs, in the kernel's decode order
   static constexpr int NPIECE = BITS == 8 ? 2 : 1;
   static constexpr float OFFQ = BITS == 4 ? 8.f : (BITS == 8 ? 136.f : 0.f);
-  static __device__ __forceinline__ void pieces(const uint32_t* wd, int half, f16x2_t (&v)[NPIECE][4]) {
+  // `magic` holds 0x64006400 in a VGPR, so mask-and-insert is one
+  // v_and_or_b32 (a VOP3 op reads at most one literal or SGPR on gfx950)
+  static __device__ __forceinline__ void pieces(const uint32_t* wd, int half, uint32_t magic,
+                                                f16x2_t (&v)[NPIECE][4]) {
     const f16x2_t k1032 = {(_Float16)-1032.f, (_Float16)-1032.f};
     const f16x2_t k1024 = {(_Float16)-1024.f, (_Float16)-1024.f};
     if constexpr (BITS == 4) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[0][i] = h2(((wd[0] >> (4 * i)) & 0x000F000Fu) | 0x64006400u) + k1032;
+      for (int i = 0; i < 4; ++i) v[0][i] = h2(((wd[0] >> (4 * i)) & 0x000F000Fu) | magic) + k1032;
     } else if constexpr (BITS == 8) {
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
-        v[0][2 * w] = h2(((wd[w] >> 4) & 0x000F000Fu) | 0x64006400u) + k1032;       // hi nibbles (c0,c2)
-        v[0][2 * w + 1] = h2(((wd[w] >> 12) & 0x000F000Fu) | 0x64006400u) + k1032;  // (c1,c3)
-        v[1][2 * w] = h2((wd[w] & 0x000F000Fu) | 0x64006400u) + k1032;              // lo nibbles
-        v[1][2 * w + 1] = h2(((wd[w] >> 8) & 0x000F000Fu) | 0x64006400u) + k1032;
+        v[0][2 * w] = h2(((wd[w] >> 4) & 0x000F000Fu) | magic) + k1032;       // hi nibbles (c0,c2)
+        v[0][2 * w + 1] = h2(((wd[w] >> 12) & 0x000F000Fu) | magic) + k1032;  // (c1,c3)
+        v[1][2 * w] = h2((wd[w] & 0x000F000Fu) | magic) + k1032;              // lo nibbles
+        v[1][2 * w + 1] = h2(((wd[w] >> 8) & 0x000F000Fu) | magic) + k1032;
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[0][i] = h2(((wd[0] >> (2 * (i + 4 * half))) & 0x00030003u) | 0x64006400u) + k1024;
+      for (int i = 0; i < 4; ++i) v[0][i] = h2(((wd[0] >> (2 * (i + 4 * half))) & 0x00030003u) | magic) + k1024;
     }
   }
   // multiplier of piece a
@@ -356,9 +359,10 @@ struct Pipe {
     }
   }
 
-  // the 16-column-step s of a tile: decode this lane's words of both n blocks
-  // and run the MFMAs against the x fragments af
-  __device__ __forceinline__ void mma_step(const St& st, int s, const f16x8_t (&af)[MB], f32x16_t (&acc)[MB][2]) const {
+  // B fragments of the 16-column step s for both n blocks: one per (code
+  // piece, scale piece)
+  static constexpr int NF = D::NPIECE * PS;
+  __device__ __forceinline__ void decode_b(const St& st, int s, uint32_t magic, f16x8_t (&bf)[2][NF]) const {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       uint32_t wd[2];
@@ -371,39 +375,76 @@ struct Pipe {
         wd[0] = st.w[nb][s >> 1];
       }
       f16x2_t vv[D::NPIECE][4];
-      D::pieces(wd, s & 1, vv);
+      D::pieces(wd, s & 1, magic, vv);
 #pragma unroll
       for (int a = 0; a < D::NPIECE; ++a)
 #pragma unroll
         for (int j = 0; j < PS; ++j) {
           f16x2_t sj = h2(st.s[nb][j] * 0x00010001u);  // (s, s)
           if (D::piece_mult(a) != 1.f) sj = sj * f16x2_t{(_Float16)16.f, (_Float16)16.f};
-          f16x8_t bfr;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const f16x2_t q = vv[a][i] * sj;
-            bfr[2 * i] = q[0];
-            bfr[2 * i + 1] = q[1];
+            bf[nb][a * PS + j][2 * i] = q[0];
+            bf[nb][a * PS + j][2 * i + 1] = q[1];
           }
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mb], bfr, acc[mb][nb], 0, 0, 0);
         }
     }
   }
 
-  // the four 16-column steps of a tile; the x fragments of step s+1 are read
-  // from LDS before the MFMAs of step s, so LDS latency hides behind them
-  __device__ __forceinline__ void compute(const St& st, const unsigned char* __restrict__ sA, f32x16_t (&acc)[MB][2]) const {
+  __device__ __forceinline__ void mfma_b(const f16x8_t (&af)[MB], const f16x8_t (&bf)[2][NF],
+                                         f32x16_t (&acc)[MB][2]) const {
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mb], bf[nb][f], acc[mb][nb], 0, 0, 0);
+  }
+
+  // Scheduling of one step: its MFMAs with the next step's decode (VALU)
+  // and the A reads two steps ahead (DS) spread between them, so VALU and
+  // LDS work co-issue with the matrix pipe instead of following it.
+  static constexpr int N_MFMA = 2 * NF * MB;
+  template <int NVALU, int NDS>
+  static __device__ __forceinline__ void interleave() {
+    constexpr int per = (NVALU + N_MFMA - 1) / N_MFMA;
+#pragma unroll
+    for (int i = 0; i < N_MFMA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      if (per > 0) __builtin_amdgcn_sched_group_barrier(0x002, per, 0);  // VALU
+      if (i < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
+    }
+  }
+
+  // the four 16-column steps of a tile, software-pipelined: step s runs its
+  // MFMAs while step s+1's B fragments are decoded and its A fragments are
+  // read from LDS
+  __device__ __forceinline__ void compute(const St& st, const unsigned char* __restrict__ sA, uint32_t magic,
+                                          f32x16_t (&acc)[MB][2]) const {
+    constexpr int DEC = 2 * NF * 16;  // VALU ops of one step's decode, roughly
     f16x8_t a0[MB], a1[MB];
+    f16x8_t b0[2][NF], b1[2][NF];
     read_a(sA, 0, a0);
+    decode_b(st, 0, magic, b0);
+    __builtin_amdgcn_sched_barrier(0);
     read_a(sA, 1, a1);
-    mma_step(st, 0, a0, acc);
+    decode_b(st, 1, magic, b1);
+    mfma_b(a0, b0, acc);
+    interleave<DEC, MB>();
+    __builtin_amdgcn_sched_barrier(0);
     read_a(sA, 2, a0);
-    mma_step(st, 1, a1, acc);
+    decode_b(st, 2, magic, b0);
+    mfma_b(a1, b1, acc);
+    interleave<DEC, MB>();
+    __builtin_amdgcn_sched_barrier(0);
     read_a(sA, 3, a1);
-    mma_step(st, 2, a0, acc);
-    mma_step(st, 3, a1, acc);
+    decode_b(st, 3, magic, b1);
+    mfma_b(a0, b0, acc);
+    interleave<DEC, MB>();
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_b(a1, b1, acc);
   }
 
   // One K tile kt:
@@ -415,13 +456,14 @@ struct Pipe {
   // Loads past the last tile read 0 (buffer range checks) and land nowhere
   // that is read, so the step has no branch.
   __device__ __forceinline__ void step(int kt, const St& cur, St& nxt, unsigned char* lds, u32x4_t (&xr)[A_DMA],
-                                       f32x16_t (&acc)[MB][2]) const {
+                                       uint32_t magic, f32x16_t (&acc)[MB][2]) const {
     __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0): own LDS writes done
     __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
     store_x(lds + ((kt + 1) & 1) * (MB * 32 * 128), xr);
     issue(kt + 2, nxt, xr);
     __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
-    compute(cur, lds + (kt & 1) * (MB * 32 * 128), acc);
+    compute(cur, lds + (kt & 1) * (MB * 32 * 128), magic, acc);
   }
 };
 
@@ -440,7 +482,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l32 = lane & 31, half = lane >> 5;
 
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * STAGE_BYTES];
-  __shared__ int em_s[BM];
+  __shared__ __attribute__((aligned(16))) int em_s[BM];
   for (int i = t; i < BM; i += 256) em_s[i] = p.em[m0 + i];
 
   f32x16_t acc[MB][2];
@@ -506,29 +548,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 
   // ---- main loop, unrolled by 3 over the ring
+  uint32_t magic = 0x64006400u;
+  asm volatile("" : "+v"(magic));
   for (int kt = 0; kt < nkt; kt += 3) {
-    P.step(kt, st0, st2, lds, xr, acc);
-    if (kt + 1 < nkt) P.step(kt + 1, st1, st0, lds, xr, acc);
-    if (kt + 2 < nkt) P.step(kt + 2, st2, st1, lds, xr, acc);
+    P.step(kt, st0, st2, lds, xr, magic, acc);
+    if (kt + 1 < nkt) P.step(kt + 1, st1, st0, lds, xr, magic, acc);
+    if (kt + 2 < nkt) P.step(kt + 2, st2, st1, lds, xr, magic, acc);
   }
 
   // ---- epilogue: y = 2^(e_m + e_n) * acc, rounded to the activation dtype.
   // 32x32 accumulator layout: lane -> column l32; register r -> row
-  // 8*(r/4) + 4*half + r%4.
+  // 8*(r/4) + 4*half + r%4.  Stores go through a buffer resource over y: a
+  // column past N starts from an out-of-range offset and a row past M lands
+  // past the range, so neither is written.
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.y, (uint32_t)p.M * p.N * 2);
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int n = n0 + wave * 64 + nb * 32 + l32;
-    if (n >= p.N) continue;
-    const int e_n = p.en[n];
+    const bool nok = n < p.N;
+    const int e_n = nok ? p.en[n] : 0;
+    const uint32_t vb = nok ? ((uint32_t)(m0 + 4 * half) * p.N + n) * 2u : 0x80000000u;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int mt = mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        const int m = m0 + mt;
-        if (m < p.M) {
-          const float val = ldexpf(acc[mb][nb][r], em_s[mt] + e_n);
-          p.y[(long)m * p.N + n] = p.out_f16 ? f32_to_f16_bits(val) : f32_to_bf16_bits(val);
+      for (int rq = 0; rq < 4; ++rq) {
+        const i32x4_t e4 = *reinterpret_cast<const i32x4_t*>(&em_s[mb * 32 + 8 * rq + 4 * half]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float val = ldexpf(acc[mb][nb][4 * rq + j], e4[j] + e_n);
+          const uint16_t h = p.out_f16 ? f32_to_f16_bits(val) : f32_to_bf16_bits(val);
+          __builtin_amdgcn_raw_buffer_store_b16(h, ry, vb + (uint32_t)((mb * 32 + 8 * rq + j) * p.N) * 2u, 0, 0);
         }
       }
   }
@@ -556,7 +605,9 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 template <int BITS, int PS>
 hipError_t run(const AffineArgs& a, hipStream_t s) {
   // buffer resources address W, the scale pieces and one x tile with 32-bit offsets
-  if (a.N * a.K * BITS / 8 >= (int64_t(1) << 31) || a.K * 2 * 256 >= (int64_t(1) << 31)) return hipErrorNotSupported;
+  if (a.N * a.K * BITS / 8 >= (int64_t(1) << 31) || a.K * 2 * 256 >= (int64_t(1) << 31) ||
+      a.M * a.N * 2 >= (int64_t(1) << 31))
+    return hipErrorNotSupported;
   const int M = (int)a.M, N = (int)a.N, K = (int)a.K, G = a.G;
   const int ng = K / G;
   const int Kt = (3 * ng + 15) / 16 * 16;
