@@ -175,17 +175,18 @@ __global__ __launch_bounds__(256) void prep_x_kernel(const void* __restrict__ x,
 }
 
 // ---------------------------------------------------------------------------
-// prep_w: one wave per padded row n.  PS = number of scale pieces.
+// prep_w: one wave per padded row n.  PS = number of scale pieces; each is
+// stored twice, as an fp16 pair (s, s), ready to multiply packed code pairs.
 template <int PS>
 __global__ __launch_bounds__(256) void prep_w_kernel(const void* __restrict__ scales, int s_dt,
                                                      const void* __restrict__ biases, int b_dt, float off, int N,
-                                                     int ng, int Kt, _Float16* __restrict__ sh,
+                                                     int ng, int Kt, f16x2_t* __restrict__ sh,
                                                      uint16_t* __restrict__ tB, int* __restrict__ en) {
   const int n = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  _Float16* srow = sh + (long)n * ng * PS;
+  f16x2_t* srow = sh + (long)n * ng * PS;
   uint16_t* trow = tB + (long)n * Kt;
   if (n >= N) {
-    for (int i = lane; i < ng * PS; i += 64) srow[i] = (_Float16)0.f;
+    for (int i = lane; i < ng * PS; i += 64) srow[i] = f16x2_t{(_Float16)0.f, (_Float16)0.f};
     for (int k = lane; k < Kt; k += 64) trow[k] = 0;
     if (lane == 0) en[n] = 0;
     return;
@@ -204,7 +205,7 @@ __global__ __launch_bounds__(256) void prep_w_kernel(const void* __restrict__ sc
 #pragma unroll
     for (int j = 0; j < PS; ++j) {
       const float p = (j == PS - 1) ? r : trunc_bf16(r);
-      srow[g * PS + j] = (_Float16)p;
+      srow[g * PS + j] = f16x2_t{(_Float16)p, (_Float16)p};
       r -= p;
     }
     const float cb = fmaf(off, s, b) * sc;
@@ -225,7 +226,7 @@ struct GemmParams {
   const uint16_t* tA;
   const int* em;
   const uint32_t* w;
-  const _Float16* sh;
+  const f16x2_t* sh;
   const uint16_t* tB;
   const int* en;
   uint16_t* y;
@@ -283,7 +284,8 @@ struct Decode {
 //     bank-conflict free;
 //   * weight words and scale pieces go through buffer loads with the K
 //     offset in an SGPR, into a 3-deep register ring (two steps ahead);
-//   * the loop is unrolled by 3 so every ring index is a constant.
+//   * the loop is unrolled by 6 so every ring index and LDS stage is a
+//     constant.
 // Rows of W past N are read through per-lane offsets past the buffer's range
 // and come back as zeros, so the last row tile needs no clamping.
 
@@ -293,7 +295,7 @@ template <int BITS, int PS, int MB>
 struct Stage {
   static constexpr int WPL = BITS;  // words per lane per K tile
   uint32_t w[2][WPL];
-  uint32_t s[2][PS];  // raw fp16 bits of the scale pieces (paired at use, not at load)
+  uint32_t s[2][PS];  // scale pieces as fp16 pairs (s, s)
 };
 
 template <int BITS, int PS, int MB>
@@ -321,7 +323,9 @@ struct Pipe {
 #pragma unroll
     for (int i = 0; i < A_DMA; ++i)
       xr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, x_off, kt * (MB * 32 * 128) + i * 4096, 0));
-    const int g = (2 * kt + half) >> gsh;
+    // group of this tile: (2*kt + half) >> gsh, whose lane part (half, for
+    // G = 32 only) is folded into s_off; the rest is uniform
+    const int sg = ((2 * kt) >> gsh) * PS * 4;
     const int so = kt * WPR * 4;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
@@ -340,7 +344,7 @@ struct Pipe {
         }
       }
 #pragma unroll
-      for (int j = 0; j < PS; ++j) st.s[nb][j] = __builtin_amdgcn_raw_buffer_load_b16(rs, s_off[nb] + (g * PS + j) * 2, 0, 0);
+      for (int j = 0; j < PS; ++j) st.s[nb][j] = __builtin_amdgcn_raw_buffer_load_b32(rs, s_off[nb] + j * 4, sg, 0);
     }
   }
 
@@ -380,7 +384,7 @@ struct Pipe {
       for (int a = 0; a < D::NPIECE; ++a)
 #pragma unroll
         for (int j = 0; j < PS; ++j) {
-          f16x2_t sj = h2(st.s[nb][j] * 0x00010001u);  // (s, s)
+          f16x2_t sj = h2(st.s[nb][j]);  // (s, s)
           if (D::piece_mult(a) != 1.f) sj = sj * f16x2_t{(_Float16)16.f, (_Float16)16.f};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -455,15 +459,18 @@ struct Pipe {
   //   compute tile kt
   // Loads past the last tile read 0 (buffer range checks) and land nowhere
   // that is read, so the step has no branch.
+  // PAR = kt & 1, a compile-time constant, so the LDS stage offsets are
+  // immediates and the stores need no address register
+  template <int PAR>
   __device__ __forceinline__ void step(int kt, const St& cur, St& nxt, unsigned char* lds, u32x4_t (&xr)[A_DMA],
                                        uint32_t magic, f32x16_t (&acc)[MB][2]) const {
     __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0): own LDS writes done
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    store_x(lds + ((kt + 1) & 1) * (MB * 32 * 128), xr);
+    store_x(lds + (1 - PAR) * (MB * 32 * 128), xr);
     issue(kt + 2, nxt, xr);
     __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
-    compute(cur, lds + (kt & 1) * (MB * 32 * 128), magic, acc);
+    compute(cur, lds + PAR * (MB * 32 * 128), magic, acc);
   }
 };
 
@@ -497,7 +504,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   Pipe<BITS, PS, MB> P;
   const uint32_t row_bytes = (uint32_t)p.K * BITS / 8;
   P.rw = make_rsrc(p.w, (uint32_t)p.N * row_bytes);
-  P.rs = make_rsrc(p.sh, (uint32_t)p.Np * p.ng * PS * 2);
+  P.rs = make_rsrc(p.sh, (uint32_t)p.Np * p.ng * PS * 4);
   P.rx = make_rsrc(p.xh + (long)m0 * p.K, (uint32_t)BM * p.K * 2);  // this row tile's blocks
   P.half = half;
   P.l32 = l32;
@@ -506,7 +513,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int nb = 0; nb < 2; ++nb) {
     const uint32_t n = n0 + wave * 64 + nb * 32 + l32;
     P.w_off[nb] = n * row_bytes + half * WPL * 4;
-    P.s_off[nb] = n * (uint32_t)p.ng * PS * 2;
+    P.s_off[nb] = (n * (uint32_t)p.ng + (p.gsh == 0 ? half : 0)) * PS * 4;
   }
   // x tile chunks: thread t moves chunks q = i*256 + t, i.e. row 32i + t/8,
   // LDS position t%8, which holds source chunk (t%8)^swz(row); swz(32i + t/8)
@@ -525,8 +532,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   P.store_x(lds, xr);
   P.issue(1, st1, xr);
 
+  // ---- main loop
+  uint32_t magic = 0x64006400u;
+  asm volatile("" : "+v"(magic));
+  // unrolled by 6 = lcm(3 ring entries, 2 LDS stages): every index is static
+  for (int kt = 0; kt < nkt; kt += 6) {
+    P.template step<0>(kt, st0, st2, lds, xr, magic, acc);
+    if (kt + 1 < nkt) P.template step<1>(kt + 1, st1, st0, lds, xr, magic, acc);
+    if (kt + 2 < nkt) P.template step<0>(kt + 2, st2, st1, lds, xr, magic, acc);
+    if (kt + 3 < nkt) P.template step<1>(kt + 3, st0, st2, lds, xr, magic, acc);
+    if (kt + 4 < nkt) P.template step<0>(kt + 4, st1, st0, lds, xr, magic, acc);
+    if (kt + 5 < nkt) P.template step<1>(kt + 5, st2, st1, lds, xr, magic, acc);
+  }
+
   // ---- tail: sum_g xs * cb on bf16 MFMA, operands straight from global
-  // (L2-resident), overlapping the first x tiles' DMA
+  // (L2-resident).  It runs after the main loop so that its loads do not
+  // blur the compiler's count of outstanding loads at the loop header.
   {
     const uint16_t* tb_row[2];
 #pragma unroll
@@ -545,15 +566,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, bt[nb], acc[mb][nb], 0, 0, 0);
       }
     }
-  }
-
-  // ---- main loop, unrolled by 3 over the ring
-  uint32_t magic = 0x64006400u;
-  asm volatile("" : "+v"(magic));
-  for (int kt = 0; kt < nkt; kt += 3) {
-    P.step(kt, st0, st2, lds, xr, magic, acc);
-    if (kt + 1 < nkt) P.step(kt + 1, st1, st0, lds, xr, magic, acc);
-    if (kt + 2 < nkt) P.step(kt + 2, st2, st1, lds, xr, magic, acc);
   }
 
   // ---- epilogue: y = 2^(e_m + e_n) * acc, rounded to the activation dtype.
@@ -618,7 +630,7 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
   const size_t o_xh = 0, s_xh = align256((size_t)Mp * K * 2);
   const size_t o_ta = o_xh + s_xh, s_ta = align256((size_t)Mp * Kt * 2);
   const size_t o_em = o_ta + s_ta, s_em = align256((size_t)Mp * 4);
-  const size_t o_sh = o_em + s_em, s_sh = align256((size_t)Np * ng * PS * 2);
+  const size_t o_sh = o_em + s_em, s_sh = align256((size_t)Np * ng * PS * 4);
   const size_t o_tb = o_sh + s_sh, s_tb = align256((size_t)Np * Kt * 2);
   const size_t o_en = o_tb + s_tb, s_en = align256((size_t)Np * 4);
   const size_t total = o_en + s_en;
@@ -631,7 +643,7 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
   _Float16* xh = (_Float16*)(scratch + o_xh);
   uint16_t* tA = (uint16_t*)(scratch + o_ta);
   int* em = (int*)(scratch + o_em);
-  _Float16* sh = (_Float16*)(scratch + o_sh);
+  f16x2_t* sh = (f16x2_t*)(scratch + o_sh);
   uint16_t* tB = (uint16_t*)(scratch + o_tb);
   int* en = (int*)(scratch + o_en);
 
