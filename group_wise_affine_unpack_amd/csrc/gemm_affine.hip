@@ -283,8 +283,8 @@ struct Decode {
 //     XOR-swizzled by row ((r ^ r>>1) & 7) so the MFMA operand reads are
 //     bank-conflict free;
 //   * weight words and scale pieces go through buffer loads with the K
-//     offset in an SGPR, into a 3-deep register ring (two steps ahead);
-//   * the loop is unrolled by 6 so every ring index and LDS stage is a
+//     offset in an SGPR, into a 4-deep register ring (three steps ahead);
+//   * the loop is unrolled by 4 so every ring index and LDS stage is a
 //     constant.
 // Rows of W past N are read through per-lane offsets past the buffer's range
 // and come back as zeros, so the last row tile needs no clamping.
@@ -318,11 +318,14 @@ struct Pipe {
   // A prefetch past the last tile re-reads the last tile: every address stays
   // inside its buffer, whatever the hardware does with soffset in its range
   // check; the data is never used.
-  __device__ __forceinline__ void issue(int kt, St& st, u32x4_t (&xr)[A_DMA]) const {
+  __device__ __forceinline__ void issue_x(int kt, u32x4_t (&xr)[A_DMA]) const {
     kt = min(kt, last_kt);
 #pragma unroll
     for (int i = 0; i < A_DMA; ++i)
       xr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, x_off, kt * (MB * 32 * 128) + i * 4096, 0));
+  }
+  __device__ __forceinline__ void issue_w(int kt, St& st) const {
+    kt = min(kt, last_kt);
     // group of this tile: (2*kt + half) >> gsh, whose lane part (half, for
     // G = 32 only) is folded into s_off; the rest is uniform
     const int sg = ((2 * kt) >> gsh) * PS * 4;
@@ -468,7 +471,8 @@ struct Pipe {
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     store_x(lds + (1 - PAR) * (MB * 32 * 128), xr);
-    issue(kt + 2, nxt, xr);
+    issue_x(kt + 2, xr);   // x two tiles ahead (L2), stored next step
+    issue_w(kt + 3, nxt);  // weights three tiles ahead (HBM), used in three steps
     __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
     compute(cur, lds + PAR * (MB * 32 * 128), magic, acc);
   }
@@ -526,23 +530,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   const int nkt = p.K / BK;
   P.last_kt = nkt - 1;
-  St st0, st1, st2;
+  St st0, st1, st2, st3;
   u32x4_t xr[MB];
-  P.issue(0, st0, xr);
+  P.issue_x(0, xr);
+  P.issue_w(0, st0);
+  P.issue_w(1, st1);
+  P.issue_w(2, st2);
   P.store_x(lds, xr);
-  P.issue(1, st1, xr);
+  P.issue_x(1, xr);
 
   // ---- main loop
   uint32_t magic = 0x64006400u;
   asm volatile("" : "+v"(magic));
-  // unrolled by 6 = lcm(3 ring entries, 2 LDS stages): every index is static
-  for (int kt = 0; kt < nkt; kt += 6) {
-    P.template step<0>(kt, st0, st2, lds, xr, magic, acc);
+  // unrolled by 4 = lcm(4 ring entries, 2 LDS stages): every index is static
+  for (int kt = 0; kt < nkt; kt += 4) {
+    P.template step<0>(kt, st0, st3, lds, xr, magic, acc);
     if (kt + 1 < nkt) P.template step<1>(kt + 1, st1, st0, lds, xr, magic, acc);
     if (kt + 2 < nkt) P.template step<0>(kt + 2, st2, st1, lds, xr, magic, acc);
-    if (kt + 3 < nkt) P.template step<1>(kt + 3, st0, st2, lds, xr, magic, acc);
-    if (kt + 4 < nkt) P.template step<0>(kt + 4, st1, st0, lds, xr, magic, acc);
-    if (kt + 5 < nkt) P.template step<1>(kt + 5, st2, st1, lds, xr, magic, acc);
+    if (kt + 3 < nkt) P.template step<1>(kt + 3, st3, st2, lds, xr, magic, acc);
   }
 
   // ---- tail: sum_g xs * cb on bf16 MFMA, operands straight from global
