@@ -628,7 +628,13 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
   const int M = (int)a.M, N = (int)a.N, K = (int)a.K, G = a.G;
   const int ng = K / G;
   const int Kt = (3 * ng + 15) / 16 * 16;
-  const int MB = M <= 64 ? 2 : 8;
+  // the largest row tile whose grid still gives every CU a workgroup
+  int MB = 2;
+  if (M > 64) {
+    const int64_t tn = (N + BN - 1) / BN;
+    if ((int64_t)((M + 255) / 256) * tn >= 256) MB = 8;
+    else if ((int64_t)((M + 127) / 128) * tn >= 256) MB = 4;
+  }
   const int BM = MB * 32;
   const int Mp = (M + BM - 1) / BM * BM, Np = (N + BN - 1) / BN * BN;
 
@@ -680,6 +686,8 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
   const dim3 grid(8 * p.per_xcd);
   if (MB == 2)
     hipLaunchKernelGGL((gemm_affine_kernel<BITS, PS, 2>), grid, dim3(256), 0, s, p);
+  else if (MB == 4)
+    hipLaunchKernelGGL((gemm_affine_kernel<BITS, PS, 4>), grid, dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL((gemm_affine_kernel<BITS, PS, 8>), grid, dim3(256), 0, s, p);
   e = hipGetLastError();
