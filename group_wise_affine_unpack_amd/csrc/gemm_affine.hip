@@ -20,9 +20,10 @@
 // hi/lo bf16 splits of xs and cb.  Everything accumulates in one fp32 tile.
 //
 // Kernels:
-//   prep_x  : per row of x: e_m, xh (fp16, permuted to the code decode order,
-//             read through k_perm when given), tail A = [xs_hi, xs_hi, xs_lo]
-//   prep_w  : per row of W: e_n, scale pieces s_j (fp16), tail B = [cb_hi, cb_lo, cb_hi]
+//   prep    : one launch, two halves.  Per row of x: e_m, xh (fp16, permuted
+//             to the code decode order, read through k_perm when given), tail
+//             A = [xs_hi, xs_hi, xs_lo].  Per row of W: e_n, scale pieces s_j
+//             (fp16 pairs), tail B = [cb_hi, cb_lo, cb_hi]
 //   gemm    : 256 threads, tile BM x 256 (4 waves along N, each BM x 64);
 //             x tiles double-buffered in LDS, stored one step ahead; packed codes go from
 //             global memory straight to registers, are decoded with the
@@ -81,12 +82,12 @@ __device__ __forceinline__ int exp_of(float v) {
 // contiguous 16 KiB..32 KiB piece, row r of it at r*64 elements, so a GEMM
 // step reads a single contiguous block.
 template <int BITS>
-__global__ __launch_bounds__(256) void prep_x_kernel(const void* __restrict__ x, int act_dt,
-                                                     const int32_t* __restrict__ k_perm, int M, int K, int G,
-                                                     int Kt, int BM, _Float16* __restrict__ xh,
-                                                     uint16_t* __restrict__ tA, int* __restrict__ em) {
+__device__ __forceinline__ void prep_x_row(int m, const void* __restrict__ x, int act_dt,
+                                           const int32_t* __restrict__ k_perm, int M, int K, int G, int Kt, int BM,
+                                           _Float16* __restrict__ xh, uint16_t* __restrict__ tA,
+                                           int* __restrict__ em) {
   constexpr int BLK = Perm<BITS>::BLK;
-  const int m = blockIdx.x, t = threadIdx.x;
+  const int t = threadIdx.x;
   const int ng = K / G;
   const int nkt = K / 64;
   // element (m, k) of xh sits at xrow[(k/64)*BM*64 + k%64]
@@ -178,11 +179,11 @@ __global__ __launch_bounds__(256) void prep_x_kernel(const void* __restrict__ x,
 // prep_w: one wave per padded row n.  PS = number of scale pieces; each is
 // stored twice, as an fp16 pair (s, s), ready to multiply packed code pairs.
 template <int PS>
-__global__ __launch_bounds__(256) void prep_w_kernel(const void* __restrict__ scales, int s_dt,
-                                                     const void* __restrict__ biases, int b_dt, float off, int N,
-                                                     int ng, int Kt, f16x2_t* __restrict__ sh,
-                                                     uint16_t* __restrict__ tB, int* __restrict__ en) {
-  const int n = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+__device__ __forceinline__ void prep_w_rows(int blk, const void* __restrict__ scales, int s_dt,
+                                            const void* __restrict__ biases, int b_dt, float off, int N, int ng,
+                                            int Kt, f16x2_t* __restrict__ sh, uint16_t* __restrict__ tB,
+                                            int* __restrict__ en) {
+  const int n = blk * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   f16x2_t* srow = sh + (long)n * ng * PS;
   uint16_t* trow = tB + (long)n * Kt;
   if (n >= N) {
@@ -216,6 +217,33 @@ __global__ __launch_bounds__(256) void prep_w_kernel(const void* __restrict__ sc
     trow[3 * g + 2] = hi;
   }
   for (int k = 3 * ng + lane; k < Kt; k += 64) trow[k] = 0;
+}
+
+// prep_x and prep_w in one launch: blocks [0, Mp) take the rows of x, the
+// rest take four rows of W each; the two halves run side by side.
+struct PrepArgs {
+  const void* x;
+  const int32_t* k_perm;
+  const void* scales;
+  const void* biases;
+  _Float16* xh;
+  uint16_t* tA;
+  int* em;
+  f16x2_t* sh;
+  uint16_t* tB;
+  int* en;
+  float off;
+  int act_dt, s_dt, b_dt;
+  int M, N, K, G, Kt, BM, Mp, ng;
+};
+
+template <int BITS, int PS>
+__global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
+  const int b = blockIdx.x;
+  if (b < a.Mp)
+    prep_x_row<BITS>(b, a.x, a.act_dt, a.k_perm, a.M, a.K, a.G, a.Kt, a.BM, a.xh, a.tA, a.em);
+  else
+    prep_w_rows<PS>(b - a.Mp, a.scales, a.s_dt, a.biases, a.b_dt, a.off, a.N, a.ng, a.Kt, a.sh, a.tB, a.en);
 }
 
 // ---------------------------------------------------------------------------
@@ -658,9 +686,30 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
   uint16_t* tB = (uint16_t*)(scratch + o_tb);
   int* en = (int*)(scratch + o_en);
 
-  hipLaunchKernelGGL((prep_x_kernel<BITS>), dim3(Mp), dim3(256), 0, s, a.x, a.act_dt, a.k_perm, M, K, G, Kt, BM, xh, tA, em);
-  hipLaunchKernelGGL((prep_w_kernel<PS>), dim3(Np / 4), dim3(256), 0, s, a.scales, a.s_dt, a.biases, a.b_dt,
-                     Decode<BITS>::OFFQ, N, ng, Kt, sh, tB, en);
+  PrepArgs pa;
+  pa.x = a.x;
+  pa.k_perm = a.k_perm;
+  pa.scales = a.scales;
+  pa.biases = a.biases;
+  pa.xh = xh;
+  pa.tA = tA;
+  pa.em = em;
+  pa.sh = sh;
+  pa.tB = tB;
+  pa.en = en;
+  pa.off = Decode<BITS>::OFFQ;
+  pa.act_dt = a.act_dt;
+  pa.s_dt = a.s_dt;
+  pa.b_dt = a.b_dt;
+  pa.M = M;
+  pa.N = N;
+  pa.K = K;
+  pa.G = G;
+  pa.Kt = Kt;
+  pa.BM = BM;
+  pa.Mp = Mp;
+  pa.ng = ng;
+  hipLaunchKernelGGL((prep_kernel<BITS, PS>), dim3(Mp + Np / 4), dim3(256), 0, s, pa);
 
   GemmParams p;
   p.xh = xh;
