@@ -17,7 +17,8 @@ with almost no launch gaps.  In the same JSON line:
   per_linear     one qmm_affine launch per linear: 112 launches
   cfg0_hot       the single 2048x2048 linear relaunched on the same weights
                  (cache-resident: NOT an HBM figure)
-  gemm_m2048     prefill GEMM, M=2048 K=4096 N=14336, 4- and 8-bit, TFLOP/s
+  gemm_m2048     prefill GEMM of an 8B decoder, M=2048: K=4096 with N = 4096,
+                 1024, 14336 and K=14336 with N=4096, 4- and 8-bit, TFLOP/s
                  against the bf16 dense MFMA peak
   w4a8_m2048     W4A8 GEMM (quantize + int8 MFMA), M=2048 N=4096 K=1024
   roofline       the grouped GEMV kernel of the headline step
@@ -174,7 +175,7 @@ class Decode:
                 self.qa.qmm_affine(self.x[d["K"]], d["w"], d["s"], d["b"], G, BITS, out=self.y[l][i])
 
 
-def time_gemm(torch, qa, si, device, bits, N=14336, K=4096, M=2048, iters=20, warmup=5):
+def time_gemm(torch, qa, si, device, bits, N=14336, K=4096, M=2048, iters=50, warmup=10):
     case = si.cfg2_case(N, K, bits, M=M, seed=(2, N, K))
     x = torch.from_numpy(case.x.view(np.int16)).view(torch.bfloat16).to(device)
     w = torch.from_numpy(case.packed.view(np.int32)).to(device)
@@ -318,8 +319,9 @@ def main():
     qa.lib()
 
     if args.skip_gemv:
-        for bits in (4, 8):
-            print(json.dumps({"gemm_m2048": time_gemm(torch, qa, si, device, bits)}), flush=True)
+        for bits in si.CFG2_BITS:
+            for N, K in si.CFG2_SHAPES:
+                print(json.dumps({"gemm_m2048": time_gemm(torch, qa, si, device, bits, N=N, K=K)}), flush=True)
         print(json.dumps({"w4a8_m2048": time_w4a8(torch, qa, si, device)}), flush=True)
         return
 
@@ -347,7 +349,7 @@ def main():
 
     gemm = w4a8 = None
     if not args.no_gemm:
-        gemm = [time_gemm(torch, qa, si, device, 4), time_gemm(torch, qa, si, device, 8)]
+        gemm = [time_gemm(torch, qa, si, device, bits, N=N, K=K) for bits in si.CFG2_BITS for N, K in si.CFG2_SHAPES]
         w4a8 = time_w4a8(torch, qa, si, device)
         for g in gemm:
             print(f"[bench] gemm b{g['bits']}: {g['us_per_call']} us, {g['tflops']} TFLOP/s", file=sys.stderr,

@@ -90,6 +90,9 @@ struct AffineArgs {
   int act_dt, s_dt, b_dt;
 };
 
+// keep stream-ordered scratch in the device pool between calls
+void keep_pool_memory(hipStream_t s);
+
 hipError_t launch_gemv_affine(const AffineArgs& a, hipStream_t s);
 // count problems that share M, G, bits and dtypes, in as few launches as possible
 hipError_t launch_gemv_grouped(const AffineArgs* probs, int count, hipStream_t s);

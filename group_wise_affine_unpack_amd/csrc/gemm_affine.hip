@@ -630,21 +630,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 // ---------------------------------------------------------------------------
 
-std::once_flag g_pool_once[64];
-
-void keep_pool_memory(hipStream_t s) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return;
-  std::call_once(g_pool_once[dev], [dev] {
-    hipMemPool_t pool;
-    if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
-      uint64_t thr = UINT64_MAX;  // keep freed scratch in the pool instead of returning it
-      (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
-    }
-  });
-  (void)s;
-}
-
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 template <int BITS, int PS>
@@ -754,6 +739,23 @@ hipError_t run_bits(const AffineArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+static std::once_flag g_pool_once[64];
+
+// Stream-ordered scratch comes from the device's default pool; keep what is
+// freed there instead of returning it to the driver after every call.
+void keep_pool_memory(hipStream_t s) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return;
+  std::call_once(g_pool_once[dev], [dev] {
+    hipMemPool_t pool;
+    if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+      uint64_t thr = UINT64_MAX;  // keep freed scratch in the pool instead of returning it
+      (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+    }
+  });
+  (void)s;
+}
 
 hipError_t launch_gemm_affine(const AffineArgs& a, hipStream_t s) {
   // whole 64-code K tiles only; otherwise the GEMV kernel runs on slices of
