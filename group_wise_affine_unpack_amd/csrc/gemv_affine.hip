@@ -29,6 +29,8 @@
 //    problems and each finds its own by a binary search over the descriptor
 //    table, which travels in the kernel arguments.  Linears that share an
 //    input (q/k/v, gate/up), or a whole set of them, then cost one launch.
+#include <type_traits>
+
 #include "common.h"
 
 namespace qaff {
@@ -412,6 +414,305 @@ __global__ __launch_bounds__(256) void gemv_affine_kernel(GemvBatch B) {
   }  // passes over x rows
 }
 
+// ---------------------------------------------------------------------------
+// Skinny MFMA path: 4-bit codes, 2 <= M <= 16, 16-bit scales and biases.
+// A dot2 GEMV spends one VALU op per code and per x row, so with several x
+// rows it is bound by VALU, not by HBM.  Here the x rows (padded to 16) are
+// the A operand of v_mfma_f32_16x16x32_{bf16,f16} and the codes, as
+// exponent-bias values (code | 0x4300 = 128 + code in bf16, code | 0x6400 =
+// 1024 + code in f16), the B operand, so a code costs well under one VALU op
+// whatever M is.
+//   * Every MFMA covers 32 codes of one group, so its result is scaled once:
+//     y += s * sum(x * (off + q)) + (b - off * s) * X_g, with X_g the group
+//     sums of x from one more MFMA against an all-ones B.
+//   * A workgroup owns 64 columns and walks K in stages of 512 codes.  The
+//     packed words of a stage (64 rows x 256 bytes) are loaded with every
+//     wave-level load covering whole 128-byte lines (4 rows x 256 bytes)
+//     into registers, three stages ahead, and written to LDS the stage
+//     before their use; the fragments are read back from LDS.  A load
+//     shaped like the MFMA operand (16 rows x 16-64 bytes per instruction)
+//     reaches well under half the bandwidth.  Scales and biases take the
+//     same route, two lanes per row.
+//   * Wave w takes span w (codes 128w .. 128w+127) of every stage for all 64
+//     columns (four 16-column blocks, one shared x fragment), and the four
+//     partial sums are added through LDS at the end.
+//   * In a span, lane (c, h) = (lane % 16, lane / 16) of block nb holds
+//     column nb*16 + c and words h*wpg .. h*wpg + wpg - 1 of every group
+//     (wpg = G / 32): MFMA j of a group takes word h*wpg + j, the x fragment
+//     of row c comes from the same 8 columns, in the decode's pair order.
+//   * LDS holds three stages in a ring; rows are 256 bytes with the 16-byte
+//     pieces XOR-swizzled by row, so the 16 columns of a fragment read hit
+//     16 different bank groups.
+//   * Accumulator layout of the 16x16 MFMA: lane (c, h) holds column c and
+//     rows 4h .. 4h+3.
+struct MfmaDesc {
+  const void* x;  // [M, K] activations
+  const void* w;  // [N, K/8] uint32
+  const void* s;  // [N, K/G] 16-bit
+  const void* b;  // [N, K/G] 16-bit
+  void* y;        // [M, N]
+  int N, K, blk0, pad;
+};
+struct MfmaBatch {
+  MfmaDesc d[MAXP];
+  int count, M;
+};
+static_assert(sizeof(MfmaBatch) <= 4096, "kernel arguments are limited to 4 KiB");
+
+template <int G>
+struct MfmaGeo {
+  static constexpr int GPS = 128 / G, WPG = G / 32;
+  static constexpr int PBR = 1024 / G;  // parameter bytes per row and stage
+  static constexpr int PRM = 64 * PBR;  // one parameter of a stage
+  static constexpr int WB = 64 * 256;   // packed words of a stage
+  static constexpr int STAGE = WB + 2 * PRM;
+  // word of the span used by lane quarter h in MFMA j
+  __device__ static constexpr int word(int h, int j) {
+    return G == 128 ? 4 * h + j : (G == 64 ? (j >> 1) * 8 + 2 * h + (j & 1) : 4 * j + h);
+  }
+};
+// a wave's share of a stage in registers: four 16-byte pieces of packed
+// words and PBR / 2 bytes of a parameter slice
+template <int G> struct WSlice {
+  u32x4_t w[4];
+  uint32_t p[1024 / G / 8 > 1 ? 1024 / G / 8 : 1];
+};
+
+// Stage t of the MFMA GEMV: write stage t+1 (loaded two stages ago) to LDS,
+// barrier (stage t+1 is in LDS, stage t was written a stage ago, and every
+// wave is done with stage t-2, whose buffer stage t+1 reuses), issue the
+// loads of stage t+3 and the x fragments of stage t+2, compute stage t.
+template <class Put, class IssueW, class IssueX, class Compute, class W, class X>
+__device__ __forceinline__ void mfma_stage(Put& put, IssueW& issue_w, IssueX& issue_x, Compute& compute, int t,
+                                           bool active, const unsigned char* cur, const X& xc, unsigned char* nxt,
+                                           const W& wn, W& wf, X& xf) {
+  put(nxt, wn);
+  __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  issue_w(t + 3, wf);
+  issue_x(t + 2, xf);
+  __builtin_amdgcn_sched_barrier(0);
+  if (active) compute(cur, xc);
+}
+
+template <bool F16, int G>
+__global__ __launch_bounds__(256, 2) void gemv_mfma4_kernel(MfmaBatch B) {
+  using Geo = MfmaGeo<G>;
+  constexpr int NB = 4, GPS = Geo::GPS, WPG = Geo::WPG, PBR = Geo::PBR;
+  using frag_t = typename std::conditional<F16, f16x8_t, bf16x8_t>::type;
+  using X = u32x4_t[4];
+  using W = WSlice<G>;
+  constexpr float OFF = F16 ? 1024.f : 128.f;
+  __shared__ __attribute__((aligned(1024))) unsigned char st0[Geo::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st1[Geo::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st2[Geo::STAGE];
+
+  const int bid = blockIdx.x;
+  int lo = 0, hi = B.count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (B.d[mid].blk0 <= bid) lo = mid; else hi = mid - 1;
+  }
+  const MfmaDesc& D = B.d[lo];
+  const int N = D.N, K = D.K, M = B.M;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col0 = (bid - D.blk0) * 64;
+  const int c = lane & 15, h = lane >> 4;
+  const int L = K >> 3, ng = K / G, nsp = K >> 7, nst = (K + 511) >> 9;
+  const int ncols = min(N - col0, 64);
+
+  // Packed words: rows 16i + 4*wave + lane/16 (i < 4), piece lane % 16 of
+  // the stage's 256 bytes, stored to LDS slot piece ^ (row % 16).  Rows past
+  // N are out of range; a piece past the row end reads the next row.
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(static_cast<const uint32_t*>(D.w) + (long)col0 * L, (uint32_t)(ncols * L * 4));
+  const int wrow = 4 * wave + (lane >> 4);
+  const uint32_t wv = (uint32_t)(wrow * L * 4 + (lane & 15) * 16);
+  const int wdst = wrow * 256 + (((lane & 15) ^ (wrow & 15)) << 4);  // + i*16*256
+  // Scales (waves 0, 1) or biases (waves 2, 3) of rows 32*(wave&1) + lane/2,
+  // half lane&1 of the row's PBR bytes.
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(
+      static_cast<const uint16_t*>((wave >> 1) ? D.b : D.s) + (long)col0 * ng, (uint32_t)(ncols * ng * 2));
+  const int prow = 32 * (wave & 1) + (lane >> 1);
+  const uint32_t pv = (uint32_t)(prow * ng * 2 + (lane & 1) * (PBR / 2));
+  const int pdst = Geo::WB + (wave >> 1) * Geo::PRM + prow * PBR + (lane & 1) * (PBR / 2);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(D.x, (uint32_t)(M * K * 2));
+  const uint32_t xv = c < M ? (uint32_t)(c * K * 2) : OOB;
+
+  // loads of stage tw's packed words and parameter slice; a stage past the
+  // end loads nothing (offsets out of range)
+  auto issue_w = [&](int tw, W& wr) __attribute__((always_inline)) {
+    const uint32_t wo = (tw < nst ? wv : OOB) + (uint32_t)tw * 256u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wr.w[i] = ld128(rw, wo + (uint32_t)(16 * i * L * 4));
+    const uint32_t po = (tw < nst ? pv : OOB) + (uint32_t)tw * PBR;
+    if constexpr (PBR / 2 == 16) {
+      const u32x4_t v = ld128(rp, po);
+      wr.p[0] = v[0]; wr.p[1] = v[1]; wr.p[2] = v[2]; wr.p[3] = v[3];
+    } else if constexpr (PBR / 2 == 8) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rp, po, 0, 0);
+      wr.p[0] = v[0]; wr.p[1] = v[1];
+    } else {
+      wr.p[0] = ld32(rp, po);
+    }
+  };
+  // x fragments of span 4*tx + wave
+  auto issue_x = [&](int tx, X& xr) __attribute__((always_inline)) {
+    const int sp = 4 * tx + wave;
+    const uint32_t xo = (sp < nsp ? xv : OOB) + (uint32_t)sp * 256u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xr[j] = ld128(rx, xo + Geo::word(h, j) * 16);
+  };
+  auto put = [&](unsigned char* st, const W& wr) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(st + wdst + i * 16 * 256) = wr.w[i];
+    if constexpr (PBR / 2 == 16) {
+      *reinterpret_cast<u32x4_t*>(st + pdst) = u32x4_t{wr.p[0], wr.p[1], wr.p[2], wr.p[3]};
+    } else if constexpr (PBR / 2 == 8) {
+      *reinterpret_cast<uint2*>(st + pdst) = uint2{wr.p[0], wr.p[1]};
+    } else {
+      *reinterpret_cast<uint32_t*>(st + pdst) = wr.p[0];
+    }
+  };
+
+  uint32_t magic = F16 ? 0x64006400u : 0x43004300u;
+  asm volatile("" : "+v"(magic));
+  const uint32_t ones = F16 ? 0x3C003C00u : 0x3F803F80u;
+  const frag_t onesf = __builtin_bit_cast(frag_t, u32x4_t{ones, ones, ones, ones});
+  f32x4_t y[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) y[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const unsigned char* st, const X& xr) __attribute__((always_inline)) {
+    // packed words of the span for the four blocks
+    u32x4_t wq[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const unsigned char* row = st + (nb * 16 + c) * 256;
+      if constexpr (G == 128) {
+        wq[nb] = *reinterpret_cast<const u32x4_t*>(row + (((4 * wave + h) ^ c) << 4));
+      } else if constexpr (G == 64) {
+        const uint2 a = *reinterpret_cast<const uint2*>(row + (((4 * wave + (h >> 1)) ^ c) << 4) + (h & 1) * 8);
+        const uint2 b = *reinterpret_cast<const uint2*>(row + (((4 * wave + 2 + (h >> 1)) ^ c) << 4) + (h & 1) * 8);
+        wq[nb] = u32x4_t{a.x, a.y, b.x, b.y};
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          wq[nb][j] = *reinterpret_cast<const uint32_t*>(row + (((4 * wave + j) ^ c) << 4) + h * 4);
+      }
+    }
+    // the span's GPS scales and biases of column nb*16 + c
+    uint32_t sp_[NB][2], bp_[NB][2];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const unsigned char* ps = st + Geo::WB + (nb * 16 + c) * PBR + 2 * GPS * wave;
+      const unsigned char* pb = ps + Geo::PRM;
+      if constexpr (GPS == 4) {
+        const uint2 a = *reinterpret_cast<const uint2*>(ps), b = *reinterpret_cast<const uint2*>(pb);
+        sp_[nb][0] = a.x; sp_[nb][1] = a.y; bp_[nb][0] = b.x; bp_[nb][1] = b.y;
+      } else if constexpr (GPS == 2) {
+        sp_[nb][0] = *reinterpret_cast<const uint32_t*>(ps); bp_[nb][0] = *reinterpret_cast<const uint32_t*>(pb);
+        sp_[nb][1] = 0; bp_[nb][1] = 0;
+      } else {
+        sp_[nb][0] = *reinterpret_cast<const uint16_t*>(ps); bp_[nb][0] = *reinterpret_cast<const uint16_t*>(pb);
+        sp_[nb][1] = 0; bp_[nb][1] = 0;
+      }
+    }
+#pragma unroll
+    for (int gi = 0; gi < GPS; ++gi) {
+      f32x4_t xs = {0.f, 0.f, 0.f, 0.f};
+      f32x4_t a[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) a[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jj = 0; jj < WPG; ++jj) {
+        const int j = gi * WPG + jj;
+        const u32x4_t rr = xr[j];
+        const frag_t af = __builtin_bit_cast(
+            frag_t, u32x4_t{pair_lo(rr[0], rr[2]), pair_hi(rr[0], rr[2]), pair_lo(rr[1], rr[3]), pair_hi(rr[1], rr[3])});
+        if constexpr (F16)
+          xs = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, onesf, xs, 0, 0, 0);
+        else
+          xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, onesf, xs, 0, 0, 0);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const uint32_t wd = wq[nb][j];
+          const frag_t bf = __builtin_bit_cast(
+              frag_t, u32x4_t{(wd & 0x000F000Fu) | magic, ((wd >> 4) & 0x000F000Fu) | magic,
+                              ((wd >> 8) & 0x000F000Fu) | magic, ((wd >> 12) & 0x000F000Fu) | magic});
+          if constexpr (F16)
+            a[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, a[nb], 0, 0, 0);
+          else
+            a[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, a[nb], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint32_t sh = (sp_[nb][gi >> 1] >> (16 * (gi & 1))) & 0xFFFFu;
+        const uint32_t bh = (bp_[nb][gi >> 1] >> (16 * (gi & 1))) & 0xFFFFu;
+        const float sv = F16 ? f16_bits_to_f32(sh) : bf16_bits_to_f32(sh);
+        const float bv = fmaf(-OFF, sv, F16 ? f16_bits_to_f32(bh) : bf16_bits_to_f32(bh));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[nb][i] = fmaf(sv, a[nb][i], fmaf(bv, xs[i], y[nb][i]));
+      }
+    }
+  };
+
+  // three stages in a ring, unrolled so that every buffer is static
+  X x0, x1, x2;
+  W w0, w1, w2;
+  // the prologue keeps the loop's load order, so that the wait counts the
+  // compiler derives at the loop head hold for both ways in
+  issue_w(0, w0);
+  issue_x(0, x0);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_w(1, w1);
+  issue_x(1, x1);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_w(2, w2);
+  __builtin_amdgcn_sched_barrier(0);
+  put(st0, w0);
+  // whole rounds of three stages: a stage past the end loads nothing and
+  // computes nothing, and the loop body has no branch around a stage
+  for (int t = 0; t < nst; t += 3) {
+    mfma_stage(put, issue_w, issue_x, compute, t, 4 * t + wave < nsp, st0, x0, st1, w1, w0, x2);
+    mfma_stage(put, issue_w, issue_x, compute, t + 1, 4 * t + 4 + wave < nsp, st1, x1, st2, w2, w1, x0);
+    mfma_stage(put, issue_w, issue_x, compute, t + 2, 4 * t + 8 + wave < nsp, st2, x2, st0, w0, w2, x1);
+  }
+
+  // the four waves' partial sums: block nb is finished by wave nb
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(st0);  // [wave][nb][i][lane]
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[((wave * NB + nb) * 4 + i) * 64 + lane] = y[nb][i];
+  __syncthreads();
+  const int col = wave * 16 + c;
+  if (col >= ncols) return;
+  uint16_t* yo = static_cast<uint16_t*>(D.y);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * h + i;
+    float v = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v += red[((q * NB + wave) * 4 + i) * 64 + lane];
+    if (row < M) yo[(long)row * N + col0 + col] = f32_to_act_bits(v, F16);
+  }
+}
+
+template <bool F16>
+void launch_mfma4(int G, dim3 grid, hipStream_t s, const MfmaBatch& b) {
+  if (G == 32) gemv_mfma4_kernel<F16, 32><<<grid, dim3(256), 0, s>>>(b);
+  else if (G == 64) gemv_mfma4_kernel<F16, 64><<<grid, dim3(256), 0, s>>>(b);
+  else gemv_mfma4_kernel<F16, 128><<<grid, dim3(256), 0, s>>>(b);
+}
+
+// x rows from which the MFMA kernel beats the dot2 one
+constexpr int MFMA_MIN_M = 2;
+
 template <int BITS, bool F16, int MT, int R>
 void launch_r(const GemvBatch& b, int blocks, int sbm, hipStream_t s) {
   if (sbm == 0)
@@ -477,6 +778,34 @@ hipError_t launch_gemv_grouped(const AffineArgs* probs, int count, hipStream_t s
       blocks += nblk;
     }
     if (blocks == 0) continue;
+    // 4-bit codes with several x rows, K a multiple of 512, 16-bit scales
+    // and biases of the activation type and no column permutation: the
+    // skinny MFMA kernel
+    bool mfma = bits == 4 && M >= MFMA_MIN_M && sbm != 2 && (a0.G == 32 || a0.G == 64 || a0.G == 128);
+    for (int i = 0; mfma && i < b.count; ++i) {
+      const GemvDesc& d = b.d[i];
+      // whole 512-code stages keep every parameter slice load aligned
+      mfma = d.kp == nullptr && d.K % 512 == 0 && (int64_t)d.K * 32 < (int64_t(1) << 31) &&
+             (((uintptr_t)d.w | (uintptr_t)d.s | (uintptr_t)d.b) & 15) == 0;
+    }
+    if (mfma) {
+      MfmaBatch bm{};
+      bm.count = b.count;
+      bm.M = M;
+      int64_t mblocks = 0;
+      for (int i = 0; i < b.count; ++i) {
+        const GemvDesc& d = b.d[i];
+        MfmaDesc& e = bm.d[i];
+        e.x = d.x; e.w = d.w; e.s = d.s; e.b = d.b; e.y = d.y;
+        e.N = d.N; e.K = d.K; e.blk0 = (int)mblocks;
+        mblocks += (d.N + 63) / 64;
+      }
+      if (f16) launch_mfma4<true>((int)a0.G, dim3((unsigned)mblocks), s, bm);
+      else launch_mfma4<false>((int)a0.G, dim3((unsigned)mblocks), s, bm);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      continue;
+    }
     switch (bits) {
       case 2: f16 ? launch_bits<2, true>(b, (int)blocks, sbm, R, s) : launch_bits<2, false>(b, (int)blocks, sbm, R, s); break;
       case 4: f16 ? launch_bits<4, true>(b, (int)blocks, sbm, R, s) : launch_bits<4, false>(b, (int)blocks, sbm, R, s); break;

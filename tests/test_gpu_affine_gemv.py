@@ -194,3 +194,47 @@ def test_grouped_mixed_k_m1():
     ys = _grouped(cases)
     for c, y in zip(cases, ys):
         assert_float_bar(y, oracle.qmm_affine_case(c), c.name)
+
+
+@pytest.mark.parametrize("K", [512, 1536, 2560, 8192])
+@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+@pytest.mark.parametrize("M", [2, 9, 16])
+def test_4bit_several_rows_matrix_core_path(K, G, M, act):
+    # 4-bit codes with 2..16 x rows and K a multiple of 512 take the MFMA
+    # kernel: 1, 3, 5 and 16 stages of 512 codes (5 leaves the last round of
+    # three with an empty stage), ragged N leaves a partly filled 64-column
+    # tile
+    case = si.affine_case(M, 333, K, G, 4, seed=(29, K, G, M), act_dtype=act, name=f"mfma_M{M}_K{K}_G{G}_{act}")
+    y = _run(case)
+    assert_float_bar(y, oracle.qmm_affine_case(case), case.name)
+
+
+@pytest.mark.parametrize("sdt,bdt", [("f32", "f32"), ("f16", "f32"), ("bf16", "bf16")])
+@pytest.mark.parametrize("G", [32, 128])
+def test_matrix_core_path_scale_bias_dtypes(sdt, bdt, G):
+    case = si.affine_case(16, 200, 1024, G, 4, seed=(30, G), sb_dtype=sdt, name=f"mfma_sb_{sdt}_{bdt}_G{G}")
+    if bdt != sdt:
+        case.biases = si.store(si.bits_to_f32(case.biases, sdt), bdt)
+        case.bias_dtype = bdt
+    y = _run(case)
+    assert_float_bar(y, oracle.qmm_affine_case(case), case.name)
+
+
+def test_matrix_core_path_extreme_codes():
+    # all codes 0 or all 15 over long rows: the offset values 128 + q (bf16)
+    # and 1024 + q (f16) must cancel against the group sums of x accurately
+    for act in ("bf16", "f16"):
+        for word in (0x00000000, 0xFFFFFFFF):
+            case = si.affine_case(16, 130, 8192, 64, 4, seed=(31,), act_dtype=act, name=f"mfma_{act}_{word:#x}")
+            case.packed[:] = np.uint32(word)
+            y = _run(case)
+            assert_float_bar(y, oracle.qmm_affine_case(case), case.name)
+
+
+@pytest.mark.parametrize("K", [128, 384, 2112])
+def test_several_rows_k_not_multiple_of_512(K):
+    # the MFMA kernel needs whole 512-code stages; the dot2 kernel runs
+    case = si.affine_case(8, 100, K, 64, 4, seed=(32, K), name=f"m8_K{K}")
+    y = _run(case)
+    assert_float_bar(y, oracle.qmm_affine_case(case), case.name)
