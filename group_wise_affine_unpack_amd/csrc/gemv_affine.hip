@@ -440,7 +440,7 @@ __global__ __launch_bounds__(256) void gemv_affine_kernel(GemvBatch B) {
 //     column nb*16 + c and words h*wpg .. h*wpg + wpg - 1 of every group
 //     (wpg = G / 32): MFMA j of a group takes word h*wpg + j, the x fragment
 //     of row c comes from the same 8 columns, in the decode's pair order.
-//   * LDS holds three stages in a ring; rows are 256 bytes with the 16-byte
+//   * LDS holds four stages in a ring; rows are 256 bytes with the 16-byte
 //     pieces XOR-swizzled by row, so the 16 columns of a fragment read hit
 //     16 different bank groups.
 //   * Accumulator layout of the 16x16 MFMA: lane (c, h) holds column c and
@@ -462,30 +462,27 @@ static_assert(sizeof(MfmaBatch) <= 4096, "kernel arguments are limited to 4 KiB"
 template <int G>
 struct MfmaGeo {
   static constexpr int GPS = 128 / G, WPG = G / 32;
-  static constexpr int PBR = 1024 / G;  // parameter bytes per row and stage
-  static constexpr int PRM = 64 * PBR;  // one parameter of a stage
-  static constexpr int WB = 64 * 256;   // packed words of a stage
-  static constexpr int STAGE = WB + 2 * PRM;
+  static constexpr int STAGE = 64 * 256;  // packed words of a stage
+  // Scales and biases arrive in chunks of 128 bytes (64 groups) per row,
+  // CS stages, into one LDS region [parameter][row][128 bytes] whose 16-byte
+  // pieces are XOR-swizzled by row.
+  static constexpr int CS = 64 * G / 512;
+  static constexpr int PREG = 2 * 64 * 128;
   // word of the span used by lane quarter h in MFMA j
   __device__ static constexpr int word(int h, int j) {
     return G == 128 ? 4 * h + j : (G == 64 ? (j >> 1) * 8 + 2 * h + (j & 1) : 4 * j + h);
   }
 };
-// a wave's share of a stage in registers: four 16-byte pieces of packed
-// words and PBR / 2 bytes of a parameter slice
-template <int G> struct WSlice {
-  u32x4_t w[4];
-  uint32_t p[1024 / G / 8 > 1 ? 1024 / G / 8 : 1];
-};
+__device__ __forceinline__ int par_swz(int r, int piece) { return r * 128 + ((piece ^ ((r >> 1) & 7)) << 4); }
 
 // Stage t of the MFMA GEMV: write stage t+1 (loaded two stages ago) to LDS,
 // barrier (stage t+1 is in LDS, stage t was written a stage ago, and every
-// wave is done with stage t-2, whose buffer stage t+1 reuses), issue the
+// wave is done with stage t-3, whose buffer stage t+1 reuses), issue the
 // loads of stage t+3 and the x fragments of stage t+2, compute stage t.
-template <class Put, class IssueW, class IssueX, class Compute, class W, class X>
+template <class Put, class IssueW, class IssueX, class Compute, class X>
 __device__ __forceinline__ void mfma_stage(Put& put, IssueW& issue_w, IssueX& issue_x, Compute& compute, int t,
                                            bool active, const unsigned char* cur, const X& xc, unsigned char* nxt,
-                                           const W& wn, W& wf, X& xf) {
+                                           const u32x4_t (&wn)[4], u32x4_t (&wf)[4], X& xf) {
   put(nxt, wn);
   __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
@@ -493,20 +490,23 @@ __device__ __forceinline__ void mfma_stage(Put& put, IssueW& issue_w, IssueX& is
   issue_w(t + 3, wf);
   issue_x(t + 2, xf);
   __builtin_amdgcn_sched_barrier(0);
-  if (active) compute(cur, xc);
+  if (active) compute(cur, xc, t);
 }
 
 template <bool F16, int G>
 __global__ __launch_bounds__(256, 2) void gemv_mfma4_kernel(MfmaBatch B) {
   using Geo = MfmaGeo<G>;
-  constexpr int NB = 4, GPS = Geo::GPS, WPG = Geo::WPG, PBR = Geo::PBR;
+  constexpr int NB = 4, GPS = Geo::GPS, WPG = Geo::WPG;
   using frag_t = typename std::conditional<F16, f16x8_t, bf16x8_t>::type;
   using X = u32x4_t[4];
-  using W = WSlice<G>;
+  using W = u32x4_t[4];
+  constexpr int CS = Geo::CS;
   constexpr float OFF = F16 ? 1024.f : 128.f;
   __shared__ __attribute__((aligned(1024))) unsigned char st0[Geo::STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char st1[Geo::STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char st2[Geo::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st3[Geo::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char prm[Geo::PREG];
 
   const int bid = blockIdx.x;
   int lo = 0, hi = B.count - 1;
@@ -530,32 +530,36 @@ __global__ __launch_bounds__(256, 2) void gemv_mfma4_kernel(MfmaBatch B) {
   const int wrow = 4 * wave + (lane >> 4);
   const uint32_t wv = (uint32_t)(wrow * L * 4 + (lane & 15) * 16);
   const int wdst = wrow * 256 + (((lane & 15) ^ (wrow & 15)) << 4);  // + i*16*256
-  // Scales (waves 0, 1) or biases (waves 2, 3) of rows 32*(wave&1) + lane/2,
-  // half lane&1 of the row's PBR bytes.
+  // Scale (waves 0, 1) or bias (waves 2, 3) chunks: rows 32*(wave&1) + 8i +
+  // lane/8 (i < 4), piece lane % 8 of the row's 128 bytes; every wave-level
+  // load covers 8 whole rows' chunks.
   const __amdgpu_buffer_rsrc_t rp = make_rsrc(
       static_cast<const uint16_t*>((wave >> 1) ? D.b : D.s) + (long)col0 * ng, (uint32_t)(ncols * ng * 2));
-  const int prow = 32 * (wave & 1) + (lane >> 1);
-  const uint32_t pv = (uint32_t)(prow * ng * 2 + (lane & 1) * (PBR / 2));
-  const int pdst = Geo::WB + (wave >> 1) * Geo::PRM + prow * PBR + (lane & 1) * (PBR / 2);
+  const int prow = 32 * (wave & 1) + (lane >> 3);
+  const uint32_t pv = (uint32_t)(prow * ng * 2 + (lane & 7) * 16);
+  int pdst[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pdst[i] = (wave >> 1) * 64 * 128 + par_swz(prow + 8 * i, lane & 7);
+  const int nchunk = (nst + CS - 1) / CS;
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(D.x, (uint32_t)(M * K * 2));
   const uint32_t xv = c < M ? (uint32_t)(c * K * 2) : OOB;
 
-  // loads of stage tw's packed words and parameter slice; a stage past the
-  // end loads nothing (offsets out of range)
+  // loads of stage tw's packed words; a stage past the end loads nothing
+  // (offsets out of range)
   auto issue_w = [&](int tw, W& wr) __attribute__((always_inline)) {
     const uint32_t wo = (tw < nst ? wv : OOB) + (uint32_t)tw * 256u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wr.w[i] = ld128(rw, wo + (uint32_t)(16 * i * L * 4));
-    const uint32_t po = (tw < nst ? pv : OOB) + (uint32_t)tw * PBR;
-    if constexpr (PBR / 2 == 16) {
-      const u32x4_t v = ld128(rp, po);
-      wr.p[0] = v[0]; wr.p[1] = v[1]; wr.p[2] = v[2]; wr.p[3] = v[3];
-    } else if constexpr (PBR / 2 == 8) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rp, po, 0, 0);
-      wr.p[0] = v[0]; wr.p[1] = v[1];
-    } else {
-      wr.p[0] = ld32(rp, po);
-    }
+    for (int i = 0; i < 4; ++i) wr[i] = ld128(rw, wo + (uint32_t)(16 * i * L * 4));
+  };
+  // loads of parameter chunk ch
+  auto issue_p = [&](int ch, u32x4_t (&pr)[4]) __attribute__((always_inline)) {
+    const uint32_t po = (ch < nchunk ? pv : OOB) + (uint32_t)ch * 128u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = ld128(rp, po + (uint32_t)(8 * i * ng * 2));
+  };
+  auto put_p = [&](const u32x4_t (&pr)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(prm + pdst[i]) = pr[i];
   };
   // x fragments of span 4*tx + wave
   auto issue_x = [&](int tx, X& xr) __attribute__((always_inline)) {
@@ -566,14 +570,7 @@ __global__ __launch_bounds__(256, 2) void gemv_mfma4_kernel(MfmaBatch B) {
   };
   auto put = [&](unsigned char* st, const W& wr) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(st + wdst + i * 16 * 256) = wr.w[i];
-    if constexpr (PBR / 2 == 16) {
-      *reinterpret_cast<u32x4_t*>(st + pdst) = u32x4_t{wr.p[0], wr.p[1], wr.p[2], wr.p[3]};
-    } else if constexpr (PBR / 2 == 8) {
-      *reinterpret_cast<uint2*>(st + pdst) = uint2{wr.p[0], wr.p[1]};
-    } else {
-      *reinterpret_cast<uint32_t*>(st + pdst) = wr.p[0];
-    }
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(st + wdst + i * 16 * 256) = wr[i];
   };
 
   uint32_t magic = F16 ? 0x64006400u : 0x43004300u;
@@ -584,7 +581,7 @@ __global__ __launch_bounds__(256, 2) void gemv_mfma4_kernel(MfmaBatch B) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) y[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const unsigned char* st, const X& xr) __attribute__((always_inline)) {
+  auto compute = [&](const unsigned char* st, const X& xr, int t) __attribute__((always_inline)) {
     // packed words of the span for the four blocks
     u32x4_t wq[NB];
 #pragma unroll
@@ -602,12 +599,14 @@ __global__ __launch_bounds__(256, 2) void gemv_mfma4_kernel(MfmaBatch B) {
           wq[nb][j] = *reinterpret_cast<const uint32_t*>(row + (((4 * wave + j) ^ c) << 4) + h * 4);
       }
     }
-    // the span's GPS scales and biases of column nb*16 + c
+    // the span's GPS scales and biases of column nb*16 + c: bytes
+    // 2 * GPS * (4u + wave) .. + 2 * GPS of the row's chunk, u = t % CS
     uint32_t sp_[NB][2], bp_[NB][2];
+    const int byte = 2 * GPS * (4 * (t % CS) + wave);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const unsigned char* ps = st + Geo::WB + (nb * 16 + c) * PBR + 2 * GPS * wave;
-      const unsigned char* pb = ps + Geo::PRM;
+      const unsigned char* ps = prm + par_swz(nb * 16 + c, byte >> 4) + (byte & 15);
+      const unsigned char* pb = ps + 64 * 128;
       if constexpr (GPS == 4) {
         const uint2 a = *reinterpret_cast<const uint2*>(ps), b = *reinterpret_cast<const uint2*>(pb);
         sp_[nb][0] = a.x; sp_[nb][1] = a.y; bp_[nb][0] = b.x; bp_[nb][1] = b.y;
@@ -659,9 +658,15 @@ __global__ __launch_bounds__(256, 2) void gemv_mfma4_kernel(MfmaBatch B) {
     }
   };
 
-  // three stages in a ring, unrolled so that every buffer is static
-  X x0, x1, x2;
-  W w0, w1, w2;
+  // four stages in a ring, unrolled so that every buffer is static
+  X x0, x1, x2, x3;
+  W w0, w1, w2, w3;
+  u32x4_t pc[4];
+  // parameter chunk 0 to LDS, chunk 1 in flight
+  issue_p(0, pc);
+  put_p(pc);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_p(1, pc);
   // the prologue keeps the loop's load order, so that the wait counts the
   // compiler derives at the loop head hold for both ways in
   issue_w(0, w0);
@@ -673,12 +678,22 @@ __global__ __launch_bounds__(256, 2) void gemv_mfma4_kernel(MfmaBatch B) {
   issue_w(2, w2);
   __builtin_amdgcn_sched_barrier(0);
   put(st0, w0);
-  // whole rounds of three stages: a stage past the end loads nothing and
-  // computes nothing, and the loop body has no branch around a stage
-  for (int t = 0; t < nst; t += 3) {
-    mfma_stage(put, issue_w, issue_x, compute, t, 4 * t + wave < nsp, st0, x0, st1, w1, w0, x2);
-    mfma_stage(put, issue_w, issue_x, compute, t + 1, 4 * t + 4 + wave < nsp, st1, x1, st2, w2, w1, x0);
-    mfma_stage(put, issue_w, issue_x, compute, t + 2, 4 * t + 8 + wave < nsp, st2, x2, st0, w0, w2, x1);
+  // Whole rounds of four stages (K = 2048 n needs no other): a stage past
+  // the end loads nothing and computes nothing, and the loop body has no
+  // branch around a stage.  A chunk of CS (a multiple of 4) stages ends with
+  // a round; then, once every wave is done with it, the next chunk's scales
+  // and biases replace it in LDS (visible after the next barrier) and the
+  // one after that is loaded.
+  for (int t = 0; t < nst; t += 4) {
+    mfma_stage(put, issue_w, issue_x, compute, t, 4 * t + wave < nsp, st0, x0, st1, w1, w3, x2);
+    mfma_stage(put, issue_w, issue_x, compute, t + 1, 4 * t + 4 + wave < nsp, st1, x1, st2, w2, w0, x3);
+    mfma_stage(put, issue_w, issue_x, compute, t + 2, 4 * t + 8 + wave < nsp, st2, x2, st3, w3, w1, x0);
+    mfma_stage(put, issue_w, issue_x, compute, t + 3, 4 * t + 12 + wave < nsp, st3, x3, st0, w0, w2, x1);
+    if ((t + 4) % CS == 0 && t + 4 < nst) {
+      __builtin_amdgcn_s_barrier();
+      put_p(pc);
+      issue_p((t + 4) / CS + 1, pc);
+    }
   }
 
   // the four waves' partial sums: block nb is finished by wave nb
@@ -784,8 +799,9 @@ hipError_t launch_gemv_grouped(const AffineArgs* probs, int count, hipStream_t s
     bool mfma = bits == 4 && M >= MFMA_MIN_M && sbm != 2 && (a0.G == 32 || a0.G == 64 || a0.G == 128);
     for (int i = 0; mfma && i < b.count; ++i) {
       const GemvDesc& d = b.d[i];
-      // whole 512-code stages keep every parameter slice load aligned
-      mfma = d.kp == nullptr && d.K % 512 == 0 && (int64_t)d.K * 32 < (int64_t(1) << 31) &&
+      // whole 512-code stages, and rows of scales and biases a multiple of
+      // 16 bytes, so that every chunk load is aligned
+      mfma = d.kp == nullptr && d.K % 512 == 0 && (d.K / a0.G) % 8 == 0 && (int64_t)d.K * 32 < (int64_t(1) << 31) &&
              (((uintptr_t)d.w | (uintptr_t)d.s | (uintptr_t)d.b) & 15) == 0;
     }
     if (mfma) {
