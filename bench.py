@@ -17,6 +17,11 @@ with almost no launch gaps.  In the same JSON line:
   per_linear     one qmm_affine launch per linear: 112 launches
   cfg0_hot       the single 2048x2048 linear relaunched on the same weights
                  (cache-resident: NOT an HBM figure)
+  decode_set_multirow
+                 the grouped decode set at M = 4 and 16 (the MFMA GEMV kernel)
+  gptq_k4096_n11008
+                 GPTQ layout (K=4096, N=11008, G=128, act-order) at M = 1 and
+                 32: the direct kernel and the repacked affine path
   gemm_m2048     prefill GEMM of an 8B decoder, M=2048: K=4096 with N = 4096,
                  1024, 14336 and K=14336 with N=4096, 4- and 8-bit, TFLOP/s
                  against the bf16 dense MFMA peak
@@ -197,6 +202,40 @@ def time_gemm(torch, qa, si, device, bits, N=14336, K=4096, M=2048, iters=50, wa
             "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4)}
 
 
+def time_decode_m(torch, qa, si, device, dec, M, steps, warmup):
+    """The decode set at M x rows (the configuration's M = 4 and 16), grouped
+    as in the headline; M >= 2 runs the MFMA GEMV kernel."""
+    xs = {K: torch.from_numpy(si.activations(M, K, seed=(1, 8, K, M)).view(np.int16)).view(torch.bfloat16).to(device)
+          for K in (2048, 8192)}
+    lins = [d for lin in dec.stack for d in lin]
+    outs = [torch.empty((M, d["N"]), dtype=torch.bfloat16, device=device) for d in lins]
+    call = qa.GroupedGemv([(xs[d["K"]], d["w"], d["s"], d["b"]) for d in lins], G, BITS, outs=outs)
+    ms = eager_time(torch, call, steps, warmup)
+    byts = sum(gemv_bytes(M, d["N"], d["K"]) for d in lins)
+    gbs = byts / (ms * 1e-3) / 1e9
+    return {"M": M, "us_per_step": round(ms * 1e3, 1), "gbs": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def time_gptq(torch, qa, si, device, M, iters=200, warmup=20):
+    """GPTQ layout, K=4096 N=11008 G=128 act-order: the direct kernel and the
+    repacked affine path, at M x rows."""
+    c = si.cfg3_case(M)
+    x = torch.from_numpy(c.x.view(np.int16)).view(torch.float16).to(device)
+    qw = torch.from_numpy(c.qweight.view(np.int32)).to(device)
+    qz = torch.from_numpy(c.qzeros.view(np.int32)).to(device)
+    sc = torch.from_numpy(c.scales.view(np.int16)).view(torch.float16).to(device)
+    gi = torch.from_numpy(c.g_idx.astype(np.int32)).to(device)
+    byts = (c.K * c.N // 2 + (c.K // c.G) * c.N * 2 + (c.K // c.G) * c.N // 2 + c.K * 4
+            + M * c.K * 2 + M * c.N * 2)
+    ms_d = eager_time(torch, lambda: qa.qmm_gptq(x, qw, qz, sc, gi, c.G), iters, warmup)
+    w, s2, b2, kp = qa.gptq_to_affine_repack(qw, qz, sc, gi, c.G)
+    ms_r = eager_time(torch, lambda: qa.qmm_affine(x, w, s2, b2, c.G, 4, k_perm=kp), iters, warmup)
+    return {"M": M, "N": c.N, "K": c.K, "G": c.G,
+            "direct_us": round(ms_d * 1e3, 2), "direct_gbs": round(byts / (ms_d * 1e-3) / 1e9, 1),
+            "repacked_affine_us": round(ms_r * 1e3, 2)}
+
+
 def time_w4a8(torch, qa, si, device, M=2048, N=4096, K=1024, iters=20, warmup=5):
     case = si.w4a8_case(M, N, K, seed=(4, N, K, M))
     x = torch.from_numpy(case.x.view(np.int16)).view(torch.float16).to(device)
@@ -347,6 +386,13 @@ def main():
     hot = lambda: [qa.qmm_affine(dec.x[2048], d0["w"], d0["s"], d0["b"], G, BITS, out=y0) for _ in range(20)]
     us_hot = graph_time(torch, hot, 20, 5) * 1e3 / 20
 
+    decode_m = [time_decode_m(torch, qa, si, device, dec, M, max(args.steps // 4, 10), args.warmup // 4 + 1)
+                for M in (4, 16)]
+    for d in decode_m:
+        print(f"[bench] decode set M={d['M']}: {d['us_per_step']} us/step, {d['gbs']} GB/s", file=sys.stderr,
+              flush=True)
+    gptq = [time_gptq(torch, qa, si, device, M) for M in (1, 32)]
+
     gemm = w4a8 = None
     if not args.no_gemm:
         gemm = [time_gemm(torch, qa, si, device, bits, N=N, K=K) for bits in si.CFG2_BITS for N, K in si.CFG2_SHAPES]
@@ -392,6 +438,8 @@ def main():
         "per_linear": {"launches_per_step": dec.n_linears, "us_per_step": round(ms_lin * 1e3, 1),
                        "gbs": round(dec.bytes_per_step / (ms_lin * 1e-3) / 1e9, 1)},
         "cfg0_hot": {"us_per_launch": round(us_hot, 2), "gbs_not_hbm": round(gemv_bytes(1, 2048, 2048) / us_hot / 1e3, 1)},
+        "decode_set_multirow": decode_m,
+        "gptq_k4096_n11008": gptq,
         "gemm_m2048": gemm,
         "w4a8_m2048": w4a8,
     }
