@@ -25,7 +25,7 @@
 //             A = [xs_hi, xs_hi, xs_lo].  Per row of W: e_n, scale pieces s_j
 //             (fp16 pairs), tail B = [cb_hi, cb_lo, cb_hi]
 //   gemm    : 256 threads, tile BM x 256 (4 waves along N, each BM x 64);
-//             x tiles double-buffered in LDS, stored one step ahead; packed codes go from
+//             x tiles in a 4-stage LDS ring, stored two steps ahead; packed codes go from
 //             global memory straight to registers, are decoded with the
 //             exponent-bias trick (code | 0x6400 = 1024 + code in fp16) and
 //             scaled with packed fp16 math; XCD-aware tile order.
@@ -306,12 +306,15 @@ struct Decode {
 // so every weight word is decoded once per BM rows.
 //
 // Pipeline:
-//   * x tiles go global -> registers (loaded two steps before use) -> LDS
-//     (stored one step before use) into two stages; 16-byte chunks are
+//   * x tiles go global -> registers (one step before the store) -> LDS,
+//     stored two steps before use into a 4-stage ring; 16-byte chunks are
 //     XOR-swizzled by row ((r ^ r>>1) & 7) so the MFMA operand reads are
 //     bank-conflict free;
 //   * weight words and scale pieces go through buffer loads with the K
 //     offset in an SGPR, into a 4-deep register ring (three steps ahead);
+//   * the A reads and the B decode of a tile's first 16-column step run
+//     during the previous tile's last step, so a tile starts with MFMAs
+//     (the tile's x is in LDS for every wave one barrier earlier);
 //   * the loop is unrolled by 4 so every ring index and LDS stage is a
 //     constant.
 // Rows of W past N are read through per-lane offsets past the buffer's range
@@ -453,17 +456,16 @@ struct Pipe {
     }
   }
 
-  // the four 16-column steps of a tile, software-pipelined: step s runs its
+  // The four 16-column steps of a tile, software-pipelined: step s runs its
   // MFMAs while step s+1's B fragments are decoded and its A fragments are
-  // read from LDS
-  __device__ __forceinline__ void compute(const St& st, const unsigned char* __restrict__ sA, uint32_t magic,
-                                          f32x16_t (&acc)[MB][2]) const {
+  // read from LDS.  a0/b0 hold step 0 of this tile on entry, and step 0 of
+  // the next tile (stage sAn, ring entry stn) on exit.
+  __device__ __forceinline__ void compute(const St& st, const unsigned char* __restrict__ sA, const St& stn,
+                                          const unsigned char* __restrict__ sAn, uint32_t magic,
+                                          f16x8_t (&a0)[MB], f16x8_t (&b0)[2][NF], f32x16_t (&acc)[MB][2]) const {
     constexpr int DEC = 2 * NF * 16;  // VALU ops of one step's decode, roughly
-    f16x8_t a0[MB], a1[MB];
-    f16x8_t b0[2][NF], b1[2][NF];
-    read_a(sA, 0, a0);
-    decode_b(st, 0, magic, b0);
-    __builtin_amdgcn_sched_barrier(0);
+    f16x8_t a1[MB];
+    f16x8_t b1[2][NF];
     read_a(sA, 1, a1);
     decode_b(st, 1, magic, b1);
     mfma_b(a0, b0, acc);
@@ -479,30 +481,35 @@ struct Pipe {
     mfma_b(a0, b0, acc);
     interleave<DEC, MB>();
     __builtin_amdgcn_sched_barrier(0);
+    read_a(sAn, 0, a0);
+    decode_b(stn, 0, magic, b0);
     mfma_b(a1, b1, acc);
+    interleave<DEC, MB>();
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  // One K tile kt:
-  //   barrier                 tile kt's x (stored last step) visible to all waves,
-  //                           everyone done with stage (kt+1)&1
-  //   store x of tile kt+1    registers loaded last step -> the other stage
-  //   issue tile kt+2         x into registers, weights/scales into the ring
-  //   compute tile kt
-  // Loads past the last tile read 0 (buffer range checks) and land nowhere
-  // that is read, so the step has no branch.
-  // PAR = kt & 1, a compile-time constant, so the LDS stage offsets are
-  // immediates and the stores need no address register
-  template <int PAR>
-  __device__ __forceinline__ void step(int kt, const St& cur, St& nxt, unsigned char* lds, u32x4_t (&xr)[A_DMA],
-                                       uint32_t magic, f32x16_t (&acc)[MB][2]) const {
+  // One K tile kt (stage kt%4, ring entry kt%4):
+  //   barrier                 tile kt+1's x (stored last step) visible to all
+  //                           waves; everyone done with tile kt-1
+  //   store x of tile kt+2    registers loaded last step -> stage (kt+2)%4
+  //   issue tile kt+3         x into registers, weights/scales into the ring
+  //   compute tile kt         ending with step 0 of tile kt+1 prepared
+  // Loads past the last tile re-read the last tile and land nowhere that is
+  // read, so the step has no branch.  S = kt % 4, a compile-time constant,
+  // so the LDS stage offsets are immediates.
+  template <int S>
+  __device__ __forceinline__ void step(int kt, const St& cur, const St& nxt, St& fut, unsigned char* lds,
+                                       u32x4_t (&xr)[A_DMA], uint32_t magic, f16x8_t (&a0)[MB], f16x8_t (&b0)[2][NF],
+                                       f32x16_t (&acc)[MB][2]) const {
+    constexpr int SB = MB * 32 * 128;  // bytes of one stage
     __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0): own LDS writes done
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    store_x(lds + (1 - PAR) * (MB * 32 * 128), xr);
-    issue_x(kt + 2, xr);   // x two tiles ahead (L2), stored next step
-    issue_w(kt + 3, nxt);  // weights three tiles ahead (HBM), used in three steps
+    store_x(lds + ((S + 2) & 3) * SB, xr);
+    issue_x(kt + 3, xr);   // x three tiles ahead (L2), stored next step
+    issue_w(kt + 3, fut);  // weights three tiles ahead (HBM)
     __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
-    compute(cur, lds + PAR * (MB * 32 * 128), magic, acc);
+    compute(cur, lds + S * SB, nxt, lds + ((S + 1) & 3) * SB, magic, a0, b0, acc);
   }
 };
 
@@ -520,7 +527,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int m0 = tm * BM, n0 = tn * BN;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l32 = lane & 31, half = lane >> 5;
 
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) int em_s[BM];
   for (int i = t; i < BM; i += 256) em_s[i] = p.em[m0 + i];
 
@@ -560,22 +567,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   P.last_kt = nkt - 1;
   St st0, st1, st2, st3;
   u32x4_t xr[MB];
+  // prologue: x of tiles 0 and 1 in LDS, tile 2 in registers, weights of
+  // tiles 0..2 in the ring, step 0 of tile 0 prepared
   P.issue_x(0, xr);
   P.issue_w(0, st0);
   P.issue_w(1, st1);
   P.issue_w(2, st2);
   P.store_x(lds, xr);
   P.issue_x(1, xr);
+  P.store_x(lds + STAGE_BYTES, xr);
+  P.issue_x(2, xr);
+  __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
 
   // ---- main loop
   uint32_t magic = 0x64006400u;
   asm volatile("" : "+v"(magic));
-  // unrolled by 4 = lcm(4 ring entries, 2 LDS stages): every index is static
+  f16x8_t a0[MB];
+  f16x8_t b0[2][Pipe<BITS, PS, MB>::NF];
+  P.read_a(lds, 0, a0);
+  P.decode_b(st0, 0, magic, b0);
+  // unrolled by 4 = the ring size and the stage count: every index is static
   for (int kt = 0; kt < nkt; kt += 4) {
-    P.template step<0>(kt, st0, st3, lds, xr, magic, acc);
-    if (kt + 1 < nkt) P.template step<1>(kt + 1, st1, st0, lds, xr, magic, acc);
-    if (kt + 2 < nkt) P.template step<0>(kt + 2, st2, st1, lds, xr, magic, acc);
-    if (kt + 3 < nkt) P.template step<1>(kt + 3, st3, st2, lds, xr, magic, acc);
+    P.template step<0>(kt, st0, st1, st3, lds, xr, magic, a0, b0, acc);
+    if (kt + 1 < nkt) P.template step<1>(kt + 1, st1, st2, st0, lds, xr, magic, a0, b0, acc);
+    if (kt + 2 < nkt) P.template step<2>(kt + 2, st2, st3, st1, lds, xr, magic, a0, b0, acc);
+    if (kt + 3 < nkt) P.template step<3>(kt + 3, st3, st0, st2, lds, xr, magic, a0, b0, acc);
   }
 
   // ---- tail: sum_g xs * cb on bf16 MFMA, operands straight from global
