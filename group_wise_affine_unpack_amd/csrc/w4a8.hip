@@ -11,8 +11,10 @@
 // Kernels:
 //   quant : one block per row; bit-exact codes and scale.
 //   gemm  : v_mfma_i32_32x32x32_i8, tile BM x BN (4 waves along N, each
-//           BM x NB*32), x_q tile double-buffered in LDS, int4 words decoded in
-//           registers; the tile shrinks until the grid covers the chip.  A nibble
+//           BM x NB*32), K in stages of 128: x_q through a 4-stage LDS ring
+//           stored two stages ahead, int4 words in a register ring three
+//           stages ahead and decoded in registers; the tile shrinks until the
+//           grid gives every CU two workgroups.  A nibble
 //           is placed in the HIGH half of its byte, which makes the byte the
 //           int8 value 16*v with no sign extension step; the accumulator is
 //           shifted right by 4 at the end (exact: every product is a multiple
@@ -47,8 +49,13 @@ __global__ __launch_bounds__(256) void w4a8_quant_kernel(const uint16_t* __restr
   }
 }
 
-constexpr int BK = 64;       // int8 codes per K tile
-constexpr int LDS_ROW = 80;  // 64 bytes + 16 bytes padding (conflict-free 16-byte reads)
+constexpr uint32_t OOB = 0x80000000u;  // a buffer offset past any range: the load reads 0
+
+__device__ __forceinline__ u32x4_t ld128(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+constexpr int BK = 128;  // int8 codes per K stage
 
 struct Params {
   const int8_t* xq;
@@ -69,19 +76,133 @@ __device__ __forceinline__ void decode_word(uint32_t w, uint32_t& d0, uint32_t& 
   d1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // (n4, n5, n6, n7)
 }
 
+__device__ __forceinline__ int xswz(int r) { return r & 7; }
+
+// One wave: rows [0, MB*32) x columns [wave*NB*32, +NB*32) of the tile.
+// Stage = 128 codes of K.  Lane (l32, h) takes, in 16-column sub-step s,
+// codes 64h + 16s .. +15 of the stage: its B fragment is words 8h+2s, 8h+2s+1
+// of its row, its A fragment the matching 16 bytes of x_q row l32.
+template <int MB, int NB>
+struct W4Pipe {
+  static constexpr int A_CH = MB;  // 16-byte x chunks per thread and stage
+  static constexpr int SB = MB * 32 * 128;  // bytes of one LDS stage
+  __amdgpu_buffer_rsrc_t rx, rw;
+  uint32_t x_off[A_CH];  // this thread's chunks (OOB for rows past M)
+  int x_dst;             // LDS offset of chunk 0 (chunk i at + i*4096)
+  uint32_t w_off[NB];    // this lane's row, word 8h
+  int l32, h, nst, K;
+
+  __device__ __forceinline__ void issue_x(int t, u32x4_t (&xr)[A_CH]) const {
+    const uint32_t k = (uint32_t)min(t, nst - 1) * BK;
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) xr[i] = ld128(rx, x_off[i] + k);
+  }
+  __device__ __forceinline__ void store_x(unsigned char* st, const u32x4_t (&xr)[A_CH]) const {
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) *reinterpret_cast<u32x4_t*>(st + x_dst + i * 4096) = xr[i];
+  }
+  // 32 codes per load; a load whose codes start at or past K is moved out
+  // of range and reads zeros (K % 32 == 0)
+  __device__ __forceinline__ void issue_w(int t, u32x4_t (&wr)[NB][2]) const {
+    t = min(t, nst - 1);
+    const uint32_t k = (uint32_t)t * (BK / 2);
+    const uint32_t o0 = t * BK + 64 * h < K ? 0u : OOB, o1 = t * BK + 64 * h + 32 < K ? 0u : OOB;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      wr[nb][0] = ld128(rw, (w_off[nb] | o0) + k);
+      wr[nb][1] = ld128(rw, (w_off[nb] | o1) + k + 16);
+    }
+  }
+  __device__ __forceinline__ void read_a(const unsigned char* __restrict__ st, int s, i32x4_t (&af)[MB]) const {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int r = mb * 32 + l32;
+      af[mb] = *reinterpret_cast<const i32x4_t*>(st + r * 128 + (((4 * h + s) ^ xswz(r)) << 4));
+    }
+  }
+  __device__ __forceinline__ void decode_b(const u32x4_t (&wr)[NB][2], int s, i32x4_t (&bf)[NB]) const {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const uint32_t w0 = wr[nb][s >> 1][2 * (s & 1)], w1 = wr[nb][s >> 1][2 * (s & 1) + 1];
+      uint32_t d0, d1, d2, d3;
+      decode_word(w0, d0, d1);
+      decode_word(w1, d2, d3);
+      bf[nb] = i32x4_t{(int)d0, (int)d1, (int)d2, (int)d3};
+    }
+  }
+  __device__ __forceinline__ void mfma(const i32x4_t (&af)[MB], const i32x4_t (&bf)[NB],
+                                       i32x16_t (&acc)[MB][NB]) const {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mb], bf[nb], acc[mb][nb], 0, 0, 0);
+  }
+  // The four 32-code sub-steps of a stage, software-pipelined: sub-step s
+  // runs its MFMAs while s+1's A fragments are read and B fragments decoded.
+  // a0/b0 hold sub-step 0 of this stage on entry and of the next stage
+  // (LDS stage stn, ring entry wn) on exit.
+  __device__ __forceinline__ void compute(const unsigned char* __restrict__ st, const u32x4_t (&wr)[NB][2],
+                                          const unsigned char* __restrict__ stn, const u32x4_t (&wn)[NB][2],
+                                          i32x4_t (&a0)[MB], i32x4_t (&b0)[NB], i32x16_t (&acc)[MB][NB]) const {
+    i32x4_t a1[MB], b1[NB];
+    read_a(st, 1, a1);
+    decode_b(wr, 1, b1);
+    mfma(a0, b0, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    read_a(st, 2, a0);
+    decode_b(wr, 2, b0);
+    mfma(a1, b1, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    read_a(st, 3, a1);
+    decode_b(wr, 3, b1);
+    mfma(a0, b0, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    read_a(stn, 0, a0);
+    decode_b(wn, 0, b0);
+    mfma(a1, b1, acc);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Stage t (LDS stage t%4 = S, ring entry t%4):
+  //   barrier              stage t+1 (stored last step) visible; every wave
+  //                        done with stage t-1
+  //   store x of t+2       registers loaded last step -> stage (t+2)%4
+  //   issue t+3            x into registers, then weight words into the ring
+  //   compute t            ending with sub-step 0 of stage t+1 prepared
+  //                        (skipped past the last stage)
+  template <int S>
+  __device__ __forceinline__ void step(int t, unsigned char* lds, u32x4_t (&xr)[A_CH], const u32x4_t (&cur)[NB][2],
+                                       const u32x4_t (&nxt)[NB][2], u32x4_t (&fut)[NB][2], i32x4_t (&a0)[MB],
+                                       i32x4_t (&b0)[NB], i32x16_t (&acc)[MB][NB]) const {
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0): own LDS writes done
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    store_x(lds + ((S + 2) & 3) * SB, xr);
+    issue_x(t + 3, xr);
+    issue_w(t + 3, fut);
+    __builtin_amdgcn_sched_barrier(0);
+    if (t < nst) compute(lds + S * SB, cur, lds + ((S + 1) & 3) * SB, nxt, a0, b0, acc);
+  }
+};
+
+// x_q tiles go global -> registers (one stage before the store) -> a 4-stage
+// LDS ring, stored two stages before use, 16-byte chunks XOR-swizzled by row;
+// int4 words go to a 4-entry register ring three stages ahead; loads past
+// the end of K or past the last row are out of range and read zeros.  The
+// A reads and B decode of a stage's first sub-step run during the previous
+// stage's last one.
 template <int MB, int NB>
 __global__ __launch_bounds__(256) void w4a8_gemm_kernel(Params p) {
   constexpr int BM = MB * 32;
   constexpr int BN = NB * 128;
-  constexpr int A_CHUNKS = BM * 4 / 256;  // 16-byte chunks of the x_q tile per thread (>= 1)
   const int b = blockIdx.x;
   const int v = (b & 7) * p.per_xcd + (b >> 3);
   if (v >= p.Tm * p.Tn) return;
   const int tm = v / p.Tn, tn = v % p.Tn;
   const int m0 = tm * BM, n0 = tn * BN;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l32 = lane & 31, half = lane >> 5;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l32 = lane & 31, h = lane >> 5;
 
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2][BM * LDS_ROW];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * W4Pipe<MB, NB>::SB];
 
   i32x16_t acc[MB][NB];
 #pragma unroll
@@ -91,76 +212,72 @@ __global__ __launch_bounds__(256) void w4a8_gemm_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-  int nrow[NB];
+  W4Pipe<MB, NB> P;
+  P.l32 = l32;
+  P.h = h;
+  P.nst = (p.K + BK - 1) / BK;
+  // the range covers the tile's rows: a row past M reads zeros.  x_q chunks
+  // past K (last stage, K % 128 != 0) read the next row; the weight words
+  // they meet are zeros (see issue_w), so they add nothing.
+  P.rx = make_rsrc(p.xq + (long)m0 * p.K, (uint32_t)(min(BM, p.M - m0) * p.K));
+  P.rw = make_rsrc(p.w, (uint32_t)((long)p.N * p.K / 2));
+  {
+    const int r = t >> 3, c = t & 7;
+#pragma unroll
+    for (int i = 0; i < MB; ++i) P.x_off[i] = (uint32_t)((32 * i + r) * p.K + c * 16);
+    P.x_dst = r * 128 + ((c ^ xswz(r)) << 4);
+  }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int n = n0 + wave * NB * 32 + nb * 32 + l32;
-    nrow[nb] = n < p.N ? n : p.N - 1;
+    P.w_off[nb] = n < p.N ? (uint32_t)((long)n * p.K / 2 + h * 32) : OOB;
   }
-  const long wrow = p.K / 8;
-  const int nkt = p.K / BK;
-  u32x4_t wcur[NB], wnxt[NB];
-  u32x4_t areg[A_CHUNKS];
+  P.K = p.K;
 
-  // x_q rows past M are read clamped to M-1; their results are not stored
-  auto a_src = [&](int kt, int c) {
-    const int ch = t + 256 * c, row = ch >> 2, col = ch & 3;
-    const int m = m0 + row < p.M ? m0 + row : p.M - 1;
-    return reinterpret_cast<const u32x4_t*>(p.xq + (long)m * p.K + kt * BK) + col;
-  };
-#pragma unroll
-  for (int c = 0; c < A_CHUNKS; ++c) areg[c] = *a_src(0, c);
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) wcur[nb] = *reinterpret_cast<const u32x4_t*>(p.w + nrow[nb] * wrow + half * 4);
-#pragma unroll
-  for (int c = 0; c < A_CHUNKS; ++c) {
-    const int ch = t + 256 * c;
-    *reinterpret_cast<u32x4_t*>(&lds[0][(ch >> 2) * LDS_ROW + (ch & 3) * 16]) = areg[c];
-  }
-  __syncthreads();
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < nkt;
-    if (more) {
-#pragma unroll
-      for (int c = 0; c < A_CHUNKS; ++c) areg[c] = *a_src(kt + 1, c);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        wnxt[nb] = *reinterpret_cast<const u32x4_t*>(p.w + nrow[nb] * wrow + (kt + 1) * 8 + half * 4);
-    }
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      i32x4_t af[MB];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        af[mb] = *reinterpret_cast<const i32x4_t*>(&lds[buf][(mb * 32 + l32) * LDS_ROW + 32 * half + 16 * s]);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const uint32_t w0 = s == 0 ? wcur[nb].x : wcur[nb].z;
-        const uint32_t w1 = s == 0 ? wcur[nb].y : wcur[nb].w;
-        uint32_t d0, d1, d2, d3;
-        decode_word(w0, d0, d1);
-        decode_word(w1, d2, d3);
-        const i32x4_t bf = {(int)d0, (int)d1, (int)d2, (int)d3};
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mb], bf, acc[mb][nb], 0, 0, 0);
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int c = 0; c < A_CHUNKS; ++c) {
-        const int ch = t + 256 * c;
-        *reinterpret_cast<u32x4_t*>(&lds[buf ^ 1][(ch >> 2) * LDS_ROW + (ch & 3) * 16]) = areg[c];
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) wcur[nb] = wnxt[nb];
-    }
-    __syncthreads();
+  u32x4_t xr[MB];
+  u32x4_t w0[NB][2], w1[NB][2], w2[NB][2], w3[NB][2];
+  // prologue in the loop's load order (x of a stage, then its weights), so
+  // that the waits the compiler derives at the loop head hold both ways in
+  P.issue_x(0, xr);
+  P.issue_w(0, w0);
+  __builtin_amdgcn_sched_barrier(0);
+  P.store_x(lds, xr);
+  P.issue_x(1, xr);
+  P.issue_w(1, w1);
+  __builtin_amdgcn_sched_barrier(0);
+  P.store_x(lds + W4Pipe<MB, NB>::SB, xr);
+  P.issue_x(2, xr);
+  P.issue_w(2, w2);
+  __builtin_amdgcn_sched_barrier(0);
+  // With every prologue load complete, the compiler's view of pending loads
+  // at the loop head is the loop's own, so its waits there stay exact.
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_barrier();
+  i32x4_t a0[MB], b0[NB];
+  P.read_a(lds, 0, a0);
+  P.decode_b(w0, 0, b0);
+  const int nst = P.nst;
+  // whole rounds of four stages: a stage past the end only loads (clamped)
+  // and waits, so the loop body has no branch around a step
+  for (int s = 0; s < nst; s += 4) {
+    P.template step<0>(s, lds, xr, w0, w1, w3, a0, b0, acc);
+    P.template step<1>(s + 1, lds, xr, w1, w2, w0, a0, b0, acc);
+    P.template step<2>(s + 2, lds, xr, w2, w3, w1, a0, b0, acc);
+    P.template step<3>(s + 3, lds, xr, w3, w0, w2, a0, b0, acc);
   }
 
-  // epilogue; 32x32 accumulator layout: lane -> column l32, register r -> row 8*(r/4) + 4*half + r%4
+  // epilogue; 32x32 accumulator layout: lane -> column l32, register r -> row 8*(r/4) + 4*h + r%4.
+  // The lane's 16 s_x values per row block are loaded together first, so the
+  // stores below never wait on a load (rows past M read 0 and are not stored).
+  const __amdgpu_buffer_rsrc_t rsx = make_rsrc(p.sx, (uint32_t)p.M * 4u);
+  float sxv[MB][16];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      sxv[mb][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsx, (uint32_t)m * 4u, 0, 0));
+    }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int n = n0 + wave * NB * 32 + nb * 32 + l32;
@@ -170,11 +287,11 @@ __global__ __launch_bounds__(256) void w4a8_gemm_kernel(Params p) {
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        const int m = m0 + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         if (m < p.M) {
           const int a = acc[mb][nb][r] >> 4;
           if (p.acc_out) p.acc_out[(long)m * p.N + n] = a;
-          p.y[(long)m * p.N + n] = f32_to_f16_bits(((float)a * p.sx[m]) * swn);
+          p.y[(long)m * p.N + n] = f32_to_f16_bits(((float)a * sxv[mb][r]) * swn);
         }
       }
   }
@@ -183,20 +300,21 @@ __global__ __launch_bounds__(256) void w4a8_gemm_kernel(Params p) {
 }  // namespace
 
 hipError_t launch_w4a8(const W4A8Args& a, hipStream_t s) {
-  if (a.K % BK != 0) return hipErrorNotSupported;
+  if (a.K % 32 != 0) return hipErrorNotSupported;
+  // buffer offsets are 32-bit
+  if (a.N * a.K / 2 >= (int64_t(1) << 31) || a.K * 256 >= (int64_t(1) << 31)) return hipErrorNotSupported;
   const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
   hipLaunchKernelGGL(w4a8_quant_kernel, dim3(M), dim3(256), 0, s, (const uint16_t*)a.x, K, a.x_q, a.s_x);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // largest tile whose grid still gives every CU at least two workgroups
   struct Tile { int mb, nb; };
-  const Tile tiles[] = {{8, 2}, {4, 2}, {4, 1}, {2, 1}};
-  Tile t = tiles[3];
+  const Tile tiles[] = {{4, 2}, {2, 2}, {2, 1}};
+  Tile t = tiles[2];
   for (const Tile& c : tiles) {
     const long tm = (M + c.mb * 32 - 1) / (c.mb * 32), tn = (N + c.nb * 128 - 1) / (c.nb * 128);
     if (tm * tn >= 512) { t = c; break; }
   }
-  if (M <= 64) t = Tile{2, 1};
   Params p;
   p.xq = a.x_q;
   p.sx = a.s_x;
@@ -211,12 +329,10 @@ hipError_t launch_w4a8(const W4A8Args& a, hipStream_t s) {
   p.Tn = (N + t.nb * 128 - 1) / (t.nb * 128);
   p.per_xcd = (p.Tm * p.Tn + 7) / 8;
   const dim3 grid(8 * p.per_xcd);
-  if (t.mb == 8)
-    hipLaunchKernelGGL((w4a8_gemm_kernel<8, 2>), grid, dim3(256), 0, s, p);
-  else if (t.mb == 4 && t.nb == 2)
+  if (t.mb == 4)
     hipLaunchKernelGGL((w4a8_gemm_kernel<4, 2>), grid, dim3(256), 0, s, p);
-  else if (t.mb == 4)
-    hipLaunchKernelGGL((w4a8_gemm_kernel<4, 1>), grid, dim3(256), 0, s, p);
+  else if (t.nb == 2)
+    hipLaunchKernelGGL((w4a8_gemm_kernel<2, 2>), grid, dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL((w4a8_gemm_kernel<2, 1>), grid, dim3(256), 0, s, p);
   return hipGetLastError();

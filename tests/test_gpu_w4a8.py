@@ -64,3 +64,12 @@ def test_ties_zero_rows_and_extremes():
     xf[3, :] = 2.0 ** -24                                  # smallest subnormal everywhere
     case.x = si.f16_bits(xf)
     _check(case)
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 70, 32), (40, 130, 96), (200, 300, 1056), (300, 520, 4000)])
+def test_k_not_multiple_of_stage(M, N, K):
+    # K % 32 == 0 is all the entry point asks; the GEMM walks K in stages of
+    # 128 codes, so these shapes end on a partial stage (32, 96, 32, 32 codes)
+    # and span several row and column tiles with ragged edges
+    case = si.w4a8_case(M, N, K, seed=(44, M, N, K), name=f"w4a8_M{M}_N{N}_K{K}")
+    _check(case)
