@@ -9,7 +9,9 @@
 //   y[m,n]   = f16((float(acc) * s_x[m]) * s_w[n])
 //
 // Kernels:
-//   quant : one block per row; bit-exact codes and scale.
+//   quant : each row held in the registers of one to four waves (16-byte
+//           loads, 8-byte stores) for K <= 16384, else one row per block
+//           in a loop; bit-exact codes and scale.
 //   gemm  : v_mfma_i32_32x32x32_i8, tile BM x BN (4 waves along N, each
 //           BM x NB*32), K in stages of 128: x_q through a 4-stage LDS ring
 //           stored two stages ahead, int4 words in a register ring three
@@ -24,6 +26,7 @@
 namespace qaff {
 namespace {
 
+// One row per block, for any K.
 __global__ __launch_bounds__(256) void w4a8_quant_kernel(const uint16_t* __restrict__ x, int K,
                                                          int8_t* __restrict__ xq, float* __restrict__ sx) {
   const int m = blockIdx.x, t = threadIdx.x;
@@ -46,6 +49,78 @@ __global__ __launch_bounds__(256) void w4a8_quant_kernel(const uint16_t* __restr
       q = fminf(fmaxf(q, -127.f), 127.f);
     }
     qrow[k] = (int8_t)(int)q;
+  }
+}
+
+// x / s rounded to nearest even, from r = 1/s refined by one Newton step:
+// q0 = x r, then the residual x - s q0 (exact in an fma) corrects q0 to the
+// rounded quotient (Markstein's division).  For s = a/127 over every finite
+// f16 a and every f16 x with |x| <= a it equals the IEEE quotient bit for
+// bit (an exhaustive test holds it to that), so rint of it gives the same
+// code as rint(x / s).  s = r = 0 (an all-zero row) gives 0.  The code
+// comes back as an exact float in [1, 255], biased by 128.
+__device__ __forceinline__ float quant_biased(uint32_t h, float s, float r) {
+  const float v = f16_bits_to_f32(h);
+  const float q0 = v * r;
+  const float q = __builtin_fmaf(__builtin_fmaf(-s, q0, v), r, q0);
+  return __builtin_amdgcn_fmed3f(rintf(q), -127.f, 127.f) + 128.f;
+}
+
+// four f16 values (two words) -> four int8 codes in one word
+__device__ __forceinline__ uint32_t quant_word(uint32_t w0, uint32_t w1, float s, float r) {
+  uint32_t o = __builtin_amdgcn_cvt_pk_u8_f32(quant_biased(w0 & 0xFFFFu, s, r), 0, 0u);
+  o = __builtin_amdgcn_cvt_pk_u8_f32(quant_biased(w0 >> 16, s, r), 1, o);
+  o = __builtin_amdgcn_cvt_pk_u8_f32(quant_biased(w1 & 0xFFFFu, s, r), 2, o);
+  o = __builtin_amdgcn_cvt_pk_u8_f32(quant_biased(w1 >> 16, s, r), 3, o);
+  return o ^ 0x80808080u;  // code + 128 -> two's complement byte
+}
+
+// One row per WPR waves (a block of four waves holds 4/WPR rows), the row
+// held in registers: thread i of the row takes the 8-value chunks
+// i, i + 64 WPR, ... (R of them, K <= 512 WPR R), read once with 16-byte
+// loads and written as 8 bytes each.  x and x_q 16-byte aligned, K % 8 == 0.
+template <int WPR, int R>
+__global__ __launch_bounds__(256) void w4a8_quant_rows_kernel(const uint16_t* __restrict__ x, int M, int K,
+                                                              int8_t* __restrict__ xq, float* __restrict__ sx) {
+  constexpr int TPR = 64 * WPR;  // threads per row
+  const int m = blockIdx.x * (4 / WPR) + (int)threadIdx.x / TPR, i = (int)threadIdx.x % TPR;
+  const int C = K >> 3;
+  const u32x4_t* row = reinterpret_cast<const u32x4_t*>(x + (long)min(m, M - 1) * K);
+  u32x4_t v[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) v[j] = i + TPR * j < C ? row[i + TPR * j] : u32x4_t{0, 0, 0, 0};
+  // |x| by clearing the sign bits, two values at a time; maxNum lets a NaN
+  // take no part in the maximum (as in a max built from ">" compares)
+  f16x2_t am2 = {0, 0};
+#pragma unroll
+  for (int j = 0; j < R; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      am2 = __builtin_elementwise_max(am2, __builtin_bit_cast(f16x2_t, v[j][e] & 0x7FFF7FFFu));
+  float am = fmaxf((float)am2[0], (float)am2[1]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o));
+  if constexpr (WPR > 1) {
+    __shared__ float red[4];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = am;
+    __syncthreads();
+    const int w0 = ((int)threadIdx.x >> 6) & ~(WPR - 1);
+#pragma unroll
+    for (int w = 0; w < WPR; ++w) am = fmaxf(am, red[w0 + w]);
+  }
+  if (m >= M) return;
+  const float s = am / 127.0f;  // correctly rounded division (HIP default)
+  if (i == 0) sx[m] = s;
+  float r = 0.f;
+  if (am != 0.f) {
+    const float r0 = __builtin_amdgcn_rcpf(s);
+    r = __builtin_fmaf(__builtin_fmaf(-s, r0, 1.0f), r0, r0);
+  }
+  u32x2_t* qrow = reinterpret_cast<u32x2_t*>(xq + (long)m * K);
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    if (i + TPR * j >= C) break;
+    qrow[i + TPR * j] = u32x2_t{quant_word(v[j][0], v[j][1], s, r), quant_word(v[j][2], v[j][3], s, r)};
   }
 }
 
@@ -304,7 +379,27 @@ hipError_t launch_w4a8(const W4A8Args& a, hipStream_t s) {
   // buffer offsets are 32-bit
   if (a.N * a.K / 2 >= (int64_t(1) << 31) || a.K * 256 >= (int64_t(1) << 31)) return hipErrorNotSupported;
   const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
-  hipLaunchKernelGGL(w4a8_quant_kernel, dim3(M), dim3(256), 0, s, (const uint16_t*)a.x, K, a.x_q, a.s_x);
+  {
+    // threads per row: one wave up to 512 values, two up to 1024, then four;
+    // chunks per thread: 1, 2, 4 or 8 (K <= 16384), else one row per block
+    const uint16_t* x = (const uint16_t*)a.x;
+    const int C = K / 8;
+    const dim3 b256(256);
+    if (C <= 64)
+      hipLaunchKernelGGL((w4a8_quant_rows_kernel<1, 1>), dim3((M + 3) / 4), b256, 0, s, x, M, K, a.x_q, a.s_x);
+    else if (C <= 128)
+      hipLaunchKernelGGL((w4a8_quant_rows_kernel<2, 1>), dim3((M + 1) / 2), b256, 0, s, x, M, K, a.x_q, a.s_x);
+    else if (C <= 256)
+      hipLaunchKernelGGL((w4a8_quant_rows_kernel<4, 1>), dim3(M), b256, 0, s, x, M, K, a.x_q, a.s_x);
+    else if (C <= 512)
+      hipLaunchKernelGGL((w4a8_quant_rows_kernel<4, 2>), dim3(M), b256, 0, s, x, M, K, a.x_q, a.s_x);
+    else if (C <= 1024)
+      hipLaunchKernelGGL((w4a8_quant_rows_kernel<4, 4>), dim3(M), b256, 0, s, x, M, K, a.x_q, a.s_x);
+    else if (C <= 2048)
+      hipLaunchKernelGGL((w4a8_quant_rows_kernel<4, 8>), dim3(M), b256, 0, s, x, M, K, a.x_q, a.s_x);
+    else
+      hipLaunchKernelGGL(w4a8_quant_kernel, dim3(M), b256, 0, s, x, K, a.x_q, a.s_x);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // largest tile whose grid still gives every CU at least two workgroups

@@ -73,3 +73,59 @@ def test_k_not_multiple_of_stage(M, N, K):
     # and span several row and column tiles with ragged edges
     case = si.w4a8_case(M, N, K, seed=(44, M, N, K), name=f"w4a8_M{M}_N{N}_K{K}")
     _check(case)
+
+
+@pytest.mark.parametrize("K", [32, 512, 544, 1024, 2048, 4096, 8192, 16384, 16416])
+def test_quantize_row_lengths(K):
+    # the quantizer holds a row in the registers of one wave (K <= 512), two
+    # (K <= 1024) or four (chunks of 8 values, 1, 2, 4 or 8 per thread up to
+    # K = 16384); K = 16416 takes the one-row-per-block loop.  M = 7 leaves
+    # the last block partly empty.
+    case = si.w4a8_case(7, 40, K, seed=(45, K), name=f"w4a8_quant_K{K}")
+    _check(case)
+
+
+def test_unaligned_activations_rejected():
+    # x one element past a 16-byte boundary: refused before any launch
+    case = si.w4a8_case(7, 96, 256, seed=(46,), name="w4a8_unaligned_x")
+    dev = require_gpu()
+    big = dev16(np.concatenate([np.zeros(1, np.uint16), case.x.reshape(-1)]), "f16", dev)
+    x = big[1:].view(case.M, case.K)
+    assert x.data_ptr() % 16 == 2
+    w = torch.from_numpy(np.ascontiguousarray(case.w_q4).view(np.int32)).to(dev)
+    sw = dev16(case.s_w, "f16", dev)
+    with pytest.raises(qa.QaffError, match="QAFF_E_ALIGN"):
+        qa.qgemm_w4a8(x, w, sw)
+
+
+def test_quantize_every_f16_activation_and_scale():
+    # Every positive finite f16 maximum a (0x0001 .. 0x7BFF) meets every f16
+    # value of magnitude 0 .. a, odd columns negated: rows of 1024 hold a
+    # followed by 1023 of those values (zeros pad the last row of each a).
+    # Codes and scales must match the oracle bit for bit, which holds the
+    # quantizer's division to the IEEE quotient over its whole domain.
+    dev = require_gpu()
+    K, P = 1024, 1023
+    a = np.arange(1, 0x7C00, dtype=np.int64)
+    per_a = (a + P) // P
+    R = int(per_a.sum())
+    row_a = np.repeat(a, per_a)
+    j = np.arange(R) - np.repeat(np.cumsum(per_a) - per_a, per_a)
+    x = np.zeros((R, K), np.uint16)
+    x[:, 0] = row_a
+    for r0 in range(0, R, 1 << 16):
+        r1 = min(R, r0 + (1 << 16))
+        vals = j[r0:r1, None] * P + np.arange(P)[None, :]
+        x[r0:r1, 1:] = np.where(vals <= row_a[r0:r1, None], vals, 0)
+    x[:, 1::2] |= 0x8000
+    print(f"[case] w4a8 quantize, every f16 pair: M={R} K={K}", flush=True)
+    xd = dev16(x, "f16", dev)
+    w = torch.zeros((32, K // 8), dtype=torch.int32, device=dev)
+    sw = torch.ones((32,), dtype=torch.float16, device=dev)
+    _, xq, sx, _ = qa.qgemm_w4a8(xd, w, sw)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.w4a8_quantize_act(x, R, K)
+    np.testing.assert_array_equal(sx.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    got = xq.cpu().numpy()
+    bad = np.argwhere(got != q_ref)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[0]}: x=0x{x[tuple(bad[0])]:04x}"
