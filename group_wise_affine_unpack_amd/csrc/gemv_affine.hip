@@ -31,6 +31,8 @@
 //    input (q/k/v, gate/up), or a whole set of them, then cost one launch.
 #include <type_traits>
 
+#include <vector>
+
 #include "common.h"
 
 namespace qaff {
@@ -201,7 +203,6 @@ struct GemvDesc {
   const void* w;      // [N, K*BITS/32] uint32
   const void* s;      // [N, K/G]
   const void* b;      // [N, K/G]
-  const int32_t* kp;  // [K] column permutation or null
   void* y;            // [M, N]
   int N, K, blk0, ks;  // ks: log2 of the waves that split a row's K
 };
@@ -283,7 +284,6 @@ __global__ __launch_bounds__(256) void gemv_affine_kernel(GemvBatch B) {
   const __amdgpu_buffer_rsrc_t rb =
       make_rsrc(static_cast<const char*>(D.b) + (long)row0 * ng * bsz, (uint32_t)(nrows * ng * bsz));
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(D.x, (uint32_t)(M * K * 2));
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(D.kp, D.kp ? (uint32_t)(K * 4) : 0u);
 
   uint16_t* y = static_cast<uint16_t*>(D.y);
   __shared__ float red[4][R * MT];
@@ -328,28 +328,12 @@ __global__ __launch_bounds__(256) void gemv_affine_kernel(GemvBatch B) {
 
     {
       u32x4_t raw[MT][C::XR];
-      if (D.kp == nullptr) {
+      {
         const uint32_t xo = jok ? k0 * 2u : OOB;
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
           for (int q = 0; q < C::XR; ++q) raw[m][q] = ld128(rx, xo + 16u * q, (uint32_t)min(m0 + m, M - 1) * K * 2u);
-      } else {
-        // act-order: x columns gathered through the permutation
-#pragma unroll
-        for (int q = 0; q < C::XR; ++q) {
-          const u32x4_t i0 = ld128(rk, jok ? (k0 + 8 * q) * 4u : OOB);
-          const u32x4_t i1 = ld128(rk, jok ? (k0 + 8 * q + 4) * 4u : OOB);
-          const uint32_t idx[8] = {i0[0], i0[1], i0[2], i0[3], i1[0], i1[1], i1[2], i1[3]};
-#pragma unroll
-          for (int m = 0; m < MT; ++m) {
-            const uint32_t base = (uint32_t)(m0 + m) * K;
-            uint32_t e[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) e[t] = ld16(rx, jok ? (base + idx[t]) * 2u : OOB);
-            raw[m][q] = u32x4_t{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
-          }
-        }
       }
       uint32_t xp[MT][C::XP];
       float xs[MT][C::NSEG];
@@ -746,9 +730,77 @@ void launch_bits(const GemvBatch& b, int blocks, int sbm, int, hipStream_t s) {
     launch_r<BITS, F16, 4, 4>(b, blocks, sbm, s);
 }
 
+// x_p[m, j] = x[m, k_perm[j]] (16-bit values): one thread per 8 outputs of
+// a row.  An index outside [0, K) reads 0.
+__global__ __launch_bounds__(256) void permute_x_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ kp,
+                                                        uint16_t* __restrict__ xp, int M, int K) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  const int cpr = K / 8;
+  if (i >= (long)M * cpr) return;
+  const int m = (int)(i / cpr), j0 = (int)(i % cpr) * 8;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp, (uint32_t)K * 4u);
+  uint32_t e[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const uint32_t k = ld32(rk, (uint32_t)(j0 + t) * 4u);
+    e[t] = ld16(rx, k < (uint32_t)K ? ((uint32_t)m * K + k) * 2u : OOB);
+  }
+  *reinterpret_cast<u32x4_t*>(xp + (long)m * K + j0) =
+      u32x4_t{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+}
+
+hipError_t launch_gemv_core(const AffineArgs* probs, int count, hipStream_t s);
+
 }  // namespace
 
+// Problems with a column permutation run on a permuted copy of x, written
+// by one small kernel per distinct (x, k_perm) pair into stream-ordered
+// scratch; then every problem takes the unpermuted kernels.
 hipError_t launch_gemv_grouped(const AffineArgs* probs, int count, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  bool any = false;
+  for (int i = 0; i < count; ++i) any |= probs[i].k_perm != nullptr;
+  if (!any) return launch_gemv_core(probs, count, s);
+  std::vector<AffineArgs> q(probs, probs + count);
+  std::vector<int> src(count, -1);  // problem whose permuted x this one shares
+  size_t total = 0;
+  std::vector<size_t> off(count, 0);
+  for (int i = 0; i < count; ++i) {
+    if (!q[i].k_perm) continue;
+    for (int j = 0; j < i && src[i] < 0; ++j)
+      if (q[j].k_perm == q[i].k_perm && probs[j].x == q[i].x && q[j].K == q[i].K) src[i] = j;
+    if (src[i] >= 0) continue;
+    if (q[i].M * q[i].K * 2 >= (int64_t(1) << 31)) return hipErrorNotSupported;
+    off[i] = total;
+    total += ((size_t)q[i].M * q[i].K * 2 + 255) & ~size_t(255);
+  }
+  keep_pool_memory(s);
+  char* scratch = nullptr;
+  hipError_t e = hipMallocAsync((void**)&scratch, total, s);
+  if (e != hipSuccess) return e;
+  for (int i = 0; i < count && e == hipSuccess; ++i) {
+    if (!q[i].k_perm) continue;
+    if (src[i] < 0) {
+      const long chunks = q[i].M * q[i].K / 8;
+      hipLaunchKernelGGL(permute_x_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
+                         static_cast<const uint16_t*>(q[i].x), q[i].k_perm, (uint16_t*)(scratch + off[i]), (int)q[i].M,
+                         (int)q[i].K);
+      e = hipGetLastError();
+      q[i].x = scratch + off[i];
+    } else {
+      q[i].x = q[src[i]].x;
+    }
+    q[i].k_perm = nullptr;
+  }
+  if (e == hipSuccess) e = launch_gemv_core(q.data(), count, s);
+  const hipError_t f = hipFreeAsync(scratch, s);
+  return e != hipSuccess ? e : f;
+}
+
+namespace {
+
+hipError_t launch_gemv_core(const AffineArgs* probs, int count, hipStream_t s) {
   if (count <= 0) return hipSuccess;
   const AffineArgs& a0 = probs[0];
   const int M = (int)a0.M, bits = a0.bits;
@@ -784,7 +836,6 @@ hipError_t launch_gemv_grouped(const AffineArgs* probs, int count, hipStream_t s
       d.w = a.w;
       d.s = a.scales;
       d.b = a.biases;
-      d.kp = a.k_perm;
       d.y = a.y;
       d.N = (int)a.N;
       d.K = (int)a.K;
@@ -794,14 +845,13 @@ hipError_t launch_gemv_grouped(const AffineArgs* probs, int count, hipStream_t s
     }
     if (blocks == 0) continue;
     // 4-bit codes with several x rows, K a multiple of 512, 16-bit scales
-    // and biases of the activation type and no column permutation: the
-    // skinny MFMA kernel
+    // and biases of the activation type: the skinny MFMA kernel
     bool mfma = bits == 4 && M >= MFMA_MIN_M && sbm != 2 && (a0.G == 32 || a0.G == 64 || a0.G == 128);
     for (int i = 0; mfma && i < b.count; ++i) {
       const GemvDesc& d = b.d[i];
       // whole 512-code stages, and rows of scales and biases a multiple of
       // 16 bytes, so that every chunk load is aligned
-      mfma = d.kp == nullptr && d.K % 512 == 0 && (d.K / a0.G) % 8 == 0 && (int64_t)d.K * 32 < (int64_t(1) << 31) &&
+      mfma = d.K % 512 == 0 && (d.K / a0.G) % 8 == 0 && (int64_t)d.K * 32 < (int64_t(1) << 31) &&
              (((uintptr_t)d.w | (uintptr_t)d.s | (uintptr_t)d.b) & 15) == 0;
     }
     if (mfma) {
@@ -832,6 +882,8 @@ hipError_t launch_gemv_grouped(const AffineArgs* probs, int count, hipStream_t s
   }
   return hipSuccess;
 }
+
+}  // namespace
 
 hipError_t launch_gemv_affine(const AffineArgs& a, hipStream_t s) { return launch_gemv_grouped(&a, 1, s); }
 

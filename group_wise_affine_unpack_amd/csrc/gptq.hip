@@ -5,119 +5,297 @@
 //   scales  [K/G, N] f16;  g_idx [K] int32 (act-order) or NULL (i/G)
 //   W[n,i] = scale[g,n] * (q - (z_stored + 1)),  g = g_idx[i]
 //
-// qmm_gptq (direct kernel): split-K over workgroups and waves, one lane per
-// output column, an LDS table for the act-order group lookup; described at
-// the kernel below.
+// qmm_gptq (direct kernel): split-K over workgroups and waves, up to four
+// adjacent output columns per lane, an LDS table for the act-order group
+// lookup; described at the kernel below.
 //
 // gptq_to_affine_repack (kernel part): gathers codes through the permutation
 // (computed on the host) into the affine [N, K/8] layout and writes the
 // transposed scales and the biases -scale*(z+1).
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 
 namespace qaff {
 namespace {
 
-constexpr int COLS = 64;   // columns per workgroup: one per lane
-constexpr int WAVES = 8;   // waves per workgroup, each on its own slice of K
-constexpr int KW_MAX = 16; // word rows a wave loads at once
+constexpr int GW = 8;      // waves per workgroup, each on its own part of the K slice
+constexpr int KB = 16;     // most word rows of one wave (all held in registers)
+constexpr uint32_t OOB = 0x80000000u;  // a buffer offset past any range: the load reads 0
+constexpr int kMaxLds = 160 * 1024;    // LDS of one CU
 
 __device__ __forceinline__ uint32_t nib(uint32_t w, int j) { return (w >> (4 * j)) & 0xFu; }
 
-// Direct GPTQ GEMV/GEMM for small M.  Workgroup (cg, sp): columns
-// [64cg, 64cg+64) (lane = column; consecutive lanes read consecutive words of
-// a qweight row, so every load is one coalesced 256-byte row piece) and K
-// slice sp of S.  Its 8 waves split the slice again.  Each wave loads all its
-// weight words first; meanwhile the workgroup builds an LDS table of
-// (scale, -scale*(z+1)) in fp32 for every group and column, so the
-// act-order lookup g_idx[k] -> table row is one LDS read per code and the
-// weight is exact in fp32: W = scale*q + bias.  x and g_idx values are
-// uniform across the wave and arrive through scalar loads.  The waves meet
-// in LDS; the slice's sum goes to an fp32 partial buffer [S][M][N], and a
-// second kernel adds the S partials into y.
-template <int MT>  // rows of x per pass
-__global__ __launch_bounds__(COLS * WAVES) void gptq_direct_kernel(
+template <int CPL> struct WordsT;
+template <> struct WordsT<1> { typedef uint32_t T; };
+template <> struct WordsT<2> { typedef u32x2_t T; };
+template <> struct WordsT<4> { typedef u32x4_t T; };
+
+// CPL consecutive qweight words of one row (buffer load; an offset past the
+// range reads zeros)
+template <int CPL>
+__device__ __forceinline__ typename WordsT<CPL>::T load_words(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (CPL == 4)
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  else if constexpr (CPL == 2)
+    return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  else
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+template <int CPL>
+__device__ __forceinline__ uint32_t word_of(const typename WordsT<CPL>::T& v, int c) {
+  if constexpr (CPL == 1) return v;
+  else return v[c];
+}
+
+// (scale, bias) table of one workgroup in LDS: per group, CPL pairs for each
+// of the 64 lanes.  Pairs of two adjacent columns of a lane form one 16-byte
+// entry and the 64 lanes' entries are consecutive, so a lane reads its
+// columns' pairs with CPL/2 conflict-free 16-byte reads (one 8-byte read
+// when CPL == 1).
+template <int CPL>
+struct GTab {
+  static constexpr int COLS = 64 * CPL;     // columns per workgroup
+  static constexpr int GBYTES = COLS * 8;   // bytes per group
+  static __device__ __forceinline__ int off(int c) {  // column c of the workgroup
+    if constexpr (CPL == 1) return c * 8;
+    const int ln = c / CPL, j = c % CPL;
+    return ((j >> 1) * 64 + ln) * 16 + (j & 1) * 8;
+  }
+};
+
+// LDS of one workgroup, in bytes: the (scale, bias) table, the slice's
+// group offsets (one int per code), MT rows of x for the slice (fp32), and
+// the waves' partial sums.
+struct DirectLds {
+  int tab, goff, xs, red, total;
+  __host__ __device__ DirectLds(int ng, int cpl, int mt, int per_sp) {
+    tab = 0;
+    goff = ng * 64 * cpl * 8;
+    xs = goff + per_sp * 8 * 4;
+    red = xs + mt * per_sp * 8 * 4;
+    total = red + GW * mt * 64 * cpl * 4;
+  }
+};
+
+// Direct GPTQ GEMV / small GEMM.  Workgroup (cg, sp): columns
+// [COLS cg, COLS cg + COLS), COLS = 64 CPL, lane l holding columns CPL l ..
+// CPL l + CPL - 1, and word rows of K slice sp of S, which its GW waves split
+// again.  A lane reads CPL adjacent qweight words of a row with one load,
+// so a wave reads 256 CPL contiguous bytes per row: whole cache lines when
+// CPL = 4.  The workgroup first builds an LDS table of (scale, -scale*(z+1))
+// in fp32 for every group and column, so the act-order lookup
+// g_idx[k] -> table row is one LDS read per code and two columns, and the
+// weight is exact in fp32: W = scale*q + bias.  The slice's table offsets
+// (from g_idx) and x values (fp32) are staged in LDS too, so the loop
+// issues LDS reads only, which complete in order and pipeline.  Codes become
+// floats with byte conversions (even and odd nibbles masked into bytes).
+// The waves meet in LDS; each slice writes fp32 partials [S][M][N], and a
+// second kernel adds the S partials into y.  Rows of x go MT at a time; the
+// table serves every pass.
+template <int CPL, int MT, bool ACT>
+__global__ __launch_bounds__(64 * GW) void gptq_direct_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint32_t* __restrict__ qz,
     const uint16_t* __restrict__ sc, const int32_t* __restrict__ g_idx, float* __restrict__ part, int M, int N,
-    int K, int G, int S) {
-  extern __shared__ float2 tab[];  // [ng][COLS] (scale, bias)
-  __shared__ float red[WAVES][MT][COLS];
-  const int ng = K / G;
+    int K, int gsh, int S) {
+  using T = GTab<CPL>;
+  using W = typename WordsT<CPL>::T;
+  constexpr int COLS = T::COLS;
+  constexpr int GB_SHIFT = CPL == 4 ? 11 : (CPL == 2 ? 10 : 9);  // log2(GBYTES)
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int ng = K >> gsh;
   const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int ncg = (N + COLS - 1) / COLS;
   const int cg = blockIdx.x % ncg, sp = blockIdx.x / ncg;
-  const int n0 = cg * COLS, n = n0 + lane;
-  const bool live = n < N;
-  const int ncol = live ? n : N - 1;
+  const int n0 = cg * COLS;
 
-  // this wave's word rows: slice sp of S, part `wave` of WAVES
+  // this wave's word rows: slice sp of S, part `wave` of GW
   const int nw = K / 8;
   const int per_sp = (nw + S - 1) / S;
   const int sp0 = sp * per_sp, sp1 = min(nw, sp0 + per_sp);
-  const int per_w = (sp1 - sp0 + WAVES - 1) / WAVES;
+  const int per_w = (sp1 - sp0 + GW - 1) / GW;
   const int kw0 = min(sp1, sp0 + wave * per_w), kw1 = min(sp1, kw0 + per_w);
+  const DirectLds L(ng, CPL, MT, per_sp);
+  int* goff = reinterpret_cast<int*>(lds + L.goff);
+  float* xs = reinterpret_cast<float*>(lds + L.xs);
+  float* red = reinterpret_cast<float*>(lds + L.red);  // [GW][MT][COLS]
 
-  // the first batch of this wave's weight words, in flight during the table build
-  uint32_t wv[KW_MAX];
-#pragma unroll
-  for (int j = 0; j < KW_MAX; ++j) wv[j] = j < kw1 - kw0 ? qw[(long)(kw0 + j) * N + ncol] : 0u;
+  // N % 8 == 0, so a lane's CPL columns are all inside N or all past it
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qw, (uint32_t)nw * (uint32_t)N * 4u);
+  const uint32_t loff = n0 + lane * CPL < N ? (uint32_t)(n0 + lane * CPL) * 4u : OOB;
+  const uint32_t row_bytes = (uint32_t)N * 4u;
 
-  for (int i = t; i < ng * COLS; i += COLS * WAVES) {
-    const int g = i / COLS, c = i % COLS, nn = n0 + c;
-    float2 e = make_float2(0.f, 0.f);
-    if (nn < N) {
-      const float sv = f16_bits_to_f32(sc[(long)g * N + nn]);
-      const float z = (float)nib(qz[(long)g * (N / 8) + nn / 8], nn % 8) + 1.f;
-      e = make_float2(sv, -sv * z);  // exact: an 11-bit scale times a 5-bit integer
-    }
-    tab[i] = e;
-  }
-  __syncthreads();
-
-  for (int m0 = 0; m0 < M; m0 += MT) {
-    float acc[MT];
+  // Set-up: every global load is issued before any is used, so the weight
+  // rows (all of this wave's: at most KB), the table sources, the codes'
+  // groups and the first rows of x share one memory latency.
+  W wv[KB];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) acc[m] = 0.f;
-    for (int kb = kw0; kb < kw1; kb += KW_MAX) {
-      const int cnt = min(KW_MAX, kw1 - kb);
-      if (kb != kw0 || m0 != 0) {
+  for (int j = 0; j < KB; ++j) wv[j] = load_words<CPL>(rq, kw0 + j < kw1 ? loff + (uint32_t)(kw0 + j) * row_bytes : OOB);
+  // table sources: chunk i = (group, 8 columns), a qzeros word and 8 scales
+  constexpr int TC = 3;  // chunks per thread: ng * COLS / 8 <= 3 * 64 * GW
+  const int nchunk = ng * (COLS / 8);
+  const bool sc16 = ((uintptr_t)sc & 15) == 0;
+  u32x4_t sv[TC];
+  uint32_t zv[TC];
 #pragma unroll
-        for (int j = 0; j < KW_MAX; ++j) wv[j] = j < cnt ? qw[(long)(kb + j) * N + ncol] : 0u;
+  for (int u = 0; u < TC; ++u) {
+    const int i = t + u * 64 * GW;
+    const int g = i / (COLS / 8), n = n0 + 8 * (i % (COLS / 8));
+    sv[u] = u32x4_t{0, 0, 0, 0};
+    zv[u] = 0;
+    if (i < nchunk && n < N) {
+      zv[u] = qz[(long)g * (N / 8) + n / 8];
+      const uint16_t* sp8 = sc + (long)g * N + n;
+      if (sc16) {
+        sv[u] = *reinterpret_cast<const u32x4_t*>(sp8);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sv[u][j] = (uint32_t)sp8[2 * j] | (uint32_t)sp8[2 * j + 1] << 16;
       }
+    }
+  }
+  // the slice's codes (at most 8 KB = 2 per thread): their groups
+  const int nk = (sp1 - sp0) * 8;
+  int gv[2];
 #pragma unroll
-      for (int j = 0; j < KW_MAX; ++j) {
-        if (j < cnt) {  // uniform
+  for (int u = 0; u < 2; ++u) {
+    const int i = t + u * 64 * GW, k = sp0 * 8 + i;
+    gv[u] = i < nk ? (ACT ? g_idx[k] : k >> gsh) : 0;
+  }
+  // x rows m0 .. m0+MT-1 over the slice, in f16 pairs (MT per thread)
+  auto load_x = [&](int m0, uint32_t (&xp)[MT]) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int k = (kb + j) * 8 + e;
-          const int g = g_idx ? g_idx[k] : k / G;
-          const float2 sb = tab[g * COLS + lane];
-          const float wk = fmaf(sb.x, (float)nib(wv[j], e), sb.y);
+    for (int u = 0; u < MT; ++u) {
+      const int i = t + u * 64 * GW, m = i / (nk / 2), kk = 2 * (i % (nk / 2));
+      xp[u] = 0;
+      if (i < MT * (nk / 2) && m0 + m < M)
+        xp[u] = *reinterpret_cast<const uint32_t*>(x + (long)(m0 + m) * K + sp0 * 8 + kk);
+    }
+  };
+  auto store_x = [&](const uint32_t (&xp)[MT]) {
+#pragma unroll
+    for (int u = 0; u < MT; ++u) {
+      const int i = t + u * 64 * GW, m = i / (nk / 2), kk = 2 * (i % (nk / 2));
+      if (i < MT * (nk / 2))
+        *reinterpret_cast<float2*>(xs + m * per_sp * 8 + kk) =
+            make_float2(f16_bits_to_f32(xp[u] & 0xFFFFu), f16_bits_to_f32(xp[u] >> 16));
+    }
+  };
+  uint32_t xp[MT];
+  load_x(0, xp);
+
+  // LDS: the table, then the offsets and x
+#pragma unroll
+  for (int u = 0; u < TC; ++u) {
+    const int i = t + u * 64 * GW;
+    if (i < nchunk) {
+      const int g = i / (COLS / 8), c8 = i % (COLS / 8);
+      unsigned char* row = lds + L.tab + g * T::GBYTES;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float sj = f16_bits_to_f32(j & 1 ? sv[u][j >> 1] >> 16 : sv[u][j >> 1] & 0xFFFFu);
+        const float z = (float)nib(zv[u], j) + 1.f;
+        // exact: an 11-bit scale times a 5-bit integer (columns past N: 0, 0)
+        *reinterpret_cast<float2*>(row + T::off(8 * c8 + j)) = make_float2(sj, -sj * z);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = t + u * 64 * GW;
+    if (i < nk) goff[i] = gv[u] << GB_SHIFT;  // the code's group row in the table
+  }
+  store_x(xp);
+
+  const int lane_off = L.tab + T::off(lane * CPL);  // this lane's first entry in a group row
+  // the nibble mask, hidden from the optimizer: knowing that each byte holds
+  // 4 bits, it would turn the byte conversions below into bit-field
+  // extracts plus a conversion
+  uint32_t m4 = 0x0F0F0F0Fu;
+  for (int m0 = 0; m0 < M; m0 += MT) {
+    // (hidden again in every pass, which also keeps the compiler from
+    // hoisting the unpacked codes of all rows out of the pass loop)
+    asm volatile("" : "+s"(m4));
+    if (m0 != 0) {
+      load_x(m0, xp);
+      __syncthreads();  // every wave done with the last pass's x and sums
+      store_x(xp);
+    }
+    __syncthreads();
+    float acc[MT][CPL];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) acc[m][c] = 0.f;
+    {
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        const int kw = kw0 + j;
+        if (kw < kw1) {  // uniform
+          const int r8 = (kw - sp0) * 8;  // the row's first code in the slice
+          uint32_t lo[CPL], hi[CPL];
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            const uint32_t w = word_of<CPL>(wv[j], c);
+            lo[c] = w & m4;          // codes 0, 2, 4, 6 in bytes 0..3
+            hi[c] = (w >> 4) & m4;   // codes 1, 3, 5, 7
+          }
+          const i32x4_t go0 = *reinterpret_cast<const i32x4_t*>(goff + r8);
+          const i32x4_t go1 = *reinterpret_cast<const i32x4_t*>(goff + r8 + 4);
+          f32x4_t xv[MT][2];
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
-            const int mm = m0 + m < M ? m0 + m : M - 1;
-            acc[m] = fmaf(f16_bits_to_f32(x[(long)mm * K + k]), wk, acc[m]);
+            xv[m][0] = *reinterpret_cast<const f32x4_t*>(xs + m * per_sp * 8 + r8);
+            xv[m][1] = *reinterpret_cast<const f32x4_t*>(xs + m * per_sp * 8 + r8 + 4);
           }
+          // all 8 codes' table reads first, so they are in flight together
+          float sb[8][2 * CPL];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int go = e < 4 ? go0[e] : go1[e - 4];
+            const unsigned char* ent = lds + go + lane_off;
+            if constexpr (CPL == 1) {
+              const float2 v = *reinterpret_cast<const float2*>(ent);
+              sb[e][0] = v.x;
+              sb[e][1] = v.y;
+            } else {
+#pragma unroll
+              for (int h = 0; h < CPL / 2; ++h) {
+                const f32x4_t v = *reinterpret_cast<const f32x4_t*>(ent + h * 1024);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sb[e][4 * h + i] = v[i];
+              }
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+              const uint32_t src = (e & 1) ? hi[c] : lo[c];
+              const float q = (float)(uint8_t)(src >> (8 * (e >> 1)));  // v_cvt_f32_ubyteN
+              const float w = fmaf(sb[e][2 * c], q, sb[e][2 * c + 1]);
+#pragma unroll
+              for (int m = 0; m < MT; ++m) acc[m][c] = fmaf(xv[m][e >> 2][e & 3], w, acc[m][c]);
+            }
         }
-        }
+        __builtin_amdgcn_sched_barrier(0);  // one row's reads at a time: bounded registers
       }
     }
 #pragma unroll
-    for (int m = 0; m < MT; ++m) red[wave][m][lane] = acc[m];
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) red[(wave * MT + m) * COLS + lane * CPL + c] = acc[m][c];
     __syncthreads();
-    if (wave == 0 && live) {
+    for (int i = t; i < MT * COLS; i += 64 * GW) {
+      const int m = i / COLS, c = i % COLS;
+      if (m0 + m < M && n0 + c < N) {
+        float v = 0.f;
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (m0 + m < M) {
-          float v = 0.f;
-#pragma unroll
-          for (int q = 0; q < WAVES; ++q) v += red[q][m][lane];
-          part[((long)sp * M + m0 + m) * N + n] = v;
-        }
+        for (int q = 0; q < GW; ++q) v += red[(q * MT + m) * COLS + c];
+        part[((long)sp * M + m0 + m) * N + n0 + c] = v;
       }
     }
-    __syncthreads();
   }
 }
 
@@ -169,30 +347,73 @@ __global__ __launch_bounds__(256) void gptq_repack_params_kernel(const uint32_t*
 
 }  // namespace
 
+template <int CPL, int MT, bool ACT>
+hipError_t launch_direct(const GptqArgs& a, float* part, int S, hipStream_t s) {
+  const int64_t ncg = (a.N + 64 * CPL - 1) / (64 * CPL);
+  const int per_sp = (int)((a.K / 8 + S - 1) / S);
+  const size_t lds = (size_t)DirectLds((int)(a.K / a.G), CPL, MT, per_sp).total;
+  const auto k = gptq_direct_kernel<CPL, MT, ACT>;
+  // the dynamic LDS limit is raised once per kernel and device, to the most
+  // any launch of it asks for
+  static std::once_flag once[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [&] {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)kMaxLds);
+  });
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k, dim3((unsigned)(ncg * S)), dim3(64 * GW), lds, s, (const uint16_t*)a.x,
+                     (const uint32_t*)a.qweight, (const uint32_t*)a.qzeros, (const uint16_t*)a.scales, a.g_idx, part,
+                     (int)a.M, (int)a.N, (int)a.K, a.G == 32 ? 5 : (a.G == 64 ? 6 : 7), S);
+  return hipGetLastError();
+}
+
+template <int CPL>
+hipError_t launch_direct_m(const GptqArgs& a, int mt, float* part, int S, hipStream_t s) {
+  if (a.g_idx) {
+    if (mt == 1) return launch_direct<CPL, 1, true>(a, part, S, s);
+    if (mt == 2) return launch_direct<CPL, 2, true>(a, part, S, s);
+    if (mt == 4) return launch_direct<CPL, 4, true>(a, part, S, s);
+    return launch_direct<CPL, 8, true>(a, part, S, s);
+  }
+  if (mt == 1) return launch_direct<CPL, 1, false>(a, part, S, s);
+  if (mt == 2) return launch_direct<CPL, 2, false>(a, part, S, s);
+  if (mt == 4) return launch_direct<CPL, 4, false>(a, part, S, s);
+  return launch_direct<CPL, 8, false>(a, part, S, s);
+}
+
 hipError_t launch_gptq_direct(const GptqArgs& a, hipStream_t s) {
-  const int ng = (int)(a.K / a.G);
-  const size_t lds = (size_t)ng * COLS * sizeof(float2);
-  if (lds > 96 * 1024) return hipErrorNotSupported;  // group table must fit in LDS
-  const int64_t ncg = (a.N + COLS - 1) / COLS;
+  const int64_t ng = a.K / a.G;
+  // columns per lane: 4 when the (scale, bias) table of 256 columns fits
+  // 64 KiB of LDS, else 2, else 1 (up to 96 KiB)
+  const int cpl = ng <= 32 ? 4 : (ng <= 64 ? 2 : 1);
+  if (ng * 64 * cpl * 8 > 96 * 1024) return hipErrorNotSupported;  // group table must fit in LDS
+  if (a.K / 8 * a.N * 4 >= (int64_t(1) << 31)) return hipErrorNotSupported;  // 32-bit buffer offsets
+  // x rows per pass (8 would spill registers at 4 columns per lane)
+  const int mt = a.M == 1 ? 1 : (a.M == 2 ? 2 : (a.M <= 4 || cpl == 4 ? 4 : 8));
+  const int64_t ncg = (a.N + 64 * cpl - 1) / (64 * cpl);
   const int64_t nw = a.K / 8;
-  // K slices: enough workgroups to fill the chip twice, each wave keeping
-  // at least 4 word rows
-  int S = (int)std::min<int64_t>((512 + ncg - 1) / ncg, std::max<int64_t>(1, nw / (4 * WAVES)));
+  // K slices: enough workgroups to give every CU one, each wave keeping at
+  // least 4 word rows; more slices when the slice's staged x and offsets
+  // would not fit in LDS
+  int S = (int)std::min<int64_t>((256 + ncg - 1) / ncg, std::max<int64_t>(1, nw / (4 * GW)));
+  // a wave holds all its word rows: at most KB, so a slice has at most KB * GW
+  S = (int)std::max<int64_t>(S, (nw + KB * GW - 1) / (KB * GW));
   if (S < 1) S = 1;
+  while (DirectLds((int)ng, cpl, mt, (int)((nw + S - 1) / S)).total > kMaxLds) {
+    if (S >= nw) return hipErrorNotSupported;
+    ++S;
+  }
   const int64_t MN = a.M * a.N;
   keep_pool_memory(s);
   float* part = nullptr;
   hipError_t e = hipMallocAsync((void**)&part, (size_t)S * MN * sizeof(float), s);
   if (e != hipSuccess) return e;
-  if (a.M == 1)
-    hipLaunchKernelGGL((gptq_direct_kernel<1>), dim3((unsigned)(ncg * S)), dim3(COLS * WAVES), lds, s,
-                       (const uint16_t*)a.x, (const uint32_t*)a.qweight, (const uint32_t*)a.qzeros,
-                       (const uint16_t*)a.scales, a.g_idx, part, (int)a.M, (int)a.N, (int)a.K, a.G, S);
-  else
-    hipLaunchKernelGGL((gptq_direct_kernel<8>), dim3((unsigned)(ncg * S)), dim3(COLS * WAVES), lds, s,
-                       (const uint16_t*)a.x, (const uint32_t*)a.qweight, (const uint32_t*)a.qzeros,
-                       (const uint16_t*)a.scales, a.g_idx, part, (int)a.M, (int)a.N, (int)a.K, a.G, S);
-  e = hipGetLastError();
+  e = cpl == 4 ? launch_direct_m<4>(a, mt, part, S, s)
+               : (cpl == 2 ? launch_direct_m<2>(a, mt, part, S, s) : launch_direct_m<1>(a, mt, part, S, s));
   if (e == hipSuccess) {
     hipLaunchKernelGGL(gptq_finalize_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, s, part,
                        (uint16_t*)a.y, (long)MN, S);

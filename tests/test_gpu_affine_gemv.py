@@ -238,3 +238,47 @@ def test_several_rows_k_not_multiple_of_512(K):
     case = si.affine_case(8, 100, K, 64, 4, seed=(32, K), name=f"m8_K{K}")
     y = _run(case)
     assert_float_bar(y, oracle.qmm_affine_case(case), case.name)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("M", [1, 2, 9, 16])
+def test_k_perm_every_width_and_kernel(bits, M):
+    # the permuted copy of x feeds the scalar kernel (M = 1, or 2- and 8-bit
+    # codes) and the matrix-core kernel (4-bit, 2 <= M <= 16, K % 512 == 0)
+    case = si.affine_case(M, 200, 2048, 64, bits, seed=(34, bits, M), name=f"kperm_b{bits}_M{M}")
+    case.k_perm = np.random.default_rng(35).permutation(case.K).astype(np.int32)
+    y = _run(case)
+    assert_float_bar(y, oracle.qmm_affine_case(case), case.name)
+
+
+def test_grouped_k_perm_shared_and_distinct():
+    # problems 0, 1 and 3 share one x tensor and one permutation tensor (one
+    # permuted copy serves them); 2 shares x with another permutation; 4 has
+    # its own x and K
+    dev = require_gpu()
+    K = 1024
+    base = si.affine_case(4, 72, K, 64, 4, seed=(36,), name="kp_shared")
+    perm_a = np.random.default_rng(37).permutation(K).astype(np.int32)
+    perm_b = np.random.default_rng(38).permutation(K).astype(np.int32)
+    cases = [si.affine_case(4, N, K, 64, 4, seed=(39, i), name=f"kp_shared{i}") for i, N in enumerate((72, 40, 96, 8))]
+    for c, p in zip(cases, (perm_a, perm_a, perm_b, perm_a)):
+        c.x = base.x
+        c.k_perm = p
+    other = si.affine_case(4, 56, 2048, 64, 4, seed=(40,), name="kp_other")
+    other.k_perm = np.random.default_rng(41).permutation(2048).astype(np.int32)
+    cases.append(other)
+    x0 = None
+    kp_dev = {}
+    probs = []
+    for c in cases:
+        x, w, s, b, kp = affine_to_device(c, dev)
+        if c.x is base.x:
+            x0 = x if x0 is None else x0
+            x = x0
+            kp = kp_dev.setdefault(id(c.k_perm), kp)
+        probs.append((x, w, s, b, kp))
+    print(f"[case] grouped k_perm shared/distinct count={len(cases)}", flush=True)
+    ys = qa.qgemv_affine_grouped(probs, 64, 4)
+    torch.cuda.synchronize()
+    for c, y in zip(cases, ys):
+        assert_float_bar(host_f64(y), oracle.qmm_affine_case(c), c.name)

@@ -104,3 +104,24 @@ def test_repack_rejects_uneven_groups():
     with pytest.raises(qa.QaffError) as ei:
         qa.gptq_to_affine_repack(qw, qz, s, gi, 64)
     assert ei.value.status == 1
+
+
+@pytest.mark.parametrize("M,N,K,G", [
+    (1, 1000, 1024, 128),   # 4 columns per lane, a partial last column group
+    (5, 2040, 4096, 64),    # 64 groups: 2 columns per lane
+    (9, 264, 4096, 32),     # 128 groups: 1 column per lane, a 64 KiB table
+    (2, 136, 6144, 32),     # 192 groups: a 96 KiB table
+    (20, 520, 2048, 128),   # three passes of x rows (8, 8, 4)
+])
+@pytest.mark.parametrize("act_order", [True, False])
+def test_direct_shapes(M, N, K, G, act_order):
+    dev = require_gpu()
+    case = si.gptq_case(M, K, N, G, seed=(33, M, N, K, G), act_order=act_order, name=f"gptq_M{M}_N{N}_K{K}_G{G}")
+    if not act_order:
+        case.g_idx = None
+    _log(case, "direct shapes")
+    x, qw, qz, s, gi = _dev(case, dev)
+    y = qa.qmm_gptq(x, qw, qz, s, gi, G)
+    torch.cuda.synchronize()
+    ref = oracle.qmm_gptq(case.x, case.qweight, case.qzeros, case.scales, case.g_idx, M, case.K, case.N, case.G)
+    assert_float_bar(host_f64(y), ref, case.name)
