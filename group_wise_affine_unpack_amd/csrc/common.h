@@ -90,8 +90,9 @@ struct AffineArgs {
   int act_dt, s_dt, b_dt;
 };
 
-// keep stream-ordered scratch in the device pool between calls
-void keep_pool_memory(hipStream_t s);
+// scratch of `bytes` for work on stream s: the stream's cached buffer (see
+// workspace.hip); valid until the next call on the same stream
+hipError_t stream_workspace(hipStream_t s, size_t bytes, void** out);
 
 hipError_t launch_gemv_affine(const AffineArgs& a, hipStream_t s);
 // count problems that share M, G, bits and dtypes, in as few launches as possible

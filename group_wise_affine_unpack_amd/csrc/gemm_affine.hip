@@ -29,6 +29,7 @@
 //             global memory straight to registers, are decoded with the
 //             exponent-bias trick (code | 0x6400 = 1024 + code in fp16) and
 //             scaled with packed fp16 math; XCD-aware tile order.
+#include <algorithm>
 #include <mutex>
 
 #include "common.h"
@@ -262,6 +263,8 @@ struct GemmParams {
   int Np, gsh;  // padded row count of the W-side scratch; log2(G) - 5
   int Tm, Tn, per_xcd;
   int out_f16;
+  int S;        // K splits; S > 1 writes fp32 partials [S][M][N] to `part`
+  float* part;
 };
 
 __device__ __forceinline__ f16x2_t h2(uint32_t v) { return __builtin_bit_cast(f16x2_t, v); }
@@ -340,7 +343,8 @@ struct Pipe {
   __amdgpu_buffer_rsrc_t rw, rs, rx;
   uint32_t w_off[2], s_off[2], x_off;
   int half, l32, gsh;
-  int last_kt;     // index of the last K tile
+  int kbase;       // first K tile of this workgroup's split
+  int last_kt;     // index of the last K tile, relative to kbase
   int a_dst;       // this thread's first LDS chunk in a stage
 
   // Loads for K tile kt: the x chunks (into registers; written to LDS one
@@ -350,13 +354,13 @@ struct Pipe {
   // inside its buffer, whatever the hardware does with soffset in its range
   // check; the data is never used.
   __device__ __forceinline__ void issue_x(int kt, u32x4_t (&xr)[A_DMA]) const {
-    kt = min(kt, last_kt);
+    kt = kbase + min(kt, last_kt);
 #pragma unroll
     for (int i = 0; i < A_DMA; ++i)
       xr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, x_off, kt * (MB * 32 * 128) + i * 4096, 0));
   }
   __device__ __forceinline__ void issue_w(int kt, St& st) const {
-    kt = min(kt, last_kt);
+    kt = kbase + min(kt, last_kt);
     // group of this tile: (2*kt + half) >> gsh, whose lane part (half, for
     // G = 32 only) is folded into s_off; the rest is uniform
     const int sg = ((2 * kt) >> gsh) * PS * 4;
@@ -521,11 +525,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int STAGE_BYTES = BM * 128; // one x tile, 64 fp16 per row, no padding
 
   const int b = blockIdx.x;
-  const int v = (b & 7) * p.per_xcd + (b >> 3);
-  if (v >= p.Tm * p.Tn) return;
+  const int vs = (b & 7) * p.per_xcd + (b >> 3);
+  if (vs >= p.Tm * p.Tn * p.S) return;
+  const int v = vs / p.S, sp = vs % p.S;
   const int tm = v / p.Tn, tn = v % p.Tn;
   const int m0 = tm * BM, n0 = tn * BN;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l32 = lane & 31, half = lane >> 5;
+  // K tiles [kt0, kt1) of split sp
+  const int nkt_all = p.K / BK, per_split = (nkt_all + p.S - 1) / p.S;
+  const int kt0 = sp * per_split, kt1 = min(nkt_all, kt0 + per_split);
 
   __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) int em_s[BM];
@@ -563,7 +571,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     P.a_dst = t * 16;
   }
 
-  const int nkt = p.K / BK;
+  const int nkt = kt1 - kt0;
+  P.kbase = kt0;
   P.last_kt = nkt - 1;
   St st0, st1, st2, st3;
   u32x4_t xr[MB];
@@ -596,9 +605,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 
   // ---- tail: sum_g xs * cb on bf16 MFMA, operands straight from global
-  // (L2-resident).  It runs after the main loop so that its loads do not
-  // blur the compiler's count of outstanding loads at the loop header.
-  {
+  // (L2-resident), in the first split only.  It runs after the main loop so
+  // that its loads do not blur the compiler's count of outstanding loads at
+  // the loop header.
+  if (sp == 0) {
     const uint16_t* tb_row[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) tb_row[nb] = p.tB + (long)(n0 + wave * 64 + nb * 32 + l32) * p.Kt + 8 * half;
@@ -623,6 +633,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // 8*(r/4) + 4*half + r%4.  Stores go through a buffer resource over y: a
   // column past N starts from an out-of-range offset and a row past M lands
   // past the range, so neither is written.
+  if (p.S > 1) {
+    // fp32 partial of split sp, scaled (exact: a power of two); rows past M
+    // land past the range, columns past N start from an out-of-range offset
+    const __amdgpu_buffer_rsrc_t rp =
+        make_rsrc(p.part + (long)sp * p.M * p.N, (uint32_t)p.M * p.N * 4);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int n = n0 + wave * 64 + nb * 32 + l32;
+      const bool nok = n < p.N;
+      const int e_n = nok ? p.en[n] : 0;
+      const uint32_t vb = nok ? ((uint32_t)(m0 + 4 * half) * p.N + n) * 4u : 0x80000000u;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const i32x4_t e4 = *reinterpret_cast<const i32x4_t*>(&em_s[mb * 32 + 8 * rq + 4 * half]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ldexpf(acc[mb][nb][4 * rq + j], e4[j] + e_n)), rp,
+                                                  vb + (uint32_t)((mb * 32 + 8 * rq + j) * p.N) * 4u, 0, 0);
+        }
+    }
+    return;
+  }
   const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.y, (uint32_t)p.M * p.N * 2);
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
@@ -647,6 +681,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 // ---------------------------------------------------------------------------
 
+// y = the sum of the S fp32 partials, rounded to the activation type
+__global__ __launch_bounds__(256) void gemm_split_sum_kernel(const float* __restrict__ part, uint16_t* __restrict__ y,
+                                                             long MN, int S, int out_f16) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= MN) return;
+  float v = 0.f;
+  for (int s = 0; s < S; ++s) v += part[(long)s * MN + i];
+  y[i] = out_f16 ? f32_to_f16_bits(v) : f32_to_bf16_bits(v);
+}
+
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 template <int BITS, int PS>
@@ -667,6 +711,16 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
   }
   const int BM = MB * 32;
   const int Mp = (M + BM - 1) / BM * BM, Np = (N + BN - 1) / BN * BN;
+  // K splits when the tiles leave CUs idle: enough workgroups for every CU,
+  // each split at least 4 K tiles, partials within 32-bit buffer offsets
+  const int64_t tiles = (int64_t)(Mp / BM) * (Np / BN);
+  int S = 1;
+  if (tiles < 256) {
+    S = (int)std::min<int64_t>((256 + tiles - 1) / tiles, std::max(1, K / BK / 4));
+    while (S > 1 && (int64_t)S * M * N * 4 >= (int64_t(1) << 31)) --S;
+    const int per = (K / BK + S - 1) / S;
+    S = (K / BK + per - 1) / per;  // no empty split
+  }
 
   const size_t o_xh = 0, s_xh = align256((size_t)Mp * K * 2);
   const size_t o_ta = o_xh + s_xh, s_ta = align256((size_t)Mp * Kt * 2);
@@ -674,11 +728,11 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
   const size_t o_sh = o_em + s_em, s_sh = align256((size_t)Np * ng * PS * 4);
   const size_t o_tb = o_sh + s_sh, s_tb = align256((size_t)Np * Kt * 2);
   const size_t o_en = o_tb + s_tb, s_en = align256((size_t)Np * 4);
-  const size_t total = o_en + s_en;
+  const size_t o_pt = o_en + s_en, s_pt = S > 1 ? align256((size_t)S * M * N * 4) : 0;
+  const size_t total = o_pt + s_pt;
 
-  keep_pool_memory(s);
   char* scratch = nullptr;
-  hipError_t e = hipMallocAsync((void**)&scratch, total, s);
+  hipError_t e = stream_workspace(s, total, (void**)&scratch);
   if (e != hipSuccess) return e;
 
   _Float16* xh = (_Float16*)(scratch + o_xh);
@@ -734,6 +788,9 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
   p.Tn = Np / BN;
   p.per_xcd = (p.Tm * p.Tn + 7) / 8;
   p.out_f16 = a.act_dt == F16;
+  p.S = S;
+  p.part = S > 1 ? (float*)(scratch + o_pt) : nullptr;
+  p.per_xcd = (p.Tm * p.Tn * S + 7) / 8;
   const dim3 grid(8 * p.per_xcd);
   if (MB == 2)
     hipLaunchKernelGGL((gemm_affine_kernel<BITS, PS, 2>), grid, dim3(256), 0, s, p);
@@ -742,8 +799,13 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
   else
     hipLaunchKernelGGL((gemm_affine_kernel<BITS, PS, 8>), grid, dim3(256), 0, s, p);
   e = hipGetLastError();
-  hipError_t f = hipFreeAsync(scratch, s);
-  return e != hipSuccess ? e : f;
+  if (e == hipSuccess && S > 1) {
+    const long MN = (long)M * N;
+    hipLaunchKernelGGL(gemm_split_sum_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, s, p.part,
+                       (uint16_t*)a.y, MN, S, p.out_f16);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 template <int BITS>
@@ -756,23 +818,6 @@ hipError_t run_bits(const AffineArgs& a, hipStream_t s) {
 }
 
 }  // namespace
-
-static std::once_flag g_pool_once[64];
-
-// Stream-ordered scratch comes from the device's default pool; keep what is
-// freed there instead of returning it to the driver after every call.
-void keep_pool_memory(hipStream_t s) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return;
-  std::call_once(g_pool_once[dev], [dev] {
-    hipMemPool_t pool;
-    if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
-      uint64_t thr = UINT64_MAX;  // keep freed scratch in the pool instead of returning it
-      (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
-    }
-  });
-  (void)s;
-}
 
 hipError_t launch_gemm_affine(const AffineArgs& a, hipStream_t s) {
   // whole 64-code K tiles only; otherwise the GEMV kernel runs on slices of

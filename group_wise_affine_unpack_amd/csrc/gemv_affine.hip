@@ -755,8 +755,8 @@ hipError_t launch_gemv_core(const AffineArgs* probs, int count, hipStream_t s);
 }  // namespace
 
 // Problems with a column permutation run on a permuted copy of x, written
-// by one small kernel per distinct (x, k_perm) pair into stream-ordered
-// scratch; then every problem takes the unpermuted kernels.
+// by one small kernel per distinct (x, k_perm) pair into the stream's
+// workspace; then every problem takes the unpermuted kernels.
 hipError_t launch_gemv_grouped(const AffineArgs* probs, int count, hipStream_t s) {
   if (count <= 0) return hipSuccess;
   bool any = false;
@@ -775,9 +775,8 @@ hipError_t launch_gemv_grouped(const AffineArgs* probs, int count, hipStream_t s
     off[i] = total;
     total += ((size_t)q[i].M * q[i].K * 2 + 255) & ~size_t(255);
   }
-  keep_pool_memory(s);
   char* scratch = nullptr;
-  hipError_t e = hipMallocAsync((void**)&scratch, total, s);
+  hipError_t e = stream_workspace(s, total, (void**)&scratch);
   if (e != hipSuccess) return e;
   for (int i = 0; i < count && e == hipSuccess; ++i) {
     if (!q[i].k_perm) continue;
@@ -794,8 +793,7 @@ hipError_t launch_gemv_grouped(const AffineArgs* probs, int count, hipStream_t s
     q[i].k_perm = nullptr;
   }
   if (e == hipSuccess) e = launch_gemv_core(q.data(), count, s);
-  const hipError_t f = hipFreeAsync(scratch, s);
-  return e != hipSuccess ? e : f;
+  return e;
 }
 
 namespace {

@@ -408,9 +408,8 @@ hipError_t launch_gptq_direct(const GptqArgs& a, hipStream_t s) {
     ++S;
   }
   const int64_t MN = a.M * a.N;
-  keep_pool_memory(s);
   float* part = nullptr;
-  hipError_t e = hipMallocAsync((void**)&part, (size_t)S * MN * sizeof(float), s);
+  hipError_t e = stream_workspace(s, (size_t)S * MN * sizeof(float), (void**)&part);
   if (e != hipSuccess) return e;
   e = cpl == 4 ? launch_direct_m<4>(a, mt, part, S, s)
                : (cpl == 2 ? launch_direct_m<2>(a, mt, part, S, s) : launch_direct_m<1>(a, mt, part, S, s));
@@ -419,8 +418,7 @@ hipError_t launch_gptq_direct(const GptqArgs& a, hipStream_t s) {
                        (uint16_t*)a.y, (long)MN, S);
     e = hipGetLastError();
   }
-  const hipError_t f = hipFreeAsync(part, s);
-  return e != hipSuccess ? e : f;
+  return e;
 }
 
 hipError_t launch_gptq_repack(const int32_t* qweight, const int32_t* qzeros, const void* scales,

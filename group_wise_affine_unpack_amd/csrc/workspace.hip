@@ -1,0 +1,58 @@
+// Per-(device, stream) scratch for the launchers that need device memory
+// beyond their arguments: the GEMM pre-pass buffers, the GPTQ split-K
+// partials and permuted activations.  Work on one stream runs in order, so a
+// stream reuses its buffer call after call and no call allocates once the
+// buffer is large enough; different streams get different buffers.  A
+// buffer only grows (to the next power of two, at least 1 MiB); a grown-out
+// buffer is kept, not freed, because a captured graph may still address it.
+// Growing is refused while the stream is being captured, so a graph is
+// captured after one eager call of the same shapes.
+#include <map>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "common.h"
+
+namespace qaff {
+
+namespace {
+
+struct Workspace {
+  void* p = nullptr;
+  size_t cap = 0;
+};
+
+std::mutex g_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+std::vector<void*> g_retired;  // grown-out buffers, still valid for graphs that captured them
+
+}  // namespace
+
+hipError_t stream_workspace(hipStream_t s, size_t bytes, void** out) {
+  *out = nullptr;
+  if (bytes == 0) return hipSuccess;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_mu);
+  Workspace& w = g_ws[{dev, s}];
+  if (w.cap < bytes) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(s, &cs);
+    if (e != hipSuccess) return e;
+    if (cs != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
+    size_t cap = size_t(1) << 20;
+    while (cap < bytes) cap <<= 1;
+    void* p = nullptr;
+    e = hipMalloc(&p, cap);
+    if (e != hipSuccess) return e;
+    if (w.p) g_retired.push_back(w.p);
+    w.p = p;
+    w.cap = cap;
+  }
+  *out = w.p;
+  return hipSuccess;
+}
+
+}  // namespace qaff

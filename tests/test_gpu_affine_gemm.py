@@ -91,3 +91,12 @@ def test_k_not_multiple_of_tile():
     case = si.affine_case(20, 96, 160, 32, 4, seed=(26,), name="gemm_k160")
     y = _run(case)
     assert_float_bar(host_f64(y), oracle.qmm_affine_case(case), case.name)
+
+
+@pytest.mark.parametrize("M,N,K,bits", [(40, 100, 4160, 4), (33, 520, 1024, 8), (300, 1100, 2048, 2)])
+def test_split_k_partials(M, N, K, bits):
+    # few tiles: K is split over workgroups (65 K tiles into 13 splits of 5
+    # for the first shape) and the fp32 partials are summed by a second kernel
+    case = si.affine_case(M, N, K, 64, bits, seed=(27, M, N, K), name=f"gemm_split_M{M}_N{N}_K{K}_b{bits}")
+    y = _run(case)
+    assert_float_bar(host_f64(y), oracle.qmm_affine_case(case), case.name)
