@@ -299,6 +299,205 @@ __global__ __launch_bounds__(64 * GW) void gptq_direct_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Direct GPTQ on the matrix cores (M >= 8): v_mfma_f32_32x32x16_f16 with the
+// weight split into exact fp16 pieces.  Per column n, with e_n the largest
+// scale exponent of the column (fp16 biased exponent E_n, e_n = E_n - 15):
+//     W[n,k] = 2^e_n * (p_hi + p_lo) * d,   d = q - (z + 1) in [-16, 14]
+// where p_hi + p_lo = scale * 2^-e_n, p_hi its top 6 significant bits and
+// p_lo the rest (5 bits).  Each piece times d has at most 11 significant
+// bits, so both B operands are exact in fp16 (for scales within 2^14 of the
+// column's largest; smaller ones round below 2^-24 of it); x is fp16 as
+// given, products and sums are fp32 in the MFMA, and y = 2^e_n * acc.
+// The per-(group, column) entry (p_hi, p_lo, -(1024 + z + 1)) sits in an LDS
+// table; d comes from the code with the exponent-bias trick:
+// (code | 0x6400) is 1024 + code in fp16.
+// Workgroup: 4 waves x 32 columns, one K slice; lane (l32, half) takes, in
+// 16-code step j, word row 2j + half of the slice: its 8 codes are the
+// lane's B fragment, ordered (c0,c4,c1,c5,c2,c6,c3,c7) by the decode, and
+// its A fragment is x of the same 8 codes, permuted to match.
+constexpr int MG_COLS = 128;
+
+__device__ __forceinline__ uint32_t pair_lo16(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pair_hi16(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
+struct MfmaLds {
+  int tab, emax, goff, total;
+  __host__ __device__ MfmaLds(int ng, int per_sp) {
+    tab = 0;
+    emax = ng * MG_COLS * 8;
+    goff = emax + MG_COLS * 4;
+    total = goff + per_sp * 8 * 4;
+  }
+};
+
+template <int MB, bool ACT>
+__global__ __launch_bounds__(256) void gptq_mfma_kernel(
+    const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint32_t* __restrict__ qz,
+    const uint16_t* __restrict__ sc, const int32_t* __restrict__ g_idx, float* __restrict__ part,
+    uint16_t* __restrict__ y, int M, int N, int K, int gsh, int S, int per_sp) {
+  // per_sp: word rows per slice, even (whole 16-code steps)
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int ng = K >> gsh;
+  const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int l32 = lane & 31, half = lane >> 5;
+  const int ncg = (N + MG_COLS - 1) / MG_COLS;
+  const int cg = blockIdx.x % ncg, sp = blockIdx.x / ncg;
+  const int n0 = cg * MG_COLS;
+  const int nw = K / 8;
+  const int sp0 = min(nw, sp * per_sp), sp1 = min(nw, sp0 + per_sp);
+  const int nsteps = (sp1 - sp0) / 2;
+  const MfmaLds L(ng, per_sp);
+  int* emax = reinterpret_cast<int*>(lds + L.emax);
+  int* goff = reinterpret_cast<int*>(lds + L.goff);
+
+  // ---- table: largest exponent per column, then the entries
+  for (int i = t; i < MG_COLS; i += 256) emax[i] = 0;
+  __syncthreads();
+  const int nchunk = ng * (MG_COLS / 8);
+  for (int i = t; i < nchunk; i += 256) {
+    const int g = i / (MG_COLS / 8), c8 = i % (MG_COLS / 8), n = n0 + 8 * c8;
+    if (n < N) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) atomicMax(&emax[8 * c8 + j], (int)((sc[(long)g * N + n + j] >> 10) & 31));
+    }
+  }
+  __syncthreads();
+  for (int i = t; i < nchunk; i += 256) {
+    const int g = i / (MG_COLS / 8), c8 = i % (MG_COLS / 8), n = n0 + 8 * c8;
+    uint2* row = reinterpret_cast<uint2*>(lds + L.tab + g * MG_COLS * 8) + 8 * c8;
+    if (n < N) {
+      const uint32_t zw = qz[(long)g * (N / 8) + n / 8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float pv = ldexpf(f16_bits_to_f32(sc[(long)g * N + n + j]), 15 - emax[8 * c8 + j]);  // exact
+        const float ph = __uint_as_float(__float_as_uint(pv) & 0xFFFC0000u);  // top 6 significant bits
+        const float pl = pv - ph;                                              // exact: the other 5
+        const uint32_t hl = (uint32_t)f32_to_f16_bits(ph) | (uint32_t)f32_to_f16_bits(pl) << 16;
+        const uint32_t no = f32_to_f16_bits(-1024.f - ((float)nib(zw, j) + 1.f));
+        row[j] = make_uint2(hl, no);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) row[j] = make_uint2(0u, 0u);
+    }
+  }
+  const int nk = (sp1 - sp0) * 8;
+  for (int i = t; i < nk; i += 256) {
+    const int k = sp0 * 8 + i;
+    goff[i] = (ACT ? g_idx[k] : k >> gsh) * (MG_COLS * 8);
+  }
+  __syncthreads();
+
+  const int cl = 32 * wave + l32;  // this lane's column in the workgroup
+  const int n = n0 + cl;
+  const int e_n = emax[cl] - 15;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qw, (uint32_t)nw * (uint32_t)N * 4u);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+  const uint32_t woff = n < N ? (uint32_t)n * 4u : OOB;
+  const unsigned char* tcol = lds + L.tab + cl * 8;
+
+  for (int m0 = 0; m0 < M; m0 += MB * 32) {
+    f32x16_t acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
+    uint32_t xoff[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = m0 + mb * 32 + l32;
+      xoff[mb] = m < M ? (uint32_t)m * (uint32_t)K * 2u : OOB;
+    }
+    auto load = [&](int j, uint32_t& wd, u32x4_t (&a)[MB]) {
+      const int kw = sp0 + 2 * min(j, nsteps - 1) + half;
+      wd = __builtin_amdgcn_raw_buffer_load_b32(rq, woff + (uint32_t)kw * (uint32_t)N * 4u, 0, 0);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        a[mb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[mb] + (uint32_t)kw * 16u, 0, 0));
+    };
+    // LDS side: a step's table offsets are read two steps ahead and its
+    // entries one step ahead, so no step waits on the offset -> entry chain
+    auto read_goff = [&](int j, i32x4_t (&g)[2]) {
+      const int r8 = (2 * min(j, nsteps - 1) + half) * 8;
+      g[0] = *reinterpret_cast<const i32x4_t*>(goff + r8);
+      g[1] = *reinterpret_cast<const i32x4_t*>(goff + r8 + 4);
+    };
+    auto read_ent = [&](const i32x4_t (&g)[2], uint2 (&en)[8]) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) en[e] = *reinterpret_cast<const uint2*>(tcol + g[e >> 2][e & 3]);
+    };
+    // One 16-code step: weight words and x fragments were loaded two steps
+    // before (global), the table entries one step before (LDS); it loads
+    // step j+2 into the buffers it frees, reads the entries of step j+1 and
+    // the offsets of step j+2.  The loop is unrolled by two so the two sets
+    // of buffers alternate without copies.
+    uint32_t magic = 0x64006400u;
+    asm volatile("" : "+v"(magic));
+    i32x4_t gn[2];  // table offsets of the step after the next
+    auto step = [&](int j, uint32_t& wd, u32x4_t (&a)[MB], uint2 (&ent)[8], uint2 (&en)[8]) {
+      const uint32_t w = wd;
+      u32x4_t ax[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) ax[mb] = a[mb];
+      load(j + 2, wd, a);    // two steps ahead (clamped past the end; unused)
+      read_ent(gn, en);      // step j+1
+      read_goff(j + 2, gn);  // step j+2 (the read of gn above is issued first)
+      u32x4_t bh, bl;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        // 1024 + (c_p, c_p+4) in fp16: one v_and_or_b32 with the constant in a VGPR
+        const f16x2_t cp = __builtin_bit_cast(f16x2_t, ((w >> (4 * p)) & 0x000F000Fu) | magic);
+        const f16x2_t d = cp + __builtin_bit_cast(f16x2_t, pair_lo16(ent[p].y, ent[p + 4].y));  // q - (z+1), exact
+        bh[p] = __builtin_bit_cast(uint32_t, d * __builtin_bit_cast(f16x2_t, pair_lo16(ent[p].x, ent[p + 4].x)));
+        bl[p] = __builtin_bit_cast(uint32_t, d * __builtin_bit_cast(f16x2_t, pair_hi16(ent[p].x, ent[p + 4].x)));
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        // x of codes (0,4),(1,5),(2,6),(3,7)
+        const u32x4_t ap = {pair_lo16(ax[mb][0], ax[mb][2]), pair_hi16(ax[mb][0], ax[mb][2]),
+                            pair_lo16(ax[mb][1], ax[mb][3]), pair_hi16(ax[mb][1], ax[mb][3])};
+        const f16x8_t af = __builtin_bit_cast(f16x8_t, ap);
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, __builtin_bit_cast(f16x8_t, bh), acc[mb], 0, 0, 0);
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, __builtin_bit_cast(f16x8_t, bl), acc[mb], 0, 0, 0);
+      }
+    };
+    uint32_t wd0, wd1;
+    u32x4_t a0[MB], a1[MB];
+    load(0, wd0, a0);
+    load(1, wd1, a1);
+    uint2 e0[8], e1[8];
+    {
+      i32x4_t gc[2];
+      read_goff(0, gc);
+      read_ent(gc, e0);
+    }
+    read_goff(1, gn);
+    int j = 0;
+    for (; j + 1 < nsteps; j += 2) {
+      step(j, wd0, a0, e0, e1);
+      step(j + 1, wd1, a1, e1, e0);
+    }
+    if (j < nsteps) step(j, wd0, a0, e0, e1);
+    // accumulator layout: lane -> column l32, register r -> row 8*(r/4) + 4*half + r%4
+    if (n < N) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (m < M) {
+            const float v = ldexpf(acc[mb][r], e_n);
+            if (S > 1)
+              part[((long)sp * M + m) * N + n] = v;
+            else
+              y[(long)m * N + n] = f32_to_f16_bits(v);
+          }
+        }
+    }
+  }
+}
+
 // y[m, n] = f16(sum over the S slices)
 __global__ __launch_bounds__(256) void gptq_finalize_kernel(const float* __restrict__ part, uint16_t* __restrict__ y,
                                                             long MN, int S) {
@@ -385,8 +584,65 @@ hipError_t launch_direct_m(const GptqArgs& a, int mt, float* part, int S, hipStr
   return launch_direct<CPL, 8, false>(a, part, S, s);
 }
 
+template <int MB, bool ACT>
+hipError_t launch_mfma_direct(const GptqArgs& a, float* part, int S, int per_sp, size_t lds, hipStream_t s) {
+  const auto k = gptq_mfma_kernel<MB, ACT>;
+  static std::once_flag once[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [&] {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)kMaxLds);
+  });
+  if (e != hipSuccess) return e;
+  const int64_t ncg = (a.N + MG_COLS - 1) / MG_COLS;
+  hipLaunchKernelGGL(k, dim3((unsigned)(ncg * S)), dim3(256), lds, s, (const uint16_t*)a.x, (const uint32_t*)a.qweight,
+                     (const uint32_t*)a.qzeros, (const uint16_t*)a.scales, a.g_idx, part, (uint16_t*)a.y, (int)a.M,
+                     (int)a.N, (int)a.K, a.G == 32 ? 5 : (a.G == 64 ? 6 : 7), S, per_sp);
+  return hipGetLastError();
+}
+
+// M >= 8 with at most 96 groups: the matrix-core kernel, K split so that
+// the workgroups cover every CU twice (each slice at most 256 word rows),
+// partials summed by the finalize kernel
+hipError_t launch_gptq_mfma(const GptqArgs& a, hipStream_t s) {
+  const int64_t ng = a.K / a.G, nw = a.K / 8;
+  const int64_t ncg = (a.N + MG_COLS - 1) / MG_COLS;
+  // two workgroups per CU (LDS allowing), so that one's waits overlap the other's work
+  int S = (int)std::min<int64_t>((512 + ncg - 1) / ncg, std::max<int64_t>(1, nw / 16));
+  S = (int)std::max<int64_t>(S, (nw + 255) / 256);
+  int per_sp = (int)(((nw + S - 1) / S + 1) & ~int64_t(1));
+  S = (int)((nw + per_sp - 1) / per_sp);  // no empty slice
+  const size_t lds = (size_t)MfmaLds((int)ng, per_sp).total;
+  if (lds > (size_t)kMaxLds) return hipErrorNotSupported;
+  const int64_t MN = a.M * a.N;
+  float* part = nullptr;
+  if (S > 1) {
+    hipError_t e = stream_workspace(s, (size_t)S * MN * sizeof(float), (void**)&part);
+    if (e != hipSuccess) return e;
+  }
+  const int mb = a.M <= 32 ? 1 : 2;
+  hipError_t e;
+  if (a.g_idx)
+    e = mb == 1 ? launch_mfma_direct<1, true>(a, part, S, per_sp, lds, s)
+                : launch_mfma_direct<2, true>(a, part, S, per_sp, lds, s);
+  else
+    e = mb == 1 ? launch_mfma_direct<1, false>(a, part, S, per_sp, lds, s)
+                : launch_mfma_direct<2, false>(a, part, S, per_sp, lds, s);
+  if (e == hipSuccess && S > 1) {
+    hipLaunchKernelGGL(gptq_finalize_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, s, part,
+                       (uint16_t*)a.y, (long)MN, S);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
 hipError_t launch_gptq_direct(const GptqArgs& a, hipStream_t s) {
   const int64_t ng = a.K / a.G;
+  if (a.M >= 8 && ng <= 96 && a.K / 8 * a.N * 4 < (int64_t(1) << 31) && a.M * a.K * 2 < (int64_t(1) << 31))
+    return launch_gptq_mfma(a, s);
   // columns per lane: 4 when the (scale, bias) table of 256 columns fits
   // 64 KiB of LDS, else 2, else 1 (up to 96 KiB)
   const int cpl = ng <= 32 ? 4 : (ng <= 64 ? 2 : 1);

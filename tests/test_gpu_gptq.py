@@ -125,3 +125,37 @@ def test_direct_shapes(M, N, K, G, act_order):
     torch.cuda.synchronize()
     ref = oracle.qmm_gptq(case.x, case.qweight, case.qzeros, case.scales, case.g_idx, M, case.K, case.N, case.G)
     assert_float_bar(host_f64(y), ref, case.name)
+
+
+@pytest.mark.parametrize("M,N,K,G", [
+    (8, 200, 1024, 128),     # the smallest M of the matrix-core kernel, a partial column group
+    (33, 1000, 2048, 64),    # two 32-row blocks, the second with one row
+    (64, 136, 6144, 64),     # 96 groups: the largest table it takes
+    (100, 264, 1024, 32),    # two passes of 64 rows
+])
+@pytest.mark.parametrize("act_order", [True, False])
+def test_direct_matrix_core_shapes(M, N, K, G, act_order):
+    dev = require_gpu()
+    case = si.gptq_case(M, K, N, G, seed=(54, M, N, K, G), act_order=act_order,
+                        name=f"gptq_mfma_M{M}_N{N}_K{K}_G{G}")
+    if not act_order:
+        case.g_idx = None
+    _log(case, "direct matrix core")
+    x, qw, qz, s, gi = _dev(case, dev)
+    y = qa.qmm_gptq(x, qw, qz, s, gi, G)
+    torch.cuda.synchronize()
+    ref = oracle.qmm_gptq(case.x, case.qweight, case.qzeros, case.scales, case.g_idx, M, case.K, case.N, case.G)
+    assert_float_bar(host_f64(y), ref, case.name)
+
+
+def test_direct_matrix_core_scale_range():
+    # scales over three decades inside each column: the fp16 weight pieces
+    # are taken relative to the column's largest scale exponent
+    dev = require_gpu()
+    case = si.gptq_case(16, 2048, 256, 128, seed=(55,), scale_range=(1e-3, 4.0), name="gptq_mfma_scale_range")
+    _log(case, "direct matrix core")
+    x, qw, qz, s, gi = _dev(case, dev)
+    y = qa.qmm_gptq(x, qw, qz, s, gi, case.G)
+    torch.cuda.synchronize()
+    ref = oracle.qmm_gptq(case.x, case.qweight, case.qzeros, case.scales, case.g_idx, case.M, case.K, case.N, case.G)
+    assert_float_bar(host_f64(y), ref, case.name)
