@@ -21,11 +21,14 @@ with almost no launch gaps.  In the same JSON line:
                  the grouped decode set at M = 4 and 16 (the MFMA GEMV kernel)
   gptq_k4096_n11008
                  GPTQ layout (K=4096, N=11008, G=128, act-order) at M = 1 and
-                 32: the direct kernel and the repacked affine path
+                 32: the direct kernel and the repacked affine path, eager and
+                 replayed from a HIP graph
   gemm_m2048     prefill GEMM of an 8B decoder, M=2048: K=4096 with N = 4096,
                  1024, 14336 and K=14336 with N=4096, 4- and 8-bit, TFLOP/s
                  against the bf16 dense MFMA peak
-  w4a8_m2048     W4A8 GEMM (quantize + int8 MFMA), M=2048 N=4096 K=1024
+  w4a8_m2048     W4A8 GEMM (quantize + int8 MFMA), M=2048 N=4096 K=1024,
+                 eager and from a HIP graph
+  w4a8_shapes    every W4A8 shape of the speech-encoder set, graph replays
   roofline       the grouped GEMV kernel of the headline step
   cpu_baseline   the fp64 CPU oracle on a bounded sample of the same workload
 Every GPU figure is timed with HIP events on the stream the kernels run on:
@@ -56,6 +59,7 @@ METRIC = "q4 GEMV GB/s & %HBM peak (M=1); qGEMM TFLOP/s & %MFMA peak (M=2048)"
 G = 64
 BITS = 4
 PER_LAUNCH = 56                # problems per grouped GEMV launch
+REPS = 20                      # calls per captured graph in the graph-replay figures
 
 
 def gemv_bytes(M, N, K, bits=BITS, group=G):
@@ -119,7 +123,9 @@ def eager_time(torch, fn, steps, warmup):
 
 def graph_time(torch, fn, steps, warmup):
     """Capture fn() in a HIP graph, replay it, time the replays with events on
-    the replay stream.  Returns ms per step."""
+    the replay stream.  Returns ms per step.  The eager warm-up call runs on
+    the capture stream, so the library's per-stream workspace is sized before
+    the capture."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -127,7 +133,7 @@ def graph_time(torch, fn, steps, warmup):
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
+    with torch.cuda.graph(g, stream=s):
         fn()
     torch.cuda.synchronize()
     for _ in range(warmup):
@@ -228,32 +234,55 @@ def time_gptq(torch, qa, si, device, M, iters=200, warmup=20):
     gi = torch.from_numpy(c.g_idx.astype(np.int32)).to(device)
     byts = (c.K * c.N // 2 + (c.K // c.G) * c.N * 2 + (c.K // c.G) * c.N // 2 + c.K * 4
             + M * c.K * 2 + M * c.N * 2)
-    ms_d = eager_time(torch, lambda: qa.qmm_gptq(x, qw, qz, sc, gi, c.G), iters, warmup)
+    direct = lambda: qa.qmm_gptq(x, qw, qz, sc, gi, c.G)
+    ms_d = eager_time(torch, direct, iters, warmup)
     w, s2, b2, kp = qa.gptq_to_affine_repack(qw, qz, sc, gi, c.G)
-    ms_r = eager_time(torch, lambda: qa.qmm_affine(x, w, s2, b2, c.G, 4, k_perm=kp), iters, warmup)
+    repacked = lambda: qa.qmm_affine(x, w, s2, b2, c.G, 4, k_perm=kp)
+    ms_r = eager_time(torch, repacked, iters, warmup)
+    # the same calls, REPS per captured HIP graph: device time per call
+    # without the per-call host work (Python binding, launches) or the cost of
+    # launching the graph itself
+    ms_dg = graph_time(torch, lambda: [direct() for _ in range(REPS)], iters // REPS + 1, 2) / REPS
+    ms_rg = graph_time(torch, lambda: [repacked() for _ in range(REPS)], iters // REPS + 1, 2) / REPS
     return {"M": M, "N": c.N, "K": c.K, "G": c.G,
             "direct_us": round(ms_d * 1e3, 2), "direct_gbs": round(byts / (ms_d * 1e-3) / 1e9, 1),
-            "repacked_affine_us": round(ms_r * 1e3, 2)}
+            "repacked_affine_us": round(ms_r * 1e3, 2),
+            "direct_graph_us": round(ms_dg * 1e3, 2), "direct_graph_gbs": round(byts / (ms_dg * 1e-3) / 1e9, 1),
+            "repacked_affine_graph_us": round(ms_rg * 1e3, 2),
+            "repacked_affine_graph_gbs": round(byts / (ms_rg * 1e-3) / 1e9, 1)}
 
 
 def time_w4a8(torch, qa, si, device, M=2048, N=4096, K=1024, iters=20, warmup=5):
+    """One W4A8 call (quantize + int8 GEMM): eager, and REPS calls per
+    captured HIP graph (device time without the per-call host work)."""
     case = si.w4a8_case(M, N, K, seed=(4, N, K, M))
     x = torch.from_numpy(case.x.view(np.int16)).view(torch.float16).to(device)
     w = torch.from_numpy(case.w_q4.view(np.int32)).to(device)
     sw = torch.from_numpy(case.s_w.view(np.int16)).view(torch.float16).to(device)
-    for _ in range(warmup):
-        qa.qgemm_w4a8(x, w, sw)
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(iters):
-        qa.qgemm_w4a8(x, w, sw)
-    end.record()
-    torch.cuda.synchronize()
-    us = start.elapsed_time(end) * 1e3 / iters
-    tops = 2.0 * M * N * K / (us * 1e-6) / 1e12
-    return {"M": M, "N": N, "K": K, "us_per_call": round(us, 2), "tops": round(tops, 1),
-            "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
+    fn = lambda: qa.qgemm_w4a8(x, w, sw)
+    us = eager_time(torch, fn, iters, warmup) * 1e3
+    usg = graph_time(torch, lambda: [fn() for _ in range(REPS)], iters, 2) * 1e3 / REPS
+    ops = 2.0 * M * N * K
+    return {"M": M, "N": N, "K": K, "us_per_call": round(us, 2), "tops": round(ops / (us * 1e-6) / 1e12, 1),
+            "frac_of_int8_peak": round(ops / (us * 1e-6) / 1e12 / INT8_PEAK_TOPS, 4),
+            "graph_us_per_call": round(usg, 2), "graph_tops": round(ops / (usg * 1e-6) / 1e12, 1)}
+
+
+def time_w4a8_shapes(torch, qa, si, device, iters=20, warmup=5):
+    """Every W4A8 shape of the speech-encoder set (d = 1024, FFN 4096): REPS
+    calls per captured graph, microseconds per call."""
+    out = []
+    for N, K in si.CFG4_SHAPES:
+        for M in si.CFG4_M:
+            case = si.w4a8_case(M, N, K, seed=(4, N, K, M))
+            x = torch.from_numpy(case.x.view(np.int16)).view(torch.float16).to(device)
+            w = torch.from_numpy(case.w_q4.view(np.int32)).to(device)
+            sw = torch.from_numpy(case.s_w.view(np.int16)).view(torch.float16).to(device)
+            fn = lambda: qa.qgemm_w4a8(x, w, sw)
+            us = graph_time(torch, lambda: [fn() for _ in range(REPS)], iters, 2) * 1e3 / REPS
+            out.append({"M": M, "N": N, "K": K, "graph_us": round(us, 2),
+                        "tops": round(2.0 * M * N * K / (us * 1e-6) / 1e12, 1)})
+    return out
 
 
 def cpu_baseline(dec, seconds):
@@ -393,10 +422,11 @@ def main():
               flush=True)
     gptq = [time_gptq(torch, qa, si, device, M) for M in (1, 32)]
 
-    gemm = w4a8 = None
+    gemm = w4a8 = w4a8_shapes = None
     if not args.no_gemm:
         gemm = [time_gemm(torch, qa, si, device, bits, N=N, K=K) for bits in si.CFG2_BITS for N, K in si.CFG2_SHAPES]
         w4a8 = time_w4a8(torch, qa, si, device)
+        w4a8_shapes = time_w4a8_shapes(torch, qa, si, device)
         for g in gemm:
             print(f"[bench] gemm b{g['bits']}: {g['us_per_call']} us, {g['tflops']} TFLOP/s", file=sys.stderr,
                   flush=True)
@@ -442,6 +472,7 @@ def main():
         "gptq_k4096_n11008": gptq,
         "gemm_m2048": gemm,
         "w4a8_m2048": w4a8,
+        "w4a8_shapes": w4a8_shapes,
     }
     print(json.dumps(out), flush=True)
 

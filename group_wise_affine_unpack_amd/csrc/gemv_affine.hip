@@ -335,6 +335,10 @@ __global__ __launch_bounds__(256) void gemv_affine_kernel(GemvBatch B) {
 #pragma unroll
           for (int q = 0; q < C::XR; ++q) raw[m][q] = ld128(rx, xo + 16u * q, (uint32_t)min(m0 + m, M - 1) * K * 2u);
       }
+      // every load of the chunk issued before any result is used: otherwise
+      // the scheduler may put each parameter's use right after its load,
+      // and each then waits for that load alone
+      __builtin_amdgcn_sched_barrier(0);
       uint32_t xp[MT][C::XP];
       float xs[MT][C::NSEG];
 #pragma unroll
