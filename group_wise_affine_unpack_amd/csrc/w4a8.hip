@@ -12,15 +12,21 @@
 //   quant : each row held in the registers of one to four waves (16-byte
 //           loads, 8-byte stores) for K <= 16384, else one row per block
 //           in a loop; bit-exact codes and scale.
+//   gemv  : M <= 16: one wave per output column, v_dot4_i32_i8 on decoded
+//           codes, exact int32 wave sums.
 //   gemm  : v_mfma_i32_32x32x32_i8, tile BM x BN (4 waves along N, each
 //           BM x NB*32), K in stages of 128: x_q through a 4-stage LDS ring
 //           stored two stages ahead, int4 words in a register ring three
 //           stages ahead and decoded in registers; the tile shrinks until the
-//           grid gives every CU two workgroups.  A nibble
+//           grid gives every CU two workgroups, and when even the smallest
+//           tile leaves CUs idle K is split over workgroups (int32 partials,
+//           summed exactly by a second kernel).  A nibble
 //           is placed in the HIGH half of its byte, which makes the byte the
 //           int8 value 16*v with no sign extension step; the accumulator is
 //           shifted right by 4 at the end (exact: every product is a multiple
 //           of 16, and |acc| * 16 < 2^31 for K <= 2^17).
+#include <algorithm>
+
 #include "common.h"
 
 namespace qaff {
@@ -141,6 +147,8 @@ struct Params {
   int32_t* acc_out;
   int M, N, K;
   int Tm, Tn, per_xcd;
+  int S, per_split;  // K splits of per_split stages; S > 1 writes int32 partials [S][M][N]
+  int32_t* part;
 };
 
 // 8 nibbles of one word -> 8 int8 (16*v) in natural k order (2 dwords)
@@ -166,9 +174,10 @@ struct W4Pipe {
   int x_dst;             // LDS offset of chunk 0 (chunk i at + i*4096)
   uint32_t w_off[NB];    // this lane's row, word 8h
   int l32, h, nst, K;
+  int st0;  // first K stage of this workgroup's split
 
   __device__ __forceinline__ void issue_x(int t, u32x4_t (&xr)[A_CH]) const {
-    const uint32_t k = (uint32_t)min(t, nst - 1) * BK;
+    const uint32_t k = (uint32_t)(st0 + min(t, nst - 1)) * BK;
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) xr[i] = ld128(rx, x_off[i] + k);
   }
@@ -179,7 +188,7 @@ struct W4Pipe {
   // 32 codes per load; a load whose codes start at or past K is moved out
   // of range and reads zeros (K % 32 == 0)
   __device__ __forceinline__ void issue_w(int t, u32x4_t (&wr)[NB][2]) const {
-    t = min(t, nst - 1);
+    t = st0 + min(t, nst - 1);
     const uint32_t k = (uint32_t)t * (BK / 2);
     const uint32_t o0 = t * BK + 64 * h < K ? 0u : OOB, o1 = t * BK + 64 * h + 32 < K ? 0u : OOB;
 #pragma unroll
@@ -271,8 +280,9 @@ __global__ __launch_bounds__(256) void w4a8_gemm_kernel(Params p) {
   constexpr int BM = MB * 32;
   constexpr int BN = NB * 128;
   const int b = blockIdx.x;
-  const int v = (b & 7) * p.per_xcd + (b >> 3);
-  if (v >= p.Tm * p.Tn) return;
+  const int vs = (b & 7) * p.per_xcd + (b >> 3);
+  if (vs >= p.Tm * p.Tn * p.S) return;
+  const int v = vs / p.S, sp = vs % p.S;
   const int tm = v / p.Tn, tn = v % p.Tn;
   const int m0 = tm * BM, n0 = tn * BN;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l32 = lane & 31, h = lane >> 5;
@@ -290,7 +300,11 @@ __global__ __launch_bounds__(256) void w4a8_gemm_kernel(Params p) {
   W4Pipe<MB, NB> P;
   P.l32 = l32;
   P.h = h;
-  P.nst = (p.K + BK - 1) / BK;
+  {
+    const int nst_all = (p.K + BK - 1) / BK;
+    P.st0 = sp * p.per_split;
+    P.nst = min(nst_all - P.st0, p.per_split);
+  }
   // the range covers the tile's rows: a row past M reads zeros.  x_q chunks
   // past K (last stage, K % 128 != 0) read the next row; the weight words
   // they meet are zeros (see issue_w), so they add nothing.
@@ -341,6 +355,22 @@ __global__ __launch_bounds__(256) void w4a8_gemm_kernel(Params p) {
     P.template step<3>(s + 3, lds, xr, w3, w0, w2, a0, b0, acc);
   }
 
+  if (p.S > 1) {
+    // int32 partial of split sp (exact: the sums of any split order agree)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int n = n0 + wave * NB * 32 + nb * 32 + l32;
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (m < p.M) p.part[((long)sp * p.M + m) * p.N + n] = acc[mb][nb][r] >> 4;
+        }
+    }
+    return;
+  }
   // epilogue; 32x32 accumulator layout: lane -> column l32, register r -> row 8*(r/4) + 4*h + r%4.
   // The lane's 16 s_x values per row block are loaded together first, so the
   // stores below never wait on a load (rows past M read 0 and are not stored).
@@ -369,6 +399,90 @@ __global__ __launch_bounds__(256) void w4a8_gemm_kernel(Params p) {
           p.y[(long)m * p.N + n] = f32_to_f16_bits(((float)a * sxv[mb][r]) * swn);
         }
       }
+  }
+}
+
+// acc = the sum of the S int32 partials; y and acc_out as in the GEMM epilogue
+__global__ __launch_bounds__(256) void w4a8_split_sum_kernel(const int32_t* __restrict__ part, int S, int M, int N,
+                                                             const float* __restrict__ sx, const uint16_t* __restrict__ sw,
+                                                             uint16_t* __restrict__ y, int32_t* __restrict__ acc_out) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  const long MN = (long)M * N;
+  if (i >= MN) return;
+  // eight partials in flight at a time (the sum is exact in any order)
+  int a = 0, s = 0;
+  for (; s + 8 <= S; s += 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[(long)(s + u) * MN + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a += v[u];
+  }
+  for (; s < S; ++s) a += part[(long)s * MN + i];
+  const int m = (int)(i / N), n = (int)(i % N);
+  if (acc_out) acc_out[i] = a;
+  y[i] = f32_to_f16_bits(((float)a * sx[m]) * f16_bits_to_f32(sw[n]));
+}
+
+// Sum over the 64 lanes of a wave, exact in int32: rotations inside each row
+// of 16 lanes (DPP), then two swaps across rows.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  v += dpp_i<0x128>(v);  // row_ror:8
+  v += dpp_i<0x124>(v);  // row_ror:4
+  v += dpp_i<0x122>(v);  // row_ror:2
+  v += dpp_i<0x121>(v);  // row_ror:1
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// W4A8 for M <= 16: one wave per output column n, lanes over K in chunks of
+// 32 codes (16 bytes of packed codes; 32 bytes of x_q per row), the codes
+// decoded to int8 (16 v, as in the GEMM) and multiplied with v_dot4_i32_i8;
+// exact int32 sums, reduced over the wave, shifted right by 4.  MT rows of
+// x_q per launch (rows past M read row M-1 and are dropped).
+template <int MT>
+__global__ __launch_bounds__(256) void w4a8_gemv_kernel(const int8_t* __restrict__ xq, const float* __restrict__ sx,
+                                                        const uint32_t* __restrict__ w, const uint16_t* __restrict__ sw,
+                                                        uint16_t* __restrict__ y, int32_t* __restrict__ acc_out, int M,
+                                                        int N, int K) {
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;  // the whole wave
+  const int nch = K / 32;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + (long)n * (K / 8), (uint32_t)(K / 2));
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(xq, (uint32_t)M * (uint32_t)K);
+  int acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = 0;
+  for (int c = lane; c < nch; c += 64) {
+    const u32x4_t wv = ld128(rw, (uint32_t)c * 16u);
+    uint32_t d[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) decode_word(wv[i], d[2 * i], d[2 * i + 1]);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const uint32_t xo = (uint32_t)min(m, M - 1) * (uint32_t)K + (uint32_t)c * 32u;
+      const u32x4_t x0 = ld128(rx, xo), x1 = ld128(rx, xo + 16u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[m] = __builtin_amdgcn_sdot4((int)d[i], (int)x0[i], acc[m], false);
+        acc[m] = __builtin_amdgcn_sdot4((int)d[4 + i], (int)x1[i], acc[m], false);
+      }
+    }
+  }
+  const float swn = f16_bits_to_f32(sw[n]);
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int a = wave_sum_i32(acc[m]) >> 4;
+    if (lane == m && m < M) {
+      if (acc_out) acc_out[(long)m * N + n] = a;
+      y[(long)m * N + n] = f32_to_f16_bits(((float)a * sx[m]) * swn);
+    }
   }
 }
 
@@ -402,6 +516,24 @@ hipError_t launch_w4a8(const W4A8Args& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (M <= 16) {
+    const dim3 grid((unsigned)((N + 3) / 4));
+    const int8_t* xq = a.x_q;
+    const uint32_t* w = a.w;
+    const uint16_t* sw = (const uint16_t*)a.s_w;
+    uint16_t* y = (uint16_t*)a.y;
+    if (M == 1)
+      hipLaunchKernelGGL(w4a8_gemv_kernel<1>, grid, dim3(256), 0, s, xq, a.s_x, w, sw, y, a.acc, M, N, K);
+    else if (M == 2)
+      hipLaunchKernelGGL(w4a8_gemv_kernel<2>, grid, dim3(256), 0, s, xq, a.s_x, w, sw, y, a.acc, M, N, K);
+    else if (M <= 4)
+      hipLaunchKernelGGL(w4a8_gemv_kernel<4>, grid, dim3(256), 0, s, xq, a.s_x, w, sw, y, a.acc, M, N, K);
+    else if (M <= 8)
+      hipLaunchKernelGGL(w4a8_gemv_kernel<8>, grid, dim3(256), 0, s, xq, a.s_x, w, sw, y, a.acc, M, N, K);
+    else
+      hipLaunchKernelGGL(w4a8_gemv_kernel<16>, grid, dim3(256), 0, s, xq, a.s_x, w, sw, y, a.acc, M, N, K);
+    return hipGetLastError();
+  }
   // largest tile whose grid still gives every CU at least two workgroups
   struct Tile { int mb, nb; };
   const Tile tiles[] = {{4, 2}, {2, 2}, {2, 1}};
@@ -422,7 +554,24 @@ hipError_t launch_w4a8(const W4A8Args& a, hipStream_t s) {
   p.K = K;
   p.Tm = (M + t.mb * 32 - 1) / (t.mb * 32);
   p.Tn = (N + t.nb * 128 - 1) / (t.nb * 128);
-  p.per_xcd = (p.Tm * p.Tn + 7) / 8;
+  // K splits when the tiles leave CUs idle: enough workgroups for every CU,
+  // whole stages per split, partials within 32-bit sizes
+  {
+    const int nst = (K + BK - 1) / BK, tiles = p.Tm * p.Tn;
+    int S = 1;
+    if (tiles < 256) {
+      S = std::min((256 + tiles - 1) / tiles, nst);
+      while (S > 1 && (int64_t)S * M * N * 4 >= (int64_t(1) << 31)) --S;
+    }
+    p.per_split = (nst + S - 1) / S;
+    p.S = (nst + p.per_split - 1) / p.per_split;  // no empty split
+    p.part = nullptr;
+    if (p.S > 1) {
+      const hipError_t e2 = stream_workspace(s, (size_t)p.S * M * N * 4, (void**)&p.part);
+      if (e2 != hipSuccess) return e2;
+    }
+  }
+  p.per_xcd = (p.Tm * p.Tn * p.S + 7) / 8;
   const dim3 grid(8 * p.per_xcd);
   if (t.mb == 4)
     hipLaunchKernelGGL((w4a8_gemm_kernel<4, 2>), grid, dim3(256), 0, s, p);
@@ -430,7 +579,14 @@ hipError_t launch_w4a8(const W4A8Args& a, hipStream_t s) {
     hipLaunchKernelGGL((w4a8_gemm_kernel<2, 2>), grid, dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL((w4a8_gemm_kernel<2, 1>), grid, dim3(256), 0, s, p);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e == hipSuccess && p.S > 1) {
+    const long MN = (long)M * N;
+    hipLaunchKernelGGL(w4a8_split_sum_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, s, p.part, p.S, M, N,
+                       p.sx, p.sw, p.y, p.acc_out);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 }  // namespace qaff
