@@ -537,7 +537,7 @@ __global__ __launch_bounds__(256, 2) void gemv_mfma4_kernel(MfmaBatch B) {
   auto issue_w = [&](int tw, W& wr) __attribute__((always_inline)) {
     const uint32_t wo = (tw < nst ? wv : OOB) + (uint32_t)tw * 256u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wr[i] = ld128(rw, wo + (uint32_t)(16 * i * L * 4));
+    for (int i = 0; i < 4; ++i) wr[i] = ld128<NT>(rw, wo + (uint32_t)(16 * i * L * 4));  // streamed once: non-temporal
   };
   // loads of parameter chunk ch
   auto issue_p = [&](int ch, u32x4_t (&pr)[4]) __attribute__((always_inline)) {
