@@ -16,8 +16,10 @@
 //           codes, exact int32 wave sums.
 //   gemm  : v_mfma_i32_32x32x32_i8, tile BM x BN (4 waves along N, each
 //           BM x NB*32), K in stages of 128: x_q through a 4-stage LDS ring
-//           stored two stages ahead, int4 words in a register ring three
-//           stages ahead and decoded in registers; the tile shrinks until the
+//           stored two stages ahead; int4 words in batches of two stages
+//           (8 rows x 128 bytes per load instruction, whole lines), two
+//           batches in flight in registers, then through a wave-private LDS
+//           region into the B fragment's shape, decoded in registers; the tile shrinks until the
 //           grid gives every CU two workgroups, and when even the smallest
 //           tile leaves CUs idle K is split over workgroups (int32 partials,
 //           summed exactly by a second kernel).  A nibble
@@ -172,7 +174,12 @@ struct W4Pipe {
   __amdgpu_buffer_rsrc_t rx, rw;
   uint32_t x_off[A_CH];  // this thread's chunks (OOB for rows past M)
   int x_dst;             // LDS offset of chunk 0 (chunk i at + i*4096)
-  uint32_t w_off[NB];    // this lane's row, word 8h
+  // weight batches (two stages = 128 bytes of a row): global loads of 8
+  // rows x 128 bytes per instruction, through a wave-private LDS region
+  static constexpr int WB = NB * 4;  // 16-byte chunks per lane and batch
+  uint32_t wb_off[WB];               // row 8i + lane/8 of the wave's rows, chunk lane%8 (OOB past N)
+  int wb_dst[WB];                    // its LDS place (chunks XOR-swizzled by row)
+  unsigned char* wreg;               // this wave's region: NB*32 rows x 128 bytes
   int l32, h, nst, K;
   int st0;  // first K stage of this workgroup's split
 
@@ -185,16 +192,29 @@ struct W4Pipe {
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) *reinterpret_cast<u32x4_t*>(st + x_dst + i * 4096) = xr[i];
   }
-  // 32 codes per load; a load whose codes start at or past K is moved out
-  // of range and reads zeros (K % 32 == 0)
-  __device__ __forceinline__ void issue_w(int t, u32x4_t (&wr)[NB][2]) const {
-    t = st0 + min(t, nst - 1);
-    const uint32_t k = (uint32_t)t * (BK / 2);
-    const uint32_t o0 = t * BK + 64 * h < K ? 0u : OOB, o1 = t * BK + 64 * h + 32 < K ? 0u : OOB;
+  // batch j (local stages 2j, 2j+1): a chunk whose codes start at or past K
+  // reads zeros (K % 32 == 0, so a chunk is wholly inside or outside)
+  __device__ __forceinline__ void issue_wb(int j, u32x4_t (&wb)[WB]) const {
+    const int byte0 = (st0 + 2 * j) * (BK / 2) + (l32 & 7) * 16;  // lane%8 == l32%8
+    const uint32_t o = 2 * byte0 < K ? 0u : OOB;
+#pragma unroll
+    for (int i = 0; i < WB; ++i) wb[i] = ld128(rw, (wb_off[i] | o) + (uint32_t)byte0);
+  }
+  __device__ __forceinline__ void put_wb(const u32x4_t (&wb)[WB]) const {
+#pragma unroll
+    for (int i = 0; i < WB; ++i) *reinterpret_cast<u32x4_t*>(wreg + wb_dst[i]) = wb[i];
+  }
+  static __device__ __forceinline__ int wswz(int r) { return (r >> 1) & 7; }
+  // the weight words of stage u (0, 1) of the batch in LDS, in the B
+  // fragment's shape: lane (l32, h), block nb takes bytes 64u + 32h .. +31
+  // of row nb*32 + l32
+  __device__ __forceinline__ void read_w(int u, u32x4_t (&wr)[NB][2]) const {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      wr[nb][0] = ld128(rw, (w_off[nb] | o0) + k);
-      wr[nb][1] = ld128(rw, (w_off[nb] | o1) + k + 16);
+      const int r = nb * 32 + l32;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        wr[nb][j] = *reinterpret_cast<const u32x4_t*>(wreg + r * 128 + (((4 * u + 2 * h + j) ^ wswz(r)) << 4));
     }
   }
   __device__ __forceinline__ void read_a(const unsigned char* __restrict__ st, int s, i32x4_t (&af)[MB]) const {
@@ -247,23 +267,31 @@ struct W4Pipe {
     mfma(a1, b1, acc);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // Stage t (LDS stage t%4 = S, ring entry t%4):
-  //   barrier              stage t+1 (stored last step) visible; every wave
-  //                        done with stage t-1
+  // Stage t (LDS stage t%4 = S):
+  //   barrier              stage t+1 of x (stored last step) visible; every
+  //                        wave done with stage t-1
   //   store x of t+2       registers loaded last step -> stage (t+2)%4
-  //   issue t+3            x into registers, then weight words into the ring
+  //   issue x of t+3
+  //   t odd: weight batch (t+1)/2 (stages t+1, t+2) from its register slot
+  //          into the wave's LDS region (the wave read the previous batch's
+  //          last stage one step ago), then batch (t+1)/2 + 2 into the slot
+  //   read stage t+1's weight words from LDS
   //   compute t            ending with sub-step 0 of stage t+1 prepared
   //                        (skipped past the last stage)
   template <int S>
-  __device__ __forceinline__ void step(int t, unsigned char* lds, u32x4_t (&xr)[A_CH], const u32x4_t (&cur)[NB][2],
-                                       const u32x4_t (&nxt)[NB][2], u32x4_t (&fut)[NB][2], i32x4_t (&a0)[MB],
+  __device__ __forceinline__ void step(int t, unsigned char* lds, u32x4_t (&xr)[A_CH], u32x4_t (&wb)[WB],
+                                       const u32x4_t (&cur)[NB][2], u32x4_t (&nxt)[NB][2], i32x4_t (&a0)[MB],
                                        i32x4_t (&b0)[NB], i32x16_t (&acc)[MB][NB]) const {
     __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0): own LDS writes done
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     store_x(lds + ((S + 2) & 3) * SB, xr);
     issue_x(t + 3, xr);
-    issue_w(t + 3, fut);
+    if constexpr (S & 1) {
+      put_wb(wb);
+      issue_wb((t + 1) / 2 + 2, wb);
+    }
+    read_w((t + 1) & 1, nxt);
     __builtin_amdgcn_sched_barrier(0);
     if (t < nst) compute(lds + S * SB, cur, lds + ((S + 1) & 3) * SB, nxt, a0, b0, acc);
   }
@@ -271,10 +299,11 @@ struct W4Pipe {
 
 // x_q tiles go global -> registers (one stage before the store) -> a 4-stage
 // LDS ring, stored two stages before use, 16-byte chunks XOR-swizzled by row;
-// int4 words go to a 4-entry register ring three stages ahead; loads past
-// the end of K or past the last row are out of range and read zeros.  The
-// A reads and B decode of a stage's first sub-step run during the previous
-// stage's last one.
+// int4 words go in two-stage batches to registers (two batches in flight)
+// and then to the wave's LDS region one step before their first stage;
+// loads past the end of K or past the last row are out of range and read
+// zeros.  The A reads and B decode of a stage's first sub-step run during
+// the previous stage's last one.
 template <int MB, int NB>
 __global__ __launch_bounds__(256) void w4a8_gemm_kernel(Params p) {
   constexpr int BM = MB * 32;
@@ -287,7 +316,7 @@ __global__ __launch_bounds__(256) void w4a8_gemm_kernel(Params p) {
   const int m0 = tm * BM, n0 = tn * BN;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l32 = lane & 31, h = lane >> 5;
 
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * W4Pipe<MB, NB>::SB];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * W4Pipe<MB, NB>::SB + 4 * NB * 32 * 128];
 
   i32x16_t acc[MB][NB];
 #pragma unroll
@@ -316,43 +345,49 @@ __global__ __launch_bounds__(256) void w4a8_gemm_kernel(Params p) {
     for (int i = 0; i < MB; ++i) P.x_off[i] = (uint32_t)((32 * i + r) * p.K + c * 16);
     P.x_dst = r * 128 + ((c ^ xswz(r)) << 4);
   }
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int n = n0 + wave * NB * 32 + nb * 32 + l32;
-    P.w_off[nb] = n < p.N ? (uint32_t)((long)n * p.K / 2 + h * 32) : OOB;
-  }
   P.K = p.K;
+#pragma unroll
+  for (int i = 0; i < W4Pipe<MB, NB>::WB; ++i) {
+    const int r = 8 * i + (lane >> 3), n = n0 + wave * NB * 32 + r;
+    P.wb_off[i] = n < p.N ? (uint32_t)((long)n * p.K / 2) : OOB;
+    P.wb_dst[i] = r * 128 + (((lane & 7) ^ W4Pipe<MB, NB>::wswz(r)) << 4);
+  }
+  P.wreg = lds + 4 * W4Pipe<MB, NB>::SB + wave * (NB * 32 * 128);
 
   u32x4_t xr[MB];
-  u32x4_t w0[NB][2], w1[NB][2], w2[NB][2], w3[NB][2];
-  // prologue in the loop's load order (x of a stage, then its weights), so
-  // that the waits the compiler derives at the loop head hold both ways in
+  u32x4_t wb0[W4Pipe<MB, NB>::WB], wb1[W4Pipe<MB, NB>::WB];  // weight batches, slot j % 2
+  u32x4_t wA[NB][2], wB[NB][2];  // weight words of the current and the next stage
+  // prologue: batch 0 in LDS, batches 1 and 2 in flight; x of stages 0 and
+  // 1 in LDS, stage 2 in flight
+  P.issue_wb(0, wb0);
+  P.issue_wb(1, wb1);
   P.issue_x(0, xr);
-  P.issue_w(0, w0);
   __builtin_amdgcn_sched_barrier(0);
   P.store_x(lds, xr);
   P.issue_x(1, xr);
-  P.issue_w(1, w1);
   __builtin_amdgcn_sched_barrier(0);
   P.store_x(lds + W4Pipe<MB, NB>::SB, xr);
+  P.put_wb(wb0);
+  P.issue_wb(2, wb0);
   P.issue_x(2, xr);
-  P.issue_w(2, w2);
   __builtin_amdgcn_sched_barrier(0);
   // With every prologue load complete, the compiler's view of pending loads
   // at the loop head is the loop's own, so its waits there stay exact.
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
   i32x4_t a0[MB], b0[NB];
+  P.read_w(0, wA);
   P.read_a(lds, 0, a0);
-  P.decode_b(w0, 0, b0);
+  P.decode_b(wA, 0, b0);
   const int nst = P.nst;
   // whole rounds of four stages: a stage past the end only loads (clamped)
-  // and waits, so the loop body has no branch around a step
+  // and waits, so the loop body has no branch around a step.  Batch slots:
+  // step 1 of a round stores batch s/2+1 (slot 1), step 3 batch s/2+2 (slot 0).
   for (int s = 0; s < nst; s += 4) {
-    P.template step<0>(s, lds, xr, w0, w1, w3, a0, b0, acc);
-    P.template step<1>(s + 1, lds, xr, w1, w2, w0, a0, b0, acc);
-    P.template step<2>(s + 2, lds, xr, w2, w3, w1, a0, b0, acc);
-    P.template step<3>(s + 3, lds, xr, w3, w0, w2, a0, b0, acc);
+    P.template step<0>(s, lds, xr, wb0, wA, wB, a0, b0, acc);
+    P.template step<1>(s + 1, lds, xr, wb1, wB, wA, a0, b0, acc);
+    P.template step<2>(s + 2, lds, xr, wb0, wA, wB, a0, b0, acc);
+    P.template step<3>(s + 3, lds, xr, wb0, wB, wA, a0, b0, acc);
   }
 
   if (p.S > 1) {
