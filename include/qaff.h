@@ -20,9 +20,14 @@
  *     comment says otherwise.  Tensors are dense and row-major.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Work is enqueued on it asynchronously; hot-path calls never synchronize.
- *   - The caller owns every buffer; the library keeps no pointer after the
- *     call returns.  Internal scratch (GEMM pre-pass buffers) is taken with
- *     stream-ordered allocation on `stream` and released on `stream`.
+ *   - The caller owns every buffer; the library keeps no pointer to them
+ *     after the call returns.  Internal scratch (GEMM pre-pass buffers and
+ *     split-K partials, GPTQ partials, permuted activations for k_perm) comes
+ *     from a buffer the library keeps per (device, stream): calls on one
+ *     stream reuse it in stream order, and once it is large enough no call
+ *     allocates.  It only grows, and growing is refused (QAFF_E_HIP) while
+ *     `stream` is being captured into a graph: capture a call after one
+ *     eager call of the same shapes on the same stream.
  *   - Errors are returned as qaff_status codes; no C++ exception crosses the
  *     ABI.  Argument checks run before any HIP call, so a rejected call has
  *     enqueued nothing.  qaff_last_error() gives a message for the calling
@@ -73,9 +78,11 @@ typedef enum {
  *   group_size G in {32, 64, 128}; bits in {2, 4, 8};
  *   K % G == 0 and K*bits % 128 == 0 (whole 16-byte loads per row).
  *
- * Dispatch: M <= 16 runs the memory-bound GEMV kernel (exact fp32
- * arithmetic on the integer codes); larger M runs a pre-pass plus the MFMA
- * GEMM kernel.  Accuracy: max|y-ref|/(|ref|+1) <= 1e-2 and relative
+ * Dispatch: M <= 16 runs a memory-bound GEMV kernel (exact fp32 arithmetic
+ * on the integer codes; 4-bit codes with 2..16 x rows on the matrix cores),
+ * after one permuting pass over x when k_perm is given; larger M runs a
+ * pre-pass plus the MFMA GEMM kernel, with K split over workgroups (and a
+ * summing pass) when the output tiles would leave CUs idle.  Accuracy: max|y-ref|/(|ref|+1) <= 1e-2 and relative
  * Frobenius error <= 5e-3 against an fp64 evaluation, for finite inputs.
  */
 int qmm_affine(const void *x, const uint32_t *w_packed, const void *scales, const void *biases,
@@ -133,7 +140,13 @@ int qgemv_affine_grouped(const qaff_gemv_problem *problems, int32_t count, int64
  *   qweight [K/8, N]  int32 (read as uint32),   qzeros [K/G, N/8] int32
  *   scales  [K/G, N]  f16;                       g_idx [K] int32 or NULL,
  *           values in [0, K/G) (not checked on the device)
- *   K % 8 == 0, K % G == 0, N % 8 == 0, G in {32, 64, 128}.
+ *   K % 8 == 0, K % G == 0, N % 8 == 0, G in {32, 64, 128}; at most 192
+ *   groups (K/G), else QAFF_E_UNSUPPORTED (the per-workgroup table of
+ *   scales and zeros must fit in LDS).
+ * Kernels: M < 8 on the VALU (w exact in fp32), M >= 8 with at most 96
+ * groups on the matrix cores (w as two exact fp16 pieces relative to each
+ * column's largest scale); fp32 partial sums over K slices, one summing
+ * pass.  Accuracy as for qmm_affine.
  */
 int qmm_gptq(const void *x, const int32_t *qweight, const int32_t *qzeros, const void *scales,
              const int32_t *g_idx, void *y, int64_t M, int64_t N, int64_t K, int32_t group_size,
@@ -155,7 +168,9 @@ int qmm_gptq(const void *x, const int32_t *qweight, const int32_t *qzeros, const
  *   x_q     [M, K]    int8 (output, caller-owned; the quantized activations)
  *   s_x     [M]       f32  (output, caller-owned)
  *   acc_out [M, N]    int32 or NULL (output; the accumulators, for checking)
- *   K % 32 == 0.  Two launches on `stream`: quantize, then the int8 GEMM.
+ *   K % 32 == 0.  Launches on `stream`: quantize, then the integer product
+ *   (a dot4 GEMV for M <= 16, else the int8 MFMA GEMM, plus a summing pass
+ *   over int32 partials when K is split).
  */
 int qgemm_w4a8(const void *x, const uint32_t *w_q4, const void *s_w, void *y, int8_t *x_q, float *s_x,
                int32_t *acc_out, int64_t M, int64_t N, int64_t K, void *stream);
