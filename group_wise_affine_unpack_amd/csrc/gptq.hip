@@ -20,8 +20,12 @@
 namespace qaff {
 namespace {
 
-constexpr int GW = 8;      // waves per workgroup, each on its own part of the K slice
-constexpr int KB = 16;     // most word rows of one wave (all held in registers)
+// Waves per workgroup of the VALU direct kernel, each on its own part of
+// the K slice, and the most word rows one wave holds in registers: 16 x 8
+// for one x row (latency hiding), 8 x 16 for more (the accumulators of
+// 16 waves would not fit); a slice has at most WROWS word rows either way.
+template <int MT> constexpr int direct_waves() { return MT == 1 ? 16 : 8; }
+constexpr int WROWS = 128;
 constexpr uint32_t OOB = 0x80000000u;  // a buffer offset past any range: the load reads 0
 constexpr int kMaxLds = 160 * 1024;    // LDS of one CU
 
@@ -75,7 +79,7 @@ struct DirectLds {
     goff = ng * 64 * cpl * 8;
     xs = goff + per_sp * 8 * 4;
     red = xs + mt * per_sp * 8 * 4;
-    total = red + GW * mt * 64 * cpl * 4;
+    total = red + (mt == 1 ? 16 : 8) * mt * 64 * cpl * 4;  // direct_waves<mt>() partial rows
   }
 };
 
@@ -95,10 +99,11 @@ struct DirectLds {
 // second kernel adds the S partials into y.  Rows of x go MT at a time; the
 // table serves every pass.
 template <int CPL, int MT, bool ACT>
-__global__ __launch_bounds__(64 * GW) void gptq_direct_kernel(
+__global__ __launch_bounds__(64 * direct_waves<MT>()) void gptq_direct_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint32_t* __restrict__ qz,
     const uint16_t* __restrict__ sc, const int32_t* __restrict__ g_idx, float* __restrict__ part, int M, int N,
     int K, int gsh, int S) {
+  constexpr int GW = direct_waves<MT>(), KB = WROWS / GW;
   using T = GTab<CPL>;
   using W = typename WordsT<CPL>::T;
   constexpr int COLS = T::COLS;
@@ -564,7 +569,7 @@ hipError_t launch_direct(const GptqArgs& a, float* part, int S, hipStream_t s) {
                             (int)kMaxLds);
   });
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3((unsigned)(ncg * S)), dim3(64 * GW), lds, s, (const uint16_t*)a.x,
+  hipLaunchKernelGGL(k, dim3((unsigned)(ncg * S)), dim3(64 * direct_waves<MT>()), lds, s, (const uint16_t*)a.x,
                      (const uint32_t*)a.qweight, (const uint32_t*)a.qzeros, (const uint16_t*)a.scales, a.g_idx, part,
                      (int)a.M, (int)a.N, (int)a.K, a.G == 32 ? 5 : (a.G == 64 ? 6 : 7), S);
   return hipGetLastError();
@@ -655,9 +660,9 @@ hipError_t launch_gptq_direct(const GptqArgs& a, hipStream_t s) {
   // K slices: enough workgroups to give every CU one, each wave keeping at
   // least 4 word rows; more slices when the slice's staged x and offsets
   // would not fit in LDS
-  int S = (int)std::min<int64_t>((256 + ncg - 1) / ncg, std::max<int64_t>(1, nw / (4 * GW)));
-  // a wave holds all its word rows: at most KB, so a slice has at most KB * GW
-  S = (int)std::max<int64_t>(S, (nw + KB * GW - 1) / (KB * GW));
+  int S = (int)std::min<int64_t>((256 + ncg - 1) / ncg, std::max<int64_t>(1, nw / 32));
+  // a wave holds all its word rows, so a slice has at most WROWS
+  S = (int)std::max<int64_t>(S, (nw + WROWS - 1) / WROWS);
   if (S < 1) S = 1;
   while (DirectLds((int)ng, cpl, mt, (int)((nw + S - 1) / S)).total > kMaxLds) {
     if (S >= nw) return hipErrorNotSupported;
