@@ -94,6 +94,11 @@ struct AffineArgs {
 // workspace.hip); valid until the next call on the same stream
 hipError_t stream_workspace(hipStream_t s, size_t bytes, void** out);
 
+// workgroups of `kernel` (`block` threads, `lds` bytes of dynamic LDS) that
+// the current device holds at once, counting at most max_per_cu per CU:
+// resident per CU times the CUs (cached per device, kernel, block and LDS)
+hipError_t resident_workgroups(const void* kernel, int block, size_t lds, int max_per_cu, int64_t* out);
+
 hipError_t launch_gemv_affine(const AffineArgs& a, hipStream_t s);
 // count problems that share M, G, bits and dtypes, in as few launches as possible
 hipError_t launch_gemv_grouped(const AffineArgs* probs, int count, hipStream_t s);

@@ -551,97 +551,126 @@ __global__ __launch_bounds__(256) void gptq_repack_params_kernel(const uint32_t*
 
 }  // namespace
 
-template <int CPL, int MT, bool ACT>
-hipError_t launch_direct(const GptqArgs& a, float* part, int S, hipStream_t s) {
-  const int64_t ncg = (a.N + 64 * CPL - 1) / (64 * CPL);
-  const int per_sp = (int)((a.K / 8 + S - 1) / S);
-  const size_t lds = (size_t)DirectLds((int)(a.K / a.G), CPL, MT, per_sp).total;
-  const auto k = gptq_direct_kernel<CPL, MT, ACT>;
-  // the dynamic LDS limit is raised once per kernel and device, to the most
-  // any launch of it asks for
-  static std::once_flag once[64];
+// The dynamic LDS limit of kernel k raised once per device (flags `once`),
+// to the most any launch of it asks for.
+inline hipError_t raise_lds_limit(const void* k, std::once_flag (&once)[64]) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  std::call_once(once[dev], [&] {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)kMaxLds);
-  });
+  std::call_once(once[dev], [&] { e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds); });
+  return e;
+}
+
+// K slices of a split-K launch over ncg column groups: as many as the
+// workgroups the device holds at once allow (`resident`), so that the grid
+// runs in one round: a grid just past that leaves its last workgroups
+// running alone, for as long again.  Each slice keeps at least min_rows word
+// rows (the per-workgroup set-up would otherwise dominate), and there are
+// never fewer than s_min slices.
+inline int64_t fill_slices(int64_t resident, int64_t ncg, int64_t nw, int64_t min_rows, int64_t s_min) {
+  return std::max(s_min, std::min(resident / ncg, nw / min_rows));
+}
+
+template <int CPL, int MT, bool ACT>
+hipError_t run_direct(const GptqArgs& a, hipStream_t s) {
+  const auto k = reinterpret_cast<const void*>(gptq_direct_kernel<CPL, MT, ACT>);
+  constexpr int block = 64 * direct_waves<MT>();
+  static std::once_flag once[64];
+  hipError_t e = raise_lds_limit(k, once);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3((unsigned)(ncg * S)), dim3(64 * direct_waves<MT>()), lds, s, (const uint16_t*)a.x,
-                     (const uint32_t*)a.qweight, (const uint32_t*)a.qzeros, (const uint16_t*)a.scales, a.g_idx, part,
-                     (int)a.M, (int)a.N, (int)a.K, a.G == 32 ? 5 : (a.G == 64 ? 6 : 7), S);
+  const int ng = (int)(a.K / a.G);
+  const int64_t ncg = (a.N + 64 * CPL - 1) / (64 * CPL), nw = a.K / 8;
+  // fewest slices: a wave holds all its word rows, so a slice has at most
+  // WROWS; more when the slice's staged x and offsets would not fit in LDS
+  int64_t s_min = std::max<int64_t>(1, (nw + WROWS - 1) / WROWS);
+  while (DirectLds(ng, CPL, MT, (int)((nw + s_min - 1) / s_min)).total > kMaxLds) {
+    if (s_min >= nw) return hipErrorNotSupported;
+    ++s_min;
+  }
+  int64_t resident = 0;
+  e = resident_workgroups(k, block, (size_t)DirectLds(ng, CPL, MT, (int)((nw + s_min - 1) / s_min)).total, 2,
+                          &resident);
+  if (e != hipSuccess) return e;
+  int64_t S = fill_slices(resident, ncg, nw, 32, s_min);
+  const int per_sp = (int)((nw + S - 1) / S);
+  S = (nw + per_sp - 1) / per_sp;  // no empty slice
+  // (the kernel derives the same per_sp from S; more slices only shrink the LDS)
+  const size_t lds = (size_t)DirectLds(ng, CPL, MT, (int)((nw + S - 1) / S)).total;
+  const int64_t MN = a.M * a.N;
+  float* part = nullptr;
+  e = stream_workspace(s, (size_t)S * MN * sizeof(float), (void**)&part);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gptq_direct_kernel<CPL, MT, ACT>), dim3((unsigned)(ncg * S)), dim3(block), lds, s,
+                     (const uint16_t*)a.x, (const uint32_t*)a.qweight, (const uint32_t*)a.qzeros,
+                     (const uint16_t*)a.scales, a.g_idx, part, (int)a.M, (int)a.N, (int)a.K,
+                     a.G == 32 ? 5 : (a.G == 64 ? 6 : 7), (int)S);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gptq_finalize_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, s, part,
+                     (uint16_t*)a.y, (long)MN, (int)S);
   return hipGetLastError();
 }
 
 template <int CPL>
-hipError_t launch_direct_m(const GptqArgs& a, int mt, float* part, int S, hipStream_t s) {
+hipError_t run_direct_m(const GptqArgs& a, int mt, hipStream_t s) {
   if (a.g_idx) {
-    if (mt == 1) return launch_direct<CPL, 1, true>(a, part, S, s);
-    if (mt == 2) return launch_direct<CPL, 2, true>(a, part, S, s);
-    if (mt == 4) return launch_direct<CPL, 4, true>(a, part, S, s);
-    return launch_direct<CPL, 8, true>(a, part, S, s);
+    if (mt == 1) return run_direct<CPL, 1, true>(a, s);
+    if (mt == 2) return run_direct<CPL, 2, true>(a, s);
+    if (mt == 4) return run_direct<CPL, 4, true>(a, s);
+    return run_direct<CPL, 8, true>(a, s);
   }
-  if (mt == 1) return launch_direct<CPL, 1, false>(a, part, S, s);
-  if (mt == 2) return launch_direct<CPL, 2, false>(a, part, S, s);
-  if (mt == 4) return launch_direct<CPL, 4, false>(a, part, S, s);
-  return launch_direct<CPL, 8, false>(a, part, S, s);
+  if (mt == 1) return run_direct<CPL, 1, false>(a, s);
+  if (mt == 2) return run_direct<CPL, 2, false>(a, s);
+  if (mt == 4) return run_direct<CPL, 4, false>(a, s);
+  return run_direct<CPL, 8, false>(a, s);
 }
 
+// M >= 8 with at most 96 groups: the matrix-core kernel, K split to fill
+// the CUs (two workgroups each, LDS allowing, so that one's waits overlap the
+// other's work; each slice 64 to 256 word rows, an even count), partials
+// summed by the finalize kernel
 template <int MB, bool ACT>
-hipError_t launch_mfma_direct(const GptqArgs& a, float* part, int S, int per_sp, size_t lds, hipStream_t s) {
-  const auto k = gptq_mfma_kernel<MB, ACT>;
+hipError_t run_mfma(const GptqArgs& a, hipStream_t s) {
+  const auto k = reinterpret_cast<const void*>(gptq_mfma_kernel<MB, ACT>);
   static std::once_flag once[64];
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  hipError_t e = raise_lds_limit(k, once);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  std::call_once(once[dev], [&] {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)kMaxLds);
-  });
+  const int ng = (int)(a.K / a.G);
+  const int64_t nw = a.K / 8, ncg = (a.N + MG_COLS - 1) / MG_COLS;
+  const int64_t s_min = std::max<int64_t>(1, (nw + 255) / 256);
+  const int per_min = (int)(((nw + s_min - 1) / s_min + 1) & ~int64_t(1));
+  if (MfmaLds(ng, per_min).total > kMaxLds) return hipErrorNotSupported;
+  int64_t resident = 0;
+  e = resident_workgroups(k, 256, (size_t)MfmaLds(ng, per_min).total, 2, &resident);
   if (e != hipSuccess) return e;
-  const int64_t ncg = (a.N + MG_COLS - 1) / MG_COLS;
-  hipLaunchKernelGGL(k, dim3((unsigned)(ncg * S)), dim3(256), lds, s, (const uint16_t*)a.x, (const uint32_t*)a.qweight,
-                     (const uint32_t*)a.qzeros, (const uint16_t*)a.scales, a.g_idx, part, (uint16_t*)a.y, (int)a.M,
-                     (int)a.N, (int)a.K, a.G == 32 ? 5 : (a.G == 64 ? 6 : 7), S, per_sp);
-  return hipGetLastError();
-}
-
-// M >= 8 with at most 96 groups: the matrix-core kernel, K split so that
-// the workgroups cover every CU twice (each slice at most 256 word rows),
-// partials summed by the finalize kernel
-hipError_t launch_gptq_mfma(const GptqArgs& a, hipStream_t s) {
-  const int64_t ng = a.K / a.G, nw = a.K / 8;
-  const int64_t ncg = (a.N + MG_COLS - 1) / MG_COLS;
-  // two workgroups per CU (LDS allowing), so that one's waits overlap the other's work
-  int S = (int)std::min<int64_t>((512 + ncg - 1) / ncg, std::max<int64_t>(1, nw / 16));
-  S = (int)std::max<int64_t>(S, (nw + 255) / 256);
-  int per_sp = (int)(((nw + S - 1) / S + 1) & ~int64_t(1));
-  S = (int)((nw + per_sp - 1) / per_sp);  // no empty slice
-  const size_t lds = (size_t)MfmaLds((int)ng, per_sp).total;
-  if (lds > (size_t)kMaxLds) return hipErrorNotSupported;
+  int64_t S = fill_slices(resident, ncg, nw, 64, s_min);
+  const int per_sp = (int)(((nw + S - 1) / S + 1) & ~int64_t(1));
+  S = (nw + per_sp - 1) / per_sp;  // no empty slice
+  const size_t lds = (size_t)MfmaLds(ng, per_sp).total;
   const int64_t MN = a.M * a.N;
   float* part = nullptr;
   if (S > 1) {
-    hipError_t e = stream_workspace(s, (size_t)S * MN * sizeof(float), (void**)&part);
+    e = stream_workspace(s, (size_t)S * MN * sizeof(float), (void**)&part);
     if (e != hipSuccess) return e;
   }
-  const int mb = a.M <= 32 ? 1 : 2;
-  hipError_t e;
-  if (a.g_idx)
-    e = mb == 1 ? launch_mfma_direct<1, true>(a, part, S, per_sp, lds, s)
-                : launch_mfma_direct<2, true>(a, part, S, per_sp, lds, s);
-  else
-    e = mb == 1 ? launch_mfma_direct<1, false>(a, part, S, per_sp, lds, s)
-                : launch_mfma_direct<2, false>(a, part, S, per_sp, lds, s);
+  hipLaunchKernelGGL((gptq_mfma_kernel<MB, ACT>), dim3((unsigned)(ncg * S)), dim3(256), lds, s, (const uint16_t*)a.x,
+                     (const uint32_t*)a.qweight, (const uint32_t*)a.qzeros, (const uint16_t*)a.scales, a.g_idx, part,
+                     (uint16_t*)a.y, (int)a.M, (int)a.N, (int)a.K, a.G == 32 ? 5 : (a.G == 64 ? 6 : 7), (int)S,
+                     per_sp);
+  e = hipGetLastError();
   if (e == hipSuccess && S > 1) {
     hipLaunchKernelGGL(gptq_finalize_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, s, part,
-                       (uint16_t*)a.y, (long)MN, S);
+                       (uint16_t*)a.y, (long)MN, (int)S);
     e = hipGetLastError();
   }
   return e;
+}
+
+hipError_t launch_gptq_mfma(const GptqArgs& a, hipStream_t s) {
+  const bool mb1 = a.M <= 32;
+  if (a.g_idx) return mb1 ? run_mfma<1, true>(a, s) : run_mfma<2, true>(a, s);
+  return mb1 ? run_mfma<1, false>(a, s) : run_mfma<2, false>(a, s);
 }
 
 hipError_t launch_gptq_direct(const GptqArgs& a, hipStream_t s) {
@@ -655,31 +684,7 @@ hipError_t launch_gptq_direct(const GptqArgs& a, hipStream_t s) {
   if (a.K / 8 * a.N * 4 >= (int64_t(1) << 31)) return hipErrorNotSupported;  // 32-bit buffer offsets
   // x rows per pass (8 would spill registers at 4 columns per lane)
   const int mt = a.M == 1 ? 1 : (a.M == 2 ? 2 : (a.M <= 4 || cpl == 4 ? 4 : 8));
-  const int64_t ncg = (a.N + 64 * cpl - 1) / (64 * cpl);
-  const int64_t nw = a.K / 8;
-  // K slices: enough workgroups to give every CU one, each wave keeping at
-  // least 4 word rows; more slices when the slice's staged x and offsets
-  // would not fit in LDS
-  int S = (int)std::min<int64_t>((256 + ncg - 1) / ncg, std::max<int64_t>(1, nw / 32));
-  // a wave holds all its word rows, so a slice has at most WROWS
-  S = (int)std::max<int64_t>(S, (nw + WROWS - 1) / WROWS);
-  if (S < 1) S = 1;
-  while (DirectLds((int)ng, cpl, mt, (int)((nw + S - 1) / S)).total > kMaxLds) {
-    if (S >= nw) return hipErrorNotSupported;
-    ++S;
-  }
-  const int64_t MN = a.M * a.N;
-  float* part = nullptr;
-  hipError_t e = stream_workspace(s, (size_t)S * MN * sizeof(float), (void**)&part);
-  if (e != hipSuccess) return e;
-  e = cpl == 4 ? launch_direct_m<4>(a, mt, part, S, s)
-               : (cpl == 2 ? launch_direct_m<2>(a, mt, part, S, s) : launch_direct_m<1>(a, mt, part, S, s));
-  if (e == hipSuccess) {
-    hipLaunchKernelGGL(gptq_finalize_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, s, part,
-                       (uint16_t*)a.y, (long)MN, S);
-    e = hipGetLastError();
-  }
-  return e;
+  return cpl == 4 ? run_direct_m<4>(a, mt, s) : (cpl == 2 ? run_direct_m<2>(a, mt, s) : run_direct_m<1>(a, mt, s));
 }
 
 hipError_t launch_gptq_repack(const int32_t* qweight, const int32_t* qzeros, const void* scales,

@@ -7,8 +7,12 @@
 // buffer is kept, not freed, because a captured graph may still address it.
 // Growing is refused while the stream is being captured, so a graph is
 // captured after one eager call of the same shapes.
+// Also here: how many workgroups of a kernel the device holds at once, by
+// which the launchers size their K splits.
+#include <algorithm>
 #include <map>
 #include <mutex>
+#include <tuple>
 #include <utility>
 #include <vector>
 
@@ -26,6 +30,9 @@ struct Workspace {
 std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 std::vector<void*> g_retired;  // grown-out buffers, still valid for graphs that captured them
+
+// (device, kernel, block, LDS) -> (CUs, resident workgroups per CU), under g_mu
+std::map<std::tuple<int, const void*, int, size_t>, std::pair<int, int>> g_resident;
 
 }  // namespace
 
@@ -52,6 +59,34 @@ hipError_t stream_workspace(hipStream_t s, size_t bytes, void** out) {
     w.cap = cap;
   }
   *out = w.p;
+  return hipSuccess;
+}
+
+hipError_t resident_workgroups(const void* kernel, int block, size_t lds, int max_per_cu, int64_t* out) {
+  *out = 0;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const auto key = std::make_tuple(dev, kernel, block, lds);
+  std::pair<int, int> r{0, 0};  // (CUs, resident per CU)
+  bool known = false;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    const auto it = g_resident.find(key);
+    if (it != g_resident.end()) {
+      r = it->second;
+      known = true;
+    }
+  }
+  if (!known) {
+    e = hipDeviceGetAttribute(&r.first, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&r.second, kernel, block, lds);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_mu);
+    g_resident[key] = r;
+  }
+  *out = (int64_t)r.first * std::min(r.second, max_per_cu);
   return hipSuccess;
 }
 
