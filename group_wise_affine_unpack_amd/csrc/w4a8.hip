@@ -589,13 +589,15 @@ hipError_t launch_w4a8(const W4A8Args& a, hipStream_t s) {
   p.K = K;
   p.Tm = (M + t.mb * 32 - 1) / (t.mb * 32);
   p.Tn = (N + t.nb * 128 - 1) / (t.nb * 128);
-  // K splits when the tiles leave CUs idle: enough workgroups for every CU,
-  // whole stages per split, partials within 32-bit sizes
+  // K splits when the tiles leave CUs idle and K has at least 16 stages:
+  // enough workgroups for every CU, at least 4 whole stages per split,
+  // partials within 32-bit sizes.  (Below 16 stages the split's second
+  // kernel and partials cost more than the shorter K loop saves.)
   {
     const int nst = (K + BK - 1) / BK, tiles = p.Tm * p.Tn;
     int S = 1;
-    if (tiles < 256) {
-      S = std::min((256 + tiles - 1) / tiles, nst);
+    if (tiles < 256 && nst >= 16) {
+      S = std::min((256 + tiles - 1) / tiles, nst / 4);
       while (S > 1 && (int64_t)S * M * N * 4 >= (int64_t(1) << 31)) --S;
     }
     p.per_split = (nst + S - 1) / S;
