@@ -159,3 +159,50 @@ def test_direct_matrix_core_scale_range():
     torch.cuda.synchronize()
     ref = oracle.qmm_gptq(case.x, case.qweight, case.qzeros, case.scales, case.g_idx, case.M, case.K, case.N, case.G)
     assert_float_bar(host_f64(y), ref, case.name)
+
+
+def test_split_k_sums_on_every_call():
+    # K split over workgroups: every call writes every output afresh.  Calls
+    # alternate between the kernels and shapes on one stream, each into an
+    # output filled with NaN first, so that a partial sum left from another
+    # call, or an output no workgroup wrote, shows as a wrong value or NaN.
+    dev = require_gpu()
+    shapes = [(1, 1000, 1024, 128), (3, 2040, 4096, 64), (8, 200, 1024, 128), (64, 136, 6144, 64),
+              (1, 264, 4096, 32)]
+    cases = []
+    for i, (M, N, K, G) in enumerate(shapes):
+        case = si.gptq_case(M, K, N, G, seed=(56, i), name=f"gptq_rep_M{M}_N{N}_K{K}_G{G}")
+        ref = oracle.qmm_gptq(case.x, case.qweight, case.qzeros, case.scales, case.g_idx, M, K, N, G)
+        cases.append((case, _dev(case, dev), ref))
+    for rep in range(3):
+        for case, (x, qw, qz, s, gi), ref in cases:
+            _log(case, f"repeated calls, pass {rep}")
+            y = torch.full((case.M, case.N), float("nan"), dtype=torch.float16, device=dev)
+            qa.qmm_gptq(x, qw, qz, s, gi, case.G, out=y)
+            torch.cuda.synchronize()
+            assert_float_bar(host_f64(y), ref, f"{case.name} pass {rep}")
+
+
+def test_split_k_sums_under_graph_replay():
+    # a captured call replayed into an output refilled with NaN each time
+    dev = require_gpu()
+    case = si.gptq_case(2, 4096, 2040, 64, seed=(57,), name="gptq_rep_graph")
+    ref = oracle.qmm_gptq(case.x, case.qweight, case.qzeros, case.scales, case.g_idx, case.M, case.K, case.N, case.G)
+    x, qw, qz, s, gi = _dev(case, dev)
+    _log(case, "graph replays")
+    y = torch.empty((case.M, case.N), dtype=torch.float16, device=dev)
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        qa.qmm_gptq(x, qw, qz, s, gi, case.G, out=y)  # sizes the stream's buffers
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        qa.qmm_gptq(x, qw, qz, s, gi, case.G, out=y)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_float_bar(host_f64(y), ref, f"{case.name} replay {rep}")
