@@ -475,6 +475,40 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
   return v;
 }
 
+// Sums over the 64 lanes of four values at once, exact in int32: two
+// permlane32 swaps, one permlane16 swap, four DPP row rotations.  Row q
+// (lanes 16q .. 16q+15) of the result holds the total of v[q].
+__device__ __forceinline__ int wave_sum4_i32(int v0, int v1, int v2, int v3) {
+  auto sw32 = [](int a, int b) {
+    const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)a, (uint32_t)b, false, false);
+    return (int)r[0] + (int)r[1];
+  };
+  const int s02 = sw32(v0, v2);  // lanes 0-31: halves of v0, lanes 32-63: halves of v2
+  const int s13 = sw32(v1, v3);
+  const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)s02, (uint32_t)s13, false, false);
+  int t = (int)r[0] + (int)r[1];  // row q: quarters of v[q]
+  t += dpp_i<0x128>(t);
+  t += dpp_i<0x124>(t);
+  t += dpp_i<0x122>(t);
+  t += dpp_i<0x121>(t);
+  return t;
+}
+
+// Maximum over the 64 lanes (every lane gets it): lanes l and l ^ 32, then
+// rows 2i and 2i+1 by swaps, then rotations inside each row of 16 lanes.
+// For non-NaN values the result does not depend on the order.
+__device__ __forceinline__ float wave_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  v = fmaxf(v, __int_as_float(dpp_i<0x128>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_i<0x124>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_i<0x122>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_i<0x121>(__float_as_int(v))));
+  return v;
+}
+
 // W4A8 for M <= 16: one wave per output column n, lanes over K in chunks of
 // 32 codes (16 bytes of packed codes; 32 bytes of x_q per row), the codes
 // decoded to int8 (16 v, as in the GEMM) and multiplied with v_dot4_i32_i8;
@@ -511,14 +545,178 @@ __global__ __launch_bounds__(256) void w4a8_gemv_kernel(const int8_t* __restrict
     }
   }
   const float swn = f16_bits_to_f32(sw[n]);
+  if constexpr (MT < 4) {
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    const int a = wave_sum_i32(acc[m]) >> 4;
-    if (lane == m && m < M) {
-      if (acc_out) acc_out[(long)m * N + n] = a;
-      y[(long)m * N + n] = f32_to_f16_bits(((float)a * sx[m]) * swn);
+    for (int m = 0; m < MT; ++m) {
+      const int a = wave_sum_i32(acc[m]) >> 4;
+      if (lane == m && m < M) {
+        if (acc_out) acc_out[(long)m * N + n] = a;
+        y[(long)m * N + n] = f32_to_f16_bits(((float)a * sx[m]) * swn);
+      }
+    }
+  } else {
+    // four rows at a time: row q of the lanes holds row 4g + q
+#pragma unroll
+    for (int g = 0; g < MT / 4; ++g) {
+      const int a = wave_sum4_i32(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]) >> 4;
+      const int m = 4 * g + (lane >> 4);
+      if ((lane & 15) == 0 && m < M) {
+        if (acc_out) acc_out[(long)m * N + n] = a;
+        y[(long)m * N + n] = f32_to_f16_bits(((float)a * sx[m]) * swn);
+      }
     }
   }
+}
+
+// W4A8 for M <= 16 and K <= 4096 in one launch.  Every workgroup first
+// quantizes all M rows of x into LDS, one wave per row with the row's
+// 8-value chunks in registers, by the same arithmetic as
+// w4a8_quant_rows_kernel (so the codes and scales are the same bits);
+// workgroup 0 also writes them to x_q and s_x.  Then each of its four waves
+// computes CW adjacent columns as w4a8_gemv_kernel computes one, reading
+// x_q from LDS once for all CW.  The weight words are loaded before the
+// quantize, so their latency overlaps it.  Every workgroup quantizes again
+// (x, at most 128 KiB, comes from L2), so CW grows with N to keep the
+// workgroups near one per CU.
+constexpr int FUSED_MAX_K = 4096;
+
+template <int MT, int CW>
+__global__ __launch_bounds__(256) void w4a8_gemv_fused_kernel(const uint16_t* __restrict__ x,
+                                                              const uint32_t* __restrict__ w,
+                                                              const uint16_t* __restrict__ sw, uint16_t* __restrict__ y,
+                                                              int8_t* __restrict__ xq_out, float* __restrict__ sx_out,
+                                                              int32_t* __restrict__ acc_out, int M, int N, int K) {
+  __shared__ __attribute__((aligned(16))) int8_t xs[MT * FUSED_MAX_K];  // [M][K] codes
+  __shared__ float ss[MT];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int n0 = (blockIdx.x * 4 + wave) * CW;
+  const int nch = K / 32;  // 32-code chunks: at most 128, two per lane
+  // weight words of the wave's columns (a column past N reads zeros)
+  u32x4_t wv[CW][2];
+#pragma unroll
+  for (int j = 0; j < CW; ++j) {
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(w + (long)min(n0 + j, N - 1) * (K / 8), n0 + j < N ? (uint32_t)(K / 2) : 0u);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) wv[j][i] = ld128(rw, lane + 64 * i < nch ? (uint32_t)(lane + 64 * i) * 16u : OOB);
+  }
+
+  const int C = K >> 3;  // 8-value chunks per row: at most 512, eight per lane
+  const bool first = blockIdx.x == 0;
+  // rows wave, wave + 4, ... two at a time, both rows' loads issued first
+  auto load_row = [&](int m, u32x4_t (&v)[8]) __attribute__((always_inline)) {
+    const u32x4_t* row = reinterpret_cast<const u32x4_t*>(x + (long)min(m, M - 1) * K);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = lane + 64 * j < C ? row[lane + 64 * j] : u32x4_t{0, 0, 0, 0};
+  };
+  auto quant_row = [&](int m, const u32x4_t (&v)[8]) __attribute__((always_inline)) {
+    f16x2_t am2 = {0, 0};
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        am2 = __builtin_elementwise_max(am2, __builtin_bit_cast(f16x2_t, v[j][e] & 0x7FFF7FFFu));
+    const float am = wave_max(fmaxf((float)am2[0], (float)am2[1]));
+    const float s = am / 127.0f;  // correctly rounded division (HIP default)
+    float r = 0.f;
+    if (am != 0.f) {
+      const float r0 = __builtin_amdgcn_rcpf(s);
+      r = __builtin_fmaf(__builtin_fmaf(-s, r0, 1.0f), r0, r0);
+    }
+    if (lane == 0) {
+      ss[m] = s;
+      if (first) sx_out[m] = s;
+    }
+    u32x2_t* qrow = reinterpret_cast<u32x2_t*>(xs + m * K);
+    u32x2_t* grow = reinterpret_cast<u32x2_t*>(xq_out + (long)m * K);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (lane + 64 * j < C) {
+        const u32x2_t q = {quant_word(v[j][0], v[j][1], s, r), quant_word(v[j][2], v[j][3], s, r)};
+        qrow[lane + 64 * j] = q;
+        if (first) grow[lane + 64 * j] = q;
+      }
+    }
+  };
+  for (int m = wave; m < M; m += 8) {
+    u32x4_t va[8], vb[8];
+    load_row(m, va);
+    if (m + 4 < M) load_row(m + 4, vb);  // uniform
+    quant_row(m, va);
+    if (m + 4 < M) quant_row(m + 4, vb);
+  }
+  __syncthreads();
+  if (n0 >= N) return;  // no barrier follows
+
+  int acc[MT][CW];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < CW; ++j) acc[m][j] = 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+      uint32_t d[CW][8];
+#pragma unroll
+      for (int j = 0; j < CW; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) decode_word(wv[j][i][q], d[j][2 * q], d[j][2 * q + 1]);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const int8_t* xr = xs + min(m, M - 1) * K + c * 32;
+        const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(xr), x1 = *reinterpret_cast<const u32x4_t*>(xr + 16);
+#pragma unroll
+        for (int j = 0; j < CW; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[m][j] = __builtin_amdgcn_sdot4((int)d[j][q], (int)x0[q], acc[m][j], false);
+            acc[m][j] = __builtin_amdgcn_sdot4((int)d[j][4 + q], (int)x1[q], acc[m][j], false);
+          }
+      }
+    }
+  }
+  // the MT x CW sums, four at a time (value v = m CW + j): row q of group g
+  // holds value 4g + q, written by the row's first lane
+  constexpr int V = MT * CW;
+  if constexpr (V < 4) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int m = v / CW, n = n0 + v % CW;
+      const int a = wave_sum_i32(acc[m][v % CW]) >> 4;
+      if (lane == 0 && m < M && n < N) {
+        if (acc_out) acc_out[(long)m * N + n] = a;
+        y[(long)m * N + n] = f32_to_f16_bits(((float)a * ss[m]) * f16_bits_to_f32(sw[n]));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < V / 4; ++g) {
+      const int t = wave_sum4_i32(acc[(4 * g) / CW][(4 * g) % CW], acc[(4 * g + 1) / CW][(4 * g + 1) % CW],
+                                  acc[(4 * g + 2) / CW][(4 * g + 2) % CW], acc[(4 * g + 3) / CW][(4 * g + 3) % CW]) >> 4;
+      const int v = 4 * g + (lane >> 4), m = v / CW, n = n0 + v % CW;
+      if ((lane & 15) == 0 && m < M && n < N) {
+        if (acc_out) acc_out[(long)m * N + n] = t;
+        y[(long)m * N + n] = f32_to_f16_bits(((float)t * ss[m]) * f16_bits_to_f32(sw[n]));
+      }
+    }
+  }
+}
+
+template <int MT>
+void launch_fused_cw(const W4A8Args& a, int M, int N, int K, hipStream_t s) {
+  const uint16_t* x = (const uint16_t*)a.x;
+  const uint16_t* sw = (const uint16_t*)a.s_w;
+  uint16_t* y = (uint16_t*)a.y;
+  // columns per wave: as many as keep 256 workgroups (4 waves each)
+  const int cw = N >= 4096 ? 4 : (N >= 2048 ? 2 : 1);
+  const dim3 grid((unsigned)((N + 4 * cw - 1) / (4 * cw))), b256(256);
+  if (cw == 4)
+    hipLaunchKernelGGL((w4a8_gemv_fused_kernel<MT, 4>), grid, b256, 0, s, x, a.w, sw, y, a.x_q, a.s_x, a.acc, M, N, K);
+  else if (cw == 2)
+    hipLaunchKernelGGL((w4a8_gemv_fused_kernel<MT, 2>), grid, b256, 0, s, x, a.w, sw, y, a.x_q, a.s_x, a.acc, M, N, K);
+  else
+    hipLaunchKernelGGL((w4a8_gemv_fused_kernel<MT, 1>), grid, b256, 0, s, x, a.w, sw, y, a.x_q, a.s_x, a.acc, M, N, K);
 }
 
 }  // namespace
@@ -528,6 +726,14 @@ hipError_t launch_w4a8(const W4A8Args& a, hipStream_t s) {
   // buffer offsets are 32-bit
   if (a.N * a.K / 2 >= (int64_t(1) << 31) || a.K * 256 >= (int64_t(1) << 31)) return hipErrorNotSupported;
   const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
+  if (M <= 16 && K <= FUSED_MAX_K) {
+    if (M == 1) launch_fused_cw<1>(a, M, N, K, s);
+    else if (M == 2) launch_fused_cw<2>(a, M, N, K, s);
+    else if (M <= 4) launch_fused_cw<4>(a, M, N, K, s);
+    else if (M <= 8) launch_fused_cw<8>(a, M, N, K, s);
+    else launch_fused_cw<16>(a, M, N, K, s);
+    return hipGetLastError();
+  }
   {
     // threads per row: one wave up to 512 values, two up to 1024, then four;
     // chunks per thread: 1, 2, 4 or 8 (K <= 16384), else one row per block

@@ -168,9 +168,11 @@ int qmm_gptq(const void *x, const int32_t *qweight, const int32_t *qzeros, const
  *   x_q     [M, K]    int8 (output, caller-owned; the quantized activations)
  *   s_x     [M]       f32  (output, caller-owned)
  *   acc_out [M, N]    int32 or NULL (output; the accumulators, for checking)
- *   K % 32 == 0.  Launches on `stream`: quantize, then the integer product
- *   (a dot4 GEMV for M <= 16, else the int8 MFMA GEMM, plus a summing pass
- *   over int32 partials when K is split).
+ *   K % 32 == 0.  Launches on `stream`: for M <= 16 and K <= 4096 one kernel
+ *   (every workgroup quantizes x into LDS, workgroup 0 also writes x_q and
+ *   s_x, then a dot4 GEMV); otherwise quantize, then the integer product (a
+ *   dot4 GEMV for M <= 16, else the int8 MFMA GEMM, plus a summing pass over
+ *   int32 partials when K is split).
  */
 int qgemm_w4a8(const void *x, const uint32_t *w_q4, const void *s_w, void *y, int8_t *x_q, float *s_x,
                int32_t *acc_out, int64_t M, int64_t N, int64_t K, void *stream);

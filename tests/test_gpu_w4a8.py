@@ -131,11 +131,14 @@ def test_quantize_every_f16_activation_and_scale():
     assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[0]}: x=0x{x[tuple(bad[0])]:04x}"
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 37, 32), (2, 64, 2048), (3, 130, 4096), (16, 70, 1056), (17, 300, 4096),
-                                   (100, 260, 8192)])
+@pytest.mark.parametrize("M,N,K", [(1, 37, 32), (2, 64, 2048), (3, 130, 4096), (16, 70, 1056), (5, 2060, 512),
+                                   (16, 4100, 4096), (9, 300, 8192), (17, 300, 4096), (100, 260, 8192)])
 def test_small_m_paths(M, N, K):
-    # M <= 16: the dot4 GEMV kernel (N not a multiple of its 4 columns per
-    # workgroup, K down to one 32-code chunk); M = 17 and 100: the MFMA GEMM
-    # with K split over workgroups and int32 partials
+    # M <= 16, K <= 4096: the fused quantize + dot4 GEMV, 1, 2 or 4 columns
+    # per wave (N below 2048, from 2048, from 4096; N not a multiple of the
+    # workgroup's columns, K down to one 32-code chunk, M = 16 at K = 4096
+    # fills its 64 KiB of LDS); M = 9 at K = 8192: the quantize kernel, then
+    # the GEMV; M = 17 and 100: the MFMA GEMM with K split over workgroups
+    # and int32 partials
     case = si.w4a8_case(M, N, K, seed=(47, M, N, K), name=f"w4a8_small_M{M}_N{N}_K{K}")
     _check(case)
