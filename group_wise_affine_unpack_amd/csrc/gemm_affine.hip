@@ -268,7 +268,6 @@ struct GemmParams {
 };
 
 __device__ __forceinline__ f16x2_t h2(uint32_t v) { return __builtin_bit_cast(f16x2_t, v); }
-__device__ __forceinline__ uint32_t u32(f16x2_t v) { return __builtin_bit_cast(uint32_t, v); }
 
 // B fragment (8 fp16 = 4 dwords) for one 32x32x16 step, one code piece, one
 // scale piece.  `wd` holds the lane's words for this step (1 for 4-bit, 2 for

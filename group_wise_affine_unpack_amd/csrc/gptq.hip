@@ -72,6 +72,12 @@ struct GTab {
 // LDS of one workgroup, in bytes: the (scale, bias) table, the slice's
 // group offsets (one int per code), MT rows of x for the slice (fp32), and
 // the waves' partial sums.
+// Groups in the direct kernel's table: every group with act-order (any code
+// may map to any group), else those a slice of per_sp word rows can touch.
+__host__ __device__ inline int table_groups(bool act, int ng, int per_sp, int gsh) {
+  return act ? ng : min(ng, ((per_sp * 8 + (1 << gsh) - 1) >> gsh) + 1);  // G = 2^gsh
+}
+
 struct DirectLds {
   int tab, goff, xs, red, total;
   __host__ __device__ DirectLds(int ng, int cpl, int mt, int per_sp) {
@@ -121,7 +127,10 @@ __global__ __launch_bounds__(64 * direct_waves<MT>()) void gptq_direct_kernel(
   const int sp0 = sp * per_sp, sp1 = min(nw, sp0 + per_sp);
   const int per_w = (sp1 - sp0 + GW - 1) / GW;
   const int kw0 = min(sp1, sp0 + wave * per_w), kw1 = min(sp1, kw0 + per_w);
-  const DirectLds L(ng, CPL, MT, per_sp);
+  // the table: all ng groups with act-order, else the slice's groups from g_lo
+  const int g_lo = ACT ? 0 : (sp0 * 8) >> gsh;
+  const int ngt = ACT ? ng : (sp1 > sp0 ? (((sp1 * 8 - 1) >> gsh) - g_lo + 1) : 0);
+  const DirectLds L(table_groups(ACT, ng, per_sp, gsh), CPL, MT, per_sp);
   int* goff = reinterpret_cast<int*>(lds + L.goff);
   float* xs = reinterpret_cast<float*>(lds + L.xs);
   float* red = reinterpret_cast<float*>(lds + L.red);  // [GW][MT][COLS]
@@ -138,15 +147,15 @@ __global__ __launch_bounds__(64 * direct_waves<MT>()) void gptq_direct_kernel(
 #pragma unroll
   for (int j = 0; j < KB; ++j) wv[j] = load_words<CPL>(rq, kw0 + j < kw1 ? loff + (uint32_t)(kw0 + j) * row_bytes : OOB);
   // table sources: chunk i = (group, 8 columns), a qzeros word and 8 scales
-  constexpr int TC = 3;  // chunks per thread: ng * COLS / 8 <= 3 * 64 * GW
-  const int nchunk = ng * (COLS / 8);
+  constexpr int TC = 3;  // chunks per thread: ngt * COLS / 8 <= 3 * 64 * GW
+  const int nchunk = ngt * (COLS / 8);
   const bool sc16 = ((uintptr_t)sc & 15) == 0;
   u32x4_t sv[TC];
   uint32_t zv[TC];
 #pragma unroll
   for (int u = 0; u < TC; ++u) {
     const int i = t + u * 64 * GW;
-    const int g = i / (COLS / 8), n = n0 + 8 * (i % (COLS / 8));
+    const int g = g_lo + i / (COLS / 8), n = n0 + 8 * (i % (COLS / 8));
     sv[u] = u32x4_t{0, 0, 0, 0};
     zv[u] = 0;
     if (i < nchunk && n < N) {
@@ -166,7 +175,7 @@ __global__ __launch_bounds__(64 * direct_waves<MT>()) void gptq_direct_kernel(
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int i = t + u * 64 * GW, k = sp0 * 8 + i;
-    gv[u] = i < nk ? (ACT ? g_idx[k] : k >> gsh) : 0;
+    gv[u] = i < nk ? (ACT ? g_idx[k] : (k >> gsh) - g_lo) : 0;
   }
   // x rows m0 .. m0+MT-1 over the slice, in f16 pairs (MT per thread)
   auto load_x = [&](int m0, uint32_t (&xp)[MT]) {
@@ -583,20 +592,25 @@ hipError_t run_direct(const GptqArgs& a, hipStream_t s) {
   const int64_t ncg = (a.N + 64 * CPL - 1) / (64 * CPL), nw = a.K / 8;
   // fewest slices: a wave holds all its word rows, so a slice has at most
   // WROWS; more when the slice's staged x and offsets would not fit in LDS
+  auto lds_of = [&](int64_t S) {
+    const int per_sp = (int)((nw + S - 1) / S);
+    return DirectLds(table_groups(ACT, ng, per_sp, a.G == 32 ? 5 : (a.G == 64 ? 6 : 7)), CPL, MT, per_sp).total;
+  };
   int64_t s_min = std::max<int64_t>(1, (nw + WROWS - 1) / WROWS);
-  while (DirectLds(ng, CPL, MT, (int)((nw + s_min - 1) / s_min)).total > kMaxLds) {
+  while (lds_of(s_min) > kMaxLds) {
     if (s_min >= nw) return hipErrorNotSupported;
     ++s_min;
   }
   int64_t resident = 0;
-  e = resident_workgroups(k, block, (size_t)DirectLds(ng, CPL, MT, (int)((nw + s_min - 1) / s_min)).total, 2,
-                          &resident);
+  // (at most 16 waves per CU: two 8-wave workgroups or one of 16; two of
+  // 16 measured slower)
+  e = resident_workgroups(k, block, (size_t)lds_of(s_min), 16 / direct_waves<MT>(), &resident);
   if (e != hipSuccess) return e;
   int64_t S = fill_slices(resident, ncg, nw, 32, s_min);
   const int per_sp = (int)((nw + S - 1) / S);
   S = (nw + per_sp - 1) / per_sp;  // no empty slice
   // (the kernel derives the same per_sp from S; more slices only shrink the LDS)
-  const size_t lds = (size_t)DirectLds(ng, CPL, MT, (int)((nw + S - 1) / S)).total;
+  const size_t lds = (size_t)lds_of(S);
   const int64_t MN = a.M * a.N;
   float* part = nullptr;
   e = stream_workspace(s, (size_t)S * MN * sizeof(float), (void**)&part);
@@ -614,16 +628,17 @@ hipError_t run_direct(const GptqArgs& a, hipStream_t s) {
 
 template <int CPL>
 hipError_t run_direct_m(const GptqArgs& a, int mt, hipStream_t s) {
+  constexpr int MT8 = CPL == 4 ? 4 : 8;  // (8 rows per pass only below 4 columns per lane)
   if (a.g_idx) {
     if (mt == 1) return run_direct<CPL, 1, true>(a, s);
     if (mt == 2) return run_direct<CPL, 2, true>(a, s);
     if (mt == 4) return run_direct<CPL, 4, true>(a, s);
-    return run_direct<CPL, 8, true>(a, s);
+    return run_direct<CPL, MT8, true>(a, s);
   }
   if (mt == 1) return run_direct<CPL, 1, false>(a, s);
   if (mt == 2) return run_direct<CPL, 2, false>(a, s);
   if (mt == 4) return run_direct<CPL, 4, false>(a, s);
-  return run_direct<CPL, 8, false>(a, s);
+  return run_direct<CPL, MT8, false>(a, s);
 }
 
 // M >= 8 with at most 96 groups: the matrix-core kernel, K split to fill
@@ -678,9 +693,10 @@ hipError_t launch_gptq_direct(const GptqArgs& a, hipStream_t s) {
   if (a.M >= 8 && ng <= 96 && a.K / 8 * a.N * 4 < (int64_t(1) << 31) && a.M * a.K * 2 < (int64_t(1) << 31))
     return launch_gptq_mfma(a, s);
   // columns per lane: 4 when the (scale, bias) table of 256 columns fits
-  // 64 KiB of LDS, else 2, else 1 (up to 96 KiB)
-  const int cpl = ng <= 32 ? 4 : (ng <= 64 ? 2 : 1);
-  if (ng * 64 * cpl * 8 > 96 * 1024) return hipErrorNotSupported;  // group table must fit in LDS
+  // 64 KiB of LDS, else 2, else 1 (up to 96 KiB).  Without act-order the
+  // table holds only a slice's groups, so 4 always.
+  const int cpl = !a.g_idx || ng <= 32 ? 4 : (ng <= 64 ? 2 : 1);
+  if (a.g_idx && ng * 64 * cpl * 8 > 96 * 1024) return hipErrorNotSupported;  // group table must fit in LDS
   if (a.K / 8 * a.N * 4 >= (int64_t(1) << 31)) return hipErrorNotSupported;  // 32-bit buffer offsets
   // x rows per pass (8 would spill registers at 4 columns per lane)
   const int mt = a.M == 1 ? 1 : (a.M == 2 ? 2 : (a.M <= 4 || cpl == 4 ? 4 : 8));

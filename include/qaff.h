@@ -140,9 +140,11 @@ int qgemv_affine_grouped(const qaff_gemv_problem *problems, int32_t count, int64
  *   qweight [K/8, N]  int32 (read as uint32),   qzeros [K/G, N/8] int32
  *   scales  [K/G, N]  f16;                       g_idx [K] int32 or NULL,
  *           values in [0, K/G) (not checked on the device)
- *   K % 8 == 0, K % G == 0, N % 8 == 0, G in {32, 64, 128}; at most 192
- *   groups (K/G), else QAFF_E_UNSUPPORTED (the per-workgroup table of
- *   scales and zeros must fit in LDS).
+ *   K % 8 == 0, K % G == 0, N % 8 == 0, G in {32, 64, 128}; with g_idx, at
+ *   most 192 groups (K/G), else QAFF_E_UNSUPPORTED (the per-workgroup table
+ *   of scales and zeros for every group must fit in LDS).  A layer without
+ *   act-order (g_idx[i] = i/G) should pass g_idx = NULL: then a workgroup's
+ *   table holds only the groups of its K slice, and any K/G is taken.
  * Kernels: M < 8 on the VALU (w exact in fp32), M >= 8 with at most 96
  * groups on the matrix cores (w as two exact fp16 pieces relative to each
  * column's largest scale); fp32 partial sums over K slices, one summing

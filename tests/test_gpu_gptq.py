@@ -128,6 +128,25 @@ def test_direct_shapes(M, N, K, G, act_order):
 
 
 @pytest.mark.parametrize("M,N,K,G", [
+    (1, 520, 8192, 32),     # 256 groups: more than a whole table can hold
+    (3, 264, 16384, 32),    # 512 groups, four columns per lane
+    (9, 136, 8192, 32),     # M >= 8 past 96 groups: the VALU kernel, passes of 4 rows
+])
+def test_direct_without_act_order_many_groups(M, N, K, G):
+    # g_idx NULL: each workgroup's table holds only its K slice's groups, so
+    # K/G is not limited by LDS
+    dev = require_gpu()
+    case = si.gptq_case(M, K, N, G, seed=(58, M, N, K, G), act_order=False, name=f"gptq_noact_M{M}_N{N}_K{K}_G{G}")
+    case.g_idx = None
+    _log(case, "direct, slice tables")
+    x, qw, qz, s, gi = _dev(case, dev)
+    y = qa.qmm_gptq(x, qw, qz, s, gi, G)
+    torch.cuda.synchronize()
+    ref = oracle.qmm_gptq(case.x, case.qweight, case.qzeros, case.scales, case.g_idx, M, case.K, case.N, case.G)
+    assert_float_bar(host_f64(y), ref, case.name)
+
+
+@pytest.mark.parametrize("M,N,K,G", [
     (8, 200, 1024, 128),     # the smallest M of the matrix-core kernel, a partial column group
     (33, 1000, 2048, 64),    # two 32-row blocks, the second with one row
     (64, 136, 6144, 64),     # 96 groups: the largest table it takes
