@@ -361,16 +361,21 @@ __global__ __launch_bounds__(256) void gptq_mfma_kernel(
   const int nw = K / 8;
   const int sp0 = min(nw, sp * per_sp), sp1 = min(nw, sp0 + per_sp);
   const int nsteps = (sp1 - sp0) / 2;
-  const MfmaLds L(ng, per_sp);
+  // the table: all ng groups with act-order, else the slice's groups from
+  // g_lo (the largest exponent is then the slice's own, which the partial
+  // carries: acc is scaled by it before the slices are added)
+  const int g_lo = ACT ? 0 : (sp0 * 8) >> gsh;
+  const int ngt = ACT ? ng : (sp1 > sp0 ? (((sp1 * 8 - 1) >> gsh) - g_lo + 1) : 0);
+  const MfmaLds L(table_groups(ACT, ng, per_sp, gsh), per_sp);
   int* emax = reinterpret_cast<int*>(lds + L.emax);
   int* goff = reinterpret_cast<int*>(lds + L.goff);
 
   // ---- table: largest exponent per column, then the entries
   for (int i = t; i < MG_COLS; i += 256) emax[i] = 0;
   __syncthreads();
-  const int nchunk = ng * (MG_COLS / 8);
+  const int nchunk = ngt * (MG_COLS / 8);
   for (int i = t; i < nchunk; i += 256) {
-    const int g = i / (MG_COLS / 8), c8 = i % (MG_COLS / 8), n = n0 + 8 * c8;
+    const int g = g_lo + i / (MG_COLS / 8), c8 = i % (MG_COLS / 8), n = n0 + 8 * c8;
     if (n < N) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) atomicMax(&emax[8 * c8 + j], (int)((sc[(long)g * N + n + j] >> 10) & 31));
@@ -378,8 +383,8 @@ __global__ __launch_bounds__(256) void gptq_mfma_kernel(
   }
   __syncthreads();
   for (int i = t; i < nchunk; i += 256) {
-    const int g = i / (MG_COLS / 8), c8 = i % (MG_COLS / 8), n = n0 + 8 * c8;
-    uint2* row = reinterpret_cast<uint2*>(lds + L.tab + g * MG_COLS * 8) + 8 * c8;
+    const int g = g_lo + i / (MG_COLS / 8), c8 = i % (MG_COLS / 8), n = n0 + 8 * c8;
+    uint2* row = reinterpret_cast<uint2*>(lds + L.tab + (g - g_lo) * MG_COLS * 8) + 8 * c8;
     if (n < N) {
       const uint32_t zw = qz[(long)g * (N / 8) + n / 8];
 #pragma unroll
@@ -399,7 +404,7 @@ __global__ __launch_bounds__(256) void gptq_mfma_kernel(
   const int nk = (sp1 - sp0) * 8;
   for (int i = t; i < nk; i += 256) {
     const int k = sp0 * 8 + i;
-    goff[i] = (ACT ? g_idx[k] : k >> gsh) * (MG_COLS * 8);
+    goff[i] = (ACT ? g_idx[k] : (k >> gsh) - g_lo) * (MG_COLS * 8);
   }
   __syncthreads();
 
@@ -653,16 +658,18 @@ hipError_t run_mfma(const GptqArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const int ng = (int)(a.K / a.G);
   const int64_t nw = a.K / 8, ncg = (a.N + MG_COLS - 1) / MG_COLS;
+  const int gsh = a.G == 32 ? 5 : (a.G == 64 ? 6 : 7);
+  auto lds_of = [&](int per_sp) { return MfmaLds(table_groups(ACT, ng, per_sp, gsh), per_sp).total; };
   const int64_t s_min = std::max<int64_t>(1, (nw + 255) / 256);
   const int per_min = (int)(((nw + s_min - 1) / s_min + 1) & ~int64_t(1));
-  if (MfmaLds(ng, per_min).total > kMaxLds) return hipErrorNotSupported;
+  if (lds_of(per_min) > kMaxLds) return hipErrorNotSupported;
   int64_t resident = 0;
-  e = resident_workgroups(k, 256, (size_t)MfmaLds(ng, per_min).total, 2, &resident);
+  e = resident_workgroups(k, 256, (size_t)lds_of(per_min), 2, &resident);
   if (e != hipSuccess) return e;
   int64_t S = fill_slices(resident, ncg, nw, 64, s_min);
   const int per_sp = (int)(((nw + S - 1) / S + 1) & ~int64_t(1));
   S = (nw + per_sp - 1) / per_sp;  // no empty slice
-  const size_t lds = (size_t)MfmaLds(ng, per_sp).total;
+  const size_t lds = (size_t)lds_of(per_sp);
   const int64_t MN = a.M * a.N;
   float* part = nullptr;
   if (S > 1) {
@@ -690,7 +697,9 @@ hipError_t launch_gptq_mfma(const GptqArgs& a, hipStream_t s) {
 
 hipError_t launch_gptq_direct(const GptqArgs& a, hipStream_t s) {
   const int64_t ng = a.K / a.G;
-  if (a.M >= 8 && ng <= 96 && a.K / 8 * a.N * 4 < (int64_t(1) << 31) && a.M * a.K * 2 < (int64_t(1) << 31))
+  // (without act-order a workgroup's table holds only its slice's groups)
+  if (a.M >= 8 && (!a.g_idx || ng <= 96) && a.K / 8 * a.N * 4 < (int64_t(1) << 31) &&
+      a.M * a.K * 2 < (int64_t(1) << 31))
     return launch_gptq_mfma(a, s);
   // columns per lane: 4 when the (scale, bias) table of 256 columns fits
   // 64 KiB of LDS, else 2, else 1 (up to 96 KiB).  Without act-order the

@@ -130,11 +130,13 @@ def test_direct_shapes(M, N, K, G, act_order):
 @pytest.mark.parametrize("M,N,K,G", [
     (1, 520, 8192, 32),     # 256 groups: more than a whole table can hold
     (3, 264, 16384, 32),    # 512 groups, four columns per lane
-    (9, 136, 8192, 32),     # M >= 8 past 96 groups: the VALU kernel, passes of 4 rows
+    (9, 136, 8192, 32),     # the matrix-core kernel past 96 groups
+    (40, 264, 16384, 64),   # the same with two 32-row blocks
 ])
 def test_direct_without_act_order_many_groups(M, N, K, G):
-    # g_idx NULL: each workgroup's table holds only its K slice's groups, so
-    # K/G is not limited by LDS
+    # g_idx NULL: each workgroup's table holds only its K slice's groups (and
+    # on the matrix cores the slice's own largest scale exponent), so K/G is
+    # not limited by LDS
     dev = require_gpu()
     case = si.gptq_case(M, K, N, G, seed=(58, M, N, K, G), act_order=False, name=f"gptq_noact_M{M}_N{N}_K{K}_G{G}")
     case.g_idx = None
