@@ -22,7 +22,8 @@ with almost no launch gaps.  In the same JSON line:
   gptq_k4096_n11008
                  GPTQ layout (K=4096, N=11008, G=128, act-order) at M = 1 and
                  32: the direct kernel and the repacked affine path, eager and
-                 replayed from a HIP graph
+                 replayed from a HIP graph; and the direct kernel on a layer
+                 without act-order (g_idx passed as NULL), from a HIP graph
   gemm_m2048     prefill GEMM of an 8B decoder, M=2048: K=4096 with N = 4096,
                  1024, 14336 and K=14336 with N=4096, 4- and 8-bit, TFLOP/s
                  against the bf16 dense MFMA peak
@@ -249,7 +250,22 @@ def time_gptq(torch, qa, si, device, M, iters=200, warmup=20):
             "repacked_affine_us": round(ms_r * 1e3, 2),
             "direct_graph_us": round(ms_dg * 1e3, 2), "direct_graph_gbs": round(byts / (ms_dg * 1e-3) / 1e9, 1),
             "repacked_affine_graph_us": round(ms_rg * 1e3, 2),
-            "repacked_affine_graph_gbs": round(byts / (ms_rg * 1e-3) / 1e9, 1)}
+            "repacked_affine_graph_gbs": round(byts / (ms_rg * 1e-3) / 1e9, 1),
+            **time_gptq_no_act(torch, qa, si, device, M, iters)}
+
+
+def time_gptq_no_act(torch, qa, si, device, M, iters):
+    """The direct kernel on the same shape without act-order, g_idx NULL (each
+    workgroup's table then holds only its K slice's groups), graph-timed."""
+    c = si.gptq_case(M, si.CFG3["K"], si.CFG3["N"], si.CFG3["G"], seed=(3, 0, M), act_order=False)
+    x = torch.from_numpy(c.x.view(np.int16)).view(torch.float16).to(device)
+    qw = torch.from_numpy(c.qweight.view(np.int32)).to(device)
+    qz = torch.from_numpy(c.qzeros.view(np.int32)).to(device)
+    sc = torch.from_numpy(c.scales.view(np.int16)).view(torch.float16).to(device)
+    byts = (c.K * c.N // 2 + (c.K // c.G) * c.N * 2 + (c.K // c.G) * c.N // 2 + M * c.K * 2 + M * c.N * 2)
+    direct = lambda: qa.qmm_gptq(x, qw, qz, sc, None, c.G)
+    ms = graph_time(torch, lambda: [direct() for _ in range(REPS)], iters // REPS + 1, 2) / REPS
+    return {"no_act_direct_graph_us": round(ms * 1e3, 2), "no_act_direct_graph_gbs": round(byts / (ms * 1e-3) / 1e9, 1)}
 
 
 def time_w4a8(torch, qa, si, device, M=2048, N=4096, K=1024, iters=20, warmup=5):
