@@ -249,7 +249,7 @@ __device__ __forceinline__ float wave_sum4(const float (&v)[4]) {
   return t;
 }
 
-// R rows per wave (a multiple of 4), MT x rows per pass (1 or 4).
+// R rows per wave (a multiple of 4), MT x rows per pass (1, 2 or 4).
 template <int BITS, bool F16, int MT, int SBM, int R>
 __global__ __launch_bounds__(256) void gemv_affine_kernel(GemvBatch B) {
   static_assert(R % 4 == 0, "rows are reduced in fours");
@@ -728,8 +728,11 @@ void launch_r(const GemvBatch& b, int blocks, int sbm, hipStream_t s) {
 
 template <int BITS, bool F16>
 void launch_bits(const GemvBatch& b, int blocks, int sbm, int, hipStream_t s) {
+  // x rows per pass: 1, 2, or 4 (passes of 4 rows from M = 3 on)
   if (b.M == 1)
     launch_r<BITS, F16, 1, 4>(b, blocks, sbm, s);
+  else if (b.M == 2)
+    launch_r<BITS, F16, 2, 4>(b, blocks, sbm, s);
   else
     launch_r<BITS, F16, 4, 4>(b, blocks, sbm, s);
 }
