@@ -59,3 +59,37 @@ def test_graph_gptq_direct():
     sc = dev16(case.scales, "f16", dev)
     gi = torch.from_numpy(np.ascontiguousarray(case.g_idx)).to(dev)
     _check_replays(lambda: qa.qmm_gptq(x, qw, qz, sc, gi, case.G), case.name)
+
+
+def test_graph_gptq_matrix_core_without_act_order():
+    dev = require_gpu()
+    case = si.gptq_case(40, 8192, 264, 32, seed=(54,), act_order=False, name="graph_gptq_mfma_slices")
+    x = dev16(case.x, "f16", dev)
+    qw = torch.from_numpy(np.ascontiguousarray(case.qweight)).to(dev)
+    qz = torch.from_numpy(np.ascontiguousarray(case.qzeros)).to(dev)
+    sc = dev16(case.scales, "f16", dev)
+    _check_replays(lambda: qa.qmm_gptq(x, qw, qz, sc, None, case.G), case.name)
+
+
+def test_graph_mfma_gemv():
+    dev = require_gpu()
+    case = si.affine_case(4, 520, 2048, 64, 4, seed=(55,), name="graph_mfma_gemv")
+    x, w, s, b, kp = affine_to_device(case, dev)
+    _check_replays(lambda: qa.qmm_affine(x, w, s, b, case.G, 4), case.name)
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 1024, 1024), (128, 1024, 4096)])
+def test_graph_w4a8(M, N, K):
+    # M = 8: the fused quantize + GEMV; M = 128, K = 4096: quantize, split-K
+    # GEMM and the partial sum.  The codes, scales and y all replay exactly.
+    dev = require_gpu()
+    case = si.w4a8_case(M, N, K, seed=(56, M, N, K), name=f"graph_w4a8_M{M}")
+    x = dev16(case.x, "f16", dev)
+    w = torch.from_numpy(np.ascontiguousarray(case.w_q4).view(np.int32)).to(dev)
+    sw = dev16(case.s_w, "f16", dev)
+
+    def call():
+        y, xq, sx, _ = qa.qgemm_w4a8(x, w, sw)
+        return torch.cat([y.view(torch.int16).flatten().to(torch.int32), xq.flatten().to(torch.int32),
+                          sx.view(torch.int32)])
+    _check_replays(call, case.name)
