@@ -145,10 +145,11 @@ int qgemv_affine_grouped(const qaff_gemv_problem *problems, int32_t count, int64
  *   of scales and zeros for every group must fit in LDS).  A layer without
  *   act-order (g_idx[i] = i/G) should pass g_idx = NULL: then a workgroup's
  *   table holds only the groups of its K slice, and any K/G is taken.
- * Kernels: M < 8 on the VALU (w exact in fp32), M >= 8 with at most 96
- * groups on the matrix cores (w as two exact fp16 pieces relative to each
- * column's largest scale); fp32 partial sums over K slices, one summing
- * pass.  Accuracy as for qmm_affine.
+ * Kernels: M < 8 on the VALU (w exact in fp32); M >= 8 on the matrix cores
+ * (w as two exact fp16 pieces relative to each column's largest scale in
+ * the table) when g_idx is NULL or there are at most 96 groups, else on
+ * the VALU; fp32 partial sums over K slices, then one summing pass.
+ * Accuracy as for qmm_affine.
  */
 int qmm_gptq(const void *x, const int32_t *qweight, const int32_t *qzeros, const void *scales,
              const int32_t *g_idx, void *y, int64_t M, int64_t N, int64_t K, int32_t group_size,
