@@ -775,13 +775,20 @@ hipError_t launch_w4a8(const W4A8Args& a, hipStream_t s) {
       hipLaunchKernelGGL(w4a8_gemv_kernel<16>, grid, dim3(256), 0, s, xq, a.s_x, w, sw, y, a.acc, M, N, K);
     return hipGetLastError();
   }
-  // largest tile whose grid still gives every CU at least two workgroups
+  // largest tile whose grid still gives every CU at least two workgroups;
+  // else 64 x 128 if that gives every CU one, else 32 x 128 (half the MFMA
+  // work per fragment read, but twice the workgroups for small M)
   struct Tile { int mb, nb; };
   const Tile tiles[] = {{4, 2}, {2, 2}, {2, 1}};
-  Tile t = tiles[2];
+  auto count = [&](const Tile& c) {
+    return (long)((M + c.mb * 32 - 1) / (c.mb * 32)) * ((N + c.nb * 128 - 1) / (c.nb * 128));
+  };
+  Tile t = count(tiles[2]) >= 256 ? tiles[2] : Tile{1, 1};
   for (const Tile& c : tiles) {
-    const long tm = (M + c.mb * 32 - 1) / (c.mb * 32), tn = (N + c.nb * 128 - 1) / (c.nb * 128);
-    if (tm * tn >= 512) { t = c; break; }
+    if (count(c) >= 512) {
+      t = c;
+      break;
+    }
   }
   Params p;
   p.xq = a.x_q;
@@ -820,8 +827,10 @@ hipError_t launch_w4a8(const W4A8Args& a, hipStream_t s) {
     hipLaunchKernelGGL((w4a8_gemm_kernel<4, 2>), grid, dim3(256), 0, s, p);
   else if (t.nb == 2)
     hipLaunchKernelGGL((w4a8_gemm_kernel<2, 2>), grid, dim3(256), 0, s, p);
-  else
+  else if (t.mb == 2)
     hipLaunchKernelGGL((w4a8_gemm_kernel<2, 1>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((w4a8_gemm_kernel<1, 1>), grid, dim3(256), 0, s, p);
   e = hipGetLastError();
   if (e == hipSuccess && p.S > 1) {
     const long MN = (long)M * N;

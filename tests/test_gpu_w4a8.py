@@ -142,3 +142,10 @@ def test_small_m_paths(M, N, K):
     # and int32 partials
     case = si.w4a8_case(M, N, K, seed=(47, M, N, K), name=f"w4a8_small_M{M}_N{N}_K{K}")
     _check(case)
+
+
+def test_largest_tile():
+    # 4096 x 4096: enough 128 x 256 tiles for two per CU, the largest tile
+    # (sampled rows against the oracle)
+    case = si.w4a8_case(4096, 4096, 256, seed=(48,), name="w4a8_tile_128x256")
+    _check(case, si.sample_indices(4096, 48, seed=(48, 1)))
