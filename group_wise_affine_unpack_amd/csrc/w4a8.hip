@@ -775,17 +775,20 @@ hipError_t launch_w4a8(const W4A8Args& a, hipStream_t s) {
       hipLaunchKernelGGL(w4a8_gemv_kernel<16>, grid, dim3(256), 0, s, xq, a.s_x, w, sw, y, a.acc, M, N, K);
     return hipGetLastError();
   }
-  // largest tile whose grid still gives every CU at least two workgroups;
-  // else 64 x 128 if that gives every CU one, else 32 x 128 (half the MFMA
-  // work per fragment read, but twice the workgroups for small M)
+  // Tile: with K of 16 stages or more, the largest whose grid gives every
+  // CU a workgroup; with shorter K (a short loop, where more workgroups
+  // overlap better) 64 x 256 or 64 x 128 if it gives every CU two.  Else
+  // 32 x 128 (half the MFMA work per fragment read, the most workgroups).
   struct Tile { int mb, nb; };
-  const Tile tiles[] = {{4, 2}, {2, 2}, {2, 1}};
   auto count = [&](const Tile& c) {
     return (long)((M + c.mb * 32 - 1) / (c.mb * 32)) * ((N + c.nb * 128 - 1) / (c.nb * 128));
   };
-  Tile t = count(tiles[2]) >= 256 ? tiles[2] : Tile{1, 1};
+  const bool long_k = K >= 16 * BK;
+  const Tile tiles[] = {{4, 2}, {2, 2}, {2, 1}};
+  Tile t{1, 1};
   for (const Tile& c : tiles) {
-    if (count(c) >= 512) {
+    if (!long_k && c.mb == 4) continue;
+    if (count(c) >= (long_k ? 256 : 512)) {
       t = c;
       break;
     }
