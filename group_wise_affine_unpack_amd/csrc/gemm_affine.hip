@@ -701,21 +701,24 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
   const int M = (int)a.M, N = (int)a.N, K = (int)a.K, G = a.G;
   const int ng = K / G;
   const int Kt = (3 * ng + 15) / 16 * 16;
-  // the largest row tile whose grid still gives every CU a workgroup
+  // the largest row tile whose grid still fills three quarters of the CUs
+  // in one round: a bigger tile's efficiency is worth a few idle CUs, and a
+  // grid just past one round runs its last tiles as a second round alone
   int MB = 2;
   if (M > 64) {
     const int64_t tn = (N + BN - 1) / BN;
-    if ((int64_t)((M + 255) / 256) * tn >= 256) MB = 8;
-    else if ((int64_t)((M + 127) / 128) * tn >= 256) MB = 4;
+    if ((int64_t)((M + 255) / 256) * tn >= 192) MB = 8;
+    else if ((int64_t)((M + 127) / 128) * tn >= 192) MB = 4;
   }
   const int BM = MB * 32;
   const int Mp = (M + BM - 1) / BM * BM, Np = (N + BN - 1) / BN * BN;
-  // K splits when the tiles leave CUs idle: enough workgroups for every CU,
-  // each split at least 4 K tiles, partials within 32-bit buffer offsets
+  // K splits when the tiles leave CUs idle: as many as keep the grid in one
+  // round of workgroups, each split at least 4 K tiles, partials within
+  // 32-bit buffer offsets
   const int64_t tiles = (int64_t)(Mp / BM) * (Np / BN);
   int S = 1;
   if (tiles < 256) {
-    S = (int)std::min<int64_t>((256 + tiles - 1) / tiles, std::max(1, K / BK / 4));
+    S = (int)std::min<int64_t>(std::max<int64_t>(1, 256 / tiles), std::max(1, K / BK / 4));
     while (S > 1 && (int64_t)S * M * N * 4 >= (int64_t(1) << 31)) --S;
     const int per = (K / BK + S - 1) / S;
     S = (K / BK + per - 1) / per;  // no empty split
