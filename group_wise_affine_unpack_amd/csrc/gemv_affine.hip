@@ -29,6 +29,7 @@
 //    problems and each finds its own by a binary search over the descriptor
 //    table, which travels in the kernel arguments.  Linears that share an
 //    input (q/k/v, gate/up), or a whole set of them, then cost one launch.
+#include <algorithm>
 #include <type_traits>
 
 #include <vector>
@@ -434,12 +435,15 @@ __global__ __launch_bounds__(256) void gemv_affine_kernel(GemvBatch B) {
 //   * Accumulator layout of the 16x16 MFMA: lane (c, h) holds column c and
 //     rows 4h .. 4h+3.
 struct MfmaDesc {
-  const void* x;  // [M, K] activations
-  const void* w;  // [N, K/8] uint32
-  const void* s;  // [N, K/G] 16-bit
+  const void* x;  // [M, K] activations (row stride kfull)
+  const void* w;  // [N, K/8] uint32 (row stride kfull/8)
+  const void* s;  // [N, K/G] 16-bit (row stride kfull/G)
   const void* b;  // [N, K/G] 16-bit
-  void* y;        // [M, N]
-  int N, K, blk0, pad;
+  void* y;        // [M, N]: activation dtype, or fp32 partial sums when part != 0
+  int N, K, blk0;
+  int kfull;      // K of the whole problem: a K slice has K < kfull
+  int part;
+  int pad;
 };
 struct MfmaBatch {
   MfmaDesc d[MAXP];
@@ -504,6 +508,7 @@ __global__ __launch_bounds__(256, 2) void gemv_mfma4_kernel(MfmaBatch B) {
   }
   const MfmaDesc& D = B.d[lo];
   const int N = D.N, K = D.K, M = B.M;
+  const int KF = D.kfull, LF = KF >> 3, ngf = KF / G;  // row strides of x (values), W (words), params
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col0 = (bid - D.blk0) * 64;
   const int c = lane & 15, h = lane >> 4;
@@ -513,37 +518,37 @@ __global__ __launch_bounds__(256, 2) void gemv_mfma4_kernel(MfmaBatch B) {
   // Packed words: rows 16i + 4*wave + lane/16 (i < 4), piece lane % 16 of
   // the stage's 256 bytes, stored to LDS slot piece ^ (row % 16).  Rows past
   // N are out of range; a piece past the row end reads the next row.
-  const __amdgpu_buffer_rsrc_t rw =
-      make_rsrc(static_cast<const uint32_t*>(D.w) + (long)col0 * L, (uint32_t)(ncols * L * 4));
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(static_cast<const uint32_t*>(D.w) + (long)col0 * LF,
+                                                (uint32_t)(((ncols - 1) * LF + L) * 4));
   const int wrow = 4 * wave + (lane >> 4);
-  const uint32_t wv = (uint32_t)(wrow * L * 4 + (lane & 15) * 16);
+  const uint32_t wv = (uint32_t)(wrow * LF * 4 + (lane & 15) * 16);
   const int wdst = wrow * 256 + (((lane & 15) ^ (wrow & 15)) << 4);  // + i*16*256
   // Scale (waves 0, 1) or bias (waves 2, 3) chunks: rows 32*(wave&1) + 8i +
   // lane/8 (i < 4), piece lane % 8 of the row's 128 bytes; every wave-level
   // load covers 8 whole rows' chunks.
-  const __amdgpu_buffer_rsrc_t rp = make_rsrc(
-      static_cast<const uint16_t*>((wave >> 1) ? D.b : D.s) + (long)col0 * ng, (uint32_t)(ncols * ng * 2));
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(static_cast<const uint16_t*>((wave >> 1) ? D.b : D.s) + (long)col0 * ngf,
+                                                (uint32_t)(((ncols - 1) * ngf + ng) * 2));
   const int prow = 32 * (wave & 1) + (lane >> 3);
-  const uint32_t pv = (uint32_t)(prow * ng * 2 + (lane & 7) * 16);
+  const uint32_t pv = (uint32_t)(prow * ngf * 2 + (lane & 7) * 16);
   int pdst[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) pdst[i] = (wave >> 1) * 64 * 128 + par_swz(prow + 8 * i, lane & 7);
   const int nchunk = (nst + CS - 1) / CS;
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(D.x, (uint32_t)(M * K * 2));
-  const uint32_t xv = c < M ? (uint32_t)(c * K * 2) : OOB;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(D.x, (uint32_t)(((M - 1) * KF + K) * 2));
+  const uint32_t xv = c < M ? (uint32_t)(c * KF * 2) : OOB;
 
   // loads of stage tw's packed words; a stage past the end loads nothing
   // (offsets out of range)
   auto issue_w = [&](int tw, W& wr) __attribute__((always_inline)) {
     const uint32_t wo = (tw < nst ? wv : OOB) + (uint32_t)tw * 256u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wr[i] = ld128<NT>(rw, wo + (uint32_t)(16 * i * L * 4));  // streamed once: non-temporal
+    for (int i = 0; i < 4; ++i) wr[i] = ld128<NT>(rw, wo + (uint32_t)(16 * i * LF * 4));  // streamed once: non-temporal
   };
   // loads of parameter chunk ch
   auto issue_p = [&](int ch, u32x4_t (&pr)[4]) __attribute__((always_inline)) {
     const uint32_t po = (ch < nchunk ? pv : OOB) + (uint32_t)ch * 128u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = ld128(rp, po + (uint32_t)(8 * i * ng * 2));
+    for (int i = 0; i < 4; ++i) pr[i] = ld128(rp, po + (uint32_t)(8 * i * ngf * 2));
   };
   auto put_p = [&](const u32x4_t (&pr)[4]) __attribute__((always_inline)) {
 #pragma unroll
@@ -702,8 +707,24 @@ __global__ __launch_bounds__(256, 2) void gemv_mfma4_kernel(MfmaBatch B) {
     float v = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) v += red[((q * NB + wave) * 4 + i) * 64 + lane];
-    if (row < M) yo[(long)row * N + col0 + col] = f32_to_act_bits(v, F16);
+    if (row < M) {
+      if (D.part)
+        static_cast<float*>(D.y)[(long)row * N + col0 + col] = v;
+      else
+        yo[(long)row * N + col0 + col] = f32_to_act_bits(v, F16);
+    }
   }
+}
+
+// y = the sum of S fp32 partial planes [S][M*N] in slice order, rounded to
+// the activation dtype
+__global__ __launch_bounds__(256) void mfma_split_sum_kernel(const float* __restrict__ part, uint16_t* __restrict__ y,
+                                                             long MN, int S, bool f16) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= MN) return;
+  float v = 0.f;
+  for (int s = 0; s < S; ++s) v += part[(long)s * MN + i];
+  y[i] = f32_to_act_bits(v, f16);
 }
 
 template <bool F16>
@@ -757,7 +778,9 @@ __global__ __launch_bounds__(256) void permute_x_kernel(const uint16_t* __restri
       u32x4_t{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
 }
 
-hipError_t launch_gemv_core(const AffineArgs* probs, int count, hipStream_t s);
+// ws_used: bytes at the start of the stream's workspace that the caller
+// still needs (permuted copies of x)
+hipError_t launch_gemv_core(const AffineArgs* probs, int count, hipStream_t s, size_t ws_used);
 
 }  // namespace
 
@@ -768,7 +791,7 @@ hipError_t launch_gemv_grouped(const AffineArgs* probs, int count, hipStream_t s
   if (count <= 0) return hipSuccess;
   bool any = false;
   for (int i = 0; i < count; ++i) any |= probs[i].k_perm != nullptr;
-  if (!any) return launch_gemv_core(probs, count, s);
+  if (!any) return launch_gemv_core(probs, count, s, 0);
   std::vector<AffineArgs> q(probs, probs + count);
   std::vector<int> src(count, -1);  // problem whose permuted x this one shares
   size_t total = 0;
@@ -799,13 +822,13 @@ hipError_t launch_gemv_grouped(const AffineArgs* probs, int count, hipStream_t s
     }
     q[i].k_perm = nullptr;
   }
-  if (e == hipSuccess) e = launch_gemv_core(q.data(), count, s);
+  if (e == hipSuccess) e = launch_gemv_core(q.data(), count, s, total);
   return e;
 }
 
 namespace {
 
-hipError_t launch_gemv_core(const AffineArgs* probs, int count, hipStream_t s) {
+hipError_t launch_gemv_core(const AffineArgs* probs, int count, hipStream_t s, size_t ws_used) {
   if (count <= 0) return hipSuccess;
   const AffineArgs& a0 = probs[0];
   const int M = (int)a0.M, bits = a0.bits;
@@ -859,22 +882,93 @@ hipError_t launch_gemv_core(const AffineArgs* probs, int count, hipStream_t s) {
       mfma = d.K % 512 == 0 && (d.K / a0.G) % 8 == 0 && (int64_t)d.K * 32 < (int64_t(1) << 31) &&
              (((uintptr_t)d.w | (uintptr_t)d.s | (uintptr_t)d.b) & 15) == 0;
     }
+    // up to 4 x rows, a grid of fewer than 128 64-column workgroups is
+    // latency-bound, and the dot2 kernel, with a workgroup per 16 rows or
+    // fewer, is faster (M = 4, N = K = 4096: 5.7 against 9.5 us)
+    if (mfma && M <= 4) {
+      int64_t mb = 0;
+      for (int i = 0; i < b.count; ++i) mb += (b.d[i].N + 63) / 64;
+      if (mb < 128) mfma = false;
+    }
     if (mfma) {
-      MfmaBatch bm{};
-      bm.count = b.count;
-      bm.M = M;
       int64_t mblocks = 0;
+      for (int i = 0; i < b.count; ++i) mblocks += (b.d[i].N + 63) / 64;
+      // K split when the grid is narrow (64 workgroups or fewer: a single
+      // call with N <= 4096): slices of whole 1024-code pieces that keep the
+      // scale rows 16-byte aligned (8 groups), as many as keep the grid
+      // within one round of 512 workgroups (two per CU) and the descriptors
+      // within one launch; each slice writes fp32 partials, and a second
+      // kernel adds them.  From 128 workgroups on, the partials and the
+      // second kernel cost more than they save (M = 4, N = 11008, K = 4096:
+      // 12.6 against 10.2 us); at 32, M = 16, N = 2048, K = 8192 goes from
+      // 16.3 to 10.4 us.
+      int S = 1;
+      const int q = std::max(1024, 8 * (int)a0.G);
+      if (mblocks <= 64) {
+        int kmin = 1 << 30;
+        for (int i = 0; i < b.count; ++i) kmin = std::min(kmin, b.d[i].K / q);
+        S = (int)std::max<int64_t>(1, std::min<int64_t>({512 / mblocks, (int64_t)kmin, (int64_t)(MAXP / b.count)}));
+      }
+      MfmaBatch bm{};
+      bm.M = M;
+      int nd = 0;
+      mblocks = 0;
+      float* part = nullptr;
+      std::vector<int> slices(b.count, 1);
+      if (S > 1) {
+        size_t bytes = 0;
+        for (int i = 0; i < b.count; ++i) {
+          const int per = (b.d[i].K / S + q - 1) / q * q;
+          slices[i] = (b.d[i].K + per - 1) / per;  // no empty slice
+          bytes += (size_t)slices[i] * M * b.d[i].N * 4;
+        }
+        const size_t base = (ws_used + 255) & ~size_t(255);
+        char* ws = nullptr;
+        hipError_t e = stream_workspace(s, base + bytes, (void**)&ws);
+        if (e != hipSuccess) return e;
+        part = reinterpret_cast<float*>(ws + base);
+      }
+      std::vector<float*> plane(b.count, nullptr);
+      float* next = part;
       for (int i = 0; i < b.count; ++i) {
         const GemvDesc& d = b.d[i];
-        MfmaDesc& e = bm.d[i];
-        e.x = d.x; e.w = d.w; e.s = d.s; e.b = d.b; e.y = d.y;
-        e.N = d.N; e.K = d.K; e.blk0 = (int)mblocks;
-        mblocks += (d.N + 63) / 64;
+        const int per = slices[i] > 1 ? (d.K / S + q - 1) / q * q : d.K;
+        plane[i] = next;
+        for (int j = 0; j < slices[i]; ++j) {
+          MfmaDesc& e = bm.d[nd++];
+          const int k0 = j * per;
+          e.x = static_cast<const uint16_t*>(d.x) + k0;
+          e.w = static_cast<const uint32_t*>(d.w) + k0 / 8;
+          e.s = static_cast<const uint16_t*>(d.s) + k0 / a0.G;
+          e.b = static_cast<const uint16_t*>(d.b) + k0 / a0.G;
+          e.N = d.N;
+          e.K = std::min(per, d.K - k0);
+          e.kfull = d.K;
+          e.blk0 = (int)mblocks;
+          if (slices[i] > 1) {
+            e.y = next + (size_t)j * M * d.N;
+            e.part = 1;
+          } else {
+            e.y = d.y;
+            e.part = 0;
+          }
+          mblocks += (d.N + 63) / 64;
+        }
+        if (slices[i] > 1) next += (size_t)slices[i] * M * d.N;
       }
+      bm.count = nd;
       if (f16) launch_mfma4<true>((int)a0.G, dim3((unsigned)mblocks), s, bm);
       else launch_mfma4<false>((int)a0.G, dim3((unsigned)mblocks), s, bm);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
+      for (int i = 0; i < b.count; ++i) {
+        if (slices[i] == 1) continue;
+        const long MN = (long)M * b.d[i].N;
+        hipLaunchKernelGGL(mfma_split_sum_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, s, plane[i],
+                           static_cast<uint16_t*>(b.d[i].y), MN, slices[i], f16);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
       continue;
     }
     switch (bits) {

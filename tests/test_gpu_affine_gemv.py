@@ -202,10 +202,21 @@ def test_grouped_mixed_k_m1():
 @pytest.mark.parametrize("M", [2, 9, 16])
 def test_4bit_several_rows_matrix_core_path(K, G, M, act):
     # 4-bit codes with 2..16 x rows and K a multiple of 512 take the MFMA
-    # kernel: 1, 3, 5 and 16 stages of 512 codes (5 leaves the last round of
-    # three with an empty stage), ragged N leaves a partly filled 64-column
-    # tile
+    # kernel (at M <= 4 only with 128 or more 64-column workgroups: M = 2
+    # here runs the dot2 kernel): 1, 3, 5 and 16 stages of 512 codes (5
+    # leaves the last round of three with an empty stage), ragged N leaves a
+    # partly filled 64-column tile
     case = si.affine_case(M, 333, K, G, 4, seed=(29, K, G, M), act_dtype=act, name=f"mfma_M{M}_K{K}_G{G}_{act}")
+    y = _run(case)
+    assert_float_bar(y, oracle.qmm_affine_case(case), case.name)
+
+
+@pytest.mark.parametrize("M,N,K,G,act", [(2, 8200, 512, 64, "bf16"), (3, 8250, 1536, 32, "f16"),
+                                        (4, 8192, 2560, 128, "bf16"), (4, 8130, 512, 64, "f16")])
+def test_4bit_few_rows_matrix_core_path_wide(M, N, K, G, act):
+    # M <= 4 takes the MFMA kernel once N gives 128 or more 64-column
+    # workgroups: exactly 128 (N = 8130, the last one ragged) and a few more
+    case = si.affine_case(M, N, K, G, 4, seed=(37, M, N, K), act_dtype=act, name=f"mfma_wide_M{M}_N{N}_K{K}")
     y = _run(case)
     assert_float_bar(y, oracle.qmm_affine_case(case), case.name)
 
@@ -243,8 +254,9 @@ def test_several_rows_k_not_multiple_of_512(K):
 @pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("M", [1, 2, 9, 16])
 def test_k_perm_every_width_and_kernel(bits, M):
-    # the permuted copy of x feeds the scalar kernel (M = 1, or 2- and 8-bit
-    # codes) and the matrix-core kernel (4-bit, 2 <= M <= 16, K % 512 == 0)
+    # the permuted copy of x feeds the scalar kernel (M = 1, 2- and 8-bit
+    # codes, and M = 2 at this N) and the matrix-core kernel (4-bit, M = 9
+    # and 16, K % 512 == 0)
     case = si.affine_case(M, 200, 2048, 64, bits, seed=(34, bits, M), name=f"kperm_b{bits}_M{M}")
     case.k_perm = np.random.default_rng(35).permutation(case.K).astype(np.int32)
     y = _run(case)

@@ -72,8 +72,10 @@ def test_graph_gptq_matrix_core_without_act_order():
 
 
 def test_graph_mfma_gemv():
+    # M = 8 on the MFMA GEMV with K split in two (nine 64-column workgroups
+    # per slice) and the partial sum
     dev = require_gpu()
-    case = si.affine_case(4, 520, 2048, 64, 4, seed=(55,), name="graph_mfma_gemv")
+    case = si.affine_case(8, 520, 2048, 64, 4, seed=(55,), name="graph_mfma_gemv")
     x, w, s, b, kp = affine_to_device(case, dev)
     _check_replays(lambda: qa.qmm_affine(x, w, s, b, case.G, 4), case.name)
 
