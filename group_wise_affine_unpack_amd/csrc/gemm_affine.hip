@@ -821,21 +821,43 @@ hipError_t run_bits(const AffineArgs& a, hipStream_t s) {
 
 }  // namespace
 
+namespace {
+
+// The GEMV on slices of 16 x rows, each slice reading W once more.
+hipError_t rows_via_gemv(const AffineArgs& a, hipStream_t s) {
+  const size_t esz = 2;  // bf16 / f16 activations and outputs
+  for (int64_t m0 = 0; m0 < a.M; m0 += 16) {
+    AffineArgs b = a;
+    b.M = a.M - m0 < 16 ? a.M - m0 : 16;
+    b.x = static_cast<const char*>(a.x) + m0 * a.K * esz;
+    b.y = static_cast<char*>(a.y) + m0 * a.N * esz;
+    const hipError_t e = launch_gemv_affine(b, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Whether a 16-row slice takes the MFMA GEMV (the conditions it checks:
+// 4-bit codes, scales and biases in the activation dtype, whole 512-code
+// stages, scale rows a multiple of 16 bytes, 16-byte aligned tensors).
+bool gemv_mfma_eligible(const AffineArgs& a) {
+  return a.bits == 4 && a.s_dt == a.act_dt && a.b_dt == a.act_dt && (a.G == 32 || a.G == 64 || a.G == 128) &&
+         a.K % 512 == 0 && (a.K / a.G) % 8 == 0 && a.K * 32 < (int64_t(1) << 31) &&
+         (((uintptr_t)a.w | (uintptr_t)a.scales | (uintptr_t)a.biases) & 15) == 0;
+}
+
+}  // namespace
+
 hipError_t launch_gemm_affine(const AffineArgs& a, hipStream_t s) {
   // whole 64-code K tiles only; otherwise the GEMV kernel runs on slices of
-  // 16 x rows (each slice reads W once more: a rare shape, not a fast path)
-  if (a.K % BK != 0) {
-    const size_t esz = 2;  // bf16 / f16 activations and outputs
-    for (int64_t m0 = 0; m0 < a.M; m0 += 16) {
-      AffineArgs b = a;
-      b.M = a.M - m0 < 16 ? a.M - m0 : 16;
-      b.x = static_cast<const char*>(a.x) + m0 * a.K * esz;
-      b.y = static_cast<char*>(a.y) + m0 * a.N * esz;
-      const hipError_t e = launch_gemv_affine(b, s);
-      if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
-  }
+  // 16 x rows (a rare shape, not a fast path)
+  if (a.K % BK != 0) return rows_via_gemv(a, s);
+  // Up to 48 x rows, 16-row slices on the 4-bit MFMA GEMV (W read once per
+  // slice, the later times mostly from the last-level cache) beat this
+  // kernel, whose 64-row tiles are a quarter or more padding there: M = 32,
+  // N = 11008, K = 4096 takes 21 us instead of 33, M = 17 17 instead of 32,
+  // M = 48 31 instead of 34; at M = 64 the GEMM is ahead (35 against 42).
+  if (a.M <= 48 && gemv_mfma_eligible(a)) return rows_via_gemv(a, s);
   switch (a.bits) {
     case 2: return run_bits<2>(a, s);
     case 4: return run_bits<4>(a, s);

@@ -43,8 +43,11 @@ def test_small_full_compare(bits, G):
     assert_float_bar(host_f64(y), oracle.qmm_affine_case(case), case.name)
 
 
-@pytest.mark.parametrize("M", [17, 32, 64, 65, 255, 257])
+@pytest.mark.parametrize("M", [17, 32, 48, 49, 64, 65, 255, 257])
 def test_m_boundaries_and_tiles(M):
+    # M <= 48 (4-bit, MFMA-eligible) runs as 16-row slices on the MFMA GEMV
+    # (M = 17: a slice of 16 and one of 1); from 49 the GEMM's 64-, 128- and
+    # 256-row tiles, each M at or just past a tile edge
     case = si.affine_case(M, 264, 2048, 64, 4, seed=(21, M), name=f"gemm_M{M}")
     y = _run(case)
     assert_float_bar(host_f64(y), oracle.qmm_affine_case(case), case.name)
@@ -63,7 +66,7 @@ def test_scale_bias_dtypes(sdt, bdt, bits):
 
 @pytest.mark.parametrize("act", ["bf16", "f16"])
 def test_k_perm_and_activation_dtype(act):
-    case = si.affine_case(48, 256, 4096, 128, 4, seed=(23,), act_dtype=act, name=f"gemm_kperm_{act}")
+    case = si.affine_case(72, 256, 4096, 128, 4, seed=(23,), act_dtype=act, name=f"gemm_kperm_{act}")
     case.k_perm = np.random.default_rng(24).permutation(case.K).astype(np.int32)
     y = _run(case)
     assert_float_bar(host_f64(y), oracle.qmm_affine_case(case), case.name)

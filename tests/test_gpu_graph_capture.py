@@ -45,7 +45,7 @@ def test_graph_gemv_with_k_perm():
 
 def test_graph_gemm_split_k():
     dev = require_gpu()
-    case = si.affine_case(48, 520, 4096, 64, 4, seed=(52,), name="graph_gemm_split")
+    case = si.affine_case(56, 520, 4096, 64, 4, seed=(52,), name="graph_gemm_split")
     x, w, s, b, kp = affine_to_device(case, dev)
     _check_replays(lambda: qa.qmm_affine(x, w, s, b, case.G, 4), case.name)
 
