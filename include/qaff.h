@@ -79,11 +79,16 @@ typedef enum {
  *   K % G == 0 and K*bits % 128 == 0 (whole 16-byte loads per row).
  *
  * Dispatch: M <= 16 runs a memory-bound GEMV kernel (exact fp32 arithmetic
- * on the integer codes; 4-bit codes with 2..16 x rows on the matrix cores),
- * after one permuting pass over x when k_perm is given; larger M runs a
- * pre-pass plus the MFMA GEMM kernel, with K split over workgroups (and a
- * summing pass) when the output tiles would leave CUs idle.  Accuracy: max|y-ref|/(|ref|+1) <= 1e-2 and relative
- * Frobenius error <= 5e-3 against an fp64 evaluation, for finite inputs.
+ * on the integer codes; 4-bit codes with 2..16 x rows on the matrix cores,
+ * except a narrow call with M <= 4; K split over workgroups, plus a summing
+ * pass, when a call gives the matrix-core kernel 64 workgroups or fewer),
+ * after one permuting pass over x when k_perm is given.  17 <= M <= 48 with
+ * 4-bit codes and scales and biases in the activation dtype runs as 16-row
+ * slices of that GEMV.  Otherwise larger M runs a pre-pass plus the MFMA
+ * GEMM kernel, with K split over workgroups (and a summing pass) when the
+ * output tiles would leave CUs idle.  Accuracy: max|y-ref|/(|ref|+1) <= 1e-2
+ * and relative Frobenius error <= 5e-3 against an fp64 evaluation, for
+ * finite inputs.
  */
 int qmm_affine(const void *x, const uint32_t *w_packed, const void *scales, const void *biases,
                const int32_t *k_perm, void *y, int64_t M, int64_t N, int64_t K,
