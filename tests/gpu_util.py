@@ -8,7 +8,7 @@ TORCH_DT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
 
 def require_gpu():
-    # On the GPU machine this must hold; a missing GPU is a failure, not a skip.
+    # GPU tests need a visible GPU: a missing one is a failure, not a skip.
     assert torch.cuda.is_available(), "GPU test run without a visible GPU"
     return torch.device("cuda:0")
 
