@@ -72,6 +72,16 @@ def test_k_perm_and_activation_dtype(act):
     assert_float_bar(host_f64(y), oracle.qmm_affine_case(case), case.name)
 
 
+@pytest.mark.parametrize("M,act", [(40, "f16"), (24, "bf16")])
+def test_row_slices_with_k_perm(M, act):
+    # M <= 48 on 16-row slices of the MFMA GEMV: each slice permutes its own
+    # rows of x, and N = 256 gives a narrow grid, so K is split as well
+    case = si.affine_case(M, 256, 4096, 128, 4, seed=(24, M), act_dtype=act, name=f"slices_kperm_M{M}_{act}")
+    case.k_perm = np.random.default_rng(24).permutation(case.K).astype(np.int32)
+    y = _run(case)
+    assert_float_bar(host_f64(y), oracle.qmm_affine_case(case), case.name)
+
+
 def test_wide_dynamic_range_rows():
     # rows of x at very different magnitudes (the per-row power-of-two scaling
     # keeps fp16 operands in range), including an all-zero row
