@@ -18,7 +18,7 @@ from typing import Optional
 import torch
 
 __all__ = ["QaffError", "qmm_affine", "qgemv_affine", "qgemv_affine_grouped", "GroupedGemv", "qmm_gptq", "qgemm_w4a8", "gptq_to_affine_repack",
-           "quantize_pack_affine", "library_path", "lib", "STATUS", "DTYPE"]
+           "quantize_pack_affine", "release_workspaces", "library_path", "lib", "STATUS", "DTYPE"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libqaff.so")
@@ -73,6 +73,8 @@ def lib():
         L.qaff_last_error.restype = C.c_char_p
         L.qaff_last_error.argtypes = []
         L.qaff_version.restype = C.c_int
+        L.qaff_release_workspaces.restype = C.c_int
+        L.qaff_release_workspaces.argtypes = [C.POINTER(C.c_uint64)]
         _lib = L
     return _lib
 
@@ -227,6 +229,16 @@ def gptq_to_affine_repack(qweight: torch.Tensor, qzeros: torch.Tensor, scales: t
                                      _ptr(b), DTYPE[bias_dtype], _ptr(kp), K, N, group_size, _stream(dev))
     _check(st, "gptq_to_affine_repack")
     return w, s, b, kp
+
+
+def release_workspaces() -> int:
+    """Free the scratch the library holds (qaff_release_workspaces).  Call it
+    only with no library work pending on any stream and no captured graph
+    that will replay a library call.  Returns the bytes of the per-stream
+    buffers that were cached."""
+    freed = C.c_uint64(0)
+    _check(lib().qaff_release_workspaces(C.byref(freed)), "qaff_release_workspaces")
+    return int(freed.value)
 
 
 def quantize_pack_affine(w: torch.Tensor, group_size: int, bits: int, sb_dtype=torch.bfloat16):

@@ -93,6 +93,9 @@ struct AffineArgs {
 // scratch of `bytes` for work on stream s: the stream's cached buffer (see
 // workspace.hip); valid until the next call on the same stream
 hipError_t stream_workspace(hipStream_t s, size_t bytes, void** out);
+// frees every cached and grown-out workspace buffer of every device;
+// *freed = bytes of the cached (current) buffers
+hipError_t release_workspaces(size_t* freed);
 
 // workgroups of `kernel` (`block` threads, `lds` bytes of dynamic LDS) that
 // the current device holds at once, counting at most max_per_cu per CU:

@@ -695,8 +695,7 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 template <int BITS, int PS>
 hipError_t run(const AffineArgs& a, hipStream_t s) {
   // buffer resources address W, the scale pieces and one x tile with 32-bit offsets
-  if (a.N * a.K * BITS / 8 >= (int64_t(1) << 31) || a.K * 2 * 256 >= (int64_t(1) << 31) ||
-      a.M * a.N * 2 >= (int64_t(1) << 31))
+  if (a.N * a.K * BITS / 8 >= (int64_t(1) << 31) || a.K * 2 * 256 >= (int64_t(1) << 31))
     return hipErrorNotSupported;
   const int M = (int)a.M, N = (int)a.N, K = (int)a.K, G = a.G;
   const int ng = K / G;
@@ -712,6 +711,11 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
   }
   const int BM = MB * 32;
   const int Mp = (M + BM - 1) / BM * BM, Np = (N + BN - 1) / BN * BN;
+  // The epilogue stores padded rows m in [M, Mp) too, relying on their
+  // offsets (m*N + n)*2 (y) or *4 (fp32 partials) landing past the buffer's
+  // range; they must not wrap around 2^32, so every padded offset stays
+  // below 2^31.
+  if ((int64_t)Mp * N * 2 >= (int64_t(1) << 31)) return hipErrorNotSupported;
   // K splits when the tiles leave CUs idle: as many as keep the grid in one
   // round of workgroups, each split at least 4 K tiles, partials within
   // 32-bit buffer offsets
@@ -719,7 +723,7 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
   int S = 1;
   if (tiles < 256) {
     S = (int)std::min<int64_t>(std::max<int64_t>(1, 256 / tiles), std::max(1, K / BK / 4));
-    while (S > 1 && (int64_t)S * M * N * 4 >= (int64_t(1) << 31)) --S;
+    if ((int64_t)Mp * N * 4 >= (int64_t(1) << 31)) S = 1;  // partial offsets as above
     const int per = (K / BK + S - 1) / S;
     S = (K / BK + per - 1) / per;  // no empty split
   }

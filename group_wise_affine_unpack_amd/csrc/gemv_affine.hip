@@ -782,6 +782,71 @@ __global__ __launch_bounds__(256) void permute_x_kernel(const uint16_t* __restri
 // still needs (permuted copies of x)
 hipError_t launch_gemv_core(const AffineArgs* probs, int count, hipStream_t s, size_t ws_used);
 
+// Rows that are not whole 16-byte chunks (K*BITS % 128 != 0; with G >= 32
+// only 2-bit codes with K an odd multiple of 32): one wave per row of W,
+// lanes over the row's words, 4-byte loads, k_perm read per code.  A plain
+// path for a rare shape, exact in the same way as the main kernel: per word
+// (never across a group, since P <= 16 <= G) s * sum(q*x) + b * sum(x).
+template <int BITS>
+__global__ __launch_bounds__(256) void gemv_tail_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ w,
+                                                        const void* __restrict__ sc, const void* __restrict__ bi,
+                                                        const int32_t* __restrict__ kp, uint16_t* __restrict__ y,
+                                                        int M, int N, int K, int G, int sdt, int bdt, bool f16) {
+  constexpr int P = 32 / BITS;
+  constexpr uint32_t MASK = (1u << BITS) - 1u;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (n >= N) return;  // a whole wave leaves together
+  const int nw = K / P, ng = K / G;
+  const uint32_t* wr = w + (long)n * nw;
+  float acc[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) acc[m] = 0.f;
+  for (int j = lane; j < nw; j += 64) {
+    const uint32_t word = wr[j];
+    const int g = j * P / G;
+    const float s = load_as_f32(sc, (long)n * ng + g, sdt);
+    const float b = load_as_f32(bi, (long)n * ng + g, bdt);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      if (m >= M) continue;  // (uniform)
+      float dq = 0.f, sx = 0.f;
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        const int k = j * P + i;
+        const uint32_t h = x[(long)m * K + (kp ? kp[k] : k)];
+        const float xv = f16 ? f16_bits_to_f32(h) : bf16_bits_to_f32(h);
+        dq = fmaf((float)((word >> (BITS * i)) & MASK), xv, dq);
+        sx += xv;
+      }
+      acc[m] = fmaf(s, dq, fmaf(b, sx, acc[m]));
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    if (m >= M) continue;  // (uniform)
+    const float v = wave_sum(acc[m]);
+    if (lane == 0) y[(long)m * N + n] = f32_to_act_bits(v, f16);
+  }
+}
+
+hipError_t launch_gemv_tail(const AffineArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((a.N + 3) / 4));
+  const bool f16 = a.act_dt == F16;
+  auto* x = static_cast<const uint16_t*>(a.x);
+  auto* y = static_cast<uint16_t*>(a.y);
+  const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
+  if (a.bits == 2)
+    hipLaunchKernelGGL(gemv_tail_kernel<2>, grid, dim3(256), 0, s, x, a.w, a.scales, a.biases, a.k_perm, y, M, N, K,
+                       a.G, a.s_dt, a.b_dt, f16);
+  else if (a.bits == 4)
+    hipLaunchKernelGGL(gemv_tail_kernel<4>, grid, dim3(256), 0, s, x, a.w, a.scales, a.biases, a.k_perm, y, M, N, K,
+                       a.G, a.s_dt, a.b_dt, f16);
+  else
+    hipLaunchKernelGGL(gemv_tail_kernel<8>, grid, dim3(256), 0, s, x, a.w, a.scales, a.biases, a.k_perm, y, M, N, K,
+                       a.G, a.s_dt, a.b_dt, f16);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // Problems with a column permutation run on a permuted copy of x, written
@@ -789,6 +854,22 @@ hipError_t launch_gemv_core(const AffineArgs* probs, int count, hipStream_t s, s
 // workspace; then every problem takes the unpermuted kernels.
 hipError_t launch_gemv_grouped(const AffineArgs* probs, int count, hipStream_t s) {
   if (count <= 0) return hipSuccess;
+  // rows that are not whole 16-byte chunks take the plain tail kernel, one
+  // launch per problem; the rest go on together
+  bool ragged = false;
+  for (int i = 0; i < count; ++i) ragged |= (probs[i].K * probs[i].bits) % 128 != 0;
+  if (ragged) {
+    std::vector<AffineArgs> rest;
+    for (int i = 0; i < count; ++i) {
+      if ((probs[i].K * probs[i].bits) % 128 != 0) {
+        const hipError_t e = launch_gemv_tail(probs[i], s);
+        if (e != hipSuccess) return e;
+      } else {
+        rest.push_back(probs[i]);
+      }
+    }
+    return rest.empty() ? hipSuccess : launch_gemv_grouped(rest.data(), (int)rest.size(), s);
+  }
   bool any = false;
   for (int i = 0; i < count; ++i) any |= probs[i].k_perm != nullptr;
   if (!any) return launch_gemv_core(probs, count, s, 0);

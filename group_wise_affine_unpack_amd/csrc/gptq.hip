@@ -78,6 +78,17 @@ __host__ __device__ inline int table_groups(bool act, int ng, int per_sp, int gs
   return act ? ng : min(ng, ((per_sp * 8 + (1 << gsh) - 1) >> gsh) + 1);  // G = 2^gsh
 }
 
+// Where the direct kernel finds a code's (scale, bias) pair:
+//   SLICE:  LDS table of the groups the workgroup's K slice touches (g_idx NULL)
+//   LDS:    LDS table of every group (act-order, the table fits in LDS)
+//   GLOBAL: act-order with more groups than the LDS holds: a table
+//           [K/G][N] of fp32 (scale, bias) pairs, written to device memory by
+//           gptq_table_kernel before the launch and read through L2
+enum TabMode : int { SLICE = 0, LDS = 1, GLOBAL = 2 };
+__host__ __device__ inline int direct_table_groups(int mode, int ng, int per_sp, int gsh) {
+  return mode == GLOBAL ? 0 : table_groups(mode == LDS, ng, per_sp, gsh);
+}
+
 struct DirectLds {
   int tab, goff, xs, red, total;
   __host__ __device__ DirectLds(int ng, int cpl, int mt, int per_sp) {
@@ -104,11 +115,12 @@ struct DirectLds {
 // The waves meet in LDS; each slice writes fp32 partials [S][M][N], and a
 // second kernel adds the S partials into y.  Rows of x go MT at a time; the
 // table serves every pass.
-template <int CPL, int MT, bool ACT>
+template <int CPL, int MT, int MODE>
 __global__ __launch_bounds__(64 * direct_waves<MT>()) void gptq_direct_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint32_t* __restrict__ qz,
-    const uint16_t* __restrict__ sc, const int32_t* __restrict__ g_idx, float* __restrict__ part, int M, int N,
-    int K, int gsh, int S) {
+    const uint16_t* __restrict__ sc, const int32_t* __restrict__ g_idx, const float2* __restrict__ gtab,
+    float* __restrict__ part, int M, int N, int K, int gsh, int S) {
+  constexpr bool ACT = MODE != SLICE;
   constexpr int GW = direct_waves<MT>(), KB = WROWS / GW;
   using T = GTab<CPL>;
   using W = typename WordsT<CPL>::T;
@@ -129,8 +141,10 @@ __global__ __launch_bounds__(64 * direct_waves<MT>()) void gptq_direct_kernel(
   const int kw0 = min(sp1, sp0 + wave * per_w), kw1 = min(sp1, kw0 + per_w);
   // the table: all ng groups with act-order, else the slice's groups from g_lo
   const int g_lo = ACT ? 0 : (sp0 * 8) >> gsh;
-  const int ngt = ACT ? ng : (sp1 > sp0 ? (((sp1 * 8 - 1) >> gsh) - g_lo + 1) : 0);
-  const DirectLds L(table_groups(ACT, ng, per_sp, gsh), CPL, MT, per_sp);
+  const int ngt = MODE == GLOBAL ? 0 : (ACT ? ng : (sp1 > sp0 ? (((sp1 * 8 - 1) >> gsh) - g_lo + 1) : 0));
+  const DirectLds L(direct_table_groups(MODE, ng, per_sp, gsh), CPL, MT, per_sp);
+  // GLOBAL: the table rows of this workgroup's columns (N*8 bytes per group)
+  const __amdgpu_buffer_rsrc_t rt = make_rsrc(gtab, MODE == GLOBAL ? (uint32_t)ng * (uint32_t)N * 8u : 0u);
   int* goff = reinterpret_cast<int*>(lds + L.goff);
   float* xs = reinterpret_cast<float*>(lds + L.xs);
   float* red = reinterpret_cast<float*>(lds + L.red);  // [GW][MT][COLS]
@@ -218,11 +232,15 @@ __global__ __launch_bounds__(64 * direct_waves<MT>()) void gptq_direct_kernel(
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int i = t + u * 64 * GW;
-    if (i < nk) goff[i] = gv[u] << GB_SHIFT;  // the code's group row in the table
+    // the code's group row in the table (GLOBAL: byte offset of row g)
+    if (i < nk) goff[i] = MODE == GLOBAL ? gv[u] * (N * 8) : gv[u] << GB_SHIFT;
   }
   store_x(xp);
 
-  const int lane_off = L.tab + T::off(lane * CPL);  // this lane's first entry in a group row
+  // this lane's first entry in a group row (GLOBAL: columns n0 + CPL*lane
+  // onwards, or out of range past N)
+  const int lane_off = MODE == GLOBAL ? (n0 + lane * CPL < N ? (n0 + lane * CPL) * 8 : (int)OOB)
+                                      : L.tab + T::off(lane * CPL);
   // the nibble mask, hidden from the optimizer: knowing that each byte holds
   // 4 bits, it would turn the byte conversions below into bit-field
   // extracts plus a conversion
@@ -268,6 +286,24 @@ __global__ __launch_bounds__(64 * direct_waves<MT>()) void gptq_direct_kernel(
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int go = e < 4 ? go0[e] : go1[e - 4];
+            if constexpr (MODE == GLOBAL) {
+              // CPL consecutive (scale, bias) pairs of row g: 8*CPL bytes.
+              // A lane past N keeps an offset past the range (reads 0).
+              const uint32_t o = lane_off == (int)OOB ? OOB : (uint32_t)go + (uint32_t)lane_off;
+              if constexpr (CPL == 1) {
+                const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rt, o, 0, 0));
+                sb[e][0] = __uint_as_float(v.x);
+                sb[e][1] = __uint_as_float(v.y);
+              } else {
+#pragma unroll
+                for (int h = 0; h < CPL / 2; ++h) {
+                  const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rt, o + 16 * h, 0, 0));
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) sb[e][4 * h + i] = __uint_as_float(v[i]);
+                }
+              }
+              continue;
+            }
             const unsigned char* ent = lds + go + lane_off;
             if constexpr (CPL == 1) {
               const float2 v = *reinterpret_cast<const float2*>(ent);
@@ -518,6 +554,19 @@ __global__ __launch_bounds__(256) void gptq_mfma_kernel(
 }
 
 // y[m, n] = f16(sum over the S slices)
+// The GLOBAL-mode table: tab[g][n] = (scale, -scale*(z+1)) in fp32 (exact:
+// an 11-bit scale times an integer in [1, 16]).
+__global__ __launch_bounds__(256) void gptq_table_kernel(const uint32_t* __restrict__ qz,
+                                                         const uint16_t* __restrict__ sc, float2* __restrict__ tab,
+                                                         int N, int ng) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long)ng * N) return;
+  const int g = (int)(i / N), n = (int)(i % N);
+  const float s = f16_bits_to_f32(sc[i]);
+  const float z = (float)nib(qz[(long)g * (N / 8) + n / 8], n % 8) + 1.f;
+  tab[i] = make_float2(s, -s * z);
+}
+
 __global__ __launch_bounds__(256) void gptq_finalize_kernel(const float* __restrict__ part, uint16_t* __restrict__ y,
                                                             long MN, int S) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
@@ -586,9 +635,9 @@ inline int64_t fill_slices(int64_t resident, int64_t ncg, int64_t nw, int64_t mi
   return std::max(s_min, std::min(resident / ncg, nw / min_rows));
 }
 
-template <int CPL, int MT, bool ACT>
+template <int CPL, int MT, int MODE>
 hipError_t run_direct(const GptqArgs& a, hipStream_t s) {
-  const auto k = reinterpret_cast<const void*>(gptq_direct_kernel<CPL, MT, ACT>);
+  const auto k = reinterpret_cast<const void*>(gptq_direct_kernel<CPL, MT, MODE>);
   constexpr int block = 64 * direct_waves<MT>();
   static std::once_flag once[64];
   hipError_t e = raise_lds_limit(k, once);
@@ -599,7 +648,7 @@ hipError_t run_direct(const GptqArgs& a, hipStream_t s) {
   // WROWS; more when the slice's staged x and offsets would not fit in LDS
   auto lds_of = [&](int64_t S) {
     const int per_sp = (int)((nw + S - 1) / S);
-    return DirectLds(table_groups(ACT, ng, per_sp, a.G == 32 ? 5 : (a.G == 64 ? 6 : 7)), CPL, MT, per_sp).total;
+    return DirectLds(direct_table_groups(MODE, ng, per_sp, a.G == 32 ? 5 : (a.G == 64 ? 6 : 7)), CPL, MT, per_sp).total;
   };
   int64_t s_min = std::max<int64_t>(1, (nw + WROWS - 1) / WROWS);
   while (lds_of(s_min) > kMaxLds) {
@@ -617,12 +666,24 @@ hipError_t run_direct(const GptqArgs& a, hipStream_t s) {
   // (the kernel derives the same per_sp from S; more slices only shrink the LDS)
   const size_t lds = (size_t)lds_of(S);
   const int64_t MN = a.M * a.N;
-  float* part = nullptr;
-  e = stream_workspace(s, (size_t)S * MN * sizeof(float), (void**)&part);
+  // workspace: the S partial planes, then (GLOBAL) the group table
+  const size_t part_bytes = ((size_t)S * MN * sizeof(float) + 255) & ~size_t(255);
+  const size_t tab_bytes = MODE == GLOBAL ? (size_t)ng * a.N * 8 : 0;
+  char* ws = nullptr;
+  e = stream_workspace(s, part_bytes + tab_bytes, (void**)&ws);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gptq_direct_kernel<CPL, MT, ACT>), dim3((unsigned)(ncg * S)), dim3(block), lds, s,
+  float* part = reinterpret_cast<float*>(ws);
+  float2* gtab = MODE == GLOBAL ? reinterpret_cast<float2*>(ws + part_bytes) : nullptr;
+  if (MODE == GLOBAL) {
+    const long ne = (long)ng * a.N;
+    hipLaunchKernelGGL(gptq_table_kernel, dim3((unsigned)((ne + 255) / 256)), dim3(256), 0, s,
+                       (const uint32_t*)a.qzeros, (const uint16_t*)a.scales, gtab, (int)a.N, ng);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((gptq_direct_kernel<CPL, MT, MODE>), dim3((unsigned)(ncg * S)), dim3(block), lds, s,
                      (const uint16_t*)a.x, (const uint32_t*)a.qweight, (const uint32_t*)a.qzeros,
-                     (const uint16_t*)a.scales, a.g_idx, part, (int)a.M, (int)a.N, (int)a.K,
+                     (const uint16_t*)a.scales, a.g_idx, (const float2*)gtab, part, (int)a.M, (int)a.N, (int)a.K,
                      a.G == 32 ? 5 : (a.G == 64 ? 6 : 7), (int)S);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -631,19 +692,19 @@ hipError_t run_direct(const GptqArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int CPL, int MODE>
+hipError_t run_direct_mode(const GptqArgs& a, int mt, hipStream_t s) {
+  constexpr int MT8 = CPL == 4 ? 4 : 8;  // (8 rows per pass only below 4 columns per lane)
+  if (mt == 1) return run_direct<CPL, 1, MODE>(a, s);
+  if (mt == 2) return run_direct<CPL, 2, MODE>(a, s);
+  if (mt == 4) return run_direct<CPL, 4, MODE>(a, s);
+  return run_direct<CPL, MT8, MODE>(a, s);
+}
+
 template <int CPL>
 hipError_t run_direct_m(const GptqArgs& a, int mt, hipStream_t s) {
-  constexpr int MT8 = CPL == 4 ? 4 : 8;  // (8 rows per pass only below 4 columns per lane)
-  if (a.g_idx) {
-    if (mt == 1) return run_direct<CPL, 1, true>(a, s);
-    if (mt == 2) return run_direct<CPL, 2, true>(a, s);
-    if (mt == 4) return run_direct<CPL, 4, true>(a, s);
-    return run_direct<CPL, MT8, true>(a, s);
-  }
-  if (mt == 1) return run_direct<CPL, 1, false>(a, s);
-  if (mt == 2) return run_direct<CPL, 2, false>(a, s);
-  if (mt == 4) return run_direct<CPL, 4, false>(a, s);
-  return run_direct<CPL, MT8, false>(a, s);
+  if (a.g_idx) return run_direct_mode<CPL, LDS>(a, mt, s);
+  return run_direct_mode<CPL, SLICE>(a, mt, s);
 }
 
 // M >= 8 with at most 96 groups: the matrix-core kernel, K split to fill
@@ -705,8 +766,14 @@ hipError_t launch_gptq_direct(const GptqArgs& a, hipStream_t s) {
   // 64 KiB of LDS, else 2, else 1 (up to 96 KiB).  Without act-order the
   // table holds only a slice's groups, so 4 always.
   const int cpl = !a.g_idx || ng <= 32 ? 4 : (ng <= 64 ? 2 : 1);
-  if (a.g_idx && ng * 64 * cpl * 8 > 96 * 1024) return hipErrorNotSupported;  // group table must fit in LDS
   if (a.K / 8 * a.N * 4 >= (int64_t(1) << 31)) return hipErrorNotSupported;  // 32-bit buffer offsets
+  if (a.g_idx && ng * 64 * cpl * 8 > 96 * 1024) {
+    // act-order with more groups than the LDS table holds (above 192): the
+    // entries come from a device-memory table, 4 columns per lane
+    if (ng * a.N * 8 >= (int64_t(1) << 31)) return hipErrorNotSupported;  // 32-bit table offsets
+    const int mt = a.M == 1 ? 1 : (a.M == 2 ? 2 : 4);
+    return run_direct_mode<4, GLOBAL>(a, mt, s);
+  }
   // x rows per pass (8 would spill registers at 4 columns per lane)
   const int mt = a.M == 1 ? 1 : (a.M == 2 ? 2 : (a.M <= 4 || cpl == 4 ? 4 : 8));
   return cpl == 4 ? run_direct_m<4>(a, mt, s) : (cpl == 2 ? run_direct_m<2>(a, mt, s) : run_direct_m<1>(a, mt, s));

@@ -46,7 +46,7 @@ int check_affine(const void* x, const uint32_t* w, const void* s, const void* b,
   if (!(bits == 2 || bits == 4 || bits == 8)) return fail(QAFF_E_INVAL, "bits must be 2, 4 or 8 (got %d)", bits);
   if (!group_ok(G)) return fail(QAFF_E_INVAL, "group_size must be 32, 64 or 128 (got %d)", G);
   if (K % G != 0) return fail(QAFF_E_INVAL, "K=%lld is not a multiple of group_size=%d", (long long)K, G);
-  if ((K * bits) % 128 != 0) return fail(QAFF_E_UNSUPPORTED, "K*bits must be a multiple of 128 (whole 16-byte row loads)");
+  if (K % (32 / bits) != 0) return fail(QAFF_E_INVAL, "K=%lld is not a multiple of 32/bits=%d", (long long)K, 32 / bits);
   if (!act_dtype_ok(act_dt)) return fail(QAFF_E_INVAL, "act_dtype must be QAFF_BF16 or QAFF_F16 (got %d)", act_dt);
   if (!sb_dtype_ok(s_dt) || !sb_dtype_ok(b_dt)) return fail(QAFF_E_INVAL, "scale/bias dtype must be BF16, F16 or F32");
   if (M == 0 || N == 0) return QAFF_OK;
@@ -82,7 +82,15 @@ extern "C" {
 
 const char* qaff_last_error(void) { return g_last_error.c_str(); }
 
-int qaff_version(void) { return 100; }
+int qaff_version(void) { return 200; }
+
+int qaff_release_workspaces(uint64_t* freed_bytes) {
+  size_t freed = 0;
+  const hipError_t e = qaff::release_workspaces(&freed);
+  if (freed_bytes) *freed_bytes = (uint64_t)freed;
+  if (e != hipSuccess) return hip_fail(e, "releasing workspaces");
+  return ok();
+}
 
 int qgemv_affine(const void* x, const uint32_t* w_packed, const void* scales, const void* biases,
                  const int32_t* k_perm, void* y, int64_t M, int64_t N, int64_t K, int32_t group_size,

@@ -6,7 +6,10 @@
 // buffer only grows (to the next power of two, at least 1 MiB); a grown-out
 // buffer is kept, not freed, because a captured graph may still address it.
 // Growing is refused while the stream is being captured, so a graph is
-// captured after one eager call of the same shapes.
+// captured after one eager call of the same shapes.  A captured graph keeps
+// the address of the buffer of the stream it was captured on: its replays
+// use that buffer whatever stream they run on.  release_workspaces() frees
+// every cached and grown-out buffer at once.
 // Also here: how many workgroups of a kernel the device holds at once, by
 // which the launchers size their K splits.
 #include <algorithm>
@@ -29,7 +32,8 @@ struct Workspace {
 
 std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
-std::vector<void*> g_retired;  // grown-out buffers, still valid for graphs that captured them
+// grown-out buffers, still valid for graphs that captured them: (device, pointer)
+std::vector<std::pair<int, void*>> g_retired;
 
 // (device, kernel, block, LDS) -> (CUs, resident workgroups per CU), under g_mu
 std::map<std::tuple<int, const void*, int, size_t>, std::pair<int, int>> g_resident;
@@ -54,12 +58,41 @@ hipError_t stream_workspace(hipStream_t s, size_t bytes, void** out) {
     void* p = nullptr;
     e = hipMalloc(&p, cap);
     if (e != hipSuccess) return e;
-    if (w.p) g_retired.push_back(w.p);
+    if (w.p) g_retired.push_back({dev, w.p});
     w.p = p;
     w.cap = cap;
   }
   *out = w.p;
   return hipSuccess;
+}
+
+hipError_t release_workspaces(size_t* freed) {
+  if (freed) *freed = 0;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (g_ws.empty() && g_retired.empty()) return hipSuccess;  // nothing held: no HIP call
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  std::vector<std::pair<int, void*>> all;
+  size_t bytes = 0;
+  for (auto& kv : g_ws) {
+    if (kv.second.p) all.push_back({kv.first.first, kv.second.p});
+    bytes += kv.second.cap;
+  }
+  all.insert(all.end(), g_retired.begin(), g_retired.end());
+  hipError_t first = hipSuccess;
+  for (auto& dp : all) {
+    // free on the buffer's own device
+    hipError_t r = hipSetDevice(dp.first);
+    if (r == hipSuccess) r = hipFree(dp.second);
+    if (r != hipSuccess && first == hipSuccess) first = r;
+  }
+  g_ws.clear();
+  g_retired.clear();
+  const hipError_t r = hipSetDevice(cur);
+  if (first == hipSuccess) first = r;
+  if (freed) *freed = bytes;
+  return first;
 }
 
 hipError_t resident_workgroups(const void* kernel, int block, size_t lds, int max_per_cu, int64_t* out) {

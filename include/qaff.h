@@ -22,12 +22,20 @@
  *     Work is enqueued on it asynchronously; hot-path calls never synchronize.
  *   - The caller owns every buffer; the library keeps no pointer to them
  *     after the call returns.  Internal scratch (GEMM pre-pass buffers and
- *     split-K partials, GPTQ partials, permuted activations for k_perm) comes
- *     from a buffer the library keeps per (device, stream): calls on one
- *     stream reuse it in stream order, and once it is large enough no call
- *     allocates.  It only grows, and growing is refused (QAFF_E_HIP) while
- *     `stream` is being captured into a graph: capture a call after one
- *     eager call of the same shapes on the same stream.
+ *     split-K partials, GPTQ partials and tables, permuted activations for
+ *     k_perm) comes from a buffer the library keeps per (device, stream):
+ *     calls on one stream reuse it in stream order, and once it is large
+ *     enough no call allocates.  It only grows, and growing is refused
+ *     (QAFF_E_HIP) while `stream` is being captured into a graph: capture a
+ *     call after one eager call of the same shapes on the same stream.
+ *     A captured graph keeps addressing the scratch of the stream it was
+ *     captured on, whatever stream it is later replayed on.  So every graph
+ *     captured on one stream (torch.cuda.graph captures on one shared
+ *     stream by default), and every eager call on that stream, share one
+ *     scratch buffer: their executions must not overlap in time, or they
+ *     race and give wrong outputs.  Replay such graphs in stream order on
+ *     one stream, or capture them on different streams.
+ *     qaff_release_workspaces() frees the scratch.
  *   - Errors are returned as qaff_status codes; no C++ exception crosses the
  *     ABI.  Argument checks run before any HIP call, so a rejected call has
  *     enqueued nothing.  qaff_last_error() gives a message for the calling
@@ -76,7 +84,10 @@ typedef enum {
  *             must lie in [0, K) (not checked on the device).
  *   y         [M, N]        act_dtype, written with round-to-nearest-even
  *   group_size G in {32, 64, 128}; bits in {2, 4, 8};
- *   K % G == 0 and K*bits % 128 == 0 (whole 16-byte loads per row).
+ *   K % G == 0 (so K % (32/bits) == 0: a row is whole words).  Rows that
+ *   are not whole 16-byte chunks (K*bits % 128 != 0: 2-bit codes with G = 32
+ *   and K an odd multiple of 32) run a plain one-wave-per-row GEMV, also
+ *   for M > 16 (in 16-row slices), slower than the main kernels.
  *
  * Dispatch: M <= 16 runs a memory-bound GEMV kernel (exact fp32 arithmetic
  * on the integer codes; 4-bit codes with 2..16 x rows on the matrix cores,
@@ -219,6 +230,26 @@ int gptq_to_affine_repack(const int32_t *qweight, const int32_t *qzeros, const v
 int quantize_pack_affine(const void *w, int32_t w_dtype, uint32_t *w_packed_out, void *scales_out,
                          void *biases_out, int32_t sb_dtype, int64_t N, int64_t K, int32_t group_size,
                          int32_t bits, void *stream);
+
+/*
+ * qaff_release_workspaces - free all scratch the library holds: the buffer
+ * kept per (device, stream) and every buffer grown out of since the last
+ * release, on every device.  This is the release half of the caller-frees-
+ * once convention of the mlx_int8.rs API page (`release` frees a weight's
+ * buffers exactly once): scratch has no other owner, so the caller decides
+ * when it goes.
+ *   Safe only when (1) no work enqueued through this library is still
+ *   pending on any stream (synchronize first), and (2) no captured graph
+ *   that contains a call of this library will be replayed again (destroy
+ *   such graphs first): their kernels hold the freed addresses.
+ *   The next call that needs scratch allocates again.
+ *   freed_bytes (HOST pointer, may be NULL) receives the bytes of the
+ *   per-stream buffers that were cached (grown-out ones not counted).
+ *   Returns QAFF_OK, or QAFF_E_HIP if a hipFree failed (every buffer is
+ *   still forgotten, and the rest are freed).  Not to be called while other
+ *   threads make library calls.
+ */
+int qaff_release_workspaces(uint64_t *freed_bytes);
 
 /* Message for the calling thread's last non-OK status ("" if none).  The
  * string is owned by the library and valid until the thread's next call. */

@@ -294,3 +294,35 @@ def test_grouped_k_perm_shared_and_distinct():
     torch.cuda.synchronize()
     for c, y in zip(cases, ys):
         assert_float_bar(host_f64(y), oracle.qmm_affine_case(c), c.name)
+
+
+# Rows that are not whole 16-byte chunks: 2-bit codes, G = 32, K an odd
+# multiple of 32 (K*bits % 128 != 0).  They run the plain tail kernel, for
+# M <= 16 directly and for larger M in 16-row slices.
+@pytest.mark.parametrize("K", [32, 96, 160, 1056])
+@pytest.mark.parametrize("M", [1, 5, 16, 33])
+def test_ragged_rows_two_bit(K, M):
+    case = si.affine_case(M, 70, K, 32, 2, seed=(40, K, M), name=f"ragged_b2_K{K}_M{M}")
+    y = _run(case)
+    assert_float_bar(y, oracle.qmm_affine_case(case), case.name)
+
+
+@pytest.mark.parametrize("act,sdt", [("f16", "f16"), ("bf16", "f32")])
+def test_ragged_rows_dtypes_and_k_perm(act, sdt):
+    case = si.affine_case(4, 33, 224, 32, 2, seed=(41,), act_dtype=act, sb_dtype=sdt, name=f"ragged_{act}_{sdt}")
+    case.k_perm = np.random.default_rng(42).permutation(case.K).astype(np.int32)
+    y = _run(case)
+    assert_float_bar(y, oracle.qmm_affine_case(case), case.name)
+
+
+def test_ragged_rows_in_a_grouped_call():
+    # a ragged problem between two regular ones: each output as alone
+    dev = require_gpu()
+    cases = [si.affine_case(2, 64, 2048, 32, 2, seed=(43, 0), name="regular0"),
+             si.affine_case(2, 40, 96, 32, 2, seed=(43, 1), name="ragged"),
+             si.affine_case(2, 48, 1024, 32, 2, seed=(43, 2), name="regular2")]
+    probs = [affine_to_device(c, dev)[:4] for c in cases]
+    ys = qa.qgemv_affine_grouped(probs, 32, 2)
+    torch.cuda.synchronize()
+    for c, y in zip(cases, ys):
+        assert_float_bar(host_f64(y), oracle.qmm_affine_case(c), "grouped " + c.name)

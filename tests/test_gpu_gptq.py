@@ -227,3 +227,18 @@ def test_split_k_sums_under_graph_replay():
         g.replay()
         torch.cuda.synchronize()
         assert_float_bar(host_f64(y), ref, f"{case.name} replay {rep}")
+
+
+# Act-order with more groups than the per-workgroup LDS table holds (above
+# 192): the (scale, bias) entries come from a table in device memory.
+@pytest.mark.parametrize("M", [1, 2, 3, 8, 33])
+@pytest.mark.parametrize("K,N,G", [(8192, 1024, 32), (6272, 520, 32), (16384, 256, 64)])
+def test_direct_act_order_beyond_lds_table(M, K, N, G):
+    dev = require_gpu()
+    case = si.gptq_case(M, K, N, G, seed=(3, 50, M, K), act_order=True)
+    _log(case, "direct global table")
+    x, qw, qz, s, gi = _dev(case, dev)
+    y = qa.qmm_gptq(x, qw, qz, s, gi, case.G)
+    torch.cuda.synchronize()
+    ref = oracle.qmm_gptq(case.x, case.qweight, case.qzeros, case.scales, case.g_idx, M, case.K, case.N, case.G)
+    assert_float_bar(host_f64(y), ref, case.name)

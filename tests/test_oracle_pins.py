@@ -434,3 +434,183 @@ def test_quantize_pack_constant_group_gives_zero_scale():
     assert not packed.any()
     np.testing.assert_array_equal(oracle.to_f64(S, "bf16"), 0.0)
     np.testing.assert_array_equal(oracle.to_f64(B, "bf16"), 0.375)
+
+
+# ---------------------------------------------------------------- dequant to a storage type
+
+def _bf16_nearest_brute(v: float) -> int:
+    """The bf16 pattern nearest to v by exact rational comparison over all
+    finite positive patterns (ties to the even pattern): no rounding formula."""
+    from fractions import Fraction
+    fv = Fraction(abs(v))
+    pats = np.arange(0, 0x7F80, dtype=np.uint32)
+    vals = (pats << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    i = int(np.searchsorted(vals, abs(v)))
+    cands = [j for j in (i - 1, i) if 0 <= j < len(vals)]
+    best = None
+    for j in cands:
+        d = abs(Fraction(vals[j]) - fv)
+        if best is None or d < best[0] or (d == best[0] and (pats[j] & 1) == 0):
+            best = (d, int(pats[j]))
+    sign = 0x8000 if np.signbit(v) else 0
+    return sign | best[1]
+
+
+def test_f64_to_bf16_equals_brute_force_nearest():
+    r = np.random.default_rng(70)
+    v = np.concatenate([r.standard_normal(300) * 10.0 ** r.integers(-30, 30, 300),
+                        # double-rounding traps: just above a bf16 tie, where
+                        # rounding through fp32 first would land on the tie
+                        [1.0 + 2.0 ** -8 + 2.0 ** -30, 1.0 + 2.0 ** -8 - 2.0 ** -30, -(3.0 + 2.0 ** -7 + 2.0 ** -40),
+                         2.0 ** -130 * (1 + 2.0 ** -5), 2.0 ** -133 * 0.5, 2.0 ** -133 * 0.75, 1.0 + 2.0 ** -8]])
+    got = oracle.f64_to_bf16(v)
+    want = np.array([_bf16_nearest_brute(float(t)) for t in v], dtype=np.uint16)
+    np.testing.assert_array_equal(got, want)
+    assert got[300] == 0x3F81 and got[306] == 0x3F80  # above the tie rounds up; the tie itself to even
+
+
+def test_f64_to_bf16_agrees_with_f32_path_on_f32_values():
+    # a value that is already an fp32 is rounded once either way
+    r = np.random.default_rng(71)
+    f = (r.standard_normal(5000) * 10.0 ** r.integers(-35, 35, 5000)).astype(np.float32)
+    np.testing.assert_array_equal(oracle.f64_to_bf16(f.astype(np.float64)), oracle.f32_to_bf16(f))
+
+
+@pytest.mark.parametrize("out", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_dequant_to_rounds_the_exact_weight_once(out, bits):
+    N, K, G = 6, 256, 64
+    packed, s, b = si.affine_weights(N, K, G, bits, seed=(72, bits), scale_range=(0.003, 0.03), bias_mode="noise")
+    exact = oracle.dequant_affine(packed, s, b, "bf16", N, K, G, bits)
+    got = oracle.dequant_affine_to(packed, s, b, "bf16", N, K, G, bits, out)
+    if out == "f32":
+        np.testing.assert_array_equal(got, exact.astype(np.float32))   # numpy's fp64->fp32 is one rounding
+    elif out == "f16":
+        np.testing.assert_array_equal(got.view(np.float16), exact.astype(np.float16))
+    else:
+        want = np.array([_bf16_nearest_brute(float(t)) for t in exact.ravel()[:300]], dtype=np.uint16)
+        np.testing.assert_array_equal(got.ravel()[:300], want)
+
+
+def test_dequant_to_codes_with_unit_scale_are_the_codes():
+    N, K, G, bits = 3, 64, 32, 8
+    codes = np.random.default_rng(73).integers(0, 256, size=(N, K))
+    packed = np.zeros((N, K // 4), dtype=np.uint32)
+    for k in range(K):
+        packed[:, k // 4] |= (codes[:, k].astype(np.uint32) << (8 * (k % 4)))
+    one = np.full((N, K // G), 0x3F80, dtype=np.uint16)        # bf16 1.0
+    zero = np.zeros((N, K // G), dtype=np.uint16)
+    got = oracle.dequant_affine_to(packed, one, zero, "bf16", N, K, G, bits, "f32")
+    np.testing.assert_array_equal(got, codes.astype(np.float32))
+
+
+# ---------------------------------------------------------------- SiLU-gated GEMV
+
+def test_silu_closed_forms():
+    t = np.concatenate([np.linspace(-30, 30, 601), [0.0, 1e-8, -1e-8, 700.0, -700.0]])
+    got = oracle.silu(t)
+    # t * sigmoid(t) with scipy's logistic function (a library routine)
+    from scipy.special import expit
+    np.testing.assert_allclose(got, t * expit(t), rtol=1e-13, atol=1e-300)
+    # and with tanh where that formula is stable (t >= 0)
+    pos = t >= 0
+    np.testing.assert_allclose(got[pos], 0.5 * t[pos] * (1.0 + np.tanh(0.5 * t[pos])), rtol=1e-13)
+    assert got[601] == 0.0
+    np.testing.assert_allclose(got - oracle.silu(-t), t, rtol=1e-12, atol=1e-12)  # silu(t) - silu(-t) = t
+    assert abs(got[604] - 700.0) < 1e-12 and got[605] <= 0.0 and got[605] > -1e-200
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_silu_gate_equals_affine_on_the_gated_input(bits):
+    M, N, K, G = 3, 40, 256, 64
+    c = si.affine_case(M, N, K, G, bits, seed=(74, bits))
+    gate = c.x
+    up = si.activations(M, K, seed=(74, bits, 9))
+    h = oracle.silu(oracle.to_f64(gate, "bf16")) * oracle.to_f64(up, "bf16")
+    # the plain affine oracle on h, through fp64 weights and numpy's matmul
+    w = oracle.dequant_affine(c.packed, c.scales, c.biases, "bf16", N, K, G, bits)
+    want = h @ w.T
+    got = oracle.qmm_affine_silu_gate(gate, up, None, "bf16", c.packed, c.scales, c.biases, "bf16", M, N, K, G, bits)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_silu_gate_residual_is_added_once():
+    M, N, K, G = 2, 24, 128, 32
+    c = si.affine_case(M, N, K, G, 4, seed=(75,), act_dtype="f16")
+    up = si.activations(M, K, seed=(75, 9), dtype="f16")
+    resid = si.activations(M, N, seed=(75, 10), dtype="f16")
+    y0 = oracle.qmm_affine_silu_gate(c.x, up, None, "f16", c.packed, c.scales, c.biases, "bf16", M, N, K, G, 4)
+    y1 = oracle.qmm_affine_silu_gate(c.x, up, resid, "f16", c.packed, c.scales, c.biases, "bf16", M, N, K, G, 4)
+    np.testing.assert_allclose(y1 - y0, resid.view(np.float16).astype(np.float64), rtol=0, atol=1e-12)
+    # up = 0 leaves exactly the residual
+    zero = np.zeros_like(up)
+    y2 = oracle.qmm_affine_silu_gate(c.x, zero, resid, "f16", c.packed, c.scales, c.biases, "bf16", M, N, K, G, 4)
+    np.testing.assert_array_equal(y2, resid.view(np.float16).astype(np.float64))
+
+
+# ---------------------------------------------------------------- SmoothQuant ahead of W4A8
+
+def test_smooth_factors_hand_values():
+    w = np.array([[1.0, -4.0, 0.0], [0.5, 2.0, 0.0]], dtype=np.float32)   # column max |w|: 1, 4, 0
+    a = np.array([4.0, 1.0, 3.0], dtype=np.float32)
+    s = oracle.smooth_factors(a, w, "f32", 2, 3, 0.5)
+    np.testing.assert_array_equal(s, np.array([2.0, 0.5, 1.0], dtype=np.float32))   # sqrt(4/1), sqrt(1/4), zero column
+    np.testing.assert_array_equal(oracle.smooth_factors(a, w, "f32", 2, 3, 1.0), np.array([4.0, 1.0, 1.0], np.float32))
+    np.testing.assert_array_equal(oracle.smooth_factors(a, w, "f32", 2, 3, 0.0), np.array([1.0, 0.25, 1.0], np.float32))
+    a0 = np.array([0.0, 1.0, 3.0], dtype=np.float32)
+    assert oracle.smooth_factors(a0, w, "f32", 2, 3, 0.5)[0] == 1.0
+
+
+def test_smoothing_is_the_identity_for_the_dense_product():
+    # (x / s) . (W diag(s))^T == x . W^T up to fp64 rounding, for the oracle's s
+    r = np.random.default_rng(76)
+    M, N, K = 5, 7, 64
+    x = r.standard_normal((M, K))
+    x[:, 3] *= 50.0                                   # an outlier channel
+    w = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    s = oracle.smooth_factors(np.abs(x).max(0).astype(np.float32), w, "f32", N, K, 0.5).astype(np.float64)
+    lhs = (x / s) @ (w.astype(np.float64) * s).T
+    np.testing.assert_allclose(lhs, x @ w.astype(np.float64).T, rtol=1e-12, atol=1e-14)
+    assert (np.abs(x / s).max(0).max() < np.abs(x).max(0).max() / 3)   # the outlier range shrinks
+
+
+def test_w4a8_weight_quantization_recovers_grid_weights():
+    r = np.random.default_rng(77)
+    N, K = 6, 64
+    codes = r.integers(-7, 8, size=(N, K))
+    codes[:, 5] = 7                                   # the row maximum is +7 steps
+    sw = np.float16(r.uniform(0.001, 0.01, size=N)).astype(np.float32)
+    w = codes * sw[:, None]                           # exact in fp32
+    wq, sw_out = oracle.w4a8_quantize_weights(w.astype(np.float32), "f32", None, N, K)
+    np.testing.assert_array_equal(sw_out.view(np.float16).astype(np.float32), sw)
+    nib = np.stack([(wq >> (4 * j)) & 0xF for j in range(8)], axis=-1).reshape(N, K).astype(np.int64)
+    np.testing.assert_array_equal(np.where(nib >= 8, nib - 16, nib), codes)
+    # smoothing by ones changes nothing; by a power of two per channel it
+    # quantizes the exactly scaled weights
+    wq1, sw1 = oracle.w4a8_quantize_weights(w.astype(np.float32), "f32", np.ones(K, np.float32), N, K)
+    np.testing.assert_array_equal(wq1, wq)
+    np.testing.assert_array_equal(sw1, sw_out)
+    p2 = (2.0 ** r.integers(-2, 3, size=K)).astype(np.float32)
+    wq2, sw2 = oracle.w4a8_quantize_weights(w.astype(np.float32), "f32", p2, N, K)
+    wq3, sw3 = oracle.w4a8_quantize_weights((w * p2).astype(np.float32), "f32", None, N, K)
+    np.testing.assert_array_equal(wq2, wq3)
+    np.testing.assert_array_equal(sw2, sw3)
+
+
+def test_w4a8_smooth_reduces_to_plain_w4a8():
+    c = si.w4a8_case(4, 16, 128, seed=(78,))
+    ones = np.ones(c.K, np.float32)
+    q0, s0, a0, y0 = oracle.w4a8(c.x, c.w_q4, c.s_w, c.M, c.N, c.K)
+    q1, s1, a1, y1 = oracle.w4a8_smooth(c.x, ones, c.w_q4, c.s_w, c.M, c.N, c.K)
+    np.testing.assert_array_equal(q1, q0)
+    np.testing.assert_array_equal(s1, s0)
+    np.testing.assert_array_equal(a1, a0)
+    # a power-of-two divisor is exact: the same as dividing x beforehand
+    p2 = (2.0 ** np.random.default_rng(79).integers(-3, 4, size=c.K)).astype(np.float32)
+    xd = (c.x.view(np.float16).astype(np.float32) / p2).astype(np.float16)
+    assert np.array_equal(xd.astype(np.float32) * p2, c.x.view(np.float16).astype(np.float32))  # no rounding in x/p2
+    q2, s2, a2, _ = oracle.w4a8_smooth(c.x, p2, c.w_q4, c.s_w, c.M, c.N, c.K)
+    q3, s3, a3, _ = oracle.w4a8(xd.view(np.uint16), c.w_q4, c.s_w, c.M, c.N, c.K)
+    np.testing.assert_array_equal(q2, q3)
+    np.testing.assert_array_equal(s2, s3)
+    np.testing.assert_array_equal(a2, a3)
