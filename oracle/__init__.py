@@ -221,3 +221,83 @@ def affine_tolerance_report(y, ref) -> dict:
     nref = float(np.linalg.norm(ref))
     frob = float(np.linalg.norm(y - ref) / nref) if nref > 0 else float(np.linalg.norm(y - ref))
     return {"max_elem": elem, "rel_frob": frob, "ok": bool(elem <= 1e-2 and frob <= 5e-3 and np.isfinite(y).all())}
+
+
+# ------------------------------------------------------------- dequant to a dtype
+
+def f64_to_bf16(v) -> np.ndarray:
+    a = _c(v, np.float64)
+    out = np.empty(a.shape, dtype=np.uint16)
+    _load().oracle_f64_to_bf16(_p(a), I64(a.size), _p(out))
+    return out
+
+
+def dequant_affine_to(packed, scales, biases, sb_dtype: str, N: int, K: int, G: int, bits: int, out_dtype: str,
+                      bias_dtype: str = None) -> np.ndarray:
+    """Every weight exactly (fp64), rounded once to ``out_dtype`` (nearest even):
+    uint16 patterns for bf16/f16, float32 for f32."""
+    bias_dtype = bias_dtype or sb_dtype
+    p, s, b = _c(packed, np.uint32), _sb(scales, sb_dtype), _sb(biases, bias_dtype)
+    out = np.empty((N, K), dtype=np.float32 if out_dtype == "f32" else np.uint16)
+    _check(_load().oracle_dequant_affine_to(_p(p), _p(s), C.c_int(_DT[sb_dtype]), _p(b), C.c_int(_DT[bias_dtype]),
+                                            I64(N), I64(K), C.c_int(G), C.c_int(bits), C.c_int(_DT[out_dtype]),
+                                            _p(out)), "dequant_affine_to")
+    return out
+
+
+# ------------------------------------------------------------- SiLU-gated GEMV
+
+def silu(v) -> np.ndarray:
+    a = _c(v, np.float64)
+    out = np.empty(a.shape, dtype=np.float64)
+    _load().oracle_silu(_p(a), I64(a.size), _p(out))
+    return out
+
+
+def qmm_affine_silu_gate(gate, up, resid, act_dtype: str, packed, scales, biases, sb_dtype: str, M: int, N: int,
+                         K: int, G: int, bits: int, bias_dtype: str = None) -> np.ndarray:
+    """y = W (silu(gate) * up) [+ resid], fp64; gate/up [M, K], resid [M, N] or None."""
+    bias_dtype = bias_dtype or sb_dtype
+    g, u = _c(gate, np.uint16), _c(up, np.uint16)
+    r = None if resid is None else _c(resid, np.uint16)
+    p, s, b = _c(packed, np.uint32), _sb(scales, sb_dtype), _sb(biases, bias_dtype)
+    y = np.empty((M, N), dtype=np.float64)
+    _check(_load().oracle_qmm_affine_silu_gate(_p(g), _p(u), _p(r), C.c_int(_DT[act_dtype]), _p(p), _p(s),
+                                               C.c_int(_DT[sb_dtype]), _p(b), C.c_int(_DT[bias_dtype]), I64(M),
+                                               I64(N), I64(K), C.c_int(G), C.c_int(bits), _p(y)),
+           "qmm_affine_silu_gate")
+    return y
+
+
+# ------------------------------------------------------------- SmoothQuant + W4A8
+
+def smooth_factors(act_absmax, w, w_dtype: str, N: int, K: int, alpha: float) -> np.ndarray:
+    a = _c(act_absmax, np.float32)
+    wa = _sb(w, w_dtype)
+    s = np.empty((K,), dtype=np.float32)
+    _check(_load().oracle_smooth_factors(_p(a), _p(wa), C.c_int(_DT[w_dtype]), I64(N), I64(K), C.c_double(alpha),
+                                         _p(s)), "smooth_factors")
+    return s
+
+
+def w4a8_quantize_weights(w, w_dtype: str, smooth, N: int, K: int):
+    """Returns (w_q4 [N, K/8] u32, s_w [N] f16 bits)."""
+    wa = _sb(w, w_dtype)
+    sm = None if smooth is None else _c(smooth, np.float32)
+    wq = np.empty((N, K // 8), dtype=np.uint32)
+    sw = np.empty((N,), dtype=np.uint16)
+    _check(_load().oracle_w4a8_quantize_weights(_p(wa), C.c_int(_DT[w_dtype]), _p(sm), I64(N), I64(K), _p(wq),
+                                                _p(sw)), "w4a8_quantize_weights")
+    return wq, sw
+
+
+def w4a8_smooth(x, smooth, w_q4, s_w, M: int, N: int, K: int):
+    """x / smooth per channel, then W4A8: (q_x, s_x, acc int64, y f64)."""
+    xa, sm, w, sw = _c(x, np.uint16), _c(smooth, np.float32), _c(w_q4, np.uint32), _c(s_w, np.uint16)
+    q = np.empty((M, K), dtype=np.int8)
+    s = np.empty((M,), dtype=np.float32)
+    acc = np.empty((M, N), dtype=np.int64)
+    y = np.empty((M, N), dtype=np.float64)
+    _check(_load().oracle_w4a8_smooth(_p(xa), _p(sm), _p(w), _p(sw), I64(M), I64(N), I64(K), _p(q), _p(s), _p(acc),
+                                      _p(y)), "w4a8_smooth")
+    return q, s, acc, y

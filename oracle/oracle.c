@@ -546,3 +546,234 @@ int oracle_quantize_pack_affine(const void *w, int w_dtype, int64_t N, int64_t K
         }
     return OR_OK;
 }
+
+/* ---------------------------------------------------------------------- */
+/* D1  dequantize to a storage type  [MLX8 `dequantize_to` (the whole      */
+/*     weight written out as BF16); METAL "Dequantize"]                    */
+/*                                                                        */
+/* Each weight is the exact fp64 value of O2, rounded ONCE to the output   */
+/* type, nearest even.  READING: the output type is BF16 (as on [MLX8]),   */
+/* F16 or F32.                                                            */
+
+/* Round a double to bfloat16 (8 significant bits, the exponent range of   */
+/* an IEEE single), nearest even, from the definition of the format.       */
+static uint16_t f64_to_bf16(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isnan(v))
+        return (uint16_t)(sign | 0x7fc0);
+    if (a < ldexp(1.0, -126)) {       /* subnormal grid: multiples of 2^-133 */
+        double m = nearbyint(ldexp(a, 133));
+        return (uint16_t)(sign | (uint16_t)m);   /* m == 128 is the smallest normal */
+    }
+    int e;
+    double f = frexp(a, &e);          /* a = f * 2^e, f in [0.5, 1) */
+    double m = nearbyint(ldexp(f, 8));  /* 8 significant bits, in [128, 256] */
+    if (m == 256.0) {
+        m = 128.0;
+        e += 1;
+    }
+    int biased = e - 1 + 127;
+    if (biased >= 255)
+        return (uint16_t)(sign | 0x7f80);
+    return (uint16_t)(sign | (uint16_t)(biased << 7) | (uint16_t)((int)m - 128));
+}
+
+void oracle_f64_to_bf16(const double *src, int64_t n, uint16_t *dst)
+{
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = f64_to_bf16(src[i]);
+}
+
+int oracle_dequant_affine_to(const uint32_t *packed, const void *scales, int s_dtype, const void *biases,
+                             int b_dtype, int64_t N, int64_t K, int G, int bits, int out_dtype, void *out)
+{
+    if (!affine_args_ok(N, K, G, bits) || !dtype_ok(s_dtype) || !dtype_ok(b_dtype) || !dtype_ok(out_dtype))
+        return OR_EARG;
+    int64_t wpr = K * bits / 32;
+    double *w = (double *)malloc(sizeof(double) * (size_t)(K + 1));
+    if (!w) return OR_EMEM;
+    for (int64_t n = 0; n < N; ++n) {
+        dequant_affine_row(packed + n * wpr, scales, s_dtype, biases, b_dtype, n, K, G, bits, w);
+        for (int64_t k = 0; k < K; ++k) {
+            if (out_dtype == OR_BF16)
+                ((uint16_t *)out)[n * K + k] = f64_to_bf16(w[k]);
+            else if (out_dtype == OR_F16)
+                ((uint16_t *)out)[n * K + k] = f64_to_f16(w[k]);
+            else
+                ((float *)out)[n * K + k] = (float)w[k];
+        }
+    }
+    free(w);
+    return OR_OK;
+}
+
+/* ---------------------------------------------------------------------- */
+/* S1  SiLU-gated input  [MLX8 `gemv_silu_gate`, `gemv_silu_gate_resid`]   */
+/*                                                                        */
+/*   h[m,k] = silu(gate[m,k]) * up[m,k],   silu(t) = t / (1 + e^-t)        */
+/*   y[m,n] = sum_{k ascending} h[m,k] * w[n,k]   (+ resid[m,n] if given)  */
+/* all in fp64 from the stored gate, up and resid values; w as in O2.     */
+static double silu(double t)
+{
+    return t / (1.0 + exp(-t));
+}
+
+void oracle_silu(const double *src, int64_t n, double *dst)
+{
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = silu(src[i]);
+}
+
+int oracle_qmm_affine_silu_gate(const void *gate, const void *up, const void *resid, int act_dtype,
+                                const uint32_t *packed, const void *scales, int s_dtype, const void *biases,
+                                int b_dtype, int64_t M, int64_t N, int64_t K, int G, int bits, double *y)
+{
+    if (!affine_args_ok(N, K, G, bits) || M < 0 || !dtype_ok(s_dtype) || !dtype_ok(b_dtype) ||
+        !dtype_ok(act_dtype))
+        return OR_EARG;
+    double *hd = (double *)malloc(sizeof(double) * (size_t)(M * K + 1));
+    if (!hd) return OR_EMEM;
+    for (int64_t i = 0; i < M * K; ++i)
+        hd[i] = silu(load_f64(gate, i, act_dtype)) * load_f64(up, i, act_dtype);
+    int64_t wpr = K * bits / 32;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *w = (double *)malloc(sizeof(double) * (size_t)(K + 1));
+        if (!w) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for schedule(static)
+        for (int64_t n = 0; n < N; ++n) {
+            if (!w) continue;
+            dequant_affine_row(packed + n * wpr, scales, s_dtype, biases, b_dtype, n, K, G, bits, w);
+            for (int64_t m = 0; m < M; ++m) {
+                const double *hr = hd + m * K;
+                double acc = 0.0;
+                for (int64_t k = 0; k < K; ++k)
+                    acc += hr[k] * w[k];
+                if (resid)
+                    acc += load_f64(resid, m * N + n, act_dtype);
+                y[m * N + n] = acc;
+            }
+        }
+        free(w);
+    }
+    free(hd);
+    return fail ? OR_EMEM : OR_OK;
+}
+
+/* ---------------------------------------------------------------------- */
+/* SQ  SmoothQuant ahead of W4A8  [GPTQ page, section 3 "SmoothQuant":     */
+/*     "Trick" (y = (x / s) . (s W), per input channel) and Xiao et al.'s  */
+/*     rule for s quoted there]                                           */
+/*                                                                        */
+/* SQ1 s[k] = act_absmax[k]^alpha / max_n |W[n,k]|^(1 - alpha), in fp64,   */
+/*     stored as fp32 (nearest even).  act_absmax[k] = max over the        */
+/*     calibration tokens of |x[:,k]|, gathered by the caller.            */
+/*     READING: a channel whose activation or weight maximum is 0 gets     */
+/*     s = 1 (the formula gives 0, inf or 0/0 there; 1 leaves it as is).   */
+int oracle_smooth_factors(const float *act_absmax, const void *w, int w_dtype, int64_t N, int64_t K, double alpha,
+                          float *s)
+{
+    if (N <= 0 || K <= 0 || !dtype_ok(w_dtype) || !(alpha >= 0.0 && alpha <= 1.0)) return OR_EARG;
+    for (int64_t k = 0; k < K; ++k) {
+        double wmax = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            double a = fabs(load_f64(w, n * K + k, w_dtype));
+            if (a > wmax) wmax = a;
+        }
+        double amax = (double)act_absmax[k];
+        if (!(amax > 0.0) || !(wmax > 0.0))
+            s[k] = 1.0f;
+        else
+            s[k] = (float)(pow(amax, alpha) / pow(wmax, 1.0 - alpha));
+    }
+    return OR_OK;
+}
+
+/* SQ2 W' = W diag(s) in our [N, K] layout (column k times s[k]), each     */
+/*     product rounded to fp32; then the per-channel int4 quantization of   */
+/*     W4A8 [W4A8 "What this adds"; symmetric rule as in QAT]:              */
+/*       s_w[n] = f16( max_k |W'[n,k]| / 7 )   (fp32 division, then RNE)   */
+/*       v[n,k] = clamp(rint(W'[n,k] / s_w[n]), -8, 7)  (fp32, s_w as stored)*/
+/*     packed as Q4 (two's complement nibbles, lowest k in the low bits).  */
+/*     smooth == NULL means s = 1 (plain W4A8 weight quantization).        */
+/*     READING: a row with max 0 (or s_w rounding to 0) gets codes 0.       */
+int oracle_w4a8_quantize_weights(const void *w, int w_dtype, const float *smooth, int64_t N, int64_t K,
+                                 uint32_t *w_q4, uint16_t *s_w)
+{
+    if (N <= 0 || K <= 0 || K % 8 || !dtype_ok(w_dtype)) return OR_EARG;
+    memset(w_q4, 0, sizeof(uint32_t) * (size_t)(N * (K / 8)));
+    for (int64_t n = 0; n < N; ++n) {
+        float wmax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = (float)load_f64(w, n * K + k, w_dtype);
+            if (smooth) v = v * smooth[k];
+            float a = fabsf(v);
+            if (a > wmax) wmax = a;
+        }
+        float sc = wmax / 7.0f;
+        uint16_t h = f64_to_f16((double)sc);
+        s_w[n] = h;
+        float sr = (float)f16_to_f64(h);
+        for (int64_t k = 0; k < K; ++k) {
+            float v = (float)load_f64(w, n * K + k, w_dtype);
+            if (smooth) v = v * smooth[k];
+            float t = 0.0f;
+            if (sr != 0.0f) {
+                t = rintf(v / sr);
+                if (t > 7.0f) t = 7.0f;
+                if (t < -8.0f) t = -8.0f;
+            }
+            uint32_t nibv = (uint32_t)((int)t & 0xF);
+            w_q4[n * (K / 8) + k / 8] |= nibv << (4 * (k % 8));
+        }
+    }
+    return OR_OK;
+}
+
+/* SQ3 the smoothed activations meet the W4A8 quantizer: per token,        */
+/*       xs[m,k] = fp32(x[m,k]) / s[k]           (IEEE single division)     */
+/*     then Q1..Q6 on xs in place of x.                                    */
+int oracle_w4a8_smooth(const uint16_t *x, const float *smooth, const uint32_t *w_q4, const uint16_t *s_w, int64_t M,
+                       int64_t N, int64_t K, int8_t *q, float *s_x, int64_t *acc, double *y)
+{
+    if (M < 0 || N < 0 || K <= 0 || K % 8) return OR_EARG;
+    float *xs = (float *)malloc(sizeof(float) * (size_t)(M * K + 1));
+    if (!xs) return OR_EMEM;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k)
+            xs[m * K + k] = (float)f16_to_f64(x[m * K + k]) / smooth[k];
+    for (int64_t m = 0; m < M; ++m) {
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf(xs[m * K + k]);
+            if (a > amax) amax = a;
+        }
+        float sc = amax / 127.0f;
+        s_x[m] = sc;
+        for (int64_t k = 0; k < K; ++k) {
+            float t = 0.0f;
+            if (sc != 0.0f) {
+                t = rintf(xs[m * K + k] / sc);
+                if (t > 127.0f) t = 127.0f;
+                if (t < -127.0f) t = -127.0f;
+            }
+            q[m * K + k] = (int8_t)t;
+        }
+    }
+    free(xs);
+    int rc = oracle_w4a8_acc(q, w_q4, M, N, K, acc);
+    if (rc) return rc;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t a = acc[m * N + n];
+            if (a > INT32_MAX || a < INT32_MIN) return OR_ERANGE;
+            y[m * N + n] = (double)a * (double)s_x[m] * f16_to_f64(s_w[n]);
+        }
+    return OR_OK;
+}
