@@ -177,51 +177,90 @@ __device__ __forceinline__ void prep_x_row(int m, const void* __restrict__ x, in
 }
 
 // ---------------------------------------------------------------------------
-// prep_w: one wave per padded row n.  PS = number of scale pieces; each is
-// stored twice, as an fp16 pair (s, s), ready to multiply packed code pairs.
+// prep_w: one block per PW = 8 padded rows n0 .. n0+7.  PS = number of scale
+// pieces; each is stored twice, as an fp16 pair (s, s), ready to multiply
+// packed code pairs.  Layout K-tile-major, sh[kt][Np][SPT][PS] (one u32
+// each, SPT = 2 groups per 64-code K tile for G = 32, else 1; a G = 128
+// group serves two K tiles and is written for both), so the 32 rows a wave
+// of the GEMM needs for one K tile are one coalesced load.
+//   1. e_n: the exponent of the row's largest |scale| (a wave per two rows)
+//   2. the bias tail row cb = (off*s + b) * 2^-e_n as bf16 (hi, lo, hi)
+//   3. the pieces, with n fastest across the threads, so the stores of a
+//      K tile's 8 rows are contiguous
+// Small blocks keep every loop short: a loop of dependent loads per thread
+// would wait out one memory latency per iteration.
+constexpr int PW = 8;
 template <int PS>
 __device__ __forceinline__ void prep_w_rows(int blk, const void* __restrict__ scales, int s_dt,
-                                            const void* __restrict__ biases, int b_dt, float off, int N, int ng,
-                                            int Kt, f16x2_t* __restrict__ sh, uint16_t* __restrict__ tB,
+                                            const void* __restrict__ biases, int b_dt, float off, int N, int Np,
+                                            int ng, int G, int Kt, uint32_t* __restrict__ sh, uint16_t* __restrict__ tB,
                                             int* __restrict__ en) {
-  const int n = blk * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  f16x2_t* srow = sh + (long)n * ng * PS;
-  uint16_t* trow = tB + (long)n * Kt;
-  if (n >= N) {
-    for (int i = lane; i < ng * PS; i += 64) srow[i] = f16x2_t{(_Float16)0.f, (_Float16)0.f};
-    for (int k = lane; k < Kt; k += 64) trow[k] = 0;
-    if (lane == 0) en[n] = 0;
-    return;
+  __shared__ int e_s[PW];
+  const int n0 = blk * PW, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  {
+    float smax[PW / 4];
+#pragma unroll
+    for (int u = 0; u < PW / 4; ++u) {
+      const int n = n0 + wave + 4 * u;
+      smax[u] = 0.f;
+      if (n < N)
+        for (int g = lane; g < ng; g += 64) smax[u] = fmaxf(smax[u], fabsf(load_as_f32(scales, (long)n * ng + g, s_dt)));
+    }
+#pragma unroll
+    for (int u = 0; u < PW / 4; ++u) {
+      const int r = wave + 4 * u;
+      const int e = exp_of(wave_max(smax[u]));
+      if (lane == 0) {
+        e_s[r] = e;
+        en[n0 + r] = e;
+      }
+    }
   }
-  const long base = (long)n * ng;
-  float smax = 0.f;
-  for (int g = lane; g < ng; g += 64) smax = fmaxf(smax, fabsf(load_as_f32(scales, base + g, s_dt)));
-  smax = wave_max(smax);
-  const int e = exp_of(smax);
-  if (lane == 0) en[n] = e;
-  const float sc = ldexpf(1.f, -e);
-  for (int g = lane; g < ng; g += 64) {
-    const float s = load_as_f32(scales, base + g, s_dt);
-    const float b = load_as_f32(biases, base + g, b_dt);
-    float r = s * sc;  // exact: a power-of-two scaling
+  __syncthreads();
+  // bias tail rows (contiguous per row)
+  for (int i = t; i < PW * Kt; i += 256) {
+    const int r = i / Kt, k = i % Kt, n = n0 + r;
+    uint16_t v = 0;
+    if (n < N && k < 3 * ng) {
+      const int g = k / 3, part = k % 3;
+      const float sv = load_as_f32(scales, (long)n * ng + g, s_dt);
+      const float cb = fmaf(off, sv, load_as_f32(biases, (long)n * ng + g, b_dt)) * ldexpf(1.f, -e_s[r]);
+      const uint16_t hi = f32_to_bf16_bits(cb);
+      v = part == 1 ? f32_to_bf16_bits(cb - bf16_bits_to_f32(hi)) : hi;
+    }
+    tB[(long)n * Kt + k] = v;
+  }
+  // scale pieces, n fastest
+  const int tpg = G == 128 ? 2 : 1;  // K tiles per group
+  for (int i = t; i < PW * ng; i += 256) {
+    const int r = i % PW, g = i / PW, n = n0 + r;
+    uint32_t pc[PS];
+    if (n < N) {
+      float rr = load_as_f32(scales, (long)n * ng + g, s_dt) * ldexpf(1.f, -e_s[r]);  // exact: a power of two
+#pragma unroll
+      for (int j = 0; j < PS; ++j) {
+        const float q = (j == PS - 1) ? rr : trunc_bf16(rr);
+        const uint32_t h = f32_to_f16_bits(q);
+        pc[j] = h | (h << 16);
+        rr -= q;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < PS; ++j) pc[j] = 0u;
+    }
 #pragma unroll
     for (int j = 0; j < PS; ++j) {
-      const float p = (j == PS - 1) ? r : trunc_bf16(r);
-      srow[g * PS + j] = f16x2_t{(_Float16)p, (_Float16)p};
-      r -= p;
+      if (G == 32) {
+        sh[(((long)(g >> 1) * Np + n) * 2 + (g & 1)) * PS + j] = pc[j];
+      } else {
+        for (int u = 0; u < tpg; ++u) sh[((long)(g * tpg + u) * Np + n) * PS + j] = pc[j];
+      }
     }
-    const float cb = fmaf(off, s, b) * sc;
-    const uint16_t hi = f32_to_bf16_bits(cb);
-    const uint16_t lo = f32_to_bf16_bits(cb - bf16_bits_to_f32(hi));
-    trow[3 * g] = hi;
-    trow[3 * g + 1] = lo;
-    trow[3 * g + 2] = hi;
   }
-  for (int k = 3 * ng + lane; k < Kt; k += 64) trow[k] = 0;
 }
 
 // prep_x and prep_w in one launch: blocks [0, Mp) take the rows of x, the
-// rest take four rows of W each; the two halves run side by side.
+// rest take PW rows of W each; the two halves run side by side.
 struct PrepArgs {
   const void* x;
   const int32_t* k_perm;
@@ -230,12 +269,12 @@ struct PrepArgs {
   _Float16* xh;
   uint16_t* tA;
   int* em;
-  f16x2_t* sh;
+  uint32_t* sh;
   uint16_t* tB;
   int* en;
   float off;
   int act_dt, s_dt, b_dt;
-  int M, N, K, G, Kt, BM, Mp, ng;
+  int M, N, K, G, Kt, BM, Mp, Np, ng;
 };
 
 template <int BITS, int PS>
@@ -244,7 +283,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   if (b < a.Mp)
     prep_x_row<BITS>(b, a.x, a.act_dt, a.k_perm, a.M, a.K, a.G, a.Kt, a.BM, a.xh, a.tA, a.em);
   else
-    prep_w_rows<PS>(b - a.Mp, a.scales, a.s_dt, a.biases, a.b_dt, a.off, a.N, a.ng, a.Kt, a.sh, a.tB, a.en);
+    prep_w_rows<PS>(b - a.Mp, a.scales, a.s_dt, a.biases, a.b_dt, a.off, a.N, a.Np, a.ng, a.G, a.Kt, a.sh, a.tB,
+                    a.en);
 }
 
 // ---------------------------------------------------------------------------
@@ -255,7 +295,7 @@ struct GemmParams {
   const uint16_t* tA;
   const int* em;
   const uint32_t* w;
-  const f16x2_t* sh;
+  const uint32_t* sh;  // scale pieces, sh[kt][Np][SPT][PS]
   const uint16_t* tB;
   const int* en;
   uint16_t* y;
@@ -303,117 +343,126 @@ struct Decode {
   static constexpr float piece_mult(int a) { return (BITS == 8 && a == 0) ? 16.f : 1.f; }
 };
 
-// Main GEMM.  256 threads = 4 waves, one per SIMD, side by side along N:
-// wave w computes rows [0, BM) x columns [64w, 64w+64) of the BM x 256 tile,
-// so every weight word is decoded once per BM rows.
+// Main GEMM.  512 threads = 8 waves, two per SIMD; tile BM x 256 with
+// BM = 64 MB.  Wave w = 4 wm + wn computes rows [32 MB wm, +32 MB) x
+// columns [64 wn, +64) of the tile (MB 32-row blocks x 2 32-column blocks).
+// The two waves of a SIMD cover each other's waits, and the VALU decode of
+// one co-issues with the MFMAs of the other.
 //
-// Pipeline:
-//   * x tiles go global -> registers (one step before the store) -> LDS,
-//     stored two steps before use into a 4-stage ring; 16-byte chunks are
-//     XOR-swizzled by row ((r ^ r>>1) & 7) so the MFMA operand reads are
-//     bank-conflict free;
-//   * weight words and scale pieces go through buffer loads with the K
-//     offset in an SGPR, into a 4-deep register ring (three steps ahead);
-//   * the A reads and the B decode of a tile's first 16-column step run
-//     during the previous tile's last step, so a tile starts with MFMAs
-//     (the tile's x is in LDS for every wave one barrier earlier);
-//   * the loop is unrolled by 4 so every ring index and LDS stage is a
-//     constant.
-// Rows of W past N are read through per-lane offsets past the buffer's range
-// and come back as zeros, so the last row tile needs no clamping.
+// Everything a K tile needs arrives in a 3-stage LDS ring by direct
+// global -> LDS copies (buffer_load ... lds, whole 16-byte pieces per lane),
+// issued two tiles ahead:
+//   x      BM rows x 64 fp16 (tile-blocked by the pre-pass: one contiguous
+//          block), 16-byte pieces XOR-swizzled by row;
+//   codes  the tile's 256 weight rows x 8*BITS bytes, copied ONCE per
+//          workgroup (wave w copies rows 32w .. 32w+31) and read back by
+//          the two waves that use them.  Loading them straight into the
+//          lanes that decode them (32 rows x 32 bytes per instruction,
+//          duplicated for both row halves) kept the texture units 75% busy
+//          with scattered requests and bounded the whole kernel.
+// Scale pieces (pre-pass layout sh[kt][Np][SPT][PS]) go to registers with
+// one coalesced load per 32 columns and tile, into a 3-entry ring.
+// Stages are separate LDS arrays, so the compiler can see that a copy into
+// one stage does not touch the one being read.
+// Rows of W past N are read through offsets past the buffer's range and
+// come back as zeros, so the last column tile needs no clamping.
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 1)) & 7; }
 
 template <int BITS, int PS, int MB>
-struct Stage {
-  static constexpr int WPL = BITS;  // words per lane per K tile
-  uint32_t w[2][WPL];
-  uint32_t s[2][PS];  // scale pieces as fp16 pairs (s, s)
-};
-
-template <int BITS, int PS, int MB>
-struct Pipe {
+struct Gemm {
   using D = Decode<BITS>;
-  using St = Stage<BITS, PS, MB>;
-  static constexpr int WPL = BITS;
-  static constexpr int WPR = 2 * BITS;
-  static constexpr int A_DMA = MB;
+  static constexpr int BM = 64 * MB;
+  static constexpr int XB = BM * 128;            // bytes of one x stage
+  static constexpr int RB = 8 * BITS;            // code bytes per weight row and K tile
+  static constexpr int WB = BN * RB;             // bytes of one code stage
+  static constexpr int A_DMA = XB / (512 * 16);  // x copies per thread and tile
+  // code copies per wave and tile: 32 rows x RB bytes, 16 (2-bit: 4) bytes a lane
+  static constexpr int W_SZ = BITS == 2 ? 4 : 16;
+  static constexpr int W_DMA = 32 * RB / (64 * W_SZ);
+  static constexpr int NF = D::NPIECE * PS;
+  static constexpr int VM_TILE = A_DMA + W_DMA + 2;  // + one scale load per 32 columns
+  static_assert(VM_TILE < 64, "vmcnt field");
+  static constexpr int WPL = BITS;                  // words per lane and 32 columns per tile
 
   __amdgpu_buffer_rsrc_t rw, rs, rx;
-  uint32_t w_off[2], s_off[2], x_off;
-  int half, l32, gsh;
-  int kbase;       // first K tile of this workgroup's split
-  int last_kt;     // index of the last K tile, relative to kbase
-  int a_dst;       // this thread's first LDS chunk in a stage
+  uint32_t x_off, w_goff[W_DMA], s_off[2];
+  int w_lds[2];                                     // this lane's code bytes in a stage, per 32-column block
+  int half, l32, wm, wave, kbase, last_kt, Np, spt;
 
-  // Loads for K tile kt: the x chunks (into registers; written to LDS one
-  // step later), then the weight words and scale pieces (into a ring entry
-  // used two steps later).
-  // A prefetch past the last tile re-reads the last tile: every address stays
-  // inside its buffer, whatever the hardware does with soffset in its range
-  // check; the data is never used.
-  __device__ __forceinline__ void issue_x(int kt, u32x4_t (&xr)[A_DMA]) const {
+  // x of tile kt into stage xs: instruction i of wave w fills bytes
+  // [(8i + w) KiB, +1 KiB); lane l's piece is chunk 64 (8i + w) + l
+  __device__ __forceinline__ void issue(int kt, unsigned char* xs, unsigned char* ws, uint32_t (&sc)[2][PS]) const {
     kt = kbase + min(kt, last_kt);
 #pragma unroll
     for (int i = 0; i < A_DMA; ++i)
-      xr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, x_off, kt * (MB * 32 * 128) + i * 4096, 0));
-  }
-  __device__ __forceinline__ void issue_w(int kt, St& st) const {
-    kt = kbase + min(kt, last_kt);
-    // group of this tile: (2*kt + half) >> gsh, whose lane part (half, for
-    // G = 32 only) is folded into s_off; the rest is uniform
-    const int sg = ((2 * kt) >> gsh) * PS * 4;
-    const int so = kt * WPR * 4;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (__attribute__((address_space(3))) void*)(xs + (i * 8 + wave) * 1024), 16, x_off, kt * XB + i * 8192, 0, 0);
+#pragma unroll
+    for (int i = 0; i < W_DMA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rw, (__attribute__((address_space(3))) void*)(ws + wave * 32 * RB + i * 64 * W_SZ), W_SZ, w_goff[i],
+          kt * RB, 0, 0);
+    const int so = __builtin_amdgcn_readfirstlane(kt * Np * spt * PS * 4);
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      if constexpr (WPL == 2) {
-        const u32x2_t u = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rw, w_off[nb], so, 0));
-        st.w[nb][0] = u.x;
-        st.w[nb][1] = u.y;
+      if constexpr (PS == 1) {
+        sc[nb][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, s_off[nb], so, 0);
+      } else if constexpr (PS == 2) {
+        const u32x2_t u = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, s_off[nb], so, 0));
+        sc[nb][0] = u.x;
+        sc[nb][1] = u.y;
+      } else {
+        typedef __attribute__((ext_vector_type(3))) uint32_t u32x3_t;
+        const u32x3_t u = __builtin_bit_cast(u32x3_t, __builtin_amdgcn_raw_buffer_load_b96(rs, s_off[nb], so, 0));
+        sc[nb][0] = u.x;
+        sc[nb][1] = u.y;
+        sc[nb][2] = u.z;
+      }
+    }
+  }
+  __device__ __forceinline__ void read_a(const unsigned char* __restrict__ xs, int s, f16x8_t (&af)[MB]) const {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int r = wm * 32 * MB + mb * 32 + l32;
+      af[mb] = *reinterpret_cast<const f16x8_t*>(xs + r * 128 + (((4 * half + s) ^ swz(r)) << 4));
+    }
+  }
+  // this lane's code words of the tile, per 32-column block
+  __device__ __forceinline__ void read_w(const unsigned char* __restrict__ ws, uint32_t (&wv)[2][WPL]) const {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      if constexpr (BITS == 2) {
+        const u32x2_t u = *reinterpret_cast<const u32x2_t*>(ws + w_lds[nb]);
+        wv[nb][0] = u.x;
+        wv[nb][1] = u.y;
       } else {
 #pragma unroll
         for (int q = 0; q < WPL / 4; ++q) {
-          const u32x4_t u = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[nb] + q * 16, so, 0));
-          st.w[nb][4 * q] = u.x;
-          st.w[nb][4 * q + 1] = u.y;
-          st.w[nb][4 * q + 2] = u.z;
-          st.w[nb][4 * q + 3] = u.w;
+          // 8-bit: the row's second 16-byte piece of this half sits one
+          // swizzle step away (piece index c ^ swizzle, c = 2 half + q)
+          const int o = BITS == 8 ? w_lds[nb] + (((2 * half + q) ^ ((w_lds[nb] >> 8) & 3)) << 4) : w_lds[nb];
+          const u32x4_t u = *reinterpret_cast<const u32x4_t*>(ws + o);
+          wv[nb][4 * q] = u.x;
+          wv[nb][4 * q + 1] = u.y;
+          wv[nb][4 * q + 2] = u.z;
+          wv[nb][4 * q + 3] = u.w;
         }
       }
-#pragma unroll
-      for (int j = 0; j < PS; ++j) st.s[nb][j] = __builtin_amdgcn_raw_buffer_load_b32(rs, s_off[nb] + j * 4, sg, 0);
     }
   }
-
-  // x chunk i of this thread lands at LDS byte a_dst + i*4096 of a stage:
-  // row 32i + t/8, position t%8 (already swizzled on the global side)
-  __device__ __forceinline__ void store_x(unsigned char* sA, const u32x4_t (&xr)[A_DMA]) const {
-#pragma unroll
-    for (int i = 0; i < A_DMA; ++i) *reinterpret_cast<u32x4_t*>(sA + a_dst + i * 4096) = xr[i];
-  }
-
-  __device__ __forceinline__ void read_a(const unsigned char* __restrict__ sA, int s, f16x8_t (&af)[MB]) const {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int r = mb * 32 + l32;
-      af[mb] = *reinterpret_cast<const f16x8_t*>(sA + r * 128 + (((4 * half + s) ^ swz(r)) << 4));
-    }
-  }
-
-  // B fragments of the 16-column step s for both n blocks: one per (code
-  // piece, scale piece)
-  static constexpr int NF = D::NPIECE * PS;
-  __device__ __forceinline__ void decode_b(const St& st, int s, uint32_t magic, f16x8_t (&bf)[2][NF]) const {
+  __device__ __forceinline__ void decode_b(const uint32_t (&wv)[2][WPL], const uint32_t (&sc)[2][PS], int s,
+                                           uint32_t magic, f16x8_t (&bf)[2][NF]) const {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       uint32_t wd[2];
       if constexpr (BITS == 4) {
-        wd[0] = st.w[nb][s];
+        wd[0] = wv[nb][s];
       } else if constexpr (BITS == 8) {
-        wd[0] = st.w[nb][2 * s];
-        wd[1] = st.w[nb][2 * s + 1];
+        wd[0] = wv[nb][2 * s];
+        wd[1] = wv[nb][2 * s + 1];
       } else {
-        wd[0] = st.w[nb][s >> 1];
+        wd[0] = wv[nb][s >> 1];
       }
       f16x2_t vv[D::NPIECE][4];
       D::pieces(wd, s & 1, magic, vv);
@@ -421,7 +470,7 @@ struct Pipe {
       for (int a = 0; a < D::NPIECE; ++a)
 #pragma unroll
         for (int j = 0; j < PS; ++j) {
-          f16x2_t sj = h2(st.s[nb][j]);  // (s, s)
+          f16x2_t sj = h2(sc[nb][j]);
           if (D::piece_mult(a) != 1.f) sj = sj * f16x2_t{(_Float16)16.f, (_Float16)16.f};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -432,7 +481,6 @@ struct Pipe {
         }
     }
   }
-
   __device__ __forceinline__ void mfma_b(const f16x8_t (&af)[MB], const f16x8_t (&bf)[2][NF],
                                          f32x16_t (&acc)[MB][2]) const {
 #pragma unroll
@@ -443,85 +491,70 @@ struct Pipe {
         for (int mb = 0; mb < MB; ++mb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mb], bf[nb][f], acc[mb][nb], 0, 0, 0);
   }
-
-  // Scheduling of one step: its MFMAs with the next step's decode (VALU)
-  // and the A reads two steps ahead (DS) spread between them, so VALU and
-  // LDS work co-issue with the matrix pipe instead of following it.
   static constexpr int N_MFMA = 2 * NF * MB;
-  template <int NVALU, int NDS>
+  // one MFMA at a time, with the VALU, DS reads and vector-memory loads of
+  // the same region spread between them
+  template <int NVALU, int NDS, int NVM = 0>
   static __device__ __forceinline__ void interleave() {
     constexpr int per = (NVALU + N_MFMA - 1) / N_MFMA;
+    constexpr int vper = (NVM + N_MFMA - 1) / N_MFMA;
 #pragma unroll
     for (int i = 0; i < N_MFMA; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // one MFMA
       if (per > 0) __builtin_amdgcn_sched_group_barrier(0x002, per, 0);  // VALU
       if (i < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
+      if (vper > 0 && i * vper < NVM) __builtin_amdgcn_sched_group_barrier(0x020, vper, 0);  // VMEM read
     }
   }
-
-  // The four 16-column steps of a tile, software-pipelined: step s runs its
-  // MFMAs while step s+1's B fragments are decoded and its A fragments are
-  // read from LDS.  a0/b0 hold step 0 of this tile on entry, and step 0 of
-  // the next tile (stage sAn, ring entry stn) on exit.
-  __device__ __forceinline__ void compute(const St& st, const unsigned char* __restrict__ sA, const St& stn,
-                                          const unsigned char* __restrict__ sAn, uint32_t magic,
-                                          f16x8_t (&a0)[MB], f16x8_t (&b0)[2][NF], f32x16_t (&acc)[MB][2]) const {
-    constexpr int DEC = 2 * NF * 16;  // VALU ops of one step's decode, roughly
-    f16x8_t a1[MB];
-    f16x8_t b1[2][NF];
-    read_a(sA, 1, a1);
-    decode_b(st, 1, magic, b1);
-    mfma_b(a0, b0, acc);
-    interleave<DEC, MB>();
-    __builtin_amdgcn_sched_barrier(0);
-    read_a(sA, 2, a0);
-    decode_b(st, 2, magic, b0);
-    mfma_b(a1, b1, acc);
-    interleave<DEC, MB>();
-    __builtin_amdgcn_sched_barrier(0);
-    read_a(sA, 3, a1);
-    decode_b(st, 3, magic, b1);
-    mfma_b(a0, b0, acc);
-    interleave<DEC, MB>();
-    __builtin_amdgcn_sched_barrier(0);
-    read_a(sAn, 0, a0);
-    decode_b(stn, 0, magic, b0);
-    mfma_b(a1, b1, acc);
-    interleave<DEC, MB>();
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  // One K tile kt (stage kt%4, ring entry kt%4):
-  //   barrier                 tile kt+1's x (stored last step) visible to all
-  //                           waves; everyone done with tile kt-1
-  //   store x of tile kt+2    registers loaded last step -> stage (kt+2)%4
-  //   issue tile kt+3         x into registers, weights/scales into the ring
-  //   compute tile kt         ending with step 0 of tile kt+1 prepared
-  // Loads past the last tile re-read the last tile and land nowhere that is
-  // read, so the step has no branch.  S = kt % 4, a compile-time constant,
-  // so the LDS stage offsets are immediates.
+  // One K tile kt in stage / ring entry S = kt % 3:
+  //   wait      this wave's copies of tile kt have landed (tile kt+1's may
+  //             still be in flight) and its LDS reads are done
+  //   barrier   so every wave's are: tile kt in LDS, stage (kt+2)%3 free
+  //   compute   its four 16-code steps, each step's MFMAs with the next
+  //             step's A reads and decode spread between them; the loads
+  //             of tile kt+2 (into stage (kt+2)%3) go out between the first
+  //             step's MFMAs, not as one burst that would stall the wave
+  //             behind a full address queue
   template <int S>
-  __device__ __forceinline__ void step(int kt, const St& cur, const St& nxt, St& fut, unsigned char* lds,
-                                       u32x4_t (&xr)[A_DMA], uint32_t magic, f16x8_t (&a0)[MB], f16x8_t (&b0)[2][NF],
-                                       f32x16_t (&acc)[MB][2]) const {
-    constexpr int SB = MB * 32 * 128;  // bytes of one stage
-    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0): own LDS writes done
+  __device__ __forceinline__ void step(int kt, unsigned char* const (&xs)[3], unsigned char* const (&ws)[3],
+                                       uint32_t (&sc)[3][2][PS], uint32_t magic, f32x16_t (&acc)[MB][2]) const {
+    __builtin_amdgcn_s_waitcnt((VM_TILE & 15) | (7 << 4) | (0 << 8) | ((VM_TILE >> 4) << 14));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    store_x(lds + ((S + 2) & 3) * SB, xr);
-    issue_x(kt + 3, xr);   // x three tiles ahead (L2), stored next step
-    issue_w(kt + 3, fut);  // weights three tiles ahead (HBM)
-    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
-    compute(cur, lds + S * SB, nxt, lds + ((S + 1) & 3) * SB, magic, a0, b0, acc);
+    constexpr int DEC = 2 * NF * 16;
+    const unsigned char* X = xs[S];
+    uint32_t wv[2][WPL];
+    read_w(ws[S], wv);
+    f16x8_t a0[MB], a1[MB];
+    f16x8_t b0[2][NF], b1[2][NF];
+    read_a(X, 0, a0);
+    decode_b(wv, sc[S], 0, magic, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_a(X, 1, a1);
+    decode_b(wv, sc[S], 1, magic, b1);
+    issue(kt + 2, xs[(S + 2) % 3], ws[(S + 2) % 3], sc[(S + 2) % 3]);
+    mfma_b(a0, b0, acc);
+    interleave<DEC, MB, VM_TILE>();
+    __builtin_amdgcn_sched_barrier(0);
+    read_a(X, 2, a0);
+    decode_b(wv, sc[S], 2, magic, b0);
+    mfma_b(a1, b1, acc);
+    interleave<DEC, MB>();
+    __builtin_amdgcn_sched_barrier(0);
+    read_a(X, 3, a1);
+    decode_b(wv, sc[S], 3, magic, b1);
+    mfma_b(a0, b0, acc);
+    interleave<DEC, MB>();
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_b(a1, b1, acc);
+    __builtin_amdgcn_sched_barrier(0);
   }
 };
 
 template <int BITS, int PS, int MB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_affine_kernel(GemmParams p) {
-  using St = Stage<BITS, PS, MB>;
-  constexpr int BM = MB * 32;
-  constexpr int WPL = BITS;
-  constexpr int STAGE_BYTES = BM * 128; // one x tile, 64 fp16 per row, no padding
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_affine_kernel(GemmParams p) {
+  using GK = Gemm<BITS, PS, MB>;
+  constexpr int BM = GK::BM, XB = GK::XB, WB = GK::WB, RB = GK::RB;
 
   const int b = blockIdx.x;
   const int vs = (b & 7) * p.per_xcd + (b >> 3);
@@ -529,14 +562,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int v = vs / p.S, sp = vs % p.S;
   const int tm = v / p.Tn, tn = v % p.Tn;
   const int m0 = tm * BM, n0 = tn * BN;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l32 = lane & 31, half = lane >> 5;
-  // K tiles [kt0, kt1) of split sp
+  const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
   const int nkt_all = p.K / BK, per_split = (nkt_all + p.S - 1) / p.S;
   const int kt0 = sp * per_split, kt1 = min(nkt_all, kt0 + per_split);
 
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char x0[XB];
+  __shared__ __attribute__((aligned(1024))) unsigned char x1[XB];
+  __shared__ __attribute__((aligned(1024))) unsigned char x2[XB];
+  __shared__ __attribute__((aligned(1024))) unsigned char w0[WB];
+  __shared__ __attribute__((aligned(1024))) unsigned char w1[WB];
+  __shared__ __attribute__((aligned(1024))) unsigned char w2[WB];
   __shared__ __attribute__((aligned(16))) int em_s[BM];
-  for (int i = t; i < BM; i += 256) em_s[i] = p.em[m0 + i];
+  for (int i = t; i < BM; i += 512) em_s[i] = p.em[m0 + i];
+  unsigned char* const xs[3] = {x0, x1, x2};
+  unsigned char* const ws[3] = {w0, w1, w2};
 
   f32x16_t acc[MB][2];
 #pragma unroll
@@ -546,80 +587,90 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // ---- buffer resources and per-lane offsets
-  Pipe<BITS, PS, MB> P;
+  GK P;
   const uint32_t row_bytes = (uint32_t)p.K * BITS / 8;
   P.rw = make_rsrc(p.w, (uint32_t)p.N * row_bytes);
-  P.rs = make_rsrc(p.sh, (uint32_t)p.Np * p.ng * PS * 4);
-  P.rx = make_rsrc(p.xh + (long)m0 * p.K, (uint32_t)BM * p.K * 2);  // this row tile's blocks
+  // (uniform values, kept in SGPRs: a buffer resource or soffset the
+  // compiler takes for divergent becomes a per-lane loop around each load)
+  P.Np = __builtin_amdgcn_readfirstlane(p.Np);
+  P.spt = __builtin_amdgcn_readfirstlane(p.G == 32 ? 2 : 1);
+  P.rs = make_rsrc(p.sh, (uint32_t)__builtin_amdgcn_readfirstlane(nkt_all * P.Np * P.spt * PS * 4));
+  P.rx = make_rsrc(p.xh + (long)m0 * p.K, (uint32_t)BM * p.K * 2);
   P.half = half;
   P.l32 = l32;
-  P.gsh = p.gsh;
+  P.wm = wm;
+  P.wave = wave;
+  {
+    // x: lane l of wave w copies chunk 64 w + l (+ 512 i): row r = 8 w + l/8
+    // (+ 64 i), LDS position l % 8, which holds source chunk (l%8)^swz(r)
+    const int r = wave * 8 + (lane >> 3);
+    P.x_off = (uint32_t)r * 128 + (((lane & 7) ^ swz(r)) << 4);
+  }
+  // Code stage layout: row r (of the tile's 256) at r*RB, its 16-byte pieces
+  // XOR-swizzled by row (4-bit: piece ^ (r>>3)&1; 8-bit: piece ^ (r>>2)&3),
+  // so that the 16 lanes of a read phase hit 16 different bank groups.
+  // Copy instruction i of wave w writes W_SZ bytes per lane from byte
+  // w*32*RB + i*64*W_SZ of the stage: lane l's LDS byte is pos = that + l*W_SZ.
+#pragma unroll
+  for (int i = 0; i < GK::W_DMA; ++i) {
+    const int pos = wave * 32 * RB + i * 64 * GK::W_SZ + lane * GK::W_SZ;
+    const int r = pos / RB, in_row = pos % RB;
+    int src = in_row;  // logical byte in the row's RB bytes of this tile
+    if constexpr (BITS == 4) src = ((((in_row >> 4) ^ (r >> 3)) & 1) << 4) | (in_row & 15);
+    if constexpr (BITS == 8) src = ((((in_row >> 4) ^ (r >> 2)) & 3) << 4) | (in_row & 15);
+    const uint32_t n = n0 + r;
+    P.w_goff[i] = n * row_bytes + (uint32_t)src;
+  }
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const uint32_t n = n0 + wave * 64 + nb * 32 + l32;
-    P.w_off[nb] = n * row_bytes + half * WPL * 4;
-    P.s_off[nb] = (n * (uint32_t)p.ng + (p.gsh == 0 ? half : 0)) * PS * 4;
+    const int r = wn * 64 + nb * 32 + l32;  // row in the tile
+    if constexpr (BITS == 4) P.w_lds[nb] = r * RB + (((half ^ (r >> 3)) & 1) << 4);
+    else if constexpr (BITS == 8) P.w_lds[nb] = r * RB;  // pieces picked per half in read_w
+    else P.w_lds[nb] = r * RB + half * 8;
+    const uint32_t n = n0 + r;
+    P.s_off[nb] = ((n * (uint32_t)P.spt + (P.spt == 2 ? half : 0)) * PS) * 4;
   }
-  // x tile chunks: thread t moves chunks q = i*256 + t, i.e. row 32i + t/8,
-  // LDS position t%8, which holds source chunk (t%8)^swz(row); swz(32i + t/8)
-  // does not depend on i.
-  {
-    const int r = t >> 3, pos = t & 7;
-    P.x_off = (uint32_t)r * 128 + ((pos ^ swz(r)) << 4);  // inside the contiguous BM x 64 block
-    P.a_dst = t * 16;
-  }
-
   const int nkt = kt1 - kt0;
   P.kbase = kt0;
   P.last_kt = nkt - 1;
-  St st0, st1, st2, st3;
-  u32x4_t xr[MB];
-  // prologue: x of tiles 0 and 1 in LDS, tile 2 in registers, weights of
-  // tiles 0..2 in the ring, step 0 of tile 0 prepared
-  P.issue_x(0, xr);
-  P.issue_w(0, st0);
-  P.issue_w(1, st1);
-  P.issue_w(2, st2);
-  P.store_x(lds, xr);
-  P.issue_x(1, xr);
-  P.store_x(lds + STAGE_BYTES, xr);
-  P.issue_x(2, xr);
-  __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
 
-  // ---- main loop
+  uint32_t sc[3][2][PS];
+  P.issue(0, xs[0], ws[0], sc[0]);
+  P.issue(1, xs[1], ws[1], sc[1]);
+
   uint32_t magic = 0x64006400u;
   asm volatile("" : "+v"(magic));
-  f16x8_t a0[MB];
-  f16x8_t b0[2][Pipe<BITS, PS, MB>::NF];
-  P.read_a(lds, 0, a0);
-  P.decode_b(st0, 0, magic, b0);
-  // unrolled by 4 = the ring size and the stage count: every index is static
-  for (int kt = 0; kt < nkt; kt += 4) {
-    P.template step<0>(kt, st0, st1, st3, lds, xr, magic, a0, b0, acc);
-    if (kt + 1 < nkt) P.template step<1>(kt + 1, st1, st2, st0, lds, xr, magic, a0, b0, acc);
-    if (kt + 2 < nkt) P.template step<2>(kt + 2, st2, st3, st1, lds, xr, magic, a0, b0, acc);
-    if (kt + 3 < nkt) P.template step<3>(kt + 3, st3, st0, st2, lds, xr, magic, a0, b0, acc);
+  // whole rounds of three tiles with no branch inside (so the compiler's
+  // count of loads in flight is the same on every path into a step), then
+  // the last one or two tiles
+  int kt = 0;
+  for (; kt + 3 <= nkt; kt += 3) {
+    P.template step<0>(kt, xs, ws, sc, magic, acc);
+    P.template step<1>(kt + 1, xs, ws, sc, magic, acc);
+    P.template step<2>(kt + 2, xs, ws, sc, magic, acc);
   }
+  if (kt < nkt) P.template step<0>(kt, xs, ws, sc, magic, acc);
+  if (kt + 1 < nkt) P.template step<1>(kt + 1, xs, ws, sc, magic, acc);
+  // copies into LDS still in flight (the prefetches past the last tile)
+  // must land before the workgroup's LDS can go to another workgroup
+  __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8) | (0 << 14));
 
+  const int row0 = wm * 32 * MB;  // this wave's first row in the tile
   // ---- tail: sum_g xs * cb on bf16 MFMA, operands straight from global
-  // (L2-resident), in the first split only.  It runs after the main loop so
-  // that its loads do not blur the compiler's count of outstanding loads at
-  // the loop header.
+  // (L2-resident), in the first split only
   if (sp == 0) {
     const uint16_t* tb_row[2];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) tb_row[nb] = p.tB + (long)(n0 + wave * 64 + nb * 32 + l32) * p.Kt + 8 * half;
-    const uint16_t* ta_row = p.tA + (long)(m0 + l32) * p.Kt + 8 * half;
+    for (int nb = 0; nb < 2; ++nb) tb_row[nb] = p.tB + (long)(n0 + wn * 64 + nb * 32 + l32) * p.Kt + 8 * half;
+    const uint16_t* ta_row = p.tA + (long)(m0 + row0 + l32) * p.Kt + 8 * half;
     const long ta_mb = (long)32 * p.Kt;
-    for (int kt = 0; kt < p.Kt; kt += 16) {
+    for (int k = 0; k < p.Kt; k += 16) {
       bf16x8_t bt[2];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) bt[nb] = *reinterpret_cast<const bf16x8_t*>(tb_row[nb] + kt);
+      for (int nb = 0; nb < 2; ++nb) bt[nb] = *reinterpret_cast<const bf16x8_t*>(tb_row[nb] + k);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const bf16x8_t at = *reinterpret_cast<const bf16x8_t*>(ta_row + mb * ta_mb + kt);
+        const bf16x8_t at = *reinterpret_cast<const bf16x8_t*>(ta_row + mb * ta_mb + k);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, bt[nb], acc[mb][nb], 0, 0, 0);
@@ -633,21 +684,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // column past N starts from an out-of-range offset and a row past M lands
   // past the range, so neither is written.
   if (p.S > 1) {
-    // fp32 partial of split sp, scaled (exact: a power of two); rows past M
-    // land past the range, columns past N start from an out-of-range offset
-    const __amdgpu_buffer_rsrc_t rp =
-        make_rsrc(p.part + (long)sp * p.M * p.N, (uint32_t)p.M * p.N * 4);
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.part + (long)sp * p.M * p.N, (uint32_t)p.M * p.N * 4);
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const int n = n0 + wave * 64 + nb * 32 + l32;
+      const int n = n0 + wn * 64 + nb * 32 + l32;
       const bool nok = n < p.N;
       const int e_n = nok ? p.en[n] : 0;
-      const uint32_t vb = nok ? ((uint32_t)(m0 + 4 * half) * p.N + n) * 4u : 0x80000000u;
+      const uint32_t vb = nok ? ((uint32_t)(m0 + row0 + 4 * half) * p.N + n) * 4u : 0x80000000u;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
-          const i32x4_t e4 = *reinterpret_cast<const i32x4_t*>(&em_s[mb * 32 + 8 * rq + 4 * half]);
+          const i32x4_t e4 = *reinterpret_cast<const i32x4_t*>(&em_s[row0 + mb * 32 + 8 * rq + 4 * half]);
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ldexpf(acc[mb][nb][4 * rq + j], e4[j] + e_n)), rp,
@@ -659,15 +707,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.y, (uint32_t)p.M * p.N * 2);
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const int n = n0 + wave * 64 + nb * 32 + l32;
+    const int n = n0 + wn * 64 + nb * 32 + l32;
     const bool nok = n < p.N;
     const int e_n = nok ? p.en[n] : 0;
-    const uint32_t vb = nok ? ((uint32_t)(m0 + 4 * half) * p.N + n) * 2u : 0x80000000u;
+    const uint32_t vb = nok ? ((uint32_t)(m0 + row0 + 4 * half) * p.N + n) * 2u : 0x80000000u;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const i32x4_t e4 = *reinterpret_cast<const i32x4_t*>(&em_s[mb * 32 + 8 * rq + 4 * half]);
+        const i32x4_t e4 = *reinterpret_cast<const i32x4_t*>(&em_s[row0 + mb * 32 + 8 * rq + 4 * half]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float val = ldexpf(acc[mb][nb][4 * rq + j], e4[j] + e_n);
@@ -677,7 +725,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
   }
 }
-
 // ---------------------------------------------------------------------------
 
 // y = the sum of the S fp32 partials, rounded to the activation type
@@ -709,6 +756,9 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
     if ((int64_t)((M + 255) / 256) * tn >= 192) MB = 8;
     else if ((int64_t)((M + 127) / 128) * tn >= 192) MB = 4;
   }
+  // 8-bit codes with three scale pieces do not fit the registers of the
+  // 256-row tile
+  if (BITS == 8 && PS == 3 && MB == 8) MB = 4;
   const int BM = MB * 32;
   const int Mp = (M + BM - 1) / BM * BM, Np = (N + BN - 1) / BN * BN;
   // The epilogue stores padded rows m in [M, Mp) too, relying on their
@@ -731,7 +781,7 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
   const size_t o_xh = 0, s_xh = align256((size_t)Mp * K * 2);
   const size_t o_ta = o_xh + s_xh, s_ta = align256((size_t)Mp * Kt * 2);
   const size_t o_em = o_ta + s_ta, s_em = align256((size_t)Mp * 4);
-  const size_t o_sh = o_em + s_em, s_sh = align256((size_t)Np * ng * PS * 4);
+  const size_t o_sh = o_em + s_em, s_sh = align256((size_t)(K / BK) * Np * (G == 32 ? 2 : 1) * PS * 4);
   const size_t o_tb = o_sh + s_sh, s_tb = align256((size_t)Np * Kt * 2);
   const size_t o_en = o_tb + s_tb, s_en = align256((size_t)Np * 4);
   const size_t o_pt = o_en + s_en, s_pt = S > 1 ? align256((size_t)S * M * N * 4) : 0;
@@ -744,7 +794,7 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
   _Float16* xh = (_Float16*)(scratch + o_xh);
   uint16_t* tA = (uint16_t*)(scratch + o_ta);
   int* em = (int*)(scratch + o_em);
-  f16x2_t* sh = (f16x2_t*)(scratch + o_sh);
+  uint32_t* sh = (uint32_t*)(scratch + o_sh);
   uint16_t* tB = (uint16_t*)(scratch + o_tb);
   int* en = (int*)(scratch + o_en);
 
@@ -770,8 +820,9 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
   pa.Kt = Kt;
   pa.BM = BM;
   pa.Mp = Mp;
+  pa.Np = Np;
   pa.ng = ng;
-  hipLaunchKernelGGL((prep_kernel<BITS, PS>), dim3(Mp + Np / 4), dim3(256), 0, s, pa);
+  hipLaunchKernelGGL((prep_kernel<BITS, PS>), dim3(Mp + Np / PW), dim3(256), 0, s, pa);
 
   GemmParams p;
   p.xh = xh;
@@ -798,12 +849,13 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
   p.part = S > 1 ? (float*)(scratch + o_pt) : nullptr;
   p.per_xcd = (p.Tm * p.Tn * S + 7) / 8;
   const dim3 grid(8 * p.per_xcd);
+  // row tile BM = 32 MB: each wave takes MB/2 32-row blocks
   if (MB == 2)
-    hipLaunchKernelGGL((gemm_affine_kernel<BITS, PS, 2>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((gemm_affine_kernel<BITS, PS, 1>), grid, dim3(512), 0, s, p);
   else if (MB == 4)
-    hipLaunchKernelGGL((gemm_affine_kernel<BITS, PS, 4>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((gemm_affine_kernel<BITS, PS, 2>), grid, dim3(512), 0, s, p);
   else
-    hipLaunchKernelGGL((gemm_affine_kernel<BITS, PS, 8>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((gemm_affine_kernel<BITS, PS, 4>), grid, dim3(512), 0, s, p);
   e = hipGetLastError();
   if (e == hipSuccess && S > 1) {
     const long MN = (long)M * N;
