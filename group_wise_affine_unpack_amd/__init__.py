@@ -18,7 +18,7 @@ from typing import Optional
 import torch
 
 __all__ = ["QaffError", "qmm_affine", "qgemv_affine", "qgemv_affine_grouped", "GroupedGemv", "qmm_gptq", "qgemm_w4a8", "gptq_to_affine_repack",
-           "quantize_pack_affine", "release_workspaces", "library_path", "lib", "STATUS", "DTYPE"]
+           "quantize_pack_affine", "dequantize_affine", "qgemv_affine_silu_gate", "release_workspaces", "library_path", "lib", "STATUS", "DTYPE"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libqaff.so")
@@ -37,6 +37,8 @@ _SIGS = {
     "gptq_to_affine_repack": [_VP] * 7 + [_I32, _VP] + [_I64] * 2 + [_I32, _VP],
     "quantize_pack_affine": [_VP, _I32, _VP, _VP, _VP, _I32, _I64, _I64, _I32, _I32, _VP],
     "qgemv_affine_grouped": [_VP, _I32, _I64] + [_I32] * 5 + [_VP],
+    "dequantize_affine": [_VP] * 4 + [_I64] * 2 + [_I32] * 5 + [_VP],
+    "qgemv_affine_silu_gate": [_VP] * 7 + [_I64] * 3 + [_I32] * 5 + [_VP],
 }
 
 
@@ -131,6 +133,19 @@ def qmm_affine(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Tensor, bi
 def qgemv_affine(x, w_packed, scales, biases, group_size: int, bits: int, k_perm=None, out=None) -> torch.Tensor:
     """As qmm_affine, always on the GEMV kernel (M <= 16)."""
     return _affine("qgemv_affine", x, w_packed, scales, biases, group_size, bits, k_perm, out)
+
+
+def qgemv_affine_silu_gate(gate, up, w_packed, scales, biases, group_size: int, bits: int, resid=None,
+                           out=None) -> torch.Tensor:
+    """y = W (silu(gate) * up) [+ resid] in one launch; gate/up [M, K], M <= 16."""
+    M, K = gate.shape
+    N = w_packed.shape[0]
+    y = out if out is not None else torch.empty((M, N), dtype=gate.dtype, device=gate.device)
+    st = lib().qgemv_affine_silu_gate(_ptr(gate), _ptr(up), _ptr(resid), _ptr(_u32(w_packed)), _ptr(scales),
+                                      _ptr(biases), _ptr(y), M, N, K, group_size, bits, _dt(gate), _dt(scales),
+                                      _dt(biases), _stream(gate.device))
+    _check(st, "qgemv_affine_silu_gate")
+    return y
 
 
 def qgemv_affine_grouped(problems, group_size: int, bits: int, outs=None):
@@ -229,6 +244,17 @@ def gptq_to_affine_repack(qweight: torch.Tensor, qzeros: torch.Tensor, scales: t
                                      _ptr(b), DTYPE[bias_dtype], _ptr(kp), K, N, group_size, _stream(dev))
     _check(st, "gptq_to_affine_repack")
     return w, s, b, kp
+
+
+def dequantize_affine(w_packed: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, K: int, group_size: int,
+                      bits: int, out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The dense weight [N, K] in out_dtype: code*scale + bias, rounded once."""
+    N = w_packed.shape[0]
+    o = out if out is not None else torch.empty((N, K), dtype=out_dtype, device=w_packed.device)
+    st = lib().dequantize_affine(_ptr(_u32(w_packed)), _ptr(scales), _ptr(biases), _ptr(o), N, K, group_size, bits,
+                                 _dt(scales), _dt(biases), _dt(o), _stream(w_packed.device))
+    _check(st, "dequantize_affine")
+    return o
 
 
 def release_workspaces() -> int:

@@ -106,6 +106,8 @@ hipError_t launch_gemv_affine(const AffineArgs& a, hipStream_t s);
 // count problems that share M, G, bits and dtypes, in as few launches as possible
 hipError_t launch_gemv_grouped(const AffineArgs* probs, int count, hipStream_t s);
 hipError_t launch_gemm_affine(const AffineArgs& a, hipStream_t s);
+// y = W (silu(a.x) * up) [+ resid], M <= 16 (a.x is the gate)
+hipError_t launch_gemv_silu(const AffineArgs& a, const void* up, const void* resid, hipStream_t s);
 
 struct GptqArgs {
   const void* x;
@@ -133,6 +135,9 @@ struct W4A8Args {
   int64_t M, N, K;
 };
 hipError_t launch_w4a8(const W4A8Args& a, hipStream_t s);
+
+hipError_t launch_dequant(const uint32_t* w, const void* s, const void* b, void* out, int64_t N, int64_t K, int G,
+                          int bits, int sdt, int bdt, int odt, hipStream_t st);
 
 hipError_t launch_quantize_pack(const void* w, int w_dt, uint32_t* packed, void* scales, void* biases, int sb_dt,
                                 int64_t N, int64_t K, int G, int bits, hipStream_t s);

@@ -211,6 +211,13 @@ struct GemvDesc {
 struct GemvBatch {
   GemvDesc d[MAXP];
   int count, M, gsh, sdt, bdt;
+  // SiLU-gated input (one problem): x of the descriptor is the gate, `up`
+  // the up projection, both [M, K]; `resid` [M, N] or NULL is added to y;
+  // act_f16 is the dtype of gate, up, resid and y (the codes always take
+  // the f16 path there)
+  const void* up;
+  const void* resid;
+  int act_f16;
 };
 static_assert(sizeof(GemvBatch) <= 4096, "kernel arguments are limited to 4 KiB");
 
@@ -250,10 +257,37 @@ __device__ __forceinline__ float wave_sum4(const float (&v)[4]) {
   return t;
 }
 
+// silu(t) = t / (1 + e^-t) in fp32, the quotient as t times the hardware
+// reciprocal (about 1 ulp; e^-t overflows to inf for t below about -88,
+// and t * rcp(inf) = t * 0 is the correct limit -0)
+__device__ __forceinline__ float silu_f32(float t) { return t * __builtin_amdgcn_rcpf(1.f + __expf(-t)); }
+
+// Eight 16-bit gate and up values -> eight f16 values of silu(gate) * up
+__device__ __forceinline__ u32x4_t silu_gate_f16(const u32x4_t& g, const u32x4_t& u, bool act_f16) {
+  u32x4_t h;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float r[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t gb = (g[i] >> (16 * j)) & 0xFFFFu, ub = (u[i] >> (16 * j)) & 0xFFFFu;
+      const float gv = act_f16 ? f16_bits_to_f32(gb) : bf16_bits_to_f32(gb);
+      const float uv = act_f16 ? f16_bits_to_f32(ub) : bf16_bits_to_f32(ub);
+      r[j] = silu_f32(gv) * uv;
+    }
+    h[i] = (uint32_t)f32_to_f16_bits(r[0]) | ((uint32_t)f32_to_f16_bits(r[1]) << 16);
+  }
+  return h;
+}
+
 // R rows per wave (a multiple of 4), MT x rows per pass (1, 2 or 4).
-template <int BITS, bool F16, int MT, int SBM, int R>
+// XM = 0: x as given.  XM = 1: x = silu(gate) * up formed in registers from
+// the gate (the descriptor's x) and B.up, rounded to f16 (F16 is then true),
+// with B.resid added to each output before its one rounding.
+template <int BITS, bool F16, int MT, int SBM, int R, int XM = 0>
 __global__ __launch_bounds__(256) void gemv_affine_kernel(GemvBatch B) {
   static_assert(R % 4 == 0, "rows are reduced in fours");
+  static_assert(XM == 0 || F16, "the gated input takes the f16 code path");
   using C = Codec<BITS, F16>;
 
   // problem of this workgroup (uniform)
@@ -285,6 +319,17 @@ __global__ __launch_bounds__(256) void gemv_affine_kernel(GemvBatch B) {
   const __amdgpu_buffer_rsrc_t rb =
       make_rsrc(static_cast<const char*>(D.b) + (long)row0 * ng * bsz, (uint32_t)(nrows * ng * bsz));
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(D.x, (uint32_t)(M * K * 2));
+  const __amdgpu_buffer_rsrc_t ru = make_rsrc(XM ? B.up : D.x, (uint32_t)(M * K * 2));
+  // output dtype, and the residual added to each output
+  const bool out_f16 = XM ? B.act_f16 != 0 : F16;
+  const uint16_t* resid = XM ? static_cast<const uint16_t*>(B.resid) : nullptr;
+  auto finish = [&](float v, int m, int n) -> uint16_t {
+    if (XM && resid) {
+      const uint32_t rb = resid[(long)m * N + n];
+      v += out_f16 ? f16_bits_to_f32(rb) : bf16_bits_to_f32(rb);
+    }
+    return f32_to_act_bits(v, out_f16);
+  };
 
   uint16_t* y = static_cast<uint16_t*>(D.y);
   __shared__ float red[4][R * MT];
@@ -335,6 +380,17 @@ __global__ __launch_bounds__(256) void gemv_affine_kernel(GemvBatch B) {
         for (int m = 0; m < MT; ++m)
 #pragma unroll
           for (int q = 0; q < C::XR; ++q) raw[m][q] = ld128(rx, xo + 16u * q, (uint32_t)min(m0 + m, M - 1) * K * 2u);
+        if constexpr (XM == 1) {
+          u32x4_t rup[MT][C::XR];
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int q = 0; q < C::XR; ++q) rup[m][q] = ld128(ru, xo + 16u * q, (uint32_t)min(m0 + m, M - 1) * K * 2u);
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int q = 0; q < C::XR; ++q) raw[m][q] = silu_gate_f16(raw[m][q], rup[m][q], B.act_f16 != 0);
+        }
       }
       // every load of the chunk issued before any result is used: otherwise
       // the scheduler may put each parameter's use right after its load,
@@ -382,7 +438,7 @@ __global__ __launch_bounds__(256) void gemv_affine_kernel(GemvBatch B) {
 #pragma unroll
         for (int m = 0; m < MT; ++m)
           if (4 * g + q < nrows && m0 + m < M)
-            y[(long)(m0 + m) * N + row0 + 4 * g + q] = f32_to_act_bits(tot[g][m], F16);
+            y[(long)(m0 + m) * N + row0 + 4 * g + q] = finish(tot[g][m], m0 + m, row0 + 4 * g + q);
     }
   } else {
     if ((lane & 15) == 0) {
@@ -396,7 +452,7 @@ __global__ __launch_bounds__(256) void gemv_affine_kernel(GemvBatch B) {
       const int r = lane / MT, m = lane % MT;
       float v = 0.f;
       for (int p = 0; p < KS; ++p) v += red[rg * KS + p][lane];
-      if (r < nrows && m0 + m < M) y[(long)(m0 + m) * N + row0 + r] = f32_to_act_bits(v, F16);
+      if (r < nrows && m0 + m < M) y[(long)(m0 + m) * N + row0 + r] = finish(v, m0 + m, row0 + r);
     }
     __syncthreads();  // red is written again by the next pass
   }
@@ -737,25 +793,25 @@ void launch_mfma4(int G, dim3 grid, hipStream_t s, const MfmaBatch& b) {
 // x rows from which the MFMA kernel beats the dot2 one
 constexpr int MFMA_MIN_M = 2;
 
-template <int BITS, bool F16, int MT, int R>
+template <int BITS, bool F16, int MT, int R, int XM = 0>
 void launch_r(const GemvBatch& b, int blocks, int sbm, hipStream_t s) {
   if (sbm == 0)
-    hipLaunchKernelGGL((gemv_affine_kernel<BITS, F16, MT, 0, R>), dim3(blocks), dim3(256), 0, s, b);
+    hipLaunchKernelGGL((gemv_affine_kernel<BITS, F16, MT, 0, R, XM>), dim3(blocks), dim3(256), 0, s, b);
   else if (sbm == 1)
-    hipLaunchKernelGGL((gemv_affine_kernel<BITS, F16, MT, 1, R>), dim3(blocks), dim3(256), 0, s, b);
+    hipLaunchKernelGGL((gemv_affine_kernel<BITS, F16, MT, 1, R, XM>), dim3(blocks), dim3(256), 0, s, b);
   else
-    hipLaunchKernelGGL((gemv_affine_kernel<BITS, F16, MT, 2, R>), dim3(blocks), dim3(256), 0, s, b);
+    hipLaunchKernelGGL((gemv_affine_kernel<BITS, F16, MT, 2, R, XM>), dim3(blocks), dim3(256), 0, s, b);
 }
 
-template <int BITS, bool F16>
+template <int BITS, bool F16, int XM = 0>
 void launch_bits(const GemvBatch& b, int blocks, int sbm, int, hipStream_t s) {
   // x rows per pass: 1, 2, or 4 (passes of 4 rows from M = 3 on)
   if (b.M == 1)
-    launch_r<BITS, F16, 1, 4>(b, blocks, sbm, s);
+    launch_r<BITS, F16, 1, 4, XM>(b, blocks, sbm, s);
   else if (b.M == 2)
-    launch_r<BITS, F16, 2, 4>(b, blocks, sbm, s);
+    launch_r<BITS, F16, 2, 4, XM>(b, blocks, sbm, s);
   else
-    launch_r<BITS, F16, 4, 4>(b, blocks, sbm, s);
+    launch_r<BITS, F16, 4, 4, XM>(b, blocks, sbm, s);
 }
 
 // x_p[m, j] = x[m, k_perm[j]] (16-bit values): one thread per 8 outputs of
@@ -1066,5 +1122,48 @@ hipError_t launch_gemv_core(const AffineArgs* probs, int count, hipStream_t s, s
 }  // namespace
 
 hipError_t launch_gemv_affine(const AffineArgs& a, hipStream_t s) { return launch_gemv_grouped(&a, 1, s); }
+
+// y = W (silu(gate) * up) [+ resid]: the dot2 kernel with the gated input
+// formed in registers (XM = 1).  a.x is the gate; rows must be whole
+// 16-byte chunks (K*bits % 128 == 0) and there is no k_perm.
+hipError_t launch_gemv_silu(const AffineArgs& a, const void* up, const void* resid, hipStream_t s) {
+  const int M = (int)a.M;
+  if (M < 1 || M > 16 || (a.K * a.bits) % 128 != 0 || a.k_perm) return hipErrorInvalidValue;
+  if (a.K * a.bits / 8 * 4 >= (int64_t(1) << 31) || a.M * a.K * 2 >= (int64_t(1) << 31)) return hipErrorNotSupported;
+  GemvBatch b{};
+  b.M = M;
+  int gsh = 0;
+  while ((1 << gsh) < a.G) ++gsh;
+  b.gsh = gsh;
+  b.sdt = a.s_dt;
+  b.bdt = a.b_dt;
+  b.up = up;
+  b.resid = resid;
+  b.act_f16 = a.act_dt == F16;
+  // the f16 code path: scales and biases take the any-dtype loader unless
+  // they are both f16
+  const int sbm = (a.s_dt == F16 && a.b_dt == F16) ? 1 : 2;
+  const int64_t L = a.K * a.bits / 128, nch = (L + 63) / 64;
+  const int ksh = nch >= 4 ? 2 : (nch >= 2 ? 1 : 0);
+  const int64_t rows_per_wg = (4 >> ksh) * 4;
+  const int64_t blocks = (a.N + rows_per_wg - 1) / rows_per_wg;
+  if (blocks >= (int64_t(1) << 31)) return hipErrorNotSupported;
+  GemvDesc& d = b.d[b.count++];
+  d.x = a.x;
+  d.w = a.w;
+  d.s = a.scales;
+  d.b = a.biases;
+  d.y = a.y;
+  d.N = (int)a.N;
+  d.K = (int)a.K;
+  d.blk0 = 0;
+  d.ks = ksh;
+  switch (a.bits) {
+    case 2: launch_bits<2, true, 1>(b, (int)blocks, sbm, 4, s); break;
+    case 4: launch_bits<4, true, 1>(b, (int)blocks, sbm, 4, s); break;
+    default: launch_bits<8, true, 1>(b, (int)blocks, sbm, 4, s); break;
+  }
+  return hipGetLastError();
+}
 
 }  // namespace qaff

@@ -108,6 +108,26 @@ int qgemv_affine(const void* x, const uint32_t* w_packed, const void* scales, co
   return ok();
 }
 
+int qgemv_affine_silu_gate(const void* gate, const void* up, const void* resid, const uint32_t* w_packed,
+                           const void* scales, const void* biases, void* y, int64_t M, int64_t N, int64_t K,
+                           int32_t group_size, int32_t bits, int32_t act_dtype, int32_t scale_dtype,
+                           int32_t bias_dtype, void* stream) {
+  int rc = check_affine(gate, w_packed, scales, biases, y, M, N, K, group_size, bits, act_dtype, scale_dtype, bias_dtype);
+  if (rc != QAFF_OK) return rc;
+  if (M > 16) return fail(QAFF_E_INVAL, "qgemv_affine_silu_gate takes M <= 16 (got %lld)", (long long)M);
+  if (M == 0 || N == 0) return ok();
+  if (!up) return fail(QAFF_E_INVAL, "null tensor pointer (up)");
+  if (!aligned16(up)) return fail(QAFF_E_ALIGN, "gate and up must be 16-byte aligned");
+  if ((K * bits) % 128 != 0) return fail(QAFF_E_UNSUPPORTED, "the gated GEMV takes rows of whole 16-byte chunks (K*bits %% 128 == 0)");
+  (void)hipGetLastError();
+  hipError_t e = qaff::launch_gemv_silu(
+      affine_args(gate, w_packed, scales, biases, nullptr, y, M, N, K, group_size, bits, act_dtype, scale_dtype, bias_dtype),
+      up, resid, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return fail(QAFF_E_UNSUPPORTED, "row or activation too large for 32-bit offsets");
+  if (e != hipSuccess) return hip_fail(e, "gated gemv launch");
+  return ok();
+}
+
 int qgemv_affine_grouped(const qaff_gemv_problem* problems, int32_t count, int64_t M, int32_t group_size,
                          int32_t bits, int32_t act_dtype, int32_t scale_dtype, int32_t bias_dtype, void* stream) {
   if (count < 0 || count > 65536) return fail(QAFF_E_INVAL, "count must be in [0, 65536] (got %d)", count);
@@ -248,6 +268,28 @@ int gptq_to_affine_repack(const int32_t* qweight, const int32_t* qzeros, const v
   // perm lives on this host stack frame: the copy must finish before returning
   e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "repack");
+  return ok();
+}
+
+int dequantize_affine(const uint32_t* w_packed, const void* scales, const void* biases, void* out, int64_t N,
+                      int64_t K, int32_t group_size, int32_t bits, int32_t scale_dtype, int32_t bias_dtype,
+                      int32_t out_dtype, void* stream) {
+  if (N < 0 || K <= 0) return fail(QAFF_E_INVAL, "sizes must satisfy N >= 0, K > 0 (got %lld, %lld)", (long long)N, (long long)K);
+  if (N > kMaxDim || K > kMaxDim) return fail(QAFF_E_UNSUPPORTED, "dimension above 2^30");
+  if (!(bits == 2 || bits == 4 || bits == 8)) return fail(QAFF_E_INVAL, "bits must be 2, 4 or 8 (got %d)", bits);
+  if (!group_ok(group_size)) return fail(QAFF_E_INVAL, "group_size must be 32, 64 or 128 (got %d)", group_size);
+  if (K % group_size != 0) return fail(QAFF_E_INVAL, "K=%lld is not a multiple of group_size=%d", (long long)K, group_size);
+  if (!sb_dtype_ok(scale_dtype) || !sb_dtype_ok(bias_dtype) || !sb_dtype_ok(out_dtype))
+    return fail(QAFF_E_INVAL, "scale, bias and output dtypes must be BF16, F16 or F32");
+  if (N == 0) return ok();
+  if (!w_packed || !scales || !biases || !out) return fail(QAFF_E_INVAL, "null tensor pointer");
+  if (!aligned16(out)) return fail(QAFF_E_ALIGN, "out must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(w_packed) & 3u) != 0) return fail(QAFF_E_ALIGN, "w_packed must be 4-byte aligned");
+  (void)hipGetLastError();
+  hipError_t e = qaff::launch_dequant(w_packed, scales, biases, out, N, K, group_size, bits, scale_dtype, bias_dtype,
+                                      out_dtype, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return fail(QAFF_E_UNSUPPORTED, "weight too large");
+  if (e != hipSuccess) return hip_fail(e, "dequantize launch");
   return ok();
 }
 

@@ -114,6 +114,29 @@ int qgemv_affine(const void *x, const uint32_t *w_packed, const void *scales, co
                  int32_t bias_dtype, void *stream);
 
 /*
+ * qgemv_affine_silu_gate - the down projection of a gated MLP in one launch,
+ * with the gated activation never written to memory (mlx_int8.rs API page,
+ * `gemv_silu_gate` and `gemv_silu_gate_resid`):
+ *     h[m,k]  = silu(gate[m,k]) * up[m,k],   silu(t) = t / (1 + e^-t)
+ *     y[m,n]  = sum_k W[n,k] * h[m,k]  (+ resid[m,n] when resid != NULL)
+ * with W as in qmm_affine.
+ *   gate, up  [M, K] act_dtype (BF16 or F16), 16-byte aligned
+ *   resid     [M, N] act_dtype or NULL; y may be the same buffer as resid
+ *             (the residual update y += W h in place)
+ *   y         [M, N] act_dtype; w_packed, scales, biases as in qmm_affine
+ *   M <= 16 (QAFF_E_INVAL otherwise); K*bits % 128 == 0 (QAFF_E_UNSUPPORTED
+ *   otherwise).
+ * h is formed in registers in fp32 (exp and a hardware reciprocal, about
+ * 1 ulp) and rounded to f16 for the dot products, so |h| must stay below
+ * 65504; the codes then take the f16 path whatever act_dtype is.  Accuracy
+ * as for qmm_affine.  Runs the dot2 GEMV kernel at every M.
+ */
+int qgemv_affine_silu_gate(const void *gate, const void *up, const void *resid, const uint32_t *w_packed,
+                           const void *scales, const void *biases, void *y, int64_t M, int64_t N, int64_t K,
+                           int32_t group_size, int32_t bits, int32_t act_dtype, int32_t scale_dtype,
+                           int32_t bias_dtype, void *stream);
+
+/*
  * qgemv_affine_grouped - `count` independent GEMVs y_i = x_i . W_i^T of the
  * qmm_affine form, computed by as few kernel launches as possible (one per
  * 56 problems).  This is the multi-weight decode GEMV: linears that read the
@@ -230,6 +253,24 @@ int gptq_to_affine_repack(const int32_t *qweight, const int32_t *qzeros, const v
 int quantize_pack_affine(const void *w, int32_t w_dtype, uint32_t *w_packed_out, void *scales_out,
                          void *biases_out, int32_t sb_dtype, int64_t N, int64_t K, int32_t group_size,
                          int32_t bits, void *stream);
+
+/*
+ * dequantize_affine - write the whole weight as a dense array (the
+ * standalone dequantization of the mlx_int8.rs API page, `dequantize_to`,
+ * which writes BF16; Transformers "Metal" page, "Dequantize"):
+ *     out[n, k] = RNE_out( q(n,k) * scales[n, k/G] + biases[n, k/G] )
+ * with q as in qmm_affine and the product and sum evaluated exactly (fp64)
+ * before the one rounding to out_dtype (round to nearest, ties to even).
+ *   w_packed [N, K*bits/32] uint32, 4-byte aligned
+ *   scales, biases [N, K/G] in scale_dtype / bias_dtype (BF16, F16, F32)
+ *   out      [N, K] out_dtype (BF16, F16 or F32), 16-byte aligned
+ *   group_size in {32, 64, 128}; bits in {2, 4, 8}; K % G == 0.
+ * Asynchronous on `stream`; allocates nothing.  Memory-bound: reads
+ * N*K*bits/8 + parameter bytes, writes N*K*sizeof(out).
+ */
+int dequantize_affine(const uint32_t *w_packed, const void *scales, const void *biases, void *out, int64_t N,
+                      int64_t K, int32_t group_size, int32_t bits, int32_t scale_dtype, int32_t bias_dtype,
+                      int32_t out_dtype, void *stream);
 
 /*
  * qaff_release_workspaces - free all scratch the library holds: the buffer
