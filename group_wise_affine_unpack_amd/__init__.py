@@ -17,7 +17,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["QaffError", "qmm_affine", "qgemv_affine", "qgemv_affine_grouped", "GroupedGemv", "qmm_gptq", "qgemm_w4a8", "gptq_to_affine_repack",
+__all__ = ["QaffError", "qmm_affine", "qmm_affine_noalloc", "qgemv_affine", "qgemv_affine_grouped", "GroupedGemv", "qmm_gptq", "qgemm_w4a8", "gptq_to_affine_repack",
            "quantize_pack_affine", "dequantize_affine", "qgemv_affine_silu_gate", "release_workspaces", "library_path", "lib", "STATUS", "DTYPE"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -32,6 +32,7 @@ _I64, _I32, _VP = C.c_int64, C.c_int32, C.c_void_p
 _SIGS = {
     "qmm_affine": [_VP] * 6 + [_I64] * 3 + [_I32] * 5 + [_VP],
     "qgemv_affine": [_VP] * 6 + [_I64] * 3 + [_I32] * 5 + [_VP],
+    "qmm_affine_noalloc": [_VP] * 6 + [_I64] * 3 + [_I32] * 5 + [_VP],
     "qmm_gptq": [_VP] * 6 + [_I64] * 3 + [_I32, _VP],
     "qgemm_w4a8": [_VP] * 7 + [_I64] * 3 + [_VP],
     "gptq_to_affine_repack": [_VP] * 7 + [_I32, _VP] + [_I64] * 2 + [_I32, _VP],
@@ -128,6 +129,13 @@ def qmm_affine(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Tensor, bi
                out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """y[M,N] = x[M,K] . W^T, W[n,k] = code*scale[n,k/G] + bias[n,k/G]."""
     return _affine("qmm_affine", x, w_packed, scales, biases, group_size, bits, k_perm, out)
+
+
+def qmm_affine_noalloc(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor,
+                       group_size: int, bits: int, k_perm: Optional[torch.Tensor] = None,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """As qmm_affine, with the library's fixed scratch array (no device allocation)."""
+    return _affine("qmm_affine_noalloc", x, w_packed, scales, biases, group_size, bits, k_perm, out)
 
 
 def qgemv_affine(x, w_packed, scales, biases, group_size: int, bits: int, k_perm=None, out=None) -> torch.Tensor:

@@ -93,6 +93,11 @@ struct AffineArgs {
 // scratch of `bytes` for work on stream s: the stream's cached buffer (see
 // workspace.hip); valid until the next call on the same stream
 hipError_t stream_workspace(hipStream_t s, size_t bytes, void** out);
+// Until scratch_override_end, stream_workspace calls on this thread return
+// `p` (cap bytes) instead of a stream buffer, and fail with
+// hipErrorOutOfMemory for more; _end returns the largest request seen.
+void scratch_override_begin(void* p, size_t cap);
+size_t scratch_override_end();
 // frees every cached and grown-out workspace buffer of every device;
 // *freed = bytes of the cached (current) buffers
 hipError_t release_workspaces(size_t* freed);
@@ -101,6 +106,10 @@ hipError_t release_workspaces(size_t* freed);
 // the current device holds at once, counting at most max_per_cu per CU:
 // resident per CU times the CUs (cached per device, kernel, block and LDS)
 hipError_t resident_workgroups(const void* kernel, int block, size_t lds, int max_per_cu, int64_t* out);
+
+// the device address of the no-allocation entry point's fixed scratch array
+// on the current device (looked up once per device) and its size
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
 
 hipError_t launch_gemv_affine(const AffineArgs& a, hipStream_t s);
 // count problems that share M, G, bits and dtypes, in as few launches as possible

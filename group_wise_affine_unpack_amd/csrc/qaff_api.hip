@@ -171,6 +171,33 @@ int qmm_affine(const void* x, const uint32_t* w_packed, const void* scales, cons
   return ok();
 }
 
+int qmm_affine_noalloc(const void* x, const uint32_t* w_packed, const void* scales, const void* biases,
+                       const int32_t* k_perm, void* y, int64_t M, int64_t N, int64_t K, int32_t group_size,
+                       int32_t bits, int32_t act_dtype, int32_t scale_dtype, int32_t bias_dtype, void* stream) {
+  int rc = check_affine(x, w_packed, scales, biases, y, M, N, K, group_size, bits, act_dtype, scale_dtype, bias_dtype);
+  if (rc != QAFF_OK) return rc;
+  if (M == 0 || N == 0) return ok();
+  const qaff::AffineArgs a =
+      affine_args(x, w_packed, scales, biases, k_perm, y, M, N, K, group_size, bits, act_dtype, scale_dtype, bias_dtype);
+  void* scratch = nullptr;
+  size_t cap = 0;
+  hipError_t e = qaff::noalloc_scratch(&scratch, &cap);
+  if (e != hipSuccess) return hip_fail(e, "looking up the scratch array");
+  (void)hipGetLastError();
+  // the launchers take their scratch from the array instead of the stream
+  // buffer; a request past its size fails in the launcher
+  qaff::scratch_override_begin(scratch, cap);
+  e = (M <= 16) ? qaff::launch_gemv_affine(a, static_cast<hipStream_t>(stream))
+                : qaff::launch_gemm_affine(a, static_cast<hipStream_t>(stream));
+  const size_t need = qaff::scratch_override_end();
+  if (need > cap)
+    return fail(QAFF_E_UNSUPPORTED, "this call needs %zu bytes of scratch; qmm_affine_noalloc has %zu (use qmm_affine)",
+                need, cap);
+  if (e == hipErrorNotSupported) return fail(QAFF_E_UNSUPPORTED, "this shape/dtype combination has no kernel");
+  if (e != hipSuccess) return hip_fail(e, M <= 16 ? "gemv launch" : "gemm launch");
+  return ok();
+}
+
 int qmm_gptq(const void* x, const int32_t* qweight, const int32_t* qzeros, const void* scales, const int32_t* g_idx,
              void* y, int64_t M, int64_t N, int64_t K, int32_t group_size, void* stream) {
   if (M < 0 || N <= 0 || K <= 0) return fail(QAFF_E_INVAL, "sizes must satisfy M >= 0, N > 0, K > 0");

@@ -35,7 +35,8 @@
  *     scratch buffer: their executions must not overlap in time, or they
  *     race and give wrong outputs.  Replay such graphs in stream order on
  *     one stream, or capture them on different streams.
- *     qaff_release_workspaces() frees the scratch.
+ *     qaff_release_workspaces() frees the scratch; qmm_affine_noalloc() is
+ *     the one entry point that never allocates.
  *   - Errors are returned as qaff_status codes; no C++ exception crosses the
  *     ABI.  Argument checks run before any HIP call, so a rejected call has
  *     enqueued nothing.  qaff_last_error() gives a message for the calling
@@ -105,6 +106,32 @@ int qmm_affine(const void *x, const uint32_t *w_packed, const void *scales, cons
                const int32_t *k_perm, void *y, int64_t M, int64_t N, int64_t K,
                int32_t group_size, int32_t bits, int32_t act_dtype, int32_t scale_dtype,
                int32_t bias_dtype, void *stream);
+
+/*
+ * qmm_affine_noalloc - qmm_affine for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, dispatch, kernels and result as
+ * qmm_affine (bit for bit), but its scratch (GEMM pre-pass buffers, split-K
+ * partials, permuted x for k_perm) is a fixed device array of
+ * QAFF_NOALLOC_SCRATCH_BYTES inside the library, one per device, held from
+ * the library's loading until the process ends.  The call never allocates
+ * or frees device memory and so may also be captured into a graph without
+ * an eager call first.
+ *   A call needing more scratch than the array holds returns
+ *   QAFF_E_UNSUPPORTED (the message gives the size it needed); it may have
+ *   enqueued kernels that wrote only the array, never y.  The 4-bit prefill
+ *   at M = 2048, K = 4096 needs about 26 MiB; M <= 16 needs at most
+ *   M*K*2 bytes (k_perm) plus split-K partials.
+ *   Every call on a device shares that device's array, and it keeps the
+ *   last call's contents (no kernel relies on it starting at zero): calls
+ *   whose executions overlap on one device (other streams, concurrent
+ *   graph replays) race on it and give wrong outputs.  Serialize them.
+ */
+#define QAFF_NOALLOC_SCRATCH_BYTES (64u << 20)
+int qmm_affine_noalloc(const void *x, const uint32_t *w_packed, const void *scales, const void *biases,
+                       const int32_t *k_perm, void *y, int64_t M, int64_t N, int64_t K,
+                       int32_t group_size, int32_t bits, int32_t act_dtype, int32_t scale_dtype,
+                       int32_t bias_dtype, void *stream);
 
 /* qgemv_affine - same arguments and result as qmm_affine, but always runs the
  * GEMV kernel; M must be <= 16 (QAFF_E_INVAL otherwise). */
