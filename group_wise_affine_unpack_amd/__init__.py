@@ -18,7 +18,8 @@ from typing import Optional
 import torch
 
 __all__ = ["QaffError", "qmm_affine", "qmm_affine_noalloc", "qgemv_affine", "qgemv_affine_grouped", "GroupedGemv", "qmm_gptq", "qgemm_w4a8", "gptq_to_affine_repack",
-           "quantize_pack_affine", "dequantize_affine", "qgemv_affine_silu_gate", "release_workspaces", "library_path", "lib", "STATUS", "DTYPE"]
+           "quantize_pack_affine", "dequantize_affine", "qgemv_affine_silu_gate", "smoothquant_factors",
+           "w4a8_quantize_weights", "qgemm_w4a8_smooth", "release_workspaces", "library_path", "lib", "STATUS", "DTYPE"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libqaff.so")
@@ -40,6 +41,10 @@ _SIGS = {
     "qgemv_affine_grouped": [_VP, _I32, _I64] + [_I32] * 5 + [_VP],
     "dequantize_affine": [_VP] * 4 + [_I64] * 2 + [_I32] * 5 + [_VP],
     "qgemv_affine_silu_gate": [_VP] * 7 + [_I64] * 3 + [_I32] * 5 + [_VP],
+    "smoothquant_factors": [_VP, _VP, _I32, C.c_double, _VP, _I64, _I64, _VP],
+    "w4a8_quantize_weights": [_VP, _I32, _VP, _VP, _VP, _I64, _I64, _VP],
+    "qgemm_w4a8_smooth": [_VP] * 8 + [_I64] * 3 + [_VP],
+    "qaff_stream_read": [_VP, C.c_uint64, _VP, _I32, _VP],
 }
 
 
@@ -238,6 +243,41 @@ def qgemm_w4a8(x: torch.Tensor, w_q4: torch.Tensor, s_w: torch.Tensor, want_acc:
     return y, x_q, s_x, acc
 
 
+def smoothquant_factors(act_absmax: torch.Tensor, w: torch.Tensor, alpha: float = 0.5) -> torch.Tensor:
+    """Per-input-channel smoothing factors s [K] f32 from calibration maxima of x and the dense weight w [N, K]."""
+    N, K = w.shape
+    s = torch.empty((K,), dtype=torch.float32, device=w.device)
+    st = lib().smoothquant_factors(_ptr(act_absmax), _ptr(w), _dt(w), float(alpha), _ptr(s), N, K, _stream(w.device))
+    _check(st, "smoothquant_factors")
+    return s
+
+
+def w4a8_quantize_weights(w: torch.Tensor, smooth: Optional[torch.Tensor] = None):
+    """(w_q4 [N, K/8] int32, s_w [N] f16): the per-channel int4 weight, smoothing folded in when given."""
+    N, K = w.shape
+    wq = torch.empty((N, K // 8), dtype=torch.int32, device=w.device)
+    sw = torch.empty((N,), dtype=torch.float16, device=w.device)
+    st = lib().w4a8_quantize_weights(_ptr(w), _dt(w), _ptr(smooth), _ptr(wq), _ptr(sw), N, K, _stream(w.device))
+    _check(st, "w4a8_quantize_weights")
+    return wq, sw
+
+
+def qgemm_w4a8_smooth(x: torch.Tensor, smooth: torch.Tensor, w_q4: torch.Tensor, s_w: torch.Tensor,
+                      want_acc: bool = False):
+    """qgemm_w4a8 on x / smooth: (y, x_q, s_x, acc or None)."""
+    M, K = x.shape
+    N = w_q4.shape[0]
+    dev = x.device
+    y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    x_q = torch.empty((M, K), dtype=torch.int8, device=dev)
+    s_x = torch.empty((M,), dtype=torch.float32, device=dev)
+    acc = torch.empty((M, N), dtype=torch.int32, device=dev) if want_acc else None
+    st = lib().qgemm_w4a8_smooth(_ptr(x), _ptr(smooth), _ptr(_u32(w_q4)), _ptr(s_w), _ptr(y), _ptr(x_q), _ptr(s_x),
+                                 _ptr(acc), M, N, K, _stream(dev))
+    _check(st, "qgemm_w4a8_smooth")
+    return y, x_q, s_x, acc
+
+
 def gptq_to_affine_repack(qweight: torch.Tensor, qzeros: torch.Tensor, scales: torch.Tensor,
                           g_idx: Optional[torch.Tensor], group_size: int, bias_dtype=torch.float32):
     """Returns (w_packed [N,K/8] int32, scales [N,K/G] f16, biases [N,K/G] bias_dtype, k_perm [K] int32)."""
@@ -263,6 +303,12 @@ def dequantize_affine(w_packed: torch.Tensor, scales: torch.Tensor, biases: torc
                                  _dt(scales), _dt(biases), _dt(o), _stream(w_packed.device))
     _check(st, "dequantize_affine")
     return o
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, blocks: int) -> None:
+    """Measurement helper: read all of `buf` once (qaff_stream_read)."""
+    st = lib().qaff_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), blocks, _stream(buf.device))
+    _check(st, "qaff_stream_read")
 
 
 def release_workspaces() -> int:

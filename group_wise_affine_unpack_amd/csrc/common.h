@@ -144,9 +144,22 @@ struct W4A8Args {
   int64_t M, N, K;
 };
 hipError_t launch_w4a8(const W4A8Args& a, hipStream_t s);
+// the integer product and epilogue of W4A8 from x_q and s_x already written
+hipError_t launch_w4a8_product(const W4A8Args& a, hipStream_t s);
+// SmoothQuant: factors, weight quantization (optional fold), smoothed quantizer
+hipError_t launch_smooth_factors(const float* amax, const void* w, int w_dt, int64_t N, int64_t K, double alpha,
+                                 float* s, hipStream_t st);
+hipError_t launch_w4a8_weights(const void* w, int w_dt, const float* smooth, int64_t N, int64_t K, uint32_t* w_q4,
+                               uint16_t* s_w, hipStream_t st);
+hipError_t launch_smooth_quant(const void* x, const float* smooth, int64_t M, int64_t K, int8_t* x_q, float* s_x,
+                               hipStream_t st);
 
 hipError_t launch_dequant(const uint32_t* w, const void* s, const void* b, void* out, int64_t N, int64_t K, int G,
                           int bits, int sdt, int bdt, int odt, hipStream_t st);
+
+// streaming read of `bytes` (a multiple of 16) by `blocks` x 256 threads;
+// sink holds blocks*256 words
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int blocks, hipStream_t s);
 
 hipError_t launch_quantize_pack(const void* w, int w_dt, uint32_t* packed, void* scales, void* biases, int sb_dt,
                                 int64_t N, int64_t K, int G, int bits, hipStream_t s);

@@ -82,6 +82,17 @@ extern "C" {
 
 const char* qaff_last_error(void) { return g_last_error.c_str(); }
 
+int qaff_stream_read(const void* src, uint64_t bytes, uint32_t* sink, int32_t blocks, void* stream) {
+  if (!src || !sink) return fail(QAFF_E_INVAL, "null pointer");
+  if (bytes == 0 || bytes % 16) return fail(QAFF_E_INVAL, "bytes must be a positive multiple of 16");
+  if (blocks <= 0) return fail(QAFF_E_INVAL, "blocks must be positive");
+  if (!aligned16(src)) return fail(QAFF_E_ALIGN, "src must be 16-byte aligned");
+  (void)hipGetLastError();
+  hipError_t e = qaff::launch_stream_read(src, (size_t)bytes, sink, blocks, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "stream read launch");
+  return ok();
+}
+
 int qaff_version(void) { return 200; }
 
 int qaff_release_workspaces(uint64_t* freed_bytes) {
@@ -250,6 +261,65 @@ int qgemm_w4a8(const void* x, const uint32_t* w_q4, const void* s_w, void* y, in
   hipError_t e = qaff::launch_w4a8(a, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return fail(QAFF_E_UNSUPPORTED, "this shape has no kernel");
   if (e != hipSuccess) return hip_fail(e, "w4a8 launch");
+  return ok();
+}
+
+int qgemm_w4a8_smooth(const void* x, const float* smooth, const uint32_t* w_q4, const void* s_w, void* y,
+                      int8_t* x_q, float* s_x, int32_t* acc_out, int64_t M, int64_t N, int64_t K, void* stream) {
+  if (M < 0 || N <= 0 || K <= 0) return fail(QAFF_E_INVAL, "sizes must satisfy M >= 0, N > 0, K > 0");
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return fail(QAFF_E_UNSUPPORTED, "dimension above 2^30");
+  if (K % 32) return fail(QAFF_E_INVAL, "K must be a multiple of 32 (got %lld)", (long long)K);
+  if (K > (int64_t(1) << 17)) return fail(QAFF_E_UNSUPPORTED, "K above 131072 could overflow the int32 accumulator");
+  if (M == 0) return ok();
+  if (!x || !smooth || !w_q4 || !s_w || !y || !x_q || !s_x) return fail(QAFF_E_INVAL, "null tensor pointer");
+  if (!aligned16(x) || !aligned16(w_q4) || !aligned16(x_q)) return fail(QAFF_E_ALIGN, "x, w_q4 and x_q must be 16-byte aligned");
+  qaff::W4A8Args a;
+  a.x = x;
+  a.w = w_q4;
+  a.s_w = s_w;
+  a.y = y;
+  a.x_q = x_q;
+  a.s_x = s_x;
+  a.acc = acc_out;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  if (N * K / 2 >= (int64_t(1) << 31) || K * 256 >= (int64_t(1) << 31))
+    return fail(QAFF_E_UNSUPPORTED, "weight too large for 32-bit offsets");
+  (void)hipGetLastError();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = qaff::launch_smooth_quant(x, smooth, M, K, x_q, s_x, st);
+  if (e == hipSuccess) e = qaff::launch_w4a8_product(a, st);
+  if (e == hipErrorNotSupported) return fail(QAFF_E_UNSUPPORTED, "this shape has no kernel");
+  if (e != hipSuccess) return hip_fail(e, "smoothed w4a8 launch");
+  return ok();
+}
+
+int smoothquant_factors(const float* act_absmax, const void* w, int32_t w_dtype, double alpha, float* smooth_out,
+                        int64_t N, int64_t K, void* stream) {
+  if (N <= 0 || K <= 0) return fail(QAFF_E_INVAL, "sizes must satisfy N > 0, K > 0");
+  if (N > kMaxDim || K > kMaxDim) return fail(QAFF_E_UNSUPPORTED, "dimension above 2^30");
+  if (!sb_dtype_ok(w_dtype)) return fail(QAFF_E_INVAL, "w_dtype must be BF16, F16 or F32");
+  if (!(alpha >= 0.0 && alpha <= 1.0)) return fail(QAFF_E_INVAL, "alpha must lie in [0, 1]");
+  if (!act_absmax || !w || !smooth_out) return fail(QAFF_E_INVAL, "null tensor pointer");
+  (void)hipGetLastError();
+  hipError_t e = qaff::launch_smooth_factors(act_absmax, w, w_dtype, N, K, alpha, smooth_out,
+                                             static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "smoothing factors launch");
+  return ok();
+}
+
+int w4a8_quantize_weights(const void* w, int32_t w_dtype, const float* smooth, uint32_t* w_q4_out, void* s_w_out,
+                          int64_t N, int64_t K, void* stream) {
+  if (N <= 0 || K <= 0) return fail(QAFF_E_INVAL, "sizes must satisfy N > 0, K > 0");
+  if (N > kMaxDim || K > kMaxDim) return fail(QAFF_E_UNSUPPORTED, "dimension above 2^30");
+  if (K % 8) return fail(QAFF_E_INVAL, "K must be a multiple of 8 (got %lld)", (long long)K);
+  if (!sb_dtype_ok(w_dtype)) return fail(QAFF_E_INVAL, "w_dtype must be BF16, F16 or F32");
+  if (!w || !w_q4_out || !s_w_out) return fail(QAFF_E_INVAL, "null tensor pointer");
+  (void)hipGetLastError();
+  hipError_t e = qaff::launch_w4a8_weights(w, w_dtype, smooth, N, K, w_q4_out, static_cast<uint16_t*>(s_w_out),
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "w4a8 weight quantization launch");
   return ok();
 }
 

@@ -520,7 +520,9 @@ __global__ __launch_bounds__(256) void w4a8_gemv_kernel(const int8_t* __restrict
                                                         uint16_t* __restrict__ y, int32_t* __restrict__ acc_out, int M,
                                                         int N, int K) {
   const int lane = threadIdx.x & 63;
-  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // the wave index kept uniform: a row base the compiler took for
+  // divergent would put a per-lane loop around every buffer load
+  const int n = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (n >= N) return;  // the whole wave
   const int nch = K / 32;
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + (long)n * (K / 8), (uint32_t)(K / 2));
@@ -757,6 +759,15 @@ hipError_t launch_w4a8(const W4A8Args& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_w4a8_product(a, s);
+}
+
+// The integer product and epilogue from x_q and s_x already in memory: the
+// dot4 GEMV for M <= 16, else the int8 MFMA GEMM (plus the summing pass when
+// K is split).
+hipError_t launch_w4a8_product(const W4A8Args& a, hipStream_t s) {
+  const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
+  hipError_t e = hipSuccess;
   if (M <= 16) {
     const dim3 grid((unsigned)((N + 3) / 4));
     const int8_t* xq = a.x_q;

@@ -247,6 +247,43 @@ int qgemm_w4a8(const void *x, const uint32_t *w_q4, const void *s_w, void *y, in
                int32_t *acc_out, int64_t M, int64_t N, int64_t K, void *stream);
 
 /*
+ * SmoothQuant ahead of W4A8 (TinyGPT "Quantization Expansion", section 3
+ * "SmoothQuant"): a per-input-channel factor s moves activation range into
+ * the weights, y = (x / s) . (s W)^T, so that outlier channels of x no
+ * longer set the per-token int8 scale.  Three calls:
+ *
+ * smoothquant_factors - setup:  smooth_out[k] = act_absmax[k]^alpha /
+ *     max_n |w[n,k]|^(1 - alpha), computed in fp64, stored fp32; a channel
+ *     whose activation or weight maximum is 0 gets 1.
+ *   act_absmax [K] f32: max over calibration tokens of |x[:, k]|, gathered
+ *              by the caller; w [N, K] w_dtype (BF16, F16, F32), the dense
+ *              weight before quantization; alpha in [0, 1] (0.5 usually).
+ *
+ * w4a8_quantize_weights - setup: the per-channel int4 weight of W4A8 from a
+ *     dense weight, with the smoothing folded in when smooth != NULL:
+ *       W'[n,k]  = W[n,k] * smooth[k]                (fp32, nearest even)
+ *       s_w[n]   = f16( max_k |W'[n,k]| / 7 )        (fp32 division, then RNE)
+ *       v[n,k]   = clamp(rint(W'[n,k] / s_w[n]), -8, 7)   (s_w as stored)
+ *   w [N, K] w_dtype; smooth [K] f32 or NULL; w_q4_out [N, K/8] uint32
+ *   (the qgemm_w4a8 layout); s_w_out [N] f16.  K % 8 == 0.  A row of zeros
+ *   gets s_w = 0 and codes 0.  Bit-exact (IEEE divisions, rint to even).
+ *
+ * qgemm_w4a8_smooth - qgemm_w4a8 on the smoothed activations:
+ *       xs[m,k] = f32(x[m,k]) / smooth[k]             (IEEE division)
+ *     then s_x, x_q, acc and y exactly as qgemm_w4a8 defines them, with xs
+ *     in place of x (w_q4 and s_w from w4a8_quantize_weights with the same
+ *     smooth).  smooth [K] f32, finite and nonzero; the other arguments as
+ *     for qgemm_w4a8.  Two launches: the smoothed quantizer, then the
+ *     integer product.
+ */
+int smoothquant_factors(const float *act_absmax, const void *w, int32_t w_dtype, double alpha, float *smooth_out,
+                        int64_t N, int64_t K, void *stream);
+int w4a8_quantize_weights(const void *w, int32_t w_dtype, const float *smooth, uint32_t *w_q4_out, void *s_w_out,
+                          int64_t N, int64_t K, void *stream);
+int qgemm_w4a8_smooth(const void *x, const float *smooth, const uint32_t *w_q4, const void *s_w, void *y,
+                      int8_t *x_q, float *s_x, int32_t *acc_out, int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
  * gptq_to_affine_repack - rewrite a GPTQ layer in the affine layout
  * (setup call; it MAY SYNCHRONIZE `stream`: it reads g_idx back to the host
  * to build the permutation and to check it).
@@ -322,6 +359,16 @@ int qaff_release_workspaces(uint64_t *freed_bytes);
 /* Message for the calling thread's last non-OK status ("" if none).  The
  * string is owned by the library and valid until the thread's next call. */
 const char *qaff_last_error(void);
+
+/*
+ * qaff_stream_read - measurement helper, not part of the matmul path: read
+ * `bytes` (a positive multiple of 16) at `src` with non-temporal 16-byte
+ * loads by `blocks` workgroups of 256 threads, and write one word per
+ * thread to `sink` (blocks*256 uint32).  Timing it over a buffer much larger
+ * than the last-level cache gives the device's achievable streaming-read
+ * rate, the ceiling quoted beside the published HBM peak.
+ */
+int qaff_stream_read(const void *src, uint64_t bytes, uint32_t *sink, int32_t blocks, void *stream);
 
 /* Library version, as major*10000 + minor*100 + patch. */
 int qaff_version(void);
