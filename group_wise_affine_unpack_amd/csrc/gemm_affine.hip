@@ -360,8 +360,8 @@ struct Decode {
 //          lanes that decode them (32 rows x 32 bytes per instruction,
 //          duplicated for both row halves) kept the texture units 75% busy
 //          with scattered requests and bounded the whole kernel.
-// Scale pieces (pre-pass layout sh[kt][Np][SPT][PS]) go to registers with
-// one coalesced load per 32 columns and tile, into a 3-entry ring.
+// Scale pieces (pre-pass layout sh[kt][Np][SPT][PS]: a tile's 256 columns
+// are one contiguous run) take the same route, a third small stage.
 // Stages are separate LDS arrays, so the compiler can see that a copy into
 // one stage does not touch the one being read.
 // Rows of W past N are read through offsets past the buffer's range and
@@ -381,18 +381,23 @@ struct Gemm {
   static constexpr int W_SZ = BITS == 2 ? 4 : 16;
   static constexpr int W_DMA = 32 * RB / (64 * W_SZ);
   static constexpr int NF = D::NPIECE * PS;
-  static constexpr int VM_TILE = A_DMA + W_DMA + 2;  // + one scale load per 32 columns
+  // scale pieces of a tile: 256 columns x SPT x PS words (SPT <= 2), copied
+  // 4 bytes a lane, 2 KiB a workgroup per copy
+  static constexpr int S_DMA = PS;
+  static constexpr int SB = S_DMA * 2048;           // bytes of one scale stage
+  static constexpr int VM_TILE = A_DMA + W_DMA + S_DMA;
   static_assert(VM_TILE < 64, "vmcnt field");
   static constexpr int WPL = BITS;                  // words per lane and 32 columns per tile
 
   __amdgpu_buffer_rsrc_t rw, rs, rx;
-  uint32_t x_off, w_goff[W_DMA], s_off[2];
+  uint32_t x_off, w_goff[W_DMA], s_goff[S_DMA];
   int w_lds[2];                                     // this lane's code bytes in a stage, per 32-column block
+  int s_lds[2];                                     // this lane's scale pieces in a stage, per 32-column block
   int half, l32, wm, wave, kbase, last_kt, Np, spt;
 
   // x of tile kt into stage xs: instruction i of wave w fills bytes
   // [(8i + w) KiB, +1 KiB); lane l's piece is chunk 64 (8i + w) + l
-  __device__ __forceinline__ void issue(int kt, unsigned char* xs, unsigned char* ws, uint32_t (&sc)[2][PS]) const {
+  __device__ __forceinline__ void issue(int kt, unsigned char* xs, unsigned char* ws, unsigned char* ss) const {
     kt = kbase + min(kt, last_kt);
 #pragma unroll
     for (int i = 0; i < A_DMA; ++i)
@@ -403,23 +408,20 @@ struct Gemm {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rw, (__attribute__((address_space(3))) void*)(ws + wave * 32 * RB + i * 64 * W_SZ), W_SZ, w_goff[i],
           kt * RB, 0, 0);
+    // the tile's scale pieces: row block n0 .. n0+255 of K tile kt, one
+    // contiguous run of 256*SPT*PS words (lanes past the run copy zeros)
     const int so = __builtin_amdgcn_readfirstlane(kt * Np * spt * PS * 4);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      if constexpr (PS == 1) {
-        sc[nb][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, s_off[nb], so, 0);
-      } else if constexpr (PS == 2) {
-        const u32x2_t u = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, s_off[nb], so, 0));
-        sc[nb][0] = u.x;
-        sc[nb][1] = u.y;
-      } else {
-        typedef __attribute__((ext_vector_type(3))) uint32_t u32x3_t;
-        const u32x3_t u = __builtin_bit_cast(u32x3_t, __builtin_amdgcn_raw_buffer_load_b96(rs, s_off[nb], so, 0));
-        sc[nb][0] = u.x;
-        sc[nb][1] = u.y;
-        sc[nb][2] = u.z;
-      }
-    }
+    for (int i = 0; i < S_DMA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(ss + i * 2048 + wave * 256),
+                                               4, s_goff[i], so, 0, 0);
+  }
+  // this lane's scale pieces of the tile, per 32-column block
+  __device__ __forceinline__ void read_s(const unsigned char* __restrict__ ss, uint32_t (&sc)[2][PS]) const {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int j = 0; j < PS; ++j) sc[nb][j] = *reinterpret_cast<const uint32_t*>(ss + s_lds[nb] + 4 * j);
   }
   __device__ __forceinline__ void read_a(const unsigned char* __restrict__ xs, int s, f16x8_t (&af)[MB]) const {
 #pragma unroll
@@ -515,34 +517,39 @@ struct Gemm {
   //             of tile kt+2 (into stage (kt+2)%3) go out between the first
   //             step's MFMAs, not as one burst that would stall the wave
   //             behind a full address queue
+  // Every load of the loop is a copy into LDS (none writes a VGPR), so the
+  // compiler adds no waits of its own for them: the one wait before the
+  // barrier covers everything.
   template <int S>
   __device__ __forceinline__ void step(int kt, unsigned char* const (&xs)[3], unsigned char* const (&ws)[3],
-                                       uint32_t (&sc)[3][2][PS], uint32_t magic, f32x16_t (&acc)[MB][2]) const {
+                                       unsigned char* const (&ss)[3], uint32_t magic, f32x16_t (&acc)[MB][2]) const {
     __builtin_amdgcn_s_waitcnt((VM_TILE & 15) | (7 << 4) | (0 << 8) | ((VM_TILE >> 4) << 14));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     constexpr int DEC = 2 * NF * 16;
     const unsigned char* X = xs[S];
     uint32_t wv[2][WPL];
+    uint32_t sc[2][PS];
     read_w(ws[S], wv);
+    read_s(ss[S], sc);
     f16x8_t a0[MB], a1[MB];
     f16x8_t b0[2][NF], b1[2][NF];
     read_a(X, 0, a0);
-    decode_b(wv, sc[S], 0, magic, b0);
+    decode_b(wv, sc, 0, magic, b0);
     __builtin_amdgcn_sched_barrier(0);
     read_a(X, 1, a1);
-    decode_b(wv, sc[S], 1, magic, b1);
-    issue(kt + 2, xs[(S + 2) % 3], ws[(S + 2) % 3], sc[(S + 2) % 3]);
+    decode_b(wv, sc, 1, magic, b1);
+    issue(kt + 2, xs[(S + 2) % 3], ws[(S + 2) % 3], ss[(S + 2) % 3]);
     mfma_b(a0, b0, acc);
     interleave<DEC, MB, VM_TILE>();
     __builtin_amdgcn_sched_barrier(0);
     read_a(X, 2, a0);
-    decode_b(wv, sc[S], 2, magic, b0);
+    decode_b(wv, sc, 2, magic, b0);
     mfma_b(a1, b1, acc);
     interleave<DEC, MB>();
     __builtin_amdgcn_sched_barrier(0);
     read_a(X, 3, a1);
-    decode_b(wv, sc[S], 3, magic, b1);
+    decode_b(wv, sc, 3, magic, b1);
     mfma_b(a0, b0, acc);
     interleave<DEC, MB>();
     __builtin_amdgcn_sched_barrier(0);
@@ -574,10 +581,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(1024))) unsigned char w0[WB];
   __shared__ __attribute__((aligned(1024))) unsigned char w1[WB];
   __shared__ __attribute__((aligned(1024))) unsigned char w2[WB];
+  __shared__ __attribute__((aligned(1024))) unsigned char s0[GK::SB];
+  __shared__ __attribute__((aligned(1024))) unsigned char s1[GK::SB];
+  __shared__ __attribute__((aligned(1024))) unsigned char s2[GK::SB];
   __shared__ __attribute__((aligned(16))) int em_s[BM];
   for (int i = t; i < BM; i += 512) em_s[i] = p.em[m0 + i];
   unsigned char* const xs[3] = {x0, x1, x2};
   unsigned char* const ws[3] = {w0, w1, w2};
+  unsigned char* const ss[3] = {s0, s1, s2};
 
   f32x16_t acc[MB][2];
 #pragma unroll
@@ -627,16 +638,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if constexpr (BITS == 4) P.w_lds[nb] = r * RB + (((half ^ (r >> 3)) & 1) << 4);
     else if constexpr (BITS == 8) P.w_lds[nb] = r * RB;  // pieces picked per half in read_w
     else P.w_lds[nb] = r * RB + half * 8;
-    const uint32_t n = n0 + r;
-    P.s_off[nb] = ((n * (uint32_t)P.spt + (P.spt == 2 ? half : 0)) * PS) * 4;
+    P.s_lds[nb] = (r * P.spt + (P.spt == 2 ? half : 0)) * PS * 4;
+  }
+  // scale copy i: lane l of wave w takes bytes 2048 i + 4 (64 w + l) of the
+  // tile's run, which starts at word n0 * SPT * PS of K tile kt's block;
+  // past the run it reads from an out-of-range offset (zeros)
+#pragma unroll
+  for (int i = 0; i < GK::S_DMA; ++i) {
+    const uint32_t run = 256u * P.spt * PS * 4;
+    const uint32_t b = (uint32_t)(2048 * i + 4 * (64 * wave + lane));
+    P.s_goff[i] = b < run ? (uint32_t)n0 * P.spt * PS * 4 + b : 0x80000000u;
   }
   const int nkt = kt1 - kt0;
   P.kbase = kt0;
   P.last_kt = nkt - 1;
 
-  uint32_t sc[3][2][PS];
-  P.issue(0, xs[0], ws[0], sc[0]);
-  P.issue(1, xs[1], ws[1], sc[1]);
+  P.issue(0, xs[0], ws[0], ss[0]);
+  P.issue(1, xs[1], ws[1], ss[1]);
 
   uint32_t magic = 0x64006400u;
   asm volatile("" : "+v"(magic));
@@ -645,12 +663,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // the last one or two tiles
   int kt = 0;
   for (; kt + 3 <= nkt; kt += 3) {
-    P.template step<0>(kt, xs, ws, sc, magic, acc);
-    P.template step<1>(kt + 1, xs, ws, sc, magic, acc);
-    P.template step<2>(kt + 2, xs, ws, sc, magic, acc);
+    P.template step<0>(kt, xs, ws, ss, magic, acc);
+    P.template step<1>(kt + 1, xs, ws, ss, magic, acc);
+    P.template step<2>(kt + 2, xs, ws, ss, magic, acc);
   }
-  if (kt < nkt) P.template step<0>(kt, xs, ws, sc, magic, acc);
-  if (kt + 1 < nkt) P.template step<1>(kt + 1, xs, ws, sc, magic, acc);
+  if (kt < nkt) P.template step<0>(kt, xs, ws, ss, magic, acc);
+  if (kt + 1 < nkt) P.template step<1>(kt + 1, xs, ws, ss, magic, acc);
   // copies into LDS still in flight (the prefetches past the last tile)
   // must land before the workgroup's LDS can go to another workgroup
   __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8) | (0 << 14));
@@ -854,7 +872,7 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((gemm_affine_kernel<BITS, PS, 1>), grid, dim3(512), 0, s, p);
   else if (MB == 4)
     hipLaunchKernelGGL((gemm_affine_kernel<BITS, PS, 2>), grid, dim3(512), 0, s, p);
-  else
+  else if constexpr (!(BITS == 8 && PS == 3))
     hipLaunchKernelGGL((gemm_affine_kernel<BITS, PS, 4>), grid, dim3(512), 0, s, p);
   e = hipGetLastError();
   if (e == hipSuccess && S > 1) {
