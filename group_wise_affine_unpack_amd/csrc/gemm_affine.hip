@@ -82,6 +82,15 @@ __device__ __forceinline__ int exp_of(float v) {
 // xh is tile-blocked: the BM x 64 block of K tile kt of row tile mt is one
 // contiguous 16 KiB..32 KiB piece, row r of it at r*64 elements, so a GEMM
 // step reads a single contiguous block.
+// Tail operands (rows x Kt bf16) are stored in the order the GEMM's MFMA
+// fragments read them: 32-row x 16-column blocks, row block major, 512
+// elements each, element (r, k) of a block at ((k/8)%2)*256 + (r%32)*8 + k%8.
+// One 16-byte load per lane (lane = r%32 + 32*((k/8)%2)) then reads a whole
+// block as 1 KiB of consecutive bytes.
+__device__ __forceinline__ long tail_idx(int r, int k, int Kt) {
+  return ((long)(r >> 5) * (Kt >> 4) + (k >> 4)) * 512 + ((k >> 3) & 1) * 256 + (r & 31) * 8 + (k & 7);
+}
+
 template <int BITS>
 __device__ __forceinline__ void prep_x_row(int m, const void* __restrict__ x, int act_dt,
                                            const int32_t* __restrict__ k_perm, int M, int K, int G, int Kt, int BM,
@@ -94,11 +103,10 @@ __device__ __forceinline__ void prep_x_row(int m, const void* __restrict__ x, in
   // element (m, k) of xh sits at xrow[(k/64)*BM*64 + k%64]
   _Float16* xrow = xh + ((long)(m / BM) * nkt * BM + (m % BM)) * 64;
   const long kt_stride = (long)BM * 64;
-  uint16_t* trow = tA + (long)m * Kt;
   if (m >= M) {  // padding rows of the tile grid are zero
     for (int c = t; c < K / 8; c += 256)
       reinterpret_cast<u32x4_t*>(xrow + (c >> 3) * kt_stride)[c & 7] = u32x4_t{0, 0, 0, 0};
-    for (int k = t; k < Kt; k += 256) trow[k] = 0;
+    for (int k = t; k < Kt; k += 256) tA[tail_idx(m, k, Kt)] = 0;
     if (t == 0) em[m] = 0;
     return;
   }
@@ -168,12 +176,12 @@ __device__ __forceinline__ void prep_x_row(int m, const void* __restrict__ x, in
       const int g = bi / bpg;
       const uint16_t hi = f32_to_bf16_bits(part);
       const uint16_t lo = f32_to_bf16_bits(part - bf16_bits_to_f32(hi));
-      trow[3 * g] = hi;
-      trow[3 * g + 1] = hi;
-      trow[3 * g + 2] = lo;
+      tA[tail_idx(m, 3 * g, Kt)] = hi;
+      tA[tail_idx(m, 3 * g + 1, Kt)] = hi;
+      tA[tail_idx(m, 3 * g + 2, Kt)] = lo;
     }
   }
-  for (int k = 3 * ng + t; k < Kt; k += 256) trow[k] = 0;
+  for (int k = 3 * ng + t; k < Kt; k += 256) tA[tail_idx(m, k, Kt)] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -217,7 +225,7 @@ __device__ __forceinline__ void prep_w_rows(int blk, const void* __restrict__ sc
     }
   }
   __syncthreads();
-  // bias tail rows (contiguous per row)
+  // bias tail rows
   for (int i = t; i < PW * Kt; i += 256) {
     const int r = i / Kt, k = i % Kt, n = n0 + r;
     uint16_t v = 0;
@@ -228,7 +236,7 @@ __device__ __forceinline__ void prep_w_rows(int blk, const void* __restrict__ sc
       const uint16_t hi = f32_to_bf16_bits(cb);
       v = part == 1 ? f32_to_bf16_bits(cb - bf16_bits_to_f32(hi)) : hi;
     }
-    tB[(long)n * Kt + k] = v;
+    tB[tail_idx(n, k, Kt)] = v;
   }
   // scale pieces, n fastest
   const int tpg = G == 128 ? 2 : 1;  // K tiles per group
@@ -653,8 +661,53 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   P.kbase = kt0;
   P.last_kt = nkt - 1;
 
+  // ---- the bias tail first: acc = sum_g xs * cb on bf16 MFMA over the Kt
+  // tail columns (a multiple of 16 TD), first split only.  Operands come
+  // straight from global memory (L2-resident), TD 16-column steps in flight;
+  // the first ones are issued ahead of the first two tiles' copies, so their
+  // latency and the copies' overlap.
+  constexpr int TD = 3;
+  const bool tail = sp == 0;
+  // (fragment-ordered operands: a 32 x 16 block is 1 KiB, lane l's 16
+  // bytes at 16 l; 32-row blocks are Kt/16 blocks apart)
+  const long tblk = (long)(p.Kt >> 4) * 512;
+  const uint16_t* ta_row = p.tA + ((m0 + wm * 32 * MB) >> 5) * tblk + lane * 8;
+  const uint16_t* tb_row = p.tB + ((n0 + wn * 64) >> 5) * tblk + lane * 8;
+  bf16x8_t ta_r[TD][MB], tb_r[TD][2];
+  auto tail_load = [&](int kk, bf16x8_t (&a)[MB], bf16x8_t (&bb)[2]) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) bb[nb] = *reinterpret_cast<const bf16x8_t*>(tb_row + nb * tblk + kk * 512);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) a[mb] = *reinterpret_cast<const bf16x8_t*>(ta_row + mb * tblk + kk * 512);
+  };
+  auto tail_mfma = [&](const bf16x8_t (&a)[MB], const bf16x8_t (&bb)[2]) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], bb[nb], acc[mb][nb], 0, 0, 0);
+  };
+  if (tail) {
+#pragma unroll
+    for (int i = 0; i < TD; ++i) tail_load(i, ta_r[i], tb_r[i]);
+  }
+
   P.issue(0, xs[0], ws[0], ss[0]);
   P.issue(1, xs[1], ws[1], ss[1]);
+
+  if (tail) {
+    const int nk = p.Kt / 16;
+    int k = 0;
+    for (; k + TD < nk; k += TD) {
+#pragma unroll
+      for (int i = 0; i < TD; ++i) {
+        tail_mfma(ta_r[i], tb_r[i]);
+        tail_load(k + TD + i, ta_r[i], tb_r[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TD; ++i) tail_mfma(ta_r[i], tb_r[i]);
+  }
 
   uint32_t magic = 0x64006400u;
   asm volatile("" : "+v"(magic));
@@ -674,28 +727,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8) | (0 << 14));
 
   const int row0 = wm * 32 * MB;  // this wave's first row in the tile
-  // ---- tail: sum_g xs * cb on bf16 MFMA, operands straight from global
-  // (L2-resident), in the first split only
-  if (sp == 0) {
-    const uint16_t* tb_row[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) tb_row[nb] = p.tB + (long)(n0 + wn * 64 + nb * 32 + l32) * p.Kt + 8 * half;
-    const uint16_t* ta_row = p.tA + (long)(m0 + row0 + l32) * p.Kt + 8 * half;
-    const long ta_mb = (long)32 * p.Kt;
-    for (int k = 0; k < p.Kt; k += 16) {
-      bf16x8_t bt[2];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) bt[nb] = *reinterpret_cast<const bf16x8_t*>(tb_row[nb] + k);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const bf16x8_t at = *reinterpret_cast<const bf16x8_t*>(ta_row + mb * ta_mb + k);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, bt[nb], acc[mb][nb], 0, 0, 0);
-      }
-    }
-  }
-
   // ---- epilogue: y = 2^(e_m + e_n) * acc, rounded to the activation dtype.
   // 32x32 accumulator layout: lane -> column l32; register r -> row
   // 8*(r/4) + 4*half + r%4.  Stores go through a buffer resource over y: a
@@ -764,7 +795,9 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
     return hipErrorNotSupported;
   const int M = (int)a.M, N = (int)a.N, K = (int)a.K, G = a.G;
   const int ng = K / G;
-  const int Kt = (3 * ng + 15) / 16 * 16;
+  // tail columns: 3 per group, padded with zeros to whole rounds of the
+  // kernel's three 16-column steps in flight
+  const int Kt = (3 * ng + 47) / 48 * 48;
   // the largest row tile whose grid still fills three quarters of the CUs
   // in one round: a bigger tile's efficiency is worth a few idle CUs, and a
   // grid just past one round runs its last tiles as a second round alone
