@@ -516,55 +516,75 @@ struct Gemm {
       if (vper > 0 && i * vper < NVM) __builtin_amdgcn_sched_group_barrier(0x020, vper, 0);  // VMEM read
     }
   }
-  // One K tile kt in stage / ring entry S = kt % 3:
-  //   wait      this wave's copies of tile kt have landed (tile kt+1's may
-  //             still be in flight) and its LDS reads are done
-  //   barrier   so every wave's are: tile kt in LDS, stage (kt+2)%3 free
-  //   compute   its four 16-code steps, each step's MFMAs with the next
-  //             step's A reads and decode spread between them; the loads
-  //             of tile kt+2 (into stage (kt+2)%3) go out between the first
-  //             step's MFMAs, not as one burst that would stall the wave
-  //             behind a full address queue
+  // What one K tile hands to the next: the tile's code words and scale
+  // pieces and its first 16-code step's A and B fragments.
+  struct Carry {
+    uint32_t wv[2][WPL];
+    uint32_t sc[2][PS];
+    f16x8_t a0[MB];
+    f16x8_t b0[2][NF];
+  };
+  // Wait until tile kt is in LDS for every wave (this wave's copies by
+  // vmcnt, with tile kt+1's still in flight; the others' by the barrier),
+  // which also orders every wave's earlier LDS reads before it.
+  static __device__ __forceinline__ void sync_tile() {
+    __builtin_amdgcn_s_waitcnt((VM_TILE & 15) | (7 << 4) | (0 << 8) | ((VM_TILE >> 4) << 14));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // the carry of the tile in stage S
+  template <int S>
+  __device__ __forceinline__ void begin(unsigned char* const (&xs)[3], unsigned char* const (&ws)[3],
+                                        unsigned char* const (&ss)[3], uint32_t magic, Carry& c) const {
+    read_w(ws[S], c.wv);
+    read_s(ss[S], c.sc);
+    read_a(xs[S], 0, c.a0);
+    decode_b(c.wv, c.sc, 0, magic, c.b0);
+  }
+  // One K tile kt in stage / ring entry S = kt % 3, its carry ready:
+  //   its four 16-code steps, each step's MFMAs with the next step's A
+  //   reads and decode spread between them; the copies of tile kt+2 (into
+  //   stage (kt+2)%3, free since the previous tile's barrier) go out
+  //   between the first step's MFMAs, not as one burst that would stall the
+  //   wave behind a full address queue;
+  //   before the last step's MFMAs: sync_tile for tile kt+1, then tile
+  //   kt+1's carry is read and decoded between those MFMAs, so no wave
+  //   leaves the barrier with nothing for the matrix unit to do.
   // Every load of the loop is a copy into LDS (none writes a VGPR), so the
   // compiler adds no waits of its own for them: the one wait before the
   // barrier covers everything.
   template <int S>
   __device__ __forceinline__ void step(int kt, unsigned char* const (&xs)[3], unsigned char* const (&ws)[3],
-                                       unsigned char* const (&ss)[3], uint32_t magic, f32x16_t (&acc)[MB][2]) const {
-    __builtin_amdgcn_s_waitcnt((VM_TILE & 15) | (7 << 4) | (0 << 8) | ((VM_TILE >> 4) << 14));
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
+                                       unsigned char* const (&ss)[3], uint32_t magic, f32x16_t (&acc)[MB][2],
+                                       Carry& c) const {
     constexpr int DEC = 2 * NF * 16;
     const unsigned char* X = xs[S];
-    uint32_t wv[2][WPL];
-    uint32_t sc[2][PS];
-    read_w(ws[S], wv);
-    read_s(ss[S], sc);
-    f16x8_t a0[MB], a1[MB];
-    f16x8_t b0[2][NF], b1[2][NF];
-    read_a(X, 0, a0);
-    decode_b(wv, sc, 0, magic, b0);
-    __builtin_amdgcn_sched_barrier(0);
+    f16x8_t a1[MB];
+    f16x8_t b1[2][NF];
     read_a(X, 1, a1);
-    decode_b(wv, sc, 1, magic, b1);
+    decode_b(c.wv, c.sc, 1, magic, b1);
     issue(kt + 2, xs[(S + 2) % 3], ws[(S + 2) % 3], ss[(S + 2) % 3]);
-    mfma_b(a0, b0, acc);
+    mfma_b(c.a0, c.b0, acc);
     interleave<DEC, MB, VM_TILE>();
     __builtin_amdgcn_sched_barrier(0);
-    read_a(X, 2, a0);
-    decode_b(wv, sc, 2, magic, b0);
+    read_a(X, 2, c.a0);
+    decode_b(c.wv, c.sc, 2, magic, c.b0);
     mfma_b(a1, b1, acc);
     interleave<DEC, MB>();
     __builtin_amdgcn_sched_barrier(0);
     read_a(X, 3, a1);
-    decode_b(wv, sc, 3, magic, b1);
-    mfma_b(a0, b0, acc);
+    decode_b(c.wv, c.sc, 3, magic, b1);
+    mfma_b(c.a0, c.b0, acc);
     interleave<DEC, MB>();
     __builtin_amdgcn_sched_barrier(0);
+    sync_tile();
+    begin<(S + 1) % 3>(xs, ws, ss, magic, c);
     mfma_b(a1, b1, acc);
+    interleave<DEC, MB + 2 + 2>();
     __builtin_amdgcn_sched_barrier(0);
   }
 };
+// ---------------------------------------------------------------------------
 
 template <int BITS, int PS, int MB>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_affine_kernel(GemmParams p) {
@@ -711,17 +731,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   uint32_t magic = 0x64006400u;
   asm volatile("" : "+v"(magic));
+  typename GK::Carry c;
+  GK::sync_tile();
+  P.template begin<0>(xs, ws, ss, magic, c);
   // whole rounds of three tiles with no branch inside (so the compiler's
   // count of loads in flight is the same on every path into a step), then
-  // the last one or two tiles
+  // the last one or two tiles.  The last tile's step reads the carry of a
+  // tile past the end (zeros or unused codes, never used).
   int kt = 0;
   for (; kt + 3 <= nkt; kt += 3) {
-    P.template step<0>(kt, xs, ws, ss, magic, acc);
-    P.template step<1>(kt + 1, xs, ws, ss, magic, acc);
-    P.template step<2>(kt + 2, xs, ws, ss, magic, acc);
+    P.template step<0>(kt, xs, ws, ss, magic, acc, c);
+    P.template step<1>(kt + 1, xs, ws, ss, magic, acc, c);
+    P.template step<2>(kt + 2, xs, ws, ss, magic, acc, c);
   }
-  if (kt < nkt) P.template step<0>(kt, xs, ws, ss, magic, acc);
-  if (kt + 1 < nkt) P.template step<1>(kt + 1, xs, ws, ss, magic, acc);
+  if (kt < nkt) P.template step<0>(kt, xs, ws, ss, magic, acc, c);
+  if (kt + 1 < nkt) P.template step<1>(kt + 1, xs, ws, ss, magic, acc, c);
   // copies into LDS still in flight (the prefetches past the last tile)
   // must land before the workgroup's LDS can go to another workgroup
   __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8) | (0 << 14));
