@@ -192,9 +192,9 @@ __device__ __forceinline__ void prep_x_row(int m, const void* __restrict__ x, in
 // group serves two K tiles and is written for both), so the 32 rows a wave
 // of the GEMM needs for one K tile are one coalesced load.
 //   1. e_n: the exponent of the row's largest |scale| (a wave per two rows)
-//   2. the bias tail row cb = (off*s + b) * 2^-e_n as bf16 (hi, lo, hi)
-//   3. the pieces, with n fastest across the threads, so the stores of a
-//      K tile's 8 rows are contiguous
+//   2. per (row, group), n fastest across the threads: the bias tail
+//      entries cb = (off*s + b) * 2^-e_n as bf16 (hi, lo, hi) and the scale
+//      pieces, from one load of the scale and the bias
 // Small blocks keep every loop short: a loop of dependent loads per thread
 // would wait out one memory latency per iteration.
 constexpr int PW = 8;
@@ -225,26 +225,22 @@ __device__ __forceinline__ void prep_w_rows(int blk, const void* __restrict__ sc
     }
   }
   __syncthreads();
-  // bias tail rows
-  for (int i = t; i < PW * Kt; i += 256) {
-    const int r = i / Kt, k = i % Kt, n = n0 + r;
-    uint16_t v = 0;
-    if (n < N && k < 3 * ng) {
-      const int g = k / 3, part = k % 3;
-      const float sv = load_as_f32(scales, (long)n * ng + g, s_dt);
-      const float cb = fmaf(off, sv, load_as_f32(biases, (long)n * ng + g, b_dt)) * ldexpf(1.f, -e_s[r]);
-      const uint16_t hi = f32_to_bf16_bits(cb);
-      v = part == 1 ? f32_to_bf16_bits(cb - bf16_bits_to_f32(hi)) : hi;
-    }
-    tB[tail_idx(n, k, Kt)] = v;
-  }
-  // scale pieces, n fastest
+  // per (row, group), n fastest: one load of the scale and the bias for the
+  // tail entries cb = (off*s + b) * 2^-e_n as bf16 (hi, lo, hi) and the
+  // scale pieces (whose stores, n fastest, are contiguous per K tile)
   const int tpg = G == 128 ? 2 : 1;  // K tiles per group
   for (int i = t; i < PW * ng; i += 256) {
     const int r = i % PW, g = i / PW, n = n0 + r;
     uint32_t pc[PS];
+    uint16_t th = 0, tl = 0;
     if (n < N) {
-      float rr = load_as_f32(scales, (long)n * ng + g, s_dt) * ldexpf(1.f, -e_s[r]);  // exact: a power of two
+      const float sv = load_as_f32(scales, (long)n * ng + g, s_dt);
+      const float bv = load_as_f32(biases, (long)n * ng + g, b_dt);
+      const float p2 = ldexpf(1.f, -e_s[r]);
+      const float cb = fmaf(off, sv, bv) * p2;
+      th = f32_to_bf16_bits(cb);
+      tl = f32_to_bf16_bits(cb - bf16_bits_to_f32(th));
+      float rr = sv * p2;  // exact: a power of two
 #pragma unroll
       for (int j = 0; j < PS; ++j) {
         const float q = (j == PS - 1) ? rr : trunc_bf16(rr);
@@ -256,6 +252,9 @@ __device__ __forceinline__ void prep_w_rows(int blk, const void* __restrict__ sc
 #pragma unroll
       for (int j = 0; j < PS; ++j) pc[j] = 0u;
     }
+    tB[tail_idx(n, 3 * g, Kt)] = th;
+    tB[tail_idx(n, 3 * g + 1, Kt)] = tl;
+    tB[tail_idx(n, 3 * g + 2, Kt)] = th;
 #pragma unroll
     for (int j = 0; j < PS; ++j) {
       if (G == 32) {
@@ -265,6 +264,9 @@ __device__ __forceinline__ void prep_w_rows(int blk, const void* __restrict__ sc
       }
     }
   }
+  // the tail's zero padding columns
+  const int pad = Kt - 3 * ng;
+  for (int i = t; i < PW * pad; i += 256) tB[tail_idx(n0 + i / pad, 3 * ng + i % pad, Kt)] = 0;
 }
 
 // prep_x and prep_w in one launch: blocks [0, Mp) take the rows of x, the
