@@ -30,14 +30,30 @@ with almost no launch gaps.  In the same JSON line:
   w4a8_m2048     W4A8 GEMM (quantize + int8 MFMA), M=2048 N=4096 K=1024,
                  eager and from a HIP graph
   w4a8_shapes    every W4A8 shape of the speech-encoder set, graph replays
+  stream_read    the achievable HBM read rate: a plain streaming read of
+                 1 GiB (qaff_stream_read), beside the 8 TB/s published peak
+  gemv_cold      one GEMV launch per call for each decode-set shape (2048x2048
+                 is also the single-linear configuration) at M = 1, 4, 16:
+                 cold = weights rotated over >= 1 GiB of replicas (every
+                 launch streams from HBM, gaps between launches included),
+                 hot = the same launches on one replica (NOT an HBM figure)
+  dequant_n14336_k4096, silu_gate_down, w4a8_smooth_m2048
+                 the standalone dequantize, the SiLU-gated down projection
+                 and W4A8 with the SmoothQuant divide
   roofline       the grouped GEMV kernel of the headline step
-  cpu_baseline   the fp64 CPU oracle on a bounded sample of the same workload
+  gemm_roofline  the 4-bit M=2048 N=14336 K=4096 prefill call
+  cpu_baseline   the fp64 CPU oracle on a bounded sample of the same
+                 workload, and (per_config) on every configuration: median
+                 of 3 runs, all host threads, plus one thread for the decode
+                 shapes; row samples for the M=2048 shapes, scaled to full M
 Every GPU figure is timed with HIP events on the stream the kernels run on:
 the headline step is launched directly (two launches, one host call), the
-many-launch figures as replays of a captured HIP graph.
+many-launch figures as replays of a captured HIP graph.  Figures with p10/p90
+come from one event pair per call (or per graph replay).
 
-    python bench.py [--steps K] [--warmup W] [--layers L] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--layers L] [--no-cpu-baseline] [--no-cold]
     python bench.py --traffic-probe   (short run for rocprofv3 --pmc passes)
+    python bench.py --summarize DB [FILTER]   (kernel-trace percentiles, no GPU)
 """
 from __future__ import annotations
 
@@ -149,6 +165,107 @@ def graph_time(torch, fn, steps, warmup):
     return start.elapsed_time(end) / steps
 
 
+def pct(v):
+    """median, p10, p90 of a list (microseconds)."""
+    a = np.asarray(v, dtype=np.float64)
+    return {"median_us": round(float(np.median(a)), 2), "p10_us": round(float(np.percentile(a, 10)), 2),
+            "p90_us": round(float(np.percentile(a, 90)), 2), "n": int(a.size)}
+
+
+def event_times(torch, fn, iters, warmup):
+    """Per-call durations (us) of fn() on the current stream, one event pair
+    around each call (for calls of tens of microseconds and more)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e3 for a, b in ev]
+
+
+def graph_replay_times(torch, fn, replays, warmup=2):
+    """Capture fn() once (after one eager call on the capture stream) and
+    return the duration (us) of each of `replays` replays."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fn()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(replays)]
+    for a, b in ev:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    del g
+    return [a.elapsed_time(b) * 1e3 for a, b in ev]
+
+
+def time_stream_read(torch, qa, device, nbytes=1 << 30, iters=20):
+    """The achievable streaming-read rate: qaff_stream_read over 1 GiB, the
+    best of three grid sizes, median of `iters` launches each."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    buf.fill_(3)
+    best = None
+    for blocks in (2048, 4096, 8192):
+        sink = torch.empty(blocks * 256, dtype=torch.int32, device=device)
+        t = pct(event_times(torch, lambda: qa.stream_read(buf, sink, blocks), iters, 3))
+        gbs = nbytes / (t["median_us"] * 1e-6) / 1e9
+        if best is None or gbs > best["gbs"]:
+            best = {"bytes": nbytes, "blocks": blocks, **t, "gbs": round(gbs, 1),
+                    "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    del buf
+    torch.cuda.empty_cache()
+    return best
+
+
+def time_cold_gemv(torch, qa, si, device, N, K, Ms=(1, 4, 16), min_bytes=1 << 30, replays=5):
+    """One affine GEMV launch per call (qmm_affine), cold and hot.
+
+    Cold: R replicas of (codes, scales, biases) with R x weight bytes >= 1 GiB,
+    more than four times the Infinity Cache, one launch per replica in a
+    captured graph, so every launch streams its weights from HBM; time per
+    launch includes the gaps between launches.  Hot: the same number of
+    launches on one replica (cache-resident: NOT an HBM figure)."""
+    packed, sc, bi = si.affine_weights(N, K, G, BITS, seed=(1, 900, N, K), scale_range=(0.005, 0.02),
+                                       bias_mode="noise")
+    wbytes = N * K * BITS // 8 + N * (K // G) * 4
+    R = -(-min_bytes // wbytes)
+    w = torch.from_numpy(packed.view(np.int32)).to(device).unsqueeze(0).repeat(R, 1, 1)
+    s = torch.from_numpy(sc.view(np.int16)).view(torch.bfloat16).to(device).unsqueeze(0).repeat(R, 1, 1)
+    b = torch.from_numpy(bi.view(np.int16)).view(torch.bfloat16).to(device).unsqueeze(0).repeat(R, 1, 1)
+    out = []
+    for M in Ms:
+        x = torch.from_numpy(si.activations(M, K, seed=(1, 901, K, M)).view(np.int16)).view(torch.bfloat16).to(device)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=device)
+        cold = lambda: [qa.qmm_affine(x, w[r], s[r], b[r], G, BITS, out=y) for r in range(R)]
+        hot = lambda: [qa.qmm_affine(x, w[0], s[0], b[0], G, BITS, out=y) for _ in range(R)]
+        tc = [t / R for t in graph_replay_times(torch, cold, replays)]
+        th = [t / R for t in graph_replay_times(torch, hot, replays)]
+        byts = gemv_bytes(M, N, K)
+        pc, ph = pct(tc), pct(th)
+        gc = byts / (pc["median_us"] * 1e-6) / 1e9
+        out.append({"M": M, "N": N, "K": K, "replicas": R, "bytes_per_launch": byts,
+                    "cold_us": pc["median_us"], "cold_p10_us": pc["p10_us"], "cold_p90_us": pc["p90_us"],
+                    "cold_gbs": round(gc, 1), "cold_frac_of_hbm_peak": round(gc / HBM_PEAK_GBS, 4),
+                    "hot_us": ph["median_us"], "hot_gbs_not_hbm": round(byts / (ph["median_us"] * 1e-6) / 1e9, 1)})
+    del w, s, b
+    torch.cuda.empty_cache()
+    return out
+
+
 class Decode:
     """The decode set on the GPU plus the three ways of running it."""
 
@@ -188,25 +305,69 @@ class Decode:
 
 
 def time_gemm(torch, qa, si, device, bits, N=14336, K=4096, M=2048, iters=50, warmup=10):
+    """One qmm_affine call at M=2048 (the pre-pass kernel plus the GEMM
+    kernel): per-call event pairs, median with p10/p90."""
     case = si.cfg2_case(N, K, bits, M=M, seed=(2, N, K))
     x = torch.from_numpy(case.x.view(np.int16)).view(torch.bfloat16).to(device)
     w = torch.from_numpy(case.packed.view(np.int32)).to(device)
     s = torch.from_numpy(case.scales.view(np.int16)).view(torch.bfloat16).to(device)
     b = torch.from_numpy(case.biases.view(np.int16)).view(torch.bfloat16).to(device)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=device)
-    for _ in range(warmup):
-        qa.qmm_affine(x, w, s, b, G, bits, out=y)
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(iters):
-        qa.qmm_affine(x, w, s, b, G, bits, out=y)
-    end.record()
-    torch.cuda.synchronize()
-    us = start.elapsed_time(end) * 1e3 / iters
+    t = pct(event_times(torch, lambda: qa.qmm_affine(x, w, s, b, G, bits, out=y), iters, warmup))
+    us = t["median_us"]
     tflops = 2.0 * M * N * K / (us * 1e-6) / 1e12
-    return {"bits": bits, "M": M, "N": N, "K": K, "us_per_call": round(us, 2), "tflops": round(tflops, 1),
-            "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4)}
+    return {"bits": bits, "M": M, "N": N, "K": K, "us_per_call": us, "p10_us": t["p10_us"], "p90_us": t["p90_us"],
+            "tflops": round(tflops, 1), "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4)}
+
+
+def time_extras(torch, qa, si, device, dec, iters=50):
+    """The other entry points on the hot path's shapes: the standalone
+    dequantize (N=14336, K=4096, 4-bit, to bf16), the SiLU-gated down
+    projection of the decode stack (M=1, one launch per layer, graph-timed),
+    and W4A8 with the SmoothQuant divide (M=2048, N=4096, K=1024)."""
+    out = {}
+    N, K = 14336, 4096
+    packed, sc, bi = si.affine_weights(N, K, G, BITS, seed=(5, N, K), scale_range=(0.002, 0.01), bias_mode="exact")
+    w = torch.from_numpy(packed.view(np.int32)).to(device)
+    s = torch.from_numpy(sc.view(np.int16)).view(torch.bfloat16).to(device)
+    b = torch.from_numpy(bi.view(np.int16)).view(torch.bfloat16).to(device)
+    o = torch.empty((N, K), dtype=torch.bfloat16, device=device)
+    t = pct(event_times(torch, lambda: qa.dequantize_affine(w, s, b, K, G, BITS, out=o), iters, 5))
+    byts = N * K * BITS // 8 + N * (K // G) * 4 + N * K * 2
+    gbs = byts / (t["median_us"] * 1e-6) / 1e9
+    out["dequant_n14336_k4096"] = {"bits": BITS, "out": "bf16", **t, "bytes": byts, "gbs": round(gbs, 1),
+                                   "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    del w, s, b, o
+    # SiLU-gated down projection: y = W_down (silu(g) * u) + resid, one per layer
+    downs = [lin[6] for lin in dec.stack]
+    Kd, Nd = downs[0]["K"], downs[0]["N"]
+    gt = torch.from_numpy(si.activations(1, Kd, seed=(5, 1)).view(np.int16)).view(torch.bfloat16).to(device)
+    up = torch.from_numpy(si.activations(1, Kd, seed=(5, 2)).view(np.int16)).view(torch.bfloat16).to(device)
+    rs = torch.from_numpy(si.activations(1, Nd, seed=(5, 3)).view(np.int16)).view(torch.bfloat16).to(device)
+    ys = [torch.empty((1, Nd), dtype=torch.bfloat16, device=device) for _ in downs]
+    fn = lambda: [qa.qgemv_affine_silu_gate(gt, up, d["w"], d["s"], d["b"], G, BITS, resid=rs, out=y)
+                  for d, y in zip(downs, ys)]
+    t = pct([v / len(downs) for v in graph_replay_times(torch, fn, 20)])
+    byts = gemv_bytes(1, Nd, Kd) + Kd * 2 + Nd * 2  # + the up row and the residual
+    gbs = byts / (t["median_us"] * 1e-6) / 1e9
+    out["silu_gate_down"] = {"M": 1, "N": Nd, "K": Kd, "launches": len(downs), "us_per_launch": t["median_us"],
+                             "p10_us": t["p10_us"], "p90_us": t["p90_us"], "bytes_per_launch": byts,
+                             "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    # W4A8 with smoothing
+    M, N, K = 2048, 4096, 1024
+    case = si.w4a8_case(M, N, K, seed=(4, N, K, M))
+    x = torch.from_numpy(case.x.view(np.int16)).view(torch.float16).to(device)
+    wq = torch.from_numpy(case.w_q4.view(np.int32)).to(device)
+    sw = torch.from_numpy(case.s_w.view(np.int16)).view(torch.float16).to(device)
+    sm = torch.from_numpy(np.random.default_rng(6).uniform(0.5, 2.0, K).astype(np.float32)).to(device)
+    fn = lambda: qa.qgemm_w4a8_smooth(x, sm, wq, sw)
+    t = pct([v / REPS for v in graph_replay_times(torch, lambda: [fn() for _ in range(REPS)], 20)])
+    ops = 2.0 * M * N * K
+    out["w4a8_smooth_m2048"] = {"M": M, "N": N, "K": K, "graph_us_per_call": t["median_us"], "p10_us": t["p10_us"],
+                                "p90_us": t["p90_us"], "tops": round(ops / (t["median_us"] * 1e-6) / 1e12, 1),
+                                "frac_of_int8_peak": round(ops / (t["median_us"] * 1e-6) / 1e12 / INT8_PEAK_TOPS, 4)}
+    torch.cuda.empty_cache()
+    return out
 
 
 def time_decode_m(torch, qa, si, device, dec, M, steps, warmup):
@@ -320,9 +481,65 @@ def cpu_baseline(dec, seconds):
                       f"{dt:.1f} s wall"}
 
 
-def traffic_probe(torch, dec):
+def oracle_timings(si):
+    """The fp64 oracle per configuration on the host cores: wall-clock median
+    of 3 runs, all threads, plus one thread for cfg0/cfg1.  cfg2 and the
+    M=2048 cfg4 shapes run on a sample of rows (stated), scaled to the full M."""
+    import oracle
+
+    def med3(fn):
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts))
+
+    cores = oracle.num_threads()
+    rows = []
+
+    def affine_row(name, case, sample_rows=None, one_thread=False):
+        x = case.x if sample_rows is None else case.x[:sample_rows]
+        m = x.shape[0]
+        fn = lambda: oracle.qmm_affine(x, case.act_dtype, case.packed, case.scales, case.biases, case.sb_dtype, m,
+                                       case.N, case.K, case.G, case.bits)
+        t = med3(fn)
+        r = {"config": name, "M": case.M, "N": case.N, "K": case.K, "bits": case.bits, "rows_run": m,
+             "s": round(t, 4), "s_full_M": round(t * case.M / m, 3)}
+        if one_thread:
+            oracle.set_num_threads(1)
+            r["s_1thread"] = round(med3(fn), 4)
+            oracle.set_num_threads(cores)
+        rows.append(r)
+
+    affine_row("cfg0", si.cfg0_case(), one_thread=True)
+    for _, N, K in si.CFG1_LINEARS:
+        if (N, K) in [(rr["N"], rr["K"]) for rr in rows if rr["config"] == "cfg1"]:
+            continue
+        for M in si.CFG1_M:
+            affine_row("cfg1", si.cfg1_case(N, K, M, seed=(1, N, K, M)), one_thread=True)
+    for bits in si.CFG2_BITS:
+        for N, K in si.CFG2_SHAPES:
+            affine_row("cfg2", si.cfg2_case(N, K, bits, seed=(2, N, K)), sample_rows=8)
+    for M in si.CFG3_M:
+        c = si.cfg3_case(M)
+        t = med3(lambda: oracle.qmm_gptq(c.x, c.qweight, c.qzeros, c.scales, c.g_idx, M, c.K, c.N, c.G))
+        rows.append({"config": "cfg3", "M": M, "N": c.N, "K": c.K, "G": c.G, "rows_run": M, "s": round(t, 4),
+                     "s_full_M": round(t, 4)})
+    for N, K in si.CFG4_SHAPES:
+        for M in si.CFG4_M:
+            c = si.cfg4_case(N, K, M, seed=(4, N, K, M))
+            m = min(M, 256)
+            t = med3(lambda: oracle.w4a8(c.x[:m], c.w_q4, c.s_w, m, N, K))
+            rows.append({"config": "cfg4", "M": M, "N": N, "K": K, "rows_run": m, "s": round(t, 4),
+                         "s_full_M": round(t * M / m, 3)})
+    return {"cores": cores, "runs": "median of 3 wall-clock runs per row", "rows": rows}
+
+
+def traffic_probe(torch, qa, si, device, dec):
     """A short, eager run for rocprofv3 --pmc passes: a plain copy of known size
-    (calibration), then three headline steps."""
+    (calibration), then three headline steps, then three 4-bit prefill calls
+    at M=2048, N=14336, K=4096."""
     n = 256 << 20
     a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
     b = torch.empty_like(a)
@@ -334,8 +551,22 @@ def traffic_probe(torch, dec):
     for _ in range(3):
         dec.run_set()
     torch.cuda.synchronize()
+    case = si.cfg2_case(14336, 4096, 4, seed=(2, 14336, 4096))
+    x = torch.from_numpy(case.x.view(np.int16)).view(torch.bfloat16).to(device)
+    w = torch.from_numpy(case.packed.view(np.int32)).to(device)
+    s = torch.from_numpy(case.scales.view(np.int16)).view(torch.bfloat16).to(device)
+    b = torch.from_numpy(case.biases.view(np.int16)).view(torch.bfloat16).to(device)
+    for _ in range(3):
+        qa.qmm_affine(x, w, s, b, G, 4)
+    torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": n, "set_bytes_per_step": dec.bytes_per_step,
                       "launches_per_step": -(-dec.n_linears // PER_LAUNCH)}), flush=True)
+
+
+def gemm_bytes(M, N, K, bits=4, group=G):
+    """Algorithmic bytes of one prefill call: codes, bf16 scales and biases,
+    bf16 x in and bf16 y out (each once)."""
+    return N * K * bits // 8 + N * (K // group) * 4 + M * K * 2 + M * N * 2
 
 
 def record_traffic(fetch_db, write_db):
@@ -344,31 +575,64 @@ def record_traffic(fetch_db, write_db):
     copy kernel of known size calibrates each counter's unit."""
     import sqlite3
 
-    def per_kernel(db, counter):
+    def per_kernel(db, counter, key):
         rows = sqlite3.connect(db).execute(
             "select kernel_name, value from counters_collection where counter_name = ?", (counter,)).fetchall()
         copy = [v for n, v in rows if "copyBuffer" in n or "copy" in n.lower()]
-        gemv = [v for n, v in rows if "gemv_affine_kernel" in n]
-        return max(copy), sum(gemv) / len(gemv)
+        sel = [v for n, v in rows if key in n]
+        return max(copy), sum(sel) / len(sel)
 
     copy_bytes = 256 << 20
-    fc, fg = per_kernel(fetch_db, "FETCH_SIZE")
-    wc, wg = per_kernel(write_db, "WRITE_SIZE")
-    f_factor = copy_bytes / (fc * 1024)
-    w_factor = copy_bytes / (wc * 1024)
-    traffic = fg * 1024 * f_factor + wg * 1024 * w_factor
-    rec = {"gemv_decode_set_m1": {
-        "src_hash": src_hash("gemv_affine.hip"),
-        "bytes_per_launch": round(traffic),
-        "fetch_kib_per_launch": round(fg, 1), "write_kib_per_launch": round(wg, 1),
-        "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
-        "calibration": "256 MiB device copy: FETCH_SIZE and WRITE_SIZE of that kernel against 256 MiB",
-        "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -- python3 bench.py --traffic-probe"}}
+    rec = {}
+    for name, key, src, alg in (
+            ("gemv_decode_set_m1", "gemv_affine_kernel", "gemv_affine.hip", None),
+            ("gemm_m2048_n14336_b4", "gemm_affine_kernel<4, 1, 4>", "gemm_affine.hip",
+             gemm_bytes(2048, 14336, 4096)),
+            ("gemm_prep_m2048_n14336_b4", "prep_kernel<4, 1>", "gemm_affine.hip", None)):
+        fc, fg = per_kernel(fetch_db, "FETCH_SIZE", key)
+        wc, wg = per_kernel(write_db, "WRITE_SIZE", key)
+        f_factor = copy_bytes / (fc * 1024)
+        w_factor = copy_bytes / (wc * 1024)
+        traffic = fg * 1024 * f_factor + wg * 1024 * w_factor
+        rec[name] = {
+            "kernel": key, "src_hash": src_hash(src),
+            "bytes_per_launch": round(traffic),
+            "fetch_kib_per_launch": round(fg, 1), "write_kib_per_launch": round(wg, 1),
+            "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
+            "calibration": "256 MiB device copy: FETCH_SIZE and WRITE_SIZE of that kernel against 256 MiB",
+            "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -- python3 bench.py --traffic-probe"}
+        if alg:
+            rec[name]["algorithmic_bytes"] = alg
     path = os.path.join(ROOT, "profiles", "traffic.json")
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
+
+
+def summarize(db, filt=""):
+    """Markdown table of per-kernel durations (calls, mean, median, p10, p90,
+    min; microseconds) from a rocprofv3 --kernel-trace database."""
+    import sqlite3
+    c = sqlite3.connect(db)
+    tables = [r[0] for r in c.execute("select name from sqlite_master where type in ('table', 'view')")]
+    tab = "kernels" if "kernels" in tables else [t for t in tables if "kernel" in t][0]
+    cols = [r[1] for r in c.execute(f"pragma table_info({tab})")]
+    name = "name" if "name" in cols else "kernel_name"
+    grid = "grid_x" if "grid_x" in cols else ("grid_size" if "grid_size" in cols else None)
+    by = {}
+    q = f"select {name}, {grid or 0}, start, end from {tab}"
+    for n, gx, a, b in c.execute(q):
+        by.setdefault((n, gx), []).append((b - a) / 1000.0)
+    print("| kernel | grid (threads) | calls | mean us | median us | p10 us | p90 us | min us |")
+    print("|---|---|---|---|---|---|---|---|")
+    for (n, gx), v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        if filt and filt not in n:
+            continue
+        v = np.asarray(v)
+        short = n.replace("void ", "").replace("qaff::(anonymous namespace)::", "").split("(")[0]
+        print(f"| `{short[:90]}` | {gx} | {v.size} | {v.mean():.2f} | {np.median(v):.2f} | "
+              f"{np.percentile(v, 10):.2f} | {np.percentile(v, 90):.2f} | {v.min():.2f} |")
 
 
 def main():
@@ -384,9 +648,15 @@ def main():
     ap.add_argument("--traffic-probe", action="store_true", help="short eager run for rocprofv3 --pmc")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="write profiles/traffic.json from two --pmc runs of --traffic-probe (no GPU needed)")
+    ap.add_argument("--summarize", nargs="+", metavar=("DB", "FILTER"),
+                    help="print per-kernel duration percentiles of a rocprofv3 --kernel-trace database (no GPU)")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold per-kernel GEMV figures")
     args = ap.parse_args()
     if args.record_traffic:
         record_traffic(*args.record_traffic)
+        return
+    if args.summarize:
+        summarize(*args.summarize[:2])
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -411,7 +681,7 @@ def main():
 
     dec = Decode(args, torch, qa, si, device)
     if args.traffic_probe:
-        traffic_probe(torch, dec)
+        traffic_probe(torch, qa, si, device, dec)
         return
 
     launches_set = -(-dec.n_linears // PER_LAUNCH)
@@ -438,7 +708,21 @@ def main():
               flush=True)
     gptq = [time_gptq(torch, qa, si, device, M) for M in (1, 32)]
 
-    gemm = w4a8 = w4a8_shapes = None
+    stream = time_stream_read(torch, qa, device)
+    print(f"[bench] streaming read: {stream['gbs']} GB/s", file=sys.stderr, flush=True)
+    cold = None
+    if not args.no_cold:
+        shapes = []
+        for _, N, K in si.CFG1_LINEARS:
+            if (N, K) not in shapes:
+                shapes.append((N, K))
+        cold = [r for N, K in shapes for r in time_cold_gemv(torch, qa, si, device, N, K)]
+        for r in cold:
+            print(f"[bench] cold M={r['M']} {r['N']}x{r['K']}: {r['cold_us']} us, {r['cold_gbs']} GB/s "
+                  f"(hot {r['hot_us']} us)", file=sys.stderr, flush=True)
+    extras = time_extras(torch, qa, si, device, dec)
+
+    gemm = w4a8 = w4a8_shapes = gemm_roofline = None
     if not args.no_gemm:
         gemm = [time_gemm(torch, qa, si, device, bits, N=N, K=K) for bits in si.CFG2_BITS for N, K in si.CFG2_SHAPES]
         w4a8 = time_w4a8(torch, qa, si, device)
@@ -447,6 +731,15 @@ def main():
             print(f"[bench] gemm b{g['bits']}: {g['us_per_call']} us, {g['tflops']} TFLOP/s", file=sys.stderr,
                   flush=True)
         print(f"[bench] w4a8: {w4a8['us_per_call']} us, {w4a8['tops']} TOPS", file=sys.stderr, flush=True)
+        g = [r for r in gemm if r["bits"] == 4 and r["N"] == 14336 and r["K"] == 4096][0]
+        flops = 2.0 * g["M"] * g["N"] * g["K"]
+        gemm_roofline = {"bound": "mfma", "achieved": g["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": g["frac_of_bf16_peak"],
+                         "traffic": load_traffic("gemm_affine.hip", "gemm_m2048_n14336_b4"),
+                         "algorithmic_bytes": gemm_bytes(g["M"], g["N"], g["K"]),
+                         "kernel": "prep_kernel<4, 1> + gemm_affine_kernel<4, 1, 4> (one qmm_affine call; "
+                                   "the achieved figure counts both kernels)",
+                         "flops_per_call": flops, "median_call_us": g["us_per_call"]}
 
     bytes_per_launch = dec.bytes_per_step / launches_set
     avg_launch_us = ms_set * 1e3 / launches_set
@@ -457,7 +750,10 @@ def main():
                 "kernel": "gemv_affine_kernel<4, bf16, M=1> (grouped, 56 linears per launch)",
                 "bytes_per_launch": round(bytes_per_launch), "avg_launch_us": round(avg_launch_us, 3)}
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(dec, args.cpu_seconds)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(dec, args.cpu_seconds)
+        cpu["per_config"] = oracle_timings(si)
 
     out = {
         "metric": METRIC,
@@ -484,6 +780,10 @@ def main():
         "per_linear": {"launches_per_step": dec.n_linears, "us_per_step": round(ms_lin * 1e3, 1),
                        "gbs": round(dec.bytes_per_step / (ms_lin * 1e-3) / 1e9, 1)},
         "cfg0_hot": {"us_per_launch": round(us_hot, 2), "gbs_not_hbm": round(gemv_bytes(1, 2048, 2048) / us_hot / 1e3, 1)},
+        "stream_read": stream,
+        "gemv_cold": cold,
+        "gemm_roofline": gemm_roofline,
+        **extras,
         "decode_set_multirow": decode_m,
         "gptq_k4096_n11008": gptq,
         "gemm_m2048": gemm,

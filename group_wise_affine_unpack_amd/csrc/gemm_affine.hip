@@ -23,12 +23,16 @@
 //   prep    : one launch, two halves.  Per row of x: e_m, xh (fp16, permuted
 //             to the code decode order, read through k_perm when given), tail
 //             A = [xs_hi, xs_hi, xs_lo].  Per row of W: e_n, scale pieces s_j
-//             (fp16 pairs), tail B = [cb_hi, cb_lo, cb_hi]
-//   gemm    : 256 threads, tile BM x 256 (4 waves along N, each BM x 64);
-//             x tiles in a 4-stage LDS ring, stored two steps ahead; packed codes go from
-//             global memory straight to registers, are decoded with the
+//             (fp16 pairs), tail B = [cb_hi, cb_lo, cb_hi].  Tail operands
+//             are stored in MFMA fragment order.
+//   gemm    : 512 threads (8 waves, 2 along M x 4 along N), tile BM x 256.
+//             The bias tail runs first.  Then per 64-code K tile: x, code
+//             and scale-piece copies go global -> LDS directly into a 3-stage
+//             ring two tiles ahead; the codes are decoded with the
 //             exponent-bias trick (code | 0x6400 = 1024 + code in fp16) and
-//             scaled with packed fp16 math; XCD-aware tile order.
+//             scaled with packed fp16 math between the MFMAs; the barrier
+//             for the next tile sits before the last 16-code step, whose
+//             MFMAs cover the next tile's first reads.  XCD-aware tile order.
 #include <algorithm>
 #include <mutex>
 

@@ -54,6 +54,11 @@ def _sb(a, dtype):
 I64 = C.c_int64
 
 
+def set_num_threads(n: int) -> None:
+    """Threads for later calls (timing only: no result depends on it)."""
+    _load().oracle_set_num_threads(C.c_int(n))
+
+
 def num_threads() -> int:
     lib = _load()
     lib.oracle_num_threads.restype = C.c_int

@@ -154,6 +154,18 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Threads for the following calls (timing of the oracle as a CPU baseline;
+ * no result depends on the thread count). */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ---------------------------------------------------------------------- */
 /* O1  affine code unpack  [MLX8 "Layout"; METAL intro]                    */
 /*                                                                        */
