@@ -86,10 +86,15 @@ def gemv_bytes(M, N, K, bits=BITS, group=G):
 
 
 def src_hash(*names):
+    """Hash of the code in the named kernel sources, ignoring // comments and
+    blank lines (a changed comment does not change the kernel)."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "group_wise_affine_unpack_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "group_wise_affine_unpack_amd", "csrc", n), encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
