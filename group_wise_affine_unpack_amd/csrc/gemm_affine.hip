@@ -195,7 +195,8 @@ __device__ __forceinline__ void prep_x_row(int m, const void* __restrict__ x, in
 // each, SPT = 2 groups per 64-code K tile for G = 32, else 1; a G = 128
 // group serves two K tiles and is written for both), so the 32 rows a wave
 // of the GEMM needs for one K tile are one coalesced load.
-//   1. e_n: the exponent of the row's largest |scale| (a wave per two rows)
+//   1. e_n: the exponent of the row's largest |scale|, less ESHIFT (a wave
+//      per two rows)
 //   2. per (row, group), n fastest across the threads: the bias tail
 //      entries cb = (off*s + b) * 2^-e_n as bf16 (hi, lo, hi) and the scale
 //      pieces, from one load of the scale and the bias
@@ -204,7 +205,8 @@ __device__ __forceinline__ void prep_x_row(int m, const void* __restrict__ x, in
 constexpr int PW = 8;
 template <int PS>
 __device__ __forceinline__ void prep_w_rows(int blk, const void* __restrict__ scales, int s_dt,
-                                            const void* __restrict__ biases, int b_dt, float off, int N, int Np,
+                                            const void* __restrict__ biases, int b_dt, float off, int eshift, int N,
+                                            int Np,
                                             int ng, int G, int Kt, uint32_t* __restrict__ sh, uint16_t* __restrict__ tB,
                                             int* __restrict__ en) {
   __shared__ int e_s[PW];
@@ -221,7 +223,7 @@ __device__ __forceinline__ void prep_w_rows(int blk, const void* __restrict__ sc
 #pragma unroll
     for (int u = 0; u < PW / 4; ++u) {
       const int r = wave + 4 * u;
-      const int e = exp_of(wave_max(smax[u]));
+      const int e = exp_of(wave_max(smax[u])) - eshift;
       if (lane == 0) {
         e_s[r] = e;
         en[n0 + r] = e;
@@ -287,6 +289,7 @@ struct PrepArgs {
   uint16_t* tB;
   int* en;
   float off;
+  int eshift;
   int act_dt, s_dt, b_dt;
   int M, N, K, G, Kt, BM, Mp, Np, ng;
 };
@@ -297,7 +300,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   if (b < a.Mp)
     prep_x_row<BITS>(b, a.x, a.act_dt, a.k_perm, a.M, a.K, a.G, a.Kt, a.BM, a.xh, a.tA, a.em);
   else
-    prep_w_rows<PS>(b - a.Mp, a.scales, a.s_dt, a.biases, a.b_dt, a.off, a.N, a.Np, a.ng, a.G, a.Kt, a.sh, a.tB,
+    prep_w_rows<PS>(b - a.Mp, a.scales, a.s_dt, a.biases, a.b_dt, a.off, a.eshift, a.N, a.Np, a.ng, a.G, a.Kt, a.sh, a.tB,
                     a.en);
 }
 
@@ -331,6 +334,11 @@ struct Decode {
   // integer pieces as exact fp16 pairs, in the kernel's decode order
   static constexpr int NPIECE = BITS == 8 ? 2 : 1;
   static constexpr float OFFQ = BITS == 4 ? 8.f : (BITS == 8 ? 136.f : 0.f);
+  // The row's largest |scale| is brought to [2^ESHIFT, 2^(ESHIFT+1)): as
+  // high as the largest code piece times scale piece still fits fp16 (4-bit:
+  // 8 * 2^12; 8-bit: 8 * 16 * 2^9; 2-bit: 3 * 2^13), so that scales down to
+  // 2^-(14+ESHIFT) of the row's largest stay normal fp16 numbers, exact.
+  static constexpr int ESHIFT = BITS == 4 ? 11 : (BITS == 8 ? 8 : 12);
   // `magic` holds 0x64006400 in a VGPR, so mask-and-insert is one
   // v_and_or_b32 (a VOP3 op reads at most one literal or SGPR on gfx950)
   static __device__ __forceinline__ void pieces(const uint32_t* wd, int half, uint32_t magic,
@@ -891,6 +899,7 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
   pa.tB = tB;
   pa.en = en;
   pa.off = Decode<BITS>::OFFQ;
+  pa.eshift = Decode<BITS>::ESHIFT;
   pa.act_dt = a.act_dt;
   pa.s_dt = a.s_dt;
   pa.b_dt = a.b_dt;

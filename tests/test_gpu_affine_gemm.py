@@ -100,7 +100,7 @@ def test_wide_dynamic_range_rows():
 
 
 def test_k_not_multiple_of_tile():
-    # K % 64 != 0 (G = 32): served by the GEMV kernel in 4-row chunks
+    # K % 64 != 0 (G = 32): served by the GEMV kernel on 16-row slices
     case = si.affine_case(20, 96, 160, 32, 4, seed=(26,), name="gemm_k160")
     y = _run(case)
     assert_float_bar(host_f64(y), oracle.qmm_affine_case(case), case.name)
@@ -113,3 +113,77 @@ def test_split_k_partials(M, N, K, bits):
     case = si.affine_case(M, N, K, 64, bits, seed=(27, M, N, K), name=f"gemm_split_M{M}_N{N}_K{K}_b{bits}")
     y = _run(case)
     assert_float_bar(host_f64(y), oracle.qmm_affine_case(case), case.name)
+
+
+@pytest.mark.parametrize("bits", si.CFG2_BITS)
+def test_cfg2_full_compare(bits):
+    # one whole prefill shape per bit width, every output against the oracle
+    N, K = 1024, 4096
+    case = si.cfg2_case(N, K, bits, seed=(2, N, K))
+    y = _run(case)
+    assert_float_bar(host_f64(y), oracle.qmm_affine_case(case), case.name + "_full")
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("M", [17, 70])
+def test_k_equals_group(bits, G, M):
+    # one group per row: K = G (K = 32 at 2 bits is a row of 8 bytes, the
+    # GEMV's tail path; K = 64 and 128 are whole GEMM K tiles)
+    case = si.affine_case(M, 136, G, G, bits, seed=(28, bits, G, M), scale_range=(0.002, 0.01),
+                          name=f"gemm_K_eq_G{G}_b{bits}_M{M}")
+    y = _run(case)
+    assert_float_bar(host_f64(y), oracle.qmm_affine_case(case), case.name)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_scales_spanning_2_pow_22_in_a_row(bits):
+    # Each row's scales spread over 2^22: groups 0-7 within 2^-6 of the row's
+    # largest (group 0), groups 8-63 between 2^-22 and 2^-15 of it
+    # (log-uniform), below fp16's normal range if the largest were brought
+    # to 1.  x is zero over groups 0-7, so every output comes from the small
+    # scales alone.  The kernel's fp16 scale pieces keep them exact
+    # (scales down to 2^-(14+ESHIFT) of the row's largest are normal fp16
+    # numbers), so against each row's largest output the error is the f16
+    # rounding of y (2^-11) and fp32 sums: bounded here by 2e-3.  Pieces
+    # rounded as subnormals (the row's largest scale brought to 1) miss it.
+    M, N, K, G = 80, 96, 2048, 32
+    case = si.affine_case(M, N, K, G, bits, seed=(29, bits), act_dtype="f16", name=f"gemm_wide_scales_b{bits}")
+    r = np.random.default_rng((29, bits, 1))
+    ng = K // G
+    e = np.concatenate([r.uniform(-6.0, 0.0, size=(N, 8)), r.uniform(-22.0, -15.0, size=(N, ng - 8))], axis=1)
+    e[:, 0] = 0.0
+    s32 = (4.0 * np.exp2(e)).astype(np.float32)
+    case.scales = si.bf16_bits(s32)
+    sb = si.bits_to_f32(case.scales, "bf16")
+    case.biases = si.bf16_bits((-(2 ** (bits - 1)) * sb).astype(np.float32))
+    xf = si.bits_to_f32(case.x, "f16").copy()
+    xf[:, :8 * G] = 0.0
+    case.x = si.store(xf, "f16")
+    y = host_f64(_run(case))
+    ref = oracle.qmm_affine_case(case)
+    worst = 0.0
+    for m in range(M):
+        sc = max(np.abs(ref[m]).max(), 1e-300)
+        assert_float_bar(y[m] / sc, ref[m] / sc, f"{case.name}_row{m}")
+        worst = max(worst, float(np.abs(y[m] - ref[m]).max() / sc))
+    print(f"[parity] {case.name} worst error / row max = {worst:.3e}", flush=True)
+    assert worst <= 2e-3, worst
+
+
+def test_padded_rows_offset_guard():
+    # M = 17 with 2-bit codes at K = 64 runs the GEMM with 64-row tiles: the
+    # padded rows' y offsets (Mp*N*2 bytes) pass 2^31 although M*N*2 does
+    # not, so the call must be refused, not wrap around into valid rows
+    dev = require_gpu()
+    M, N, K, G, bits = 17, 20_000_000, 64, 64, 2
+    assert M * N * 2 < 2 ** 31 <= 64 * N * 2
+    x = torch.zeros((M, K), dtype=torch.bfloat16, device=dev)
+    w = torch.zeros((N, K * bits // 32), dtype=torch.int32, device=dev)
+    s = torch.zeros((N, K // G), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    print("[case] padded-row guard M=17 N=2e7 K=64 2-bit", flush=True)
+    with pytest.raises(qa.QaffError) as ei:
+        qa.qmm_affine(x, w, s, s, G, bits, out=y)
+    torch.cuda.synchronize()
+    assert ei.value.status == 2, str(ei.value)   # QAFF_E_UNSUPPORTED

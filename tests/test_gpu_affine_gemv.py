@@ -165,9 +165,9 @@ def test_grouped_with_k_perm_and_plain_mixed():
 
 
 @pytest.mark.parametrize("bits,act", [(4, "bf16"), (8, "f16"), (2, "bf16")])
-def test_grouped_large_launch_eight_rows_per_wave(bits, act):
-    # a launch with >= 64 MiB of weights at M = 1 takes the 8-rows-per-wave kernel;
-    # ragged N and a K that splits across waves are mixed in
+def test_grouped_large_launch(bits, act):
+    # one grouped launch with >= 64 MiB of weights at M = 1 (the headline's
+    # launch size); ragged N and a K that splits across waves are mixed in
     shapes = [(8192, 2048)] * (8 if bits == 4 else (4 if bits == 8 else 16)) + [(1001, 4096), (300, 8192)]
     cases = [si.affine_case(1, N, K, 64, bits, seed=(26, i, bits), act_dtype=act, name=f"big{i}_N{N}_K{K}")
              for i, (N, K) in enumerate(shapes)]

@@ -45,6 +45,13 @@ def test_cfg4(N, K, M):
     _check(case, rows)
 
 
+def test_cfg4_every_row_at_m2048():
+    # one M = 2048 shape of the set with every row of x_q, s_x and acc
+    # against the oracle (the other M = 2048 shapes check sampled rows)
+    case = si.cfg4_case(1024, 1024, 2048, seed=(4, 1024, 1024, 2048))
+    _check(case)
+
+
 def test_every_nibble_and_ragged_shapes():
     case = si.w4a8_case(13, 200, 192, seed=(40,), name="w4a8_ragged")
     r = np.random.default_rng(41)
