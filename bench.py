@@ -467,6 +467,54 @@ def time_w4a8_shapes(torch, qa, si, device, iters=20, warmup=5):
     return out
 
 
+W4A8_TILES = [(32, 128), (64, 128), (64, 256), (128, 256)]
+
+
+def time_w4a8_sweep(torch, qa, si, device, replays=10):
+    """Both W4A8 lowerings (staged: quantize inside the GEMM; full-K:
+    quantize kernel, then the GEMM) at every built tile, for each shape of
+    the set with M > 16.  Each configuration is checked first (x_q, s_x, acc
+    and y the same bits as the default call), then timed: REPS calls per
+    captured graph, median of `replays`.  The fastest passing configuration
+    is reported beside the default's time."""
+    out = []
+    for N, K in si.CFG4_SHAPES:
+        for M in si.CFG4_M:
+            if M <= 16:
+                continue
+            case = si.w4a8_case(M, N, K, seed=(4, N, K, M))
+            x = torch.from_numpy(case.x.view(np.int16)).view(torch.float16).to(device)
+            w = torch.from_numpy(case.w_q4.view(np.int32)).to(device)
+            sw = torch.from_numpy(case.s_w.view(np.int16)).view(torch.float16).to(device)
+            ref = qa.qgemm_w4a8(x, w, sw, want_acc=True)
+            fn = lambda: qa.qgemm_w4a8(x, w, sw)
+            t = pct([v / REPS for v in graph_replay_times(torch, lambda: [fn() for _ in range(REPS)], replays)])
+            row = {"M": M, "N": N, "K": K, "default_us": t["median_us"], "configs": []}
+            for staged in (0, 1):
+                for bm, bn in W4A8_TILES:
+                    got = qa.qgemm_w4a8_tiled(x, w, sw, staged, bm, bn, want_acc=True)
+                    ok = all(torch.equal(a.view(torch.int8) if a.dtype == torch.int8 else a, b)
+                             for a, b in ((got[1], ref[1]), (got[3], ref[3]))) and \
+                        torch.equal(got[0].view(torch.int16), ref[0].view(torch.int16)) and \
+                        torch.equal(got[2].view(torch.int32), ref[2].view(torch.int32))
+                    c = {"staged": staged, "bm": bm, "bn": bn, "same_bits": bool(ok)}
+                    if ok:
+                        f = lambda: qa.qgemm_w4a8_tiled(x, w, sw, staged, bm, bn)
+                        tc = pct([v / REPS for v in graph_replay_times(torch, lambda: [f() for _ in range(REPS)],
+                                                                       replays)])
+                        c["us"] = tc["median_us"]
+                    row["configs"].append(c)
+            passing = [c for c in row["configs"] if c["same_bits"]]
+            best = min(passing, key=lambda c: c["us"]) if passing else None
+            row["best"] = best
+            ops = 2.0 * M * N * K
+            if best:
+                row["best_tops"] = round(ops / (best["us"] * 1e-6) / 1e12, 1)
+            out.append(row)
+            torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(dec, seconds):
     """The fp64 oracle on the host cores over the layer-0 linears of the same
     decode workload (M=1), repeated until `seconds` of work."""
@@ -656,6 +704,8 @@ def main():
     ap.add_argument("--summarize", nargs="+", metavar=("DB", "FILTER"),
                     help="print per-kernel duration percentiles of a rocprofv3 --kernel-trace database (no GPU)")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold per-kernel GEMV figures")
+    ap.add_argument("--w4a8-sweep", action="store_true",
+                    help="only the W4A8 lowering x tile sweep (checked, then timed) as one JSON line")
     args = ap.parse_args()
     if args.record_traffic:
         record_traffic(*args.record_traffic)
@@ -682,6 +732,9 @@ def main():
             for N, K in si.CFG2_SHAPES:
                 print(json.dumps({"gemm_m2048": time_gemm(torch, qa, si, device, bits, N=N, K=K)}), flush=True)
         print(json.dumps({"w4a8_m2048": time_w4a8(torch, qa, si, device)}), flush=True)
+        return
+    if args.w4a8_sweep:
+        print(json.dumps({"w4a8_sweep": time_w4a8_sweep(torch, qa, si, device)}), flush=True)
         return
 
     dec = Decode(args, torch, qa, si, device)

@@ -17,7 +17,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["QaffError", "qmm_affine", "qmm_affine_noalloc", "qgemv_affine", "qgemv_affine_grouped", "GroupedGemv", "qmm_gptq", "qgemm_w4a8", "gptq_to_affine_repack",
+__all__ = ["QaffError", "qmm_affine", "qmm_affine_noalloc", "qgemv_affine", "qgemv_affine_grouped", "GroupedGemv", "qmm_gptq", "qgemm_w4a8", "qgemm_w4a8_tiled", "gptq_to_affine_repack",
            "quantize_pack_affine", "dequantize_affine", "qgemv_affine_silu_gate", "smoothquant_factors",
            "w4a8_quantize_weights", "qgemm_w4a8_smooth", "release_workspaces", "library_path", "lib", "STATUS", "DTYPE"]
 
@@ -36,6 +36,7 @@ _SIGS = {
     "qmm_affine_noalloc": [_VP] * 6 + [_I64] * 3 + [_I32] * 5 + [_VP],
     "qmm_gptq": [_VP] * 6 + [_I64] * 3 + [_I32, _VP],
     "qgemm_w4a8": [_VP] * 7 + [_I64] * 3 + [_VP],
+    "qgemm_w4a8_tiled": [_VP] * 7 + [_I64] * 3 + [_I32] * 3 + [_VP],
     "gptq_to_affine_repack": [_VP] * 7 + [_I32, _VP] + [_I64] * 2 + [_I32, _VP],
     "quantize_pack_affine": [_VP, _I32, _VP, _VP, _VP, _I32, _I64, _I64, _I32, _I32, _VP],
     "qgemv_affine_grouped": [_VP, _I32, _I64] + [_I32] * 5 + [_VP],
@@ -240,6 +241,22 @@ def qgemm_w4a8(x: torch.Tensor, w_q4: torch.Tensor, s_w: torch.Tensor, want_acc:
     st = lib().qgemm_w4a8(_ptr(x), _ptr(_u32(w_q4)), _ptr(s_w), _ptr(y), _ptr(x_q), _ptr(s_x), _ptr(acc), M, N, K,
                           _stream(dev))
     _check(st, "qgemm_w4a8")
+    return y, x_q, s_x, acc
+
+
+def qgemm_w4a8_tiled(x: torch.Tensor, w_q4: torch.Tensor, s_w: torch.Tensor, staged: bool, bm: int, bn: int,
+                     want_acc: bool = False):
+    """qgemm_w4a8 (M > 16) with the lowering (staged or full-K) and the bm x bn tile chosen."""
+    M, K = x.shape
+    N = w_q4.shape[0]
+    dev = x.device
+    y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    x_q = torch.empty((M, K), dtype=torch.int8, device=dev)
+    s_x = torch.empty((M,), dtype=torch.float32, device=dev)
+    acc = torch.empty((M, N), dtype=torch.int32, device=dev) if want_acc else None
+    st = lib().qgemm_w4a8_tiled(_ptr(x), _ptr(_u32(w_q4)), _ptr(s_w), _ptr(y), _ptr(x_q), _ptr(s_x), _ptr(acc), M, N,
+                                K, int(bool(staged)), bm, bn, _stream(dev))
+    _check(st, "qgemm_w4a8_tiled")
     return y, x_q, s_x, acc
 
 

@@ -146,6 +146,9 @@ struct W4A8Args {
 hipError_t launch_w4a8(const W4A8Args& a, hipStream_t s);
 // the integer product and epilogue of W4A8 from x_q and s_x already written
 hipError_t launch_w4a8_product(const W4A8Args& a, hipStream_t s);
+// M > 16 with a chosen lowering (staged: quantize inside the GEMM; else the
+// quantize kernel, then the full-K GEMM) and tile bm x bn
+hipError_t launch_w4a8_config(const W4A8Args& a, int staged, int bm, int bn, hipStream_t s);
 // SmoothQuant: factors, weight quantization (optional fold), smoothed quantizer
 hipError_t launch_smooth_factors(const float* amax, const void* w, int w_dt, int64_t N, int64_t K, double alpha,
                                  float* s, hipStream_t st);

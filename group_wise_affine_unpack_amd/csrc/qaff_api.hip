@@ -264,6 +264,39 @@ int qgemm_w4a8(const void* x, const uint32_t* w_q4, const void* s_w, void* y, in
   return ok();
 }
 
+int qgemm_w4a8_tiled(const void* x, const uint32_t* w_q4, const void* s_w, void* y, int8_t* x_q, float* s_x,
+                     int32_t* acc_out, int64_t M, int64_t N, int64_t K, int32_t staged, int32_t bm, int32_t bn,
+                     void* stream) {
+  if (M < 0 || N <= 0 || K <= 0) return fail(QAFF_E_INVAL, "sizes must satisfy M >= 0, N > 0, K > 0");
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return fail(QAFF_E_UNSUPPORTED, "dimension above 2^30");
+  if (K % 32) return fail(QAFF_E_INVAL, "K must be a multiple of 32 (got %lld)", (long long)K);
+  if (K > (int64_t(1) << 17)) return fail(QAFF_E_UNSUPPORTED, "K above 131072 could overflow the int32 accumulator");
+  if (staged != 0 && staged != 1) return fail(QAFF_E_INVAL, "staged must be 0 or 1");
+  const bool tile_ok = (bm == 32 && bn == 128) || (bm == 64 && bn == 128) || (bm == 64 && bn == 256) ||
+                       (bm == 128 && bn == 256);
+  if (!tile_ok) return fail(QAFF_E_UNSUPPORTED, "tile %dx%d is not built (32x128, 64x128, 64x256, 128x256)", bm, bn);
+  if (M == 0) return ok();
+  if (M <= 16) return fail(QAFF_E_UNSUPPORTED, "M <= 16 runs the GEMV paths, which have no tile (use qgemm_w4a8)");
+  if (!x || !w_q4 || !s_w || !y || !x_q || !s_x) return fail(QAFF_E_INVAL, "null tensor pointer");
+  if (!aligned16(x) || !aligned16(w_q4) || !aligned16(x_q)) return fail(QAFF_E_ALIGN, "x, w_q4 and x_q must be 16-byte aligned");
+  qaff::W4A8Args a;
+  a.x = x;
+  a.w = w_q4;
+  a.s_w = s_w;
+  a.y = y;
+  a.x_q = x_q;
+  a.s_x = s_x;
+  a.acc = acc_out;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  (void)hipGetLastError();
+  hipError_t e = qaff::launch_w4a8_config(a, staged, bm, bn, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return fail(QAFF_E_UNSUPPORTED, "this shape has no kernel");
+  if (e != hipSuccess) return hip_fail(e, "w4a8 launch");
+  return ok();
+}
+
 int qgemm_w4a8_smooth(const void* x, const float* smooth, const uint32_t* w_q4, const void* s_w, void* y,
                       int8_t* x_q, float* s_x, int32_t* acc_out, int64_t M, int64_t N, int64_t K, void* stream) {
   if (M < 0 || N <= 0 || K <= 0) return fail(QAFF_E_INVAL, "sizes must satisfy M >= 0, N > 0, K > 0");

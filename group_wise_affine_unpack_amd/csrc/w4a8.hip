@@ -143,6 +143,9 @@ constexpr int BK = 128;  // int8 codes per K stage
 struct Params {
   const int8_t* xq;
   const float* sx;
+  const uint16_t* x;   // staged lowering: the f16 activations
+  int8_t* xq_out;      // staged lowering: x_q and s_x, written by the
+  float* sx_out;       //   workgroups of the first column tile
   const uint32_t* w;
   const uint16_t* sw;
   uint16_t* y;
@@ -167,13 +170,21 @@ __device__ __forceinline__ int xswz(int r) { return r & 7; }
 // Stage = 128 codes of K.  Lane (l32, h) takes, in 16-column sub-step s,
 // codes 64h + 16s .. +15 of the stage: its B fragment is words 8h+2s, 8h+2s+1
 // of its row, its A fragment the matching 16 bytes of x_q row l32.
-template <int MB, int NB>
+template <int MB, int NB, bool STAGED>
 struct W4Pipe {
-  static constexpr int A_CH = MB;  // 16-byte x chunks per thread and stage
+  // 16-byte x chunks per thread and stage: x_q codes, or (staged) f16
+  // values, 8 per chunk, quantized on their way into LDS
+  static constexpr int A_CH = STAGED ? 2 * MB : MB;
   static constexpr int SB = MB * 32 * 128;  // bytes of one LDS stage
-  __amdgpu_buffer_rsrc_t rx, rw;
+  __amdgpu_buffer_rsrc_t rx, rw, rq;
   uint32_t x_off[A_CH];  // this thread's chunks (OOB for rows past M)
-  int x_dst;             // LDS offset of chunk 0 (chunk i at + i*4096)
+  int x_dst;             // LDS offset of chunk 0 (chunk i at + i*4096; staged + i*2048)
+  // staged: the scale and refined reciprocal of each chunk's row, and
+  // whether this workgroup writes x_q (the first column tile does)
+  float qs[A_CH], qr[A_CH];
+  uint32_t q_off[A_CH];  // x_q byte offset of the chunk's first code, stage 0
+  int q_col;             // the chunk's first code within a stage
+  bool wq;
   // weight batches (two stages = 128 bytes of a row): global loads of 8
   // rows x 128 bytes per instruction, through a wave-private LDS region
   static constexpr int WB = NB * 4;  // 16-byte chunks per lane and batch
@@ -184,13 +195,28 @@ struct W4Pipe {
   int st0;  // first K stage of this workgroup's split
 
   __device__ __forceinline__ void issue_x(int t, u32x4_t (&xr)[A_CH]) const {
-    const uint32_t k = (uint32_t)(st0 + min(t, nst - 1)) * BK;
+    const uint32_t k = (uint32_t)(st0 + min(t, nst - 1)) * BK * (STAGED ? 2 : 1);
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) xr[i] = ld128(rx, x_off[i] + k);
   }
-  __device__ __forceinline__ void store_x(unsigned char* st, const u32x4_t (&xr)[A_CH]) const {
+  // x of stage t into an LDS stage; staged: quantized first (the same
+  // arithmetic as the quantize kernel, so the same bits), and the first
+  // column tile's workgroups also store the codes to x_q (a chunk past K
+  // is not stored; a row past M is past the range)
+  __device__ __forceinline__ void store_x(unsigned char* st, const u32x4_t (&xr)[A_CH], int t) const {
+    if constexpr (STAGED) {
+      const int k0 = (st0 + min(t, nst - 1)) * BK;
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) *reinterpret_cast<u32x4_t*>(st + x_dst + i * 4096) = xr[i];
+      for (int i = 0; i < A_CH; ++i) {
+        const u32x2_t c{quant_word(xr[i][0], xr[i][1], qs[i], qr[i]), quant_word(xr[i][2], xr[i][3], qs[i], qr[i])};
+        *reinterpret_cast<u32x2_t*>(st + x_dst + i * 2048) = c;
+        if (wq && k0 + q_col < K)
+          __builtin_amdgcn_raw_buffer_store_b64(c, rq, q_off[i] + (uint32_t)k0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < A_CH; ++i) *reinterpret_cast<u32x4_t*>(st + x_dst + i * 4096) = xr[i];
+    }
   }
   // batch j (local stages 2j, 2j+1): a chunk whose codes start at or past K
   // reads zeros (K % 32 == 0, so a chunk is wholly inside or outside)
@@ -285,7 +311,7 @@ struct W4Pipe {
     __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0): own LDS writes done
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    store_x(lds + ((S + 2) & 3) * SB, xr);
+    store_x(lds + ((S + 2) & 3) * SB, xr, t + 2);
     issue_x(t + 3, xr);
     if constexpr (S & 1) {
       put_wb(wb);
@@ -304,7 +330,7 @@ struct W4Pipe {
 // loads past the end of K or past the last row are out of range and read
 // zeros.  The A reads and B decode of a stage's first sub-step run during
 // the previous stage's last one.
-template <int MB, int NB>
+template <int MB, int NB, bool STAGED>
 __global__ __launch_bounds__(256) void w4a8_gemm_kernel(Params p) {
   constexpr int BM = MB * 32;
   constexpr int BN = NB * 128;
@@ -316,7 +342,9 @@ __global__ __launch_bounds__(256) void w4a8_gemm_kernel(Params p) {
   const int m0 = tm * BM, n0 = tn * BN;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l32 = lane & 31, h = lane >> 5;
 
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * W4Pipe<MB, NB>::SB + 4 * NB * 32 * 128];
+  using PIPE = W4Pipe<MB, NB, STAGED>;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * PIPE::SB + 4 * NB * 32 * 128];
+  __shared__ float qsh[STAGED ? 2 * BM : 1];  // staged: per row of the tile, s then r
 
   i32x16_t acc[MB][NB];
 #pragma unroll
@@ -326,7 +354,7 @@ __global__ __launch_bounds__(256) void w4a8_gemm_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-  W4Pipe<MB, NB> P;
+  PIPE P;
   P.l32 = l32;
   P.h = h;
   {
@@ -337,9 +365,23 @@ __global__ __launch_bounds__(256) void w4a8_gemm_kernel(Params p) {
   // the range covers the tile's rows: a row past M reads zeros.  x_q chunks
   // past K (last stage, K % 128 != 0) read the next row; the weight words
   // they meet are zeros (see issue_w), so they add nothing.
-  P.rx = make_rsrc(p.xq + (long)m0 * p.K, (uint32_t)(min(BM, p.M - m0) * p.K));
   P.rw = make_rsrc(p.w, (uint32_t)((long)p.N * p.K / 2));
-  {
+  if constexpr (STAGED) {
+    // f16 rows of the tile; thread t takes row t/16 (+ 16 i), 8-value chunk
+    // t%16 of each 128-value stage: 8 codes, half of a 16-byte LDS chunk
+    P.rx = make_rsrc(p.x + (long)m0 * p.K, (uint32_t)(min(BM, p.M - m0) * p.K * 2));
+    P.rq = make_rsrc(p.xq_out + (long)m0 * p.K, (uint32_t)(min(BM, p.M - m0) * p.K));
+    const int r = t >> 4, c = t & 15;
+#pragma unroll
+    for (int i = 0; i < PIPE::A_CH; ++i) {
+      P.x_off[i] = (uint32_t)((16 * i + r) * p.K * 2 + c * 16);
+      P.q_off[i] = (uint32_t)((16 * i + r) * p.K + c * 8);
+    }
+    P.q_col = c * 8;
+    P.x_dst = r * 128 + (((c >> 1) ^ xswz(r)) << 4) + (c & 1) * 8;
+    P.wq = tn == 0;
+  } else {
+    P.rx = make_rsrc(p.xq + (long)m0 * p.K, (uint32_t)(min(BM, p.M - m0) * p.K));
     const int r = t >> 3, c = t & 7;
 #pragma unroll
     for (int i = 0; i < MB; ++i) P.x_off[i] = (uint32_t)((32 * i + r) * p.K + c * 16);
@@ -347,26 +389,67 @@ __global__ __launch_bounds__(256) void w4a8_gemm_kernel(Params p) {
   }
   P.K = p.K;
 #pragma unroll
-  for (int i = 0; i < W4Pipe<MB, NB>::WB; ++i) {
+  for (int i = 0; i < PIPE::WB; ++i) {
     const int r = 8 * i + (lane >> 3), n = n0 + wave * NB * 32 + r;
     P.wb_off[i] = n < p.N ? (uint32_t)((long)n * p.K / 2) : OOB;
-    P.wb_dst[i] = r * 128 + (((lane & 7) ^ W4Pipe<MB, NB>::wswz(r)) << 4);
+    P.wb_dst[i] = r * 128 + (((lane & 7) ^ PIPE::wswz(r)) << 4);
   }
-  P.wreg = lds + 4 * W4Pipe<MB, NB>::SB + wave * (NB * 32 * 128);
+  P.wreg = lds + 4 * PIPE::SB + wave * (NB * 32 * 128);
 
-  u32x4_t xr[MB];
-  u32x4_t wb0[W4Pipe<MB, NB>::WB], wb1[W4Pipe<MB, NB>::WB];  // weight batches, slot j % 2
+  u32x4_t xr[PIPE::A_CH];
+  u32x4_t wb0[PIPE::WB], wb1[PIPE::WB];  // weight batches, slot j % 2
   u32x4_t wA[NB][2], wB[NB][2];  // weight words of the current and the next stage
   // prologue: batch 0 in LDS, batches 1 and 2 in flight; x of stages 0 and
   // 1 in LDS, stage 2 in flight
   P.issue_wb(0, wb0);
   P.issue_wb(1, wb1);
+  if constexpr (STAGED) {
+    // The row maxima over all of K first (the weight batches above are in
+    // flight meanwhile): TPR threads per row, eight 16-byte loads in flight
+    // per thread, |x| by clearing sign bits, maxNum so that a NaN takes no
+    // part (as in the quantize kernel); then s = max/127 and r = 1/s refined,
+    // per row, into LDS.  The first column tile's first split writes s_x.
+    constexpr int TPR = 256 / BM;
+    const int row = t / TPR, part = t % TPR, C = p.K / 8;
+    f16x2_t am2 = {0, 0};
+    for (int j0 = part; j0 < C; j0 += 8 * TPR) {
+      u32x4_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = j0 + u * TPR < C ? ld128(P.rx, (uint32_t)(row * p.K * 2 + (j0 + u * TPR) * 16)) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          am2 = __builtin_elementwise_max(am2, __builtin_bit_cast(f16x2_t, v[u][e] & 0x7FFF7FFFu));
+    }
+    float am = fmaxf((float)am2[0], (float)am2[1]);
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) am = fmaxf(am, __shfl_xor(am, o));
+    if (part == 0) {
+      const float sv = am / 127.0f;  // correctly rounded division (HIP default)
+      float rv = 0.f;
+      if (am != 0.f) {
+        const float r0 = __builtin_amdgcn_rcpf(sv);
+        rv = __builtin_fmaf(__builtin_fmaf(-sv, r0, 1.0f), r0, r0);
+      }
+      qsh[row] = sv;
+      qsh[BM + row] = rv;
+      if (tn == 0 && sp == 0 && m0 + row < p.M) p.sx_out[m0 + row] = sv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PIPE::A_CH; ++i) {
+      P.qs[i] = qsh[(t >> 4) + 16 * i];
+      P.qr[i] = qsh[BM + (t >> 4) + 16 * i];
+    }
+  }
   P.issue_x(0, xr);
   __builtin_amdgcn_sched_barrier(0);
-  P.store_x(lds, xr);
+  P.store_x(lds, xr, 0);
   P.issue_x(1, xr);
   __builtin_amdgcn_sched_barrier(0);
-  P.store_x(lds + W4Pipe<MB, NB>::SB, xr);
+  P.store_x(lds + PIPE::SB, xr, 1);
   P.put_wb(wb0);
   P.issue_wb(2, wb0);
   P.issue_x(2, xr);
@@ -415,8 +498,11 @@ __global__ __launch_bounds__(256) void w4a8_gemm_kernel(Params p) {
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int m = m0 + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-      sxv[mb][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsx, (uint32_t)m * 4u, 0, 0));
+      const int rr = mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      if constexpr (STAGED)
+        sxv[mb][r] = qsh[rr];  // this workgroup's own scales (another may still be writing s_x)
+      else
+        sxv[mb][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsx, (uint32_t)(m0 + rr) * 4u, 0, 0));
     }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -723,90 +809,71 @@ void launch_fused_cw(const W4A8Args& a, int M, int N, int K, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_w4a8(const W4A8Args& a, hipStream_t s) {
-  if (a.K % 32 != 0) return hipErrorNotSupported;
-  // buffer offsets are 32-bit
-  if (a.N * a.K / 2 >= (int64_t(1) << 31) || a.K * 256 >= (int64_t(1) << 31)) return hipErrorNotSupported;
-  const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
-  if (M <= 16 && K <= FUSED_MAX_K) {
-    if (M == 1) launch_fused_cw<1>(a, M, N, K, s);
-    else if (M == 2) launch_fused_cw<2>(a, M, N, K, s);
-    else if (M <= 4) launch_fused_cw<4>(a, M, N, K, s);
-    else if (M <= 8) launch_fused_cw<8>(a, M, N, K, s);
-    else launch_fused_cw<16>(a, M, N, K, s);
-    return hipGetLastError();
-  }
-  {
-    // threads per row: one wave up to 512 values, two up to 1024, then four;
-    // chunks per thread: 1, 2, 4 or 8 (K <= 16384), else one row per block
-    const uint16_t* x = (const uint16_t*)a.x;
-    const int C = K / 8;
-    const dim3 b256(256);
-    if (C <= 64)
-      hipLaunchKernelGGL((w4a8_quant_rows_kernel<1, 1>), dim3((M + 3) / 4), b256, 0, s, x, M, K, a.x_q, a.s_x);
-    else if (C <= 128)
-      hipLaunchKernelGGL((w4a8_quant_rows_kernel<2, 1>), dim3((M + 1) / 2), b256, 0, s, x, M, K, a.x_q, a.s_x);
-    else if (C <= 256)
-      hipLaunchKernelGGL((w4a8_quant_rows_kernel<4, 1>), dim3(M), b256, 0, s, x, M, K, a.x_q, a.s_x);
-    else if (C <= 512)
-      hipLaunchKernelGGL((w4a8_quant_rows_kernel<4, 2>), dim3(M), b256, 0, s, x, M, K, a.x_q, a.s_x);
-    else if (C <= 1024)
-      hipLaunchKernelGGL((w4a8_quant_rows_kernel<4, 4>), dim3(M), b256, 0, s, x, M, K, a.x_q, a.s_x);
-    else if (C <= 2048)
-      hipLaunchKernelGGL((w4a8_quant_rows_kernel<4, 8>), dim3(M), b256, 0, s, x, M, K, a.x_q, a.s_x);
-    else
-      hipLaunchKernelGGL(w4a8_quant_kernel, dim3(M), b256, 0, s, x, K, a.x_q, a.s_x);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_w4a8_product(a, s);
+struct GemmTile {
+  int mb, nb;  // tile (32 mb) x (128 nb)
+};
+
+// the quantize kernel: x -> x_q, s_x
+static hipError_t launch_quant(const W4A8Args& a, hipStream_t s) {
+  // threads per row: one wave up to 512 values, two up to 1024, then four;
+  // chunks per thread: 1, 2, 4 or 8 (K <= 16384), else one row per block
+  const int M = (int)a.M, K = (int)a.K;
+  const uint16_t* x = (const uint16_t*)a.x;
+  const int C = K / 8;
+  const dim3 b256(256);
+  if (C <= 64)
+    hipLaunchKernelGGL((w4a8_quant_rows_kernel<1, 1>), dim3((M + 3) / 4), b256, 0, s, x, M, K, a.x_q, a.s_x);
+  else if (C <= 128)
+    hipLaunchKernelGGL((w4a8_quant_rows_kernel<2, 1>), dim3((M + 1) / 2), b256, 0, s, x, M, K, a.x_q, a.s_x);
+  else if (C <= 256)
+    hipLaunchKernelGGL((w4a8_quant_rows_kernel<4, 1>), dim3(M), b256, 0, s, x, M, K, a.x_q, a.s_x);
+  else if (C <= 512)
+    hipLaunchKernelGGL((w4a8_quant_rows_kernel<4, 2>), dim3(M), b256, 0, s, x, M, K, a.x_q, a.s_x);
+  else if (C <= 1024)
+    hipLaunchKernelGGL((w4a8_quant_rows_kernel<4, 4>), dim3(M), b256, 0, s, x, M, K, a.x_q, a.s_x);
+  else if (C <= 2048)
+    hipLaunchKernelGGL((w4a8_quant_rows_kernel<4, 8>), dim3(M), b256, 0, s, x, M, K, a.x_q, a.s_x);
+  else
+    hipLaunchKernelGGL(w4a8_quant_kernel, dim3(M), b256, 0, s, x, K, a.x_q, a.s_x);
+  return hipGetLastError();
 }
 
-// The integer product and epilogue from x_q and s_x already in memory: the
-// dot4 GEMV for M <= 16, else the int8 MFMA GEMM (plus the summing pass when
-// K is split).
-hipError_t launch_w4a8_product(const W4A8Args& a, hipStream_t s) {
-  const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
-  hipError_t e = hipSuccess;
-  if (M <= 16) {
-    const dim3 grid((unsigned)((N + 3) / 4));
-    const int8_t* xq = a.x_q;
-    const uint32_t* w = a.w;
-    const uint16_t* sw = (const uint16_t*)a.s_w;
-    uint16_t* y = (uint16_t*)a.y;
-    if (M == 1)
-      hipLaunchKernelGGL(w4a8_gemv_kernel<1>, grid, dim3(256), 0, s, xq, a.s_x, w, sw, y, a.acc, M, N, K);
-    else if (M == 2)
-      hipLaunchKernelGGL(w4a8_gemv_kernel<2>, grid, dim3(256), 0, s, xq, a.s_x, w, sw, y, a.acc, M, N, K);
-    else if (M <= 4)
-      hipLaunchKernelGGL(w4a8_gemv_kernel<4>, grid, dim3(256), 0, s, xq, a.s_x, w, sw, y, a.acc, M, N, K);
-    else if (M <= 8)
-      hipLaunchKernelGGL(w4a8_gemv_kernel<8>, grid, dim3(256), 0, s, xq, a.s_x, w, sw, y, a.acc, M, N, K);
-    else
-      hipLaunchKernelGGL(w4a8_gemv_kernel<16>, grid, dim3(256), 0, s, xq, a.s_x, w, sw, y, a.acc, M, N, K);
-    return hipGetLastError();
-  }
-  // Tile: with K of 16 stages or more, the largest whose grid gives every
-  // CU a workgroup; with shorter K (a short loop, where more workgroups
-  // overlap better) 64 x 256 or 64 x 128 if it gives every CU two.  Else
-  // 32 x 128 (half the MFMA work per fragment read, the most workgroups).
-  struct Tile { int mb, nb; };
-  auto count = [&](const Tile& c) {
+static bool shape_ok(const W4A8Args& a) {
+  // K whole 32-code chunks; buffer offsets are 32-bit
+  return a.K % 32 == 0 && a.N * a.K / 2 < (int64_t(1) << 31) && a.K * 256 < (int64_t(1) << 31) &&
+         a.M * a.K * 2 < (int64_t(1) << 31);
+}
+
+// Tile: with K of 16 stages or more, the largest whose grid gives every
+// CU a workgroup; with shorter K (a short loop, where more workgroups
+// overlap better) 64 x 256 or 64 x 128 if it gives every CU two.  Else
+// 32 x 128 (half the MFMA work per fragment read, the most workgroups).
+// The sweep of both lowerings and every tile (bench.py --w4a8-sweep) finds
+// this choice the fastest, or within 3% of it, on each shape of the set.
+static GemmTile auto_tile(int M, int N, int K) {
+  auto count = [&](const GemmTile& c) {
     return (long)((M + c.mb * 32 - 1) / (c.mb * 32)) * ((N + c.nb * 128 - 1) / (c.nb * 128));
   };
   const bool long_k = K >= 16 * BK;
-  const Tile tiles[] = {{4, 2}, {2, 2}, {2, 1}};
-  Tile t{1, 1};
-  for (const Tile& c : tiles) {
+  const GemmTile tiles[] = {{4, 2}, {2, 2}, {2, 1}};
+  for (const GemmTile& c : tiles) {
     if (!long_k && c.mb == 4) continue;
-    if (count(c) >= (long_k ? 256 : 512)) {
-      t = c;
-      break;
-    }
+    if (count(c) >= (long_k ? 256 : 512)) return c;
   }
+  return GemmTile{1, 1};
+}
+
+// The integer product and epilogue on one tile shape: from x_q (full-K
+// lowering, x_q and s_x already written) or from x (staged lowering, which
+// writes x_q and s_x itself).
+static hipError_t launch_gemm_tile(const W4A8Args& a, bool staged, GemmTile t, hipStream_t s) {
+  const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
   Params p;
   p.xq = a.x_q;
   p.sx = a.s_x;
+  p.x = (const uint16_t*)a.x;
+  p.xq_out = a.x_q;
+  p.sx_out = a.s_x;
   p.w = a.w;
   p.sw = (const uint16_t*)a.s_w;
   p.y = (uint16_t*)a.y;
@@ -837,15 +904,24 @@ hipError_t launch_w4a8_product(const W4A8Args& a, hipStream_t s) {
   }
   p.per_xcd = (p.Tm * p.Tn * p.S + 7) / 8;
   const dim3 grid(8 * p.per_xcd);
-  if (t.mb == 4)
-    hipLaunchKernelGGL((w4a8_gemm_kernel<4, 2>), grid, dim3(256), 0, s, p);
-  else if (t.nb == 2)
-    hipLaunchKernelGGL((w4a8_gemm_kernel<2, 2>), grid, dim3(256), 0, s, p);
-  else if (t.mb == 2)
-    hipLaunchKernelGGL((w4a8_gemm_kernel<2, 1>), grid, dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((w4a8_gemm_kernel<1, 1>), grid, dim3(256), 0, s, p);
-  e = hipGetLastError();
+#define QAFF_W4A8_LAUNCH(MB, NB)                                                      \
+  if (staged)                                                                        \
+    hipLaunchKernelGGL((w4a8_gemm_kernel<MB, NB, true>), grid, dim3(256), 0, s, p);  \
+  else                                                                               \
+    hipLaunchKernelGGL((w4a8_gemm_kernel<MB, NB, false>), grid, dim3(256), 0, s, p);
+  if (t.mb == 4 && t.nb == 2) {
+    QAFF_W4A8_LAUNCH(4, 2)
+  } else if (t.mb == 2 && t.nb == 2) {
+    QAFF_W4A8_LAUNCH(2, 2)
+  } else if (t.mb == 2 && t.nb == 1) {
+    QAFF_W4A8_LAUNCH(2, 1)
+  } else if (t.mb == 1 && t.nb == 1) {
+    QAFF_W4A8_LAUNCH(1, 1)
+  } else {
+    return hipErrorNotSupported;
+  }
+#undef QAFF_W4A8_LAUNCH
+  hipError_t e = hipGetLastError();
   if (e == hipSuccess && p.S > 1) {
     const long MN = (long)M * N;
     hipLaunchKernelGGL(w4a8_split_sum_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, s, p.part, p.S, M, N,
@@ -853,6 +929,76 @@ hipError_t launch_w4a8_product(const W4A8Args& a, hipStream_t s) {
     e = hipGetLastError();
   }
   return e;
+}
+
+// Which lowering runs when the caller does not choose (M > 16): the
+// full-K one.  The staged lowering quantizes x once per column tile inside
+// the GEMM; on every shape of the sweep that repeated work cost more than
+// the x_q round trip it saves (qgemm_w4a8_tiled still runs it).
+static bool staged_default(int M, int N, int K) {
+  (void)M;
+  (void)N;
+  (void)K;
+  return false;
+}
+
+hipError_t launch_w4a8_product(const W4A8Args& a, hipStream_t s) {
+  const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
+  if (M <= 16) {
+    const dim3 grid((unsigned)((N + 3) / 4));
+    const int8_t* xq = a.x_q;
+    const uint32_t* w = a.w;
+    const uint16_t* sw = (const uint16_t*)a.s_w;
+    uint16_t* y = (uint16_t*)a.y;
+    if (M == 1)
+      hipLaunchKernelGGL(w4a8_gemv_kernel<1>, grid, dim3(256), 0, s, xq, a.s_x, w, sw, y, a.acc, M, N, K);
+    else if (M == 2)
+      hipLaunchKernelGGL(w4a8_gemv_kernel<2>, grid, dim3(256), 0, s, xq, a.s_x, w, sw, y, a.acc, M, N, K);
+    else if (M <= 4)
+      hipLaunchKernelGGL(w4a8_gemv_kernel<4>, grid, dim3(256), 0, s, xq, a.s_x, w, sw, y, a.acc, M, N, K);
+    else if (M <= 8)
+      hipLaunchKernelGGL(w4a8_gemv_kernel<8>, grid, dim3(256), 0, s, xq, a.s_x, w, sw, y, a.acc, M, N, K);
+    else
+      hipLaunchKernelGGL(w4a8_gemv_kernel<16>, grid, dim3(256), 0, s, xq, a.s_x, w, sw, y, a.acc, M, N, K);
+    return hipGetLastError();
+  }
+  return launch_gemm_tile(a, false, auto_tile(M, N, K), s);
+}
+
+hipError_t launch_w4a8(const W4A8Args& a, hipStream_t s) {
+  if (!shape_ok(a)) return hipErrorNotSupported;
+  const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
+  if (M <= 16 && K <= FUSED_MAX_K) {
+    if (M == 1) launch_fused_cw<1>(a, M, N, K, s);
+    else if (M == 2) launch_fused_cw<2>(a, M, N, K, s);
+    else if (M <= 4) launch_fused_cw<4>(a, M, N, K, s);
+    else if (M <= 8) launch_fused_cw<8>(a, M, N, K, s);
+    else launch_fused_cw<16>(a, M, N, K, s);
+    return hipGetLastError();
+  }
+  if (M <= 16) {
+    const hipError_t e = launch_quant(a, s);
+    if (e != hipSuccess) return e;
+    return launch_w4a8_product(a, s);
+  }
+  const GemmTile t = auto_tile(M, N, K);
+  if (!staged_default(M, N, K)) {
+    const hipError_t e = launch_quant(a, s);
+    if (e != hipSuccess) return e;
+    return launch_gemm_tile(a, false, t, s);
+  }
+  return launch_gemm_tile(a, true, t, s);
+}
+
+hipError_t launch_w4a8_config(const W4A8Args& a, int staged, int bm, int bn, hipStream_t s) {
+  if (!shape_ok(a) || a.M <= 16) return hipErrorNotSupported;
+  const GemmTile t{bm / 32, bn / 128};
+  if (bm % 32 || bn % 128) return hipErrorNotSupported;
+  if (!staged) {
+    const hipError_t e = launch_quant(a, s);
+    if (e != hipSuccess) return e;
+  }
+  return launch_gemm_tile(a, staged != 0, t, s);
 }
 
 }  // namespace qaff

@@ -247,6 +247,29 @@ int qgemm_w4a8(const void *x, const uint32_t *w_q4, const void *s_w, void *y, in
                int32_t *acc_out, int64_t M, int64_t N, int64_t K, void *stream);
 
 /*
+ * qgemm_w4a8_tiled - qgemm_w4a8 for M > 16 with the lowering and the tile
+ * chosen by the caller, for tile sweeps and tests (executorch PR #24467,
+ * "What this adds": the two lowerings and their tile template parameters).
+ *   staged = 0: the full-K lowering, as qgemm_w4a8 runs it: the per-token
+ *     quantize kernel writes x_q and s_x, then the int8 x int4 GEMM reads
+ *     them.
+ *   staged = 1: one kernel.  Each workgroup takes the maxima of its rows of
+ *     x, then quantizes x one 128-code K tile at a time into LDS on its way
+ *     to the matrix cores (the workgroups of the first column tile also
+ *     store x_q and s_x).  No x_q round trip through memory; the quantize
+ *     work is repeated once per column tile.
+ *   bm x bn: the output tile, one of 32x128, 64x128, 64x256, 128x256 (the
+ *     K tile is 128 codes).
+ * Outputs are the same bits for every lowering and tile (x_q, s_x and acc
+ * exact; y the same f16 rounding of the same products), as qgemm_w4a8
+ * defines them.  Other tiles and M <= 16 (the GEMV paths) return
+ * QAFF_E_UNSUPPORTED; the other arguments and errors as for qgemm_w4a8.
+ */
+int qgemm_w4a8_tiled(const void *x, const uint32_t *w_q4, const void *s_w, void *y, int8_t *x_q, float *s_x,
+                     int32_t *acc_out, int64_t M, int64_t N, int64_t K, int32_t staged, int32_t bm, int32_t bn,
+                     void *stream);
+
+/*
  * SmoothQuant ahead of W4A8 (TinyGPT "Quantization Expansion", section 3
  * "SmoothQuant"): a per-input-channel factor s moves activation range into
  * the weights, y = (x / s) . (s W)^T, so that outlier channels of x no

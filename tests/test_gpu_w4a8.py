@@ -156,3 +156,73 @@ def test_largest_tile():
     # largest tile (sampled rows against the oracle)
     case = si.w4a8_case(2048, 4096, 2048, seed=(48,), name="w4a8_tile_128x256")
     _check(case, si.sample_indices(2048, 48, seed=(48, 1)))
+
+
+TILES = [(32, 128), (64, 128), (64, 256), (128, 256)]
+
+
+def _check_tiled(case, staged, bm, bn, rows=None):
+    dev = require_gpu()
+    print(f"[case] {case.name} staged={staged} tile={bm}x{bn} M={case.M} N={case.N} K={case.K}", flush=True)
+    x = dev16(case.x, "f16", dev)
+    w = torch.from_numpy(np.ascontiguousarray(case.w_q4).view(np.int32)).to(dev)
+    sw = dev16(case.s_w, "f16", dev)
+    y, xq, sx, acc = qa.qgemm_w4a8_tiled(x, w, sw, staged, bm, bn, want_acc=True)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.w4a8_quantize_act(case.x, case.M, case.K)
+    np.testing.assert_array_equal(xq.cpu().numpy(), q_ref)
+    np.testing.assert_array_equal(sx.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    rows = np.arange(case.M) if rows is None else rows
+    acc_ref = oracle.w4a8_acc(q_ref[rows], case.w_q4, len(rows), case.N, case.K)
+    np.testing.assert_array_equal(acc.cpu().numpy()[rows].astype(np.int64), acc_ref)
+    y_ref = acc_ref.astype(np.float64) * s_ref[rows].astype(np.float64)[:, None] * \
+        oracle.to_f64(case.s_w, "f16")[None, :]
+    assert_float_bar(host_f64(y)[rows], y_ref, case.name)
+    return y, acc
+
+
+@pytest.mark.parametrize("staged", [0, 1])
+@pytest.mark.parametrize("bm,bn", TILES)
+@pytest.mark.parametrize("M", [128, 2048])
+@pytest.mark.parametrize("N,K", si.CFG4_SHAPES)
+def test_cfg4_each_lowering_and_tile(N, K, M, bm, bn, staged):
+    # both lowerings, every built tile, on the set's M > 16 shapes: codes,
+    # scales and accumulators exact against the oracle (sampled rows at
+    # M = 2048), y within the float bar
+    case = si.cfg4_case(N, K, M, seed=(4, N, K, M))
+    rows = None if M <= 128 else si.sample_indices(M, 40, seed=(4, 10, M))
+    _check_tiled(case, staged, bm, bn, rows)
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 1000, 1056), (100, 520, 4128), (300, 2056, 160), (33, 136, 8192)])
+@pytest.mark.parametrize("bm,bn", [(32, 128), (128, 256)])
+def test_staged_ragged_and_split(M, N, K, bm, bn):
+    # rows past M, columns past N, a last K tile of 32 or 96 codes; few
+    # tiles with a long K split it over workgroups (int32 partials)
+    case = si.w4a8_case(M, N, K, seed=(49, M, N, K), name=f"w4a8_staged_M{M}_N{N}_K{K}")
+    _check_tiled(case, 1, bm, bn)
+
+
+def test_staged_same_bits_as_full_k():
+    # the two lowerings give the same y bits (the same integer sums, scales
+    # and rounding), on a shape where each runs its own kernels
+    case = si.w4a8_case(256, 1024, 2048, seed=(50,), name="w4a8_staged_vs_fullk")
+    y0, a0 = _check_tiled(case, 0, 64, 128)
+    y1, a1 = _check_tiled(case, 1, 64, 128)
+    assert torch.equal(a0, a1)
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+
+
+def test_tiled_rejects_small_m_and_unbuilt_tiles():
+    dev = require_gpu()
+    case = si.w4a8_case(16, 256, 256, seed=(51,), name="w4a8_small")
+    x = dev16(case.x, "f16", dev)
+    w = torch.from_numpy(np.ascontiguousarray(case.w_q4).view(np.int32)).to(dev)
+    sw = dev16(case.s_w, "f16", dev)
+    with pytest.raises(qa.QaffError) as e1:
+        qa.qgemm_w4a8_tiled(x, w, sw, True, 64, 128)
+    assert e1.value.status == 2
+    x2 = torch.zeros((64, 256), dtype=torch.float16, device=dev)
+    with pytest.raises(qa.QaffError) as e2:
+        qa.qgemm_w4a8_tiled(x2, w, sw, True, 96, 128)
+    assert e2.value.status == 2
