@@ -523,19 +523,20 @@ struct MfmaGeo {
 };
 __device__ __forceinline__ int par_swz(int r, int piece) { return r * 128 + ((piece ^ ((r >> 1) & 7)) << 4); }
 
-// Stage t of the MFMA GEMV: write stage t+1 (loaded two stages ago) to LDS,
-// barrier (stage t+1 is in LDS, stage t was written a stage ago, and every
-// wave is done with stage t-3, whose buffer stage t+1 reuses), issue the
-// loads of stage t+3 and the x fragments of stage t+2, compute stage t.
-template <class Put, class IssueW, class IssueX, class Compute, class X>
-__device__ __forceinline__ void mfma_stage(Put& put, IssueW& issue_w, IssueX& issue_x, Compute& compute, int t,
-                                           bool active, const unsigned char* cur, const X& xc, unsigned char* nxt,
-                                           const u32x4_t (&wn)[4], u32x4_t (&wf)[4], X& xf) {
-  put(nxt, wn);
-  __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+// Stage t of the MFMA GEMV: wait for this wave's copies of stage t's packed
+// words (issued three stages ago; the 16 vector-memory operations issued
+// since, two stages of copies and x loads, may still be in flight, and a
+// parameter chunk's loads in between only make the wait stricter), barrier
+// (stage t is in LDS for every wave, and every wave is done with stage t-1,
+// whose buffer the copies of stage t+3 reuse), copy stage t+3 into LDS,
+// load the x fragments of stage t+2, compute stage t.
+template <class IssueW, class IssueX, class Compute, class X>
+__device__ __forceinline__ void mfma_stage(IssueW& issue_w, IssueX& issue_x, Compute& compute, int t, bool active,
+                                           const unsigned char* cur, const X& xc, unsigned char* nxt3, X& xf) {
+  __builtin_amdgcn_s_waitcnt((16 & 15) | (7 << 4) | (0 << 8) | ((16 >> 4) << 14));  // vmcnt(16) lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  issue_w(t + 3, wf);
+  issue_w(t + 3, nxt3);
   issue_x(t + 2, xf);
   __builtin_amdgcn_sched_barrier(0);
   if (active) compute(cur, xc, t);
@@ -571,14 +572,15 @@ __global__ __launch_bounds__(256, 2) void gemv_mfma4_kernel(MfmaBatch B) {
   const int L = K >> 3, ng = K / G, nsp = K >> 7, nst = (K + 511) >> 9;
   const int ncols = min(N - col0, 64);
 
-  // Packed words: rows 16i + 4*wave + lane/16 (i < 4), piece lane % 16 of
-  // the stage's 256 bytes, stored to LDS slot piece ^ (row % 16).  Rows past
-  // N are out of range; a piece past the row end reads the next row.
+  // Packed words go global -> LDS directly (a copy of 16 bytes per lane,
+  // lane l of a wave's copy i landing at row 16i + 4*wave + l/16, slot
+  // l % 16).  Slot s of row r holds the stage's 16-byte piece s ^ (r % 16),
+  // so lane l reads that piece.  Rows past N are out of range (zeros); a
+  // piece past the row end reads the next row.
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(static_cast<const uint32_t*>(D.w) + (long)col0 * LF,
                                                 (uint32_t)(((ncols - 1) * LF + L) * 4));
   const int wrow = 4 * wave + (lane >> 4);
-  const uint32_t wv = (uint32_t)(wrow * LF * 4 + (lane & 15) * 16);
-  const int wdst = wrow * 256 + (((lane & 15) ^ (wrow & 15)) << 4);  // + i*16*256
+  const uint32_t wv = (uint32_t)(wrow * LF * 4 + (((lane & 15) ^ (wrow & 15)) * 16));
   // Scale (waves 0, 1) or bias (waves 2, 3) chunks: rows 32*(wave&1) + 8i +
   // lane/8 (i < 4), piece lane % 8 of the row's 128 bytes; every wave-level
   // load covers 8 whole rows' chunks.
@@ -593,12 +595,16 @@ __global__ __launch_bounds__(256, 2) void gemv_mfma4_kernel(MfmaBatch B) {
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(D.x, (uint32_t)(((M - 1) * KF + K) * 2));
   const uint32_t xv = c < M ? (uint32_t)(c * KF * 2) : OOB;
 
-  // loads of stage tw's packed words; a stage past the end loads nothing
-  // (offsets out of range)
-  auto issue_w = [&](int tw, W& wr) __attribute__((always_inline)) {
-    const uint32_t wo = (tw < nst ? wv : OOB) + (uint32_t)tw * 256u;
+  // copies of stage tw's packed words into LDS stage st; a stage past the
+  // end copies zeros (offsets out of range) into a buffer no one reads
+  auto issue_w = [&](int tw, unsigned char* __restrict__ st) __attribute__((always_inline)) {
+    const uint32_t wo = (tw < nst ? wv : OOB);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wr[i] = ld128<NT>(rw, wo + (uint32_t)(16 * i * LF * 4));  // streamed once: non-temporal
+    for (int i = 0; i < 4; ++i) {
+      const int so = __builtin_amdgcn_readfirstlane(tw * 256 + 16 * i * LF * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void*)(st + (16 * i + 4 * wave) * 256),
+                                               16, wo, so, 0, 2);  // streamed once: non-temporal
+    }
   };
   // loads of parameter chunk ch
   auto issue_p = [&](int ch, u32x4_t (&pr)[4]) __attribute__((always_inline)) {
@@ -617,10 +623,6 @@ __global__ __launch_bounds__(256, 2) void gemv_mfma4_kernel(MfmaBatch B) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) xr[j] = ld128(rx, xo + Geo::word(h, j) * 16);
   };
-  auto put = [&](unsigned char* st, const W& wr) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(st + wdst + i * 16 * 256) = wr[i];
-  };
 
   uint32_t magic = F16 ? 0x64006400u : 0x43004300u;
   asm volatile("" : "+v"(magic));
@@ -630,7 +632,7 @@ __global__ __launch_bounds__(256, 2) void gemv_mfma4_kernel(MfmaBatch B) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) y[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const unsigned char* st, const X& xr, int t) __attribute__((always_inline)) {
+  auto compute = [&](const unsigned char* __restrict__ st, const X& xr, int t) __attribute__((always_inline)) {
     // packed words of the span for the four blocks
     u32x4_t wq[NB];
 #pragma unroll
@@ -639,9 +641,13 @@ __global__ __launch_bounds__(256, 2) void gemv_mfma4_kernel(MfmaBatch B) {
       if constexpr (G == 128) {
         wq[nb] = *reinterpret_cast<const u32x4_t*>(row + (((4 * wave + h) ^ c) << 4));
       } else if constexpr (G == 64) {
-        const uint2 a = *reinterpret_cast<const uint2*>(row + (((4 * wave + (h >> 1)) ^ c) << 4) + (h & 1) * 8);
-        const uint2 b = *reinterpret_cast<const uint2*>(row + (((4 * wave + 2 + (h >> 1)) ^ c) << 4) + (h & 1) * 8);
-        wq[nb] = u32x4_t{a.x, a.y, b.x, b.y};
+        // whole 16-byte pieces, the lane's half selected after: two 8-byte
+        // reads would be merged into one instruction that the compiler can
+        // no longer tell apart from the LDS copies in flight (and would wait
+        // for all of them)
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(row + (((4 * wave + (h >> 1)) ^ c) << 4));
+        const u32x4_t b = *reinterpret_cast<const u32x4_t*>(row + (((4 * wave + 2 + (h >> 1)) ^ c) << 4));
+        wq[nb] = (h & 1) ? u32x4_t{a.z, a.w, b.z, b.w} : u32x4_t{a.x, a.y, b.x, b.y};
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -709,24 +715,23 @@ __global__ __launch_bounds__(256, 2) void gemv_mfma4_kernel(MfmaBatch B) {
 
   // four stages in a ring, unrolled so that every buffer is static
   X x0, x1, x2, x3;
-  W w0, w1, w2, w3;
   u32x4_t pc[4];
   // parameter chunk 0 to LDS, chunk 1 in flight
   issue_p(0, pc);
   put_p(pc);
   __builtin_amdgcn_sched_barrier(0);
   issue_p(1, pc);
-  // the prologue keeps the loop's load order, so that the wait counts the
-  // compiler derives at the loop head hold for both ways in
-  issue_w(0, w0);
+  // the prologue keeps the loop's load order (copies of stage t, then x of
+  // stage t), so that 16 operations follow stage t's copies when stage t
+  // waits for them
+  issue_w(0, st0);
   issue_x(0, x0);
   __builtin_amdgcn_sched_barrier(0);
-  issue_w(1, w1);
+  issue_w(1, st1);
   issue_x(1, x1);
   __builtin_amdgcn_sched_barrier(0);
-  issue_w(2, w2);
+  issue_w(2, st2);
   __builtin_amdgcn_sched_barrier(0);
-  put(st0, w0);
   // Whole rounds of four stages (K = 2048 n needs no other): a stage past
   // the end loads nothing and computes nothing, and the loop body has no
   // branch around a stage.  A chunk of CS (a multiple of 4) stages ends with
@@ -734,10 +739,10 @@ __global__ __launch_bounds__(256, 2) void gemv_mfma4_kernel(MfmaBatch B) {
   // and biases replace it in LDS (visible after the next barrier) and the
   // one after that is loaded.
   for (int t = 0; t < nst; t += 4) {
-    mfma_stage(put, issue_w, issue_x, compute, t, 4 * t + wave < nsp, st0, x0, st1, w1, w3, x2);
-    mfma_stage(put, issue_w, issue_x, compute, t + 1, 4 * t + 4 + wave < nsp, st1, x1, st2, w2, w0, x3);
-    mfma_stage(put, issue_w, issue_x, compute, t + 2, 4 * t + 8 + wave < nsp, st2, x2, st3, w3, w1, x0);
-    mfma_stage(put, issue_w, issue_x, compute, t + 3, 4 * t + 12 + wave < nsp, st3, x3, st0, w0, w2, x1);
+    mfma_stage(issue_w, issue_x, compute, t, 4 * t + wave < nsp, st0, x0, st3, x2);
+    mfma_stage(issue_w, issue_x, compute, t + 1, 4 * t + 4 + wave < nsp, st1, x1, st0, x3);
+    mfma_stage(issue_w, issue_x, compute, t + 2, 4 * t + 8 + wave < nsp, st2, x2, st1, x0);
+    mfma_stage(issue_w, issue_x, compute, t + 3, 4 * t + 12 + wave < nsp, st3, x3, st2, x1);
     if ((t + 4) % CS == 0 && t + 4 < nst) {
       __builtin_amdgcn_s_barrier();
       put_p(pc);
