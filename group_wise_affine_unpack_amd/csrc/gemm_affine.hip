@@ -13,7 +13,9 @@
 // fp16's normal range.  Then
 //     y[m,n] = 2^(e_m+e_n) * ( sum_k xh[m,k] * sum_{a,j} c_a p_a s_j
 //                            + sum_g xs[m,g] * cb[n,g] )
-// with xs the group sums of xh and cb = (OFF*scale + bias) * 2^-e_n.  The
+// with xs the group sums of xh and cb = (OFF*scale + bias) * 2^-e_n.  (At
+// 4-bit every B value carries an extra factor 16, a free by-product of the
+// decode; the tail entries carry it too and e_n is 4 lower.)  The
 // first sum runs on v_mfma_f32_32x32x16_f16 (one pass per (a, j) pair: 1 for
 // 4-bit codes with bf16 scales, 2 for 8-bit codes or f16 scales); the second
 // is a short tail of v_mfma_f32_32x32x16_bf16 over 3*K/G columns carrying
@@ -196,7 +198,7 @@ __device__ __forceinline__ void prep_x_row(int m, const void* __restrict__ x, in
 // group serves two K tiles and is written for both), so the 32 rows a wave
 // of the GEMM needs for one K tile are one coalesced load.
 //   1. e_n: the exponent of the row's largest |scale|, less ESHIFT (a wave
-//      per two rows)
+//      per two rows); the tail entries and the output use e_n - MSHIFT
 //   2. per (row, group), n fastest across the threads: the bias tail
 //      entries cb = (off*s + b) * 2^-e_n as bf16 (hi, lo, hi) and the scale
 //      pieces, from one load of the scale and the bias
@@ -205,7 +207,8 @@ __device__ __forceinline__ void prep_x_row(int m, const void* __restrict__ x, in
 constexpr int PW = 8;
 template <int PS>
 __device__ __forceinline__ void prep_w_rows(int blk, const void* __restrict__ scales, int s_dt,
-                                            const void* __restrict__ biases, int b_dt, float off, int eshift, int N,
+                                            const void* __restrict__ biases, int b_dt, float off, int eshift, int mshift,
+                                            int N,
                                             int Np,
                                             int ng, int G, int Kt, uint32_t* __restrict__ sh, uint16_t* __restrict__ tB,
                                             int* __restrict__ en) {
@@ -223,10 +226,10 @@ __device__ __forceinline__ void prep_w_rows(int blk, const void* __restrict__ sc
 #pragma unroll
     for (int u = 0; u < PW / 4; ++u) {
       const int r = wave + 4 * u;
-      const int e = exp_of(wave_max(smax[u])) - eshift;
+      const int e = exp_of(wave_max(smax[u])) - eshift;  // of the scale pieces
       if (lane == 0) {
         e_s[r] = e;
-        en[n0 + r] = e;
+        en[n0 + r] = e - mshift;  // the output's: B values carry 2^mshift
       }
     }
   }
@@ -243,7 +246,7 @@ __device__ __forceinline__ void prep_w_rows(int blk, const void* __restrict__ sc
       const float sv = load_as_f32(scales, (long)n * ng + g, s_dt);
       const float bv = load_as_f32(biases, (long)n * ng + g, b_dt);
       const float p2 = ldexpf(1.f, -e_s[r]);
-      const float cb = fmaf(off, sv, bv) * p2;
+      const float cb = fmaf(off, sv, bv) * ldexpf(p2, mshift);  // with the B values' factor 2^mshift
       th = f32_to_bf16_bits(cb);
       tl = f32_to_bf16_bits(cb - bf16_bits_to_f32(th));
       float rr = sv * p2;  // exact: a power of two
@@ -289,7 +292,7 @@ struct PrepArgs {
   uint16_t* tB;
   int* en;
   float off;
-  int eshift;
+  int eshift, mshift;
   int act_dt, s_dt, b_dt;
   int M, N, K, G, Kt, BM, Mp, Np, ng;
 };
@@ -300,7 +303,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   if (b < a.Mp)
     prep_x_row<BITS>(b, a.x, a.act_dt, a.k_perm, a.M, a.K, a.G, a.Kt, a.BM, a.xh, a.tA, a.em);
   else
-    prep_w_rows<PS>(b - a.Mp, a.scales, a.s_dt, a.biases, a.b_dt, a.off, a.eshift, a.N, a.Np, a.ng, a.G, a.Kt, a.sh, a.tB,
+    prep_w_rows<PS>(b - a.Mp, a.scales, a.s_dt, a.biases, a.b_dt, a.off, a.eshift, a.mshift, a.N, a.Np, a.ng, a.G, a.Kt, a.sh, a.tB,
                     a.en);
 }
 
@@ -336,33 +339,50 @@ struct Decode {
   static constexpr float OFFQ = BITS == 4 ? 8.f : (BITS == 8 ? 136.f : 0.f);
   // The row's largest |scale| is brought to [2^ESHIFT, 2^(ESHIFT+1)): as
   // high as the largest code piece times scale piece still fits fp16 (4-bit:
-  // 8 * 2^12; 8-bit: 8 * 16 * 2^9; 2-bit: 3 * 2^13), so that scales down to
-  // 2^-(14+ESHIFT) of the row's largest stay normal fp16 numbers, exact.
-  static constexpr int ESHIFT = BITS == 4 ? 11 : (BITS == 8 ? 8 : 12);
+  // 128 * 2^8, with the factor 16 below; 8-bit: 128 * 2^9; 2-bit:
+  // 3 * 2^13), so that scales down to 2^-(14+ESHIFT) of the row's largest
+  // stay normal fp16 numbers, exact.
+  static constexpr int ESHIFT = BITS == 4 ? 7 : (BITS == 8 ? 8 : 12);
+  // 4-bit B values carry a factor 16 (below); the pre-pass takes it out of
+  // the row exponent e_n that scales the tail operand and the output
+  static constexpr int MSHIFT = BITS == 4 ? 4 : 0;
   // `magic` holds 0x64006400 in a VGPR, so mask-and-insert is one
-  // v_and_or_b32 (a VOP3 op reads at most one literal or SGPR on gfx950)
+  // v_and_or_b32 (a VOP3 op reads at most one literal or SGPR on gfx950).
+  // A nibble masked in place at bits 0-3 of a half gives 1024 + q; one at
+  // bits 4-7 gives 1024 + 16 q with no shift (the fp16 ulp at 1024 is 1), so
+  // a 32-bit word needs one shift (by 8) for its four nibble positions.
+  // 4-bit: v[0][i] = (q - 8) for i even, 16 (q - 8) for i odd; decode_b
+  // multiplies the even ones by 16 s, the odd ones by s: every B value is
+  // 16 (q - 8) s, exact (at most 128 * 2^8 < 2^15 in magnitude).
+  // 8-bit: the high nibble (weight 16) is placed at bits 4-7, the low one at
+  // bits 0-3, both multiplied by s.
   static __device__ __forceinline__ void pieces(const uint32_t* wd, int half, uint32_t magic,
                                                 f16x2_t (&v)[NPIECE][4]) {
     const f16x2_t k1032 = {(_Float16)-1032.f, (_Float16)-1032.f};
+    const f16x2_t k1152 = {(_Float16)-1152.f, (_Float16)-1152.f};
     const f16x2_t k1024 = {(_Float16)-1024.f, (_Float16)-1024.f};
     if constexpr (BITS == 4) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[0][i] = h2(((wd[0] >> (4 * i)) & 0x000F000Fu) | magic) + k1032;
+      const uint32_t t = wd[0] >> 8;
+      v[0][0] = h2((wd[0] & 0x000F000Fu) | magic) + k1032;  // codes (c0, c4)
+      v[0][1] = h2((wd[0] & 0x00F000F0u) | magic) + k1152;  // (c1, c5), x16
+      v[0][2] = h2((t & 0x000F000Fu) | magic) + k1032;      // (c2, c6)
+      v[0][3] = h2((t & 0x00F000F0u) | magic) + k1152;      // (c3, c7), x16
     } else if constexpr (BITS == 8) {
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
-        v[0][2 * w] = h2(((wd[w] >> 4) & 0x000F000Fu) | magic) + k1032;       // hi nibbles (c0,c2)
-        v[0][2 * w + 1] = h2(((wd[w] >> 12) & 0x000F000Fu) | magic) + k1032;  // (c1,c3)
-        v[1][2 * w] = h2((wd[w] & 0x000F000Fu) | magic) + k1032;              // lo nibbles
-        v[1][2 * w + 1] = h2(((wd[w] >> 8) & 0x000F000Fu) | magic) + k1032;
+        const uint32_t t = wd[w] >> 8;
+        v[0][2 * w] = h2((wd[w] & 0x00F000F0u) | magic) + k1152;  // hi nibbles (c0,c2), x16
+        v[0][2 * w + 1] = h2((t & 0x00F000F0u) | magic) + k1152;   // (c1,c3), x16
+        v[1][2 * w] = h2((wd[w] & 0x000F000Fu) | magic) + k1032;  // lo nibbles
+        v[1][2 * w + 1] = h2((t & 0x000F000Fu) | magic) + k1032;
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[0][i] = h2(((wd[0] >> (2 * (i + 4 * half))) & 0x00030003u) | magic) + k1024;
     }
   }
-  // multiplier of piece a
-  static constexpr float piece_mult(int a) { return (BITS == 8 && a == 0) ? 16.f : 1.f; }
+  // factor of the scale piece for entry i of piece a (4-bit even entries)
+  static constexpr bool times16(int i) { return BITS == 4 && (i & 1) == 0; }
 };
 
 // Main GEMM.  512 threads = 8 waves, two per SIMD; tile BM x 256 with
@@ -494,11 +514,11 @@ struct Gemm {
       for (int a = 0; a < D::NPIECE; ++a)
 #pragma unroll
         for (int j = 0; j < PS; ++j) {
-          f16x2_t sj = h2(sc[nb][j]);
-          if (D::piece_mult(a) != 1.f) sj = sj * f16x2_t{(_Float16)16.f, (_Float16)16.f};
+          const f16x2_t sj = h2(sc[nb][j]);
+          const f16x2_t sj16 = sj * f16x2_t{(_Float16)16.f, (_Float16)16.f};  // (unused unless 4-bit)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const f16x2_t q = vv[a][i] * sj;
+            const f16x2_t q = vv[a][i] * (D::times16(i) ? sj16 : sj);
             bf[nb][a * PS + j][2 * i] = q[0];
             bf[nb][a * PS + j][2 * i + 1] = q[1];
           }
@@ -900,6 +920,7 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
   pa.en = en;
   pa.off = Decode<BITS>::OFFQ;
   pa.eshift = Decode<BITS>::ESHIFT;
+  pa.mshift = Decode<BITS>::MSHIFT;
   pa.act_dt = a.act_dt;
   pa.s_dt = a.s_dt;
   pa.b_dt = a.b_dt;
