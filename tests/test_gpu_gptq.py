@@ -204,10 +204,11 @@ def test_split_k_sums_on_every_call():
             assert_float_bar(host_f64(y), ref, f"{case.name} pass {rep}")
 
 
-def test_split_k_sums_under_graph_replay():
+@pytest.mark.parametrize("M,N,G", [(2, 2040, 64), (1, 2040, 64), (1, 4104, 128)])
+def test_split_k_sums_under_graph_replay(M, N, G):
     # a captured call replayed into an output refilled with NaN each time
     dev = require_gpu()
-    case = si.gptq_case(2, 4096, 2040, 64, seed=(57,), name="gptq_rep_graph")
+    case = si.gptq_case(M, 4096, N, G, seed=(57, M, N), name=f"gptq_rep_graph_M{M}_N{N}")
     ref = oracle.qmm_gptq(case.x, case.qweight, case.qzeros, case.scales, case.g_idx, case.M, case.K, case.N, case.G)
     x, qw, qz, s, gi = _dev(case, dev)
     _log(case, "graph replays")
@@ -227,6 +228,46 @@ def test_split_k_sums_under_graph_replay():
         g.replay()
         torch.cuda.synchronize()
         assert_float_bar(host_f64(y), ref, f"{case.name} replay {rep}")
+
+
+# One x row over shapes that stress the direct kernel's split of columns
+# and K: few and many column groups, one group, a short last K slice.
+@pytest.mark.parametrize("N,K,G", [
+    (2040, 4096, 64),    # 64 groups
+    (136, 2048, 32),     # 64 groups, most lanes of the last column group past N
+    (8, 4096, 128),      # one column group, most lanes past N
+    (512, 128, 128),     # one group
+    (11008, 1024, 32),   # 32 groups, many column groups
+    (1000, 2816, 128),   # 22 groups, a short last slice
+])
+@pytest.mark.parametrize("act_order", [True, False])
+def test_one_row_shapes(N, K, G, act_order):
+    dev = require_gpu()
+    case = si.gptq_case(1, K, N, G, seed=(59, N, K, G), act_order=act_order, name=f"gptq_row_N{N}_K{K}_G{G}")
+    if not act_order:
+        case.g_idx = None
+    _log(case, "direct, one row")
+    x, qw, qz, s, gi = _dev(case, dev)
+    y = torch.full((1, N), float("nan"), dtype=torch.float16, device=dev)
+    qa.qmm_gptq(x, qw, qz, s, gi, G, out=y)
+    torch.cuda.synchronize()
+    ref = oracle.qmm_gptq(case.x, case.qweight, case.qzeros, case.scales, case.g_idx, 1, K, N, G)
+    assert_float_bar(host_f64(y), ref, case.name)
+
+
+def test_one_row_scale_range():
+    # scales over three decades and activations 8x the usual (outputs up to
+    # about 2e4, inside fp16): the weights are exact in fp32 whatever the
+    # range
+    dev = require_gpu()
+    case = si.gptq_case(1, 4096, 1024, 128, seed=(60,), scale_range=(1e-3, 4.0), name="gptq_row_scale_range")
+    case.x = si.f16_bits(si.bits_to_f32(case.x, "f16") * np.float32(8.0))
+    _log(case, "direct, one row")
+    x, qw, qz, s, gi = _dev(case, dev)
+    y = qa.qmm_gptq(x, qw, qz, s, gi, case.G)
+    torch.cuda.synchronize()
+    ref = oracle.qmm_gptq(case.x, case.qweight, case.qzeros, case.scales, case.g_idx, 1, case.K, case.N, case.G)
+    assert_float_bar(host_f64(y), ref, case.name)
 
 
 # Act-order with more groups than the per-workgroup LDS table holds (above
