@@ -14,6 +14,11 @@ entry point (qgemv_affine_grouped: 56 problems per launch, so 2 launches for
 with almost no launch gaps.  In the same JSON line:
   decode_chain   the same linears in decoder dependency order, one grouped
                  call per dependent step (qkv, o, gate+up, down): 64 launches
+  decode_chain_one_launch
+                 a decoder chain of the same weights whose stages really depend
+                 on each other (o reads q and adds h, gate/up read o, down reads
+                 silu(gate)*up and adds o, the next layer reads down), all 64
+                 stages in one launch (qgemv_affine_chain_run)
   per_linear     one qmm_affine launch per linear: 112 launches
   cfg0_hot       the single 2048x2048 linear relaunched on the same weights
                  (cache-resident: NOT an HBM figure)
@@ -302,6 +307,22 @@ class Decode:
     def run_chain(self):
         for c in self.chain:
             c()
+
+    def chain_plan(self):
+        """The decoder chain with real dependencies, one plan for the stack:
+        q/k/v read h; o reads q (the attention output's stand-in) plus h;
+        gate/up read o; down reads silu(gate) * up plus o, and is the next h."""
+        lins, h = [], self.x[2048][0]
+        for l, lin in enumerate(self.stack):
+            y = [t[0] for t in self.y[l]]
+            d = lambda i, **kw: dict(w=lin[i]["w"], s=lin[i]["s"], b=lin[i]["b"], y=y[i], **kw)
+            st = 4 * l
+            lins += [d(0, x=h, stage=st), d(1, x=h, stage=st), d(2, x=h, stage=st),
+                     d(3, x=y[0], resid=h, stage=st + 1),
+                     d(4, x=y[3], stage=st + 2), d(5, x=y[3], stage=st + 2),
+                     d(6, x=y[5], gate=y[4], resid=y[3], stage=st + 3)]
+            h = y[6]
+        return self.qa.GemvChain(lins, G, BITS)
 
     def run_per_linear(self):
         for l, lin in enumerate(self.stack):
@@ -750,6 +771,11 @@ def main():
     chain_steps = max(args.steps // 4, 10)  # the GPU clock needs ~100 ms of load to settle
     ms_chain = graph_time(torch, dec.run_chain, chain_steps, args.warmup)
     ms_lin = graph_time(torch, dec.run_per_linear, chain_steps, args.warmup)
+    chain = dec.chain_plan()
+    ms_chain1 = eager_time(torch, chain, chain_steps, args.warmup)
+    chain_timed_out = chain.timed_out()
+    chain.close()
+    print(f"[bench] decode chain in one launch: {ms_chain1*1e3:.1f} us/step", file=sys.stderr, flush=True)
     print(f"[bench] decode chain (64 launches): {ms_chain*1e3:.1f} us/step; per linear (112 launches): "
           f"{ms_lin*1e3:.1f} us/step", file=sys.stderr, flush=True)
 
@@ -835,6 +861,12 @@ def main():
         "cpu_baseline": cpu,
         "decode_chain": {"launches_per_step": 4 * args.layers, "us_per_step": round(ms_chain * 1e3, 1),
                          "gbs": round(dec.bytes_per_step / (ms_chain * 1e-3) / 1e9, 1)},
+        "decode_chain_one_launch": {"launches_per_step": 1, "stages": 4 * args.layers,
+                                    "us_per_step": round(ms_chain1 * 1e3, 1),
+                                    "gbs": round(dec.bytes_per_step / (ms_chain1 * 1e-3) / 1e9, 1),
+                                    "frac_of_hbm_peak": round(dec.bytes_per_step / (ms_chain1 * 1e-3) / 1e9
+                                                              / HBM_PEAK_GBS, 4),
+                                    "wait_gave_up": chain_timed_out},
         "per_linear": {"launches_per_step": dec.n_linears, "us_per_step": round(ms_lin * 1e3, 1),
                        "gbs": round(dec.bytes_per_step / (ms_lin * 1e-3) / 1e9, 1)},
         "cfg0_hot": {"us_per_launch": round(us_hot, 2), "gbs_not_hbm": round(gemv_bytes(1, 2048, 2048) / us_hot / 1e3, 1)},

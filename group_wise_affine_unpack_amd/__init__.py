@@ -19,7 +19,8 @@ import torch
 
 __all__ = ["QaffError", "qmm_affine", "qmm_affine_noalloc", "qgemv_affine", "qgemv_affine_grouped", "GroupedGemv", "qmm_gptq", "qgemm_w4a8", "qgemm_w4a8_tiled", "gptq_to_affine_repack",
            "quantize_pack_affine", "dequantize_affine", "qgemv_affine_silu_gate", "smoothquant_factors",
-           "w4a8_quantize_weights", "qgemm_w4a8_smooth", "release_workspaces", "library_path", "lib", "STATUS", "DTYPE"]
+           "w4a8_quantize_weights", "qgemm_w4a8_smooth", "release_workspaces", "GemvChain", "library_path", "lib",
+           "STATUS", "DTYPE"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libqaff.so")
@@ -46,6 +47,10 @@ _SIGS = {
     "w4a8_quantize_weights": [_VP, _I32, _VP, _VP, _VP, _I64, _I64, _VP],
     "qgemm_w4a8_smooth": [_VP] * 8 + [_I64] * 3 + [_VP],
     "qaff_stream_read": [_VP, C.c_uint64, _VP, _I32, _VP],
+    "qgemv_affine_chain_plan": [_VP, _I32, _I32, _I32, _I32, C.POINTER(_VP)],
+    "qgemv_affine_chain_run": [_VP, _VP],
+    "qgemv_affine_chain_status": [_VP, C.POINTER(_I32)],
+    "qgemv_affine_chain_free": [_VP],
 }
 
 
@@ -53,6 +58,12 @@ class GemvProblem(C.Structure):
     """qaff_gemv_problem (include/qaff.h)."""
     _fields_ = [("x", _VP), ("w_packed", _VP), ("scales", _VP), ("biases", _VP), ("k_perm", _VP), ("y", _VP),
                 ("N", _I64), ("K", _I64)]
+
+
+class ChainLinear(C.Structure):
+    """qaff_chain_linear (include/qaff.h)."""
+    _fields_ = [("x", _VP), ("gate", _VP), ("resid", _VP), ("w_packed", _VP), ("scales", _VP), ("biases", _VP),
+                ("y", _VP), ("N", _I64), ("K", _I64), ("stage", _I32)]
 
 
 class QaffError(RuntimeError):
@@ -215,6 +226,58 @@ class GroupedGemv:
         st = lib().qgemv_affine_grouped(C.cast(self.arr, _VP), *self.args, _stream(self.device))
         _check(st, "qgemv_affine_grouped")
         return self.ys
+
+
+class GemvChain:
+    """qgemv_affine_chain_plan / _run / _status / _free: linears of a decode
+    step (one x row, 4-bit codes) in dependency stages, one launch per run.
+
+    `linears`: dicts with x, w, s, b, y, stage and optionally gate, resid
+    (tensors; x, gate [1, K] or [K], y and resid [1, N] or [N]).  Holds
+    references to every tensor it points at; calling it enqueues the chain
+    on the current stream of the device of the first x.
+    """
+
+    def __init__(self, linears, group_size: int, bits: int = 4):
+        self.linears = [dict(l) for l in linears]
+        arr = (ChainLinear * max(len(self.linears), 1))()
+        for i, l in enumerate(self.linears):
+            N, K = l["w"].shape[0], l["x"].shape[-1]
+            arr[i] = ChainLinear(_ptr(l["x"]), _ptr(l.get("gate")), _ptr(l.get("resid")), _ptr(_u32(l["w"])),
+                                 _ptr(l["s"]), _ptr(l["b"]), _ptr(l["y"]), N, K, int(l["stage"]))
+        x0 = self.linears[0]["x"]
+        self.device = x0.device
+        self.plan = None
+        h = _VP()
+        with torch.cuda.device(self.device):
+            st = lib().qgemv_affine_chain_plan(C.cast(arr, _VP), len(self.linears), group_size, bits, _dt(x0),
+                                               C.byref(h))
+        _check(st, "qgemv_affine_chain_plan")
+        self.plan = h.value
+
+    def __call__(self):
+        st = lib().qgemv_affine_chain_run(self.plan, _stream(self.device))
+        _check(st, "qgemv_affine_chain_run")
+
+    def timed_out(self) -> bool:
+        v = _I32(0)
+        with torch.cuda.device(self.device):
+            st = lib().qgemv_affine_chain_status(self.plan, C.byref(v))
+        _check(st, "qgemv_affine_chain_status")
+        return bool(v.value)
+
+    def close(self):
+        if self.plan is not None:
+            with torch.cuda.device(self.device):
+                st = lib().qgemv_affine_chain_free(self.plan)
+            self.plan = None
+            _check(st, "qgemv_affine_chain_free")
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def qmm_gptq(x: torch.Tensor, qweight: torch.Tensor, qzeros: torch.Tensor, scales: torch.Tensor,

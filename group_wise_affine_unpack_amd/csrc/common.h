@@ -118,6 +118,24 @@ hipError_t launch_gemm_affine(const AffineArgs& a, hipStream_t s);
 // y = W (silu(a.x) * up) [+ resid], M <= 16 (a.x is the gate)
 hipError_t launch_gemv_silu(const AffineArgs& a, const void* up, const void* resid, hipStream_t s);
 
+// A decode chain (gemv_affine.hip): 4-bit linears at M = 1, in stages; the
+// plan holds the device descriptors and counts, each run is one launch.
+struct ChainSpec {
+  const void* x;      // [K]; with a gate, the up projection
+  const void* gate;   // [K] or null
+  const void* resid;  // [N] or null
+  const void* w;
+  const void* scales;
+  const void* biases;
+  void* y;            // [N]
+  int64_t N, K;
+  int stage;          // nondecreasing
+};
+hipError_t chain_plan_create(const ChainSpec* spec, int count, int G, int act_f16, void** out);
+hipError_t chain_plan_run(void* plan, hipStream_t s);
+hipError_t chain_plan_status(void* plan, int* timed_out);
+hipError_t chain_plan_free(void* plan);
+
 struct GptqArgs {
   const void* x;
   const int32_t* qweight;

@@ -30,6 +30,7 @@
 //    table, which travels in the kernel arguments.  Linears that share an
 //    input (q/k/v, gate/up), or a whole set of them, then cost one launch.
 #include <algorithm>
+#include <new>
 #include <type_traits>
 
 #include <vector>
@@ -1169,6 +1170,447 @@ hipError_t launch_gemv_silu(const AffineArgs& a, const void* up, const void* res
     default: launch_bits<8, true, 1>(b, (int)blocks, sbm, 4, s); break;
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Decode chain: the linears of a decode step in dependency order, one launch.
+//
+// A decode step runs its linears in stages: q/k/v read the hidden state, o
+// reads their result, gate/up read o's, down reads silu(gate) * up (the
+// fused inputs of the mlx_int8.rs API page: `gemv_gate_up`,
+// `gemv_silu_gate`, `gemv_silu_gate_resid`).  Here one cooperative launch
+// of two workgroups per CU runs every stage:
+//   * a stage's linears are cut into items of about 16 KiB of codes (16 rows
+//     at K <= 2048, 8 at K <= 4096, 4 beyond, the waves then splitting K),
+//     dealt to the workgroups in turn;
+//   * a workgroup loads the weights, scales and biases of its next item
+//     before it computes the current one, and the first item of a stage
+//     before it waits for the stage before: weights do not depend on the
+//     chain, so their latency overlaps the previous stage and the wait;
+//   * a workgroup reads an item's input once per stage into LDS (x, or
+//     silu(gate) * x rounded to f16, as in qgemv_affine_silu_gate), and its
+//     waves read it from there;
+//   * stages meet at arrival counts: a workgroup waits for its stores, then
+//     adds 1 to one of CHAIN_SUB sub counts of the stage, and the last
+//     arrival of a sub count raises the stage's top count; a workgroup with
+//     an item in the next stage polls the top count.  Outputs are written
+//     through to memory and inputs read from it at device scope (sc1), and
+//     the counts are device-scope atomics, so no cache is written back or
+//     invalidated and the XCDs' L2s keep their lines.  The wait is bounded:
+//     past CHAIN_POLLS polls it sets an error word and goes on, so no launch
+//     can hang (with a cooperative launch every workgroup is resident and
+//     the bound is never reached);
+//   * the last workgroup to finish sets the counts back to zero.
+// The arithmetic of an item is the dot2 GEMV's (4-bit codes, exact weights,
+// fp32 sums).
+namespace {
+
+constexpr int CP_DEV = 16;                   // cache policy sc1: device scope
+constexpr uint32_t CHAIN_POLLS = 1u << 20;   // polls of one count before giving up
+// Arrival counts: per stage CHAIN_SUB counts (workgroup bid counts in
+// bid % CHAIN_SUB) and a top count that the last arrival of each sub count
+// raises; every count on a cache line of its own.
+constexpr int CHAIN_SUB = 16;
+constexpr int CHAIN_LINE = 32;                       // uint32 per 128-byte line
+constexpr int CHAIN_STAGE = (CHAIN_SUB + 1) * CHAIN_LINE;  // uint32 per stage
+
+struct ChainLin {
+  const uint16_t* x;      // [K]; with a gate: the up projection
+  const uint16_t* gate;   // [K] or null: the input is silu(gate) * x
+  const uint16_t* resid;  // [N] or null: added to y before its rounding
+  const void* w;          // [N, K/8]
+  const void* s;          // [N, K/G]
+  const void* b;          // [N, K/G]
+  uint16_t* y;            // [N]
+  int N, K, ks;           // ks: log2 of the waves that split a row's K
+};
+
+// The weights, scales and biases of one item's first K chunk, per wave
+struct ChainRegs {
+  u32x4_t wv[4];
+  float sv[4], bv[4];
+};
+
+template <int SBM>
+__device__ __forceinline__ void chain_load(const ChainLin& D, int row0base, int gsh, ChainRegs& g) {
+  constexpr int R = 4;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ksh = D.ks, N = D.N, K = D.K;
+  const int row0 = row0base + (wave >> ksh) * R, kpart = wave & ((1 << ksh) - 1);
+  const int L = K / 32, ng = K >> gsh;  // 16-byte chunks per row (4-bit)
+  const int nrows = __builtin_amdgcn_readfirstlane(min(max(N - row0, 0), R));
+  const int rlast = max(nrows - 1, 0);
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(static_cast<const uint32_t*>(D.w) + (long)row0 * L * 4, (uint32_t)(nrows * L * 16));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(static_cast<const char*>(D.s) + (long)row0 * ng * 2, (uint32_t)(nrows * ng * 2));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(static_cast<const char*>(D.b) + (long)row0 * ng * 2, (uint32_t)(nrows * ng * 2));
+  const int j = kpart * 64 + lane;
+  const bool jok = j < L;
+  const uint32_t wo = jok ? (uint32_t)j * 16u : OOB;
+  const uint32_t gr = ((uint32_t)j * 32u) >> gsh;
+  const uint32_t po = jok ? gr * 2u : OOB;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t rr = (uint32_t)min(r, rlast);
+    g.wv[r] = ld128<NT>(rw, wo, rr * (uint32_t)L * 16u);
+    g.sv[r] = load_param<SBM>(rs, po, rr * (uint32_t)ng * 2u, 0);
+    g.bv[r] = load_param<SBM>(rb, po, rr * (uint32_t)ng * 2u, 0);
+  }
+}
+
+// The stage's top count polled by thread 0 until every sub count has
+// closed (min(P, CHAIN_SUB) of them), then a barrier.
+__device__ __forceinline__ void chain_wait(uint32_t* stage, int P, uint32_t* err) {
+  if (threadIdx.x == 0) {
+    uint32_t n = 0;
+    const uint32_t want = (uint32_t)min(P, CHAIN_SUB);
+    while (__hip_atomic_load(stage + CHAIN_SUB * CHAIN_LINE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++n == CHAIN_POLLS) {
+        __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Every wave's stores done (written through), then one arrival in the sub
+// count of bid; the sub count's last arrival raises the top count.
+__device__ __forceinline__ void chain_arrive(uint32_t* stage, int P, int bid) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int g = bid % CHAIN_SUB;
+    const uint32_t size = (uint32_t)(P / CHAIN_SUB + (g < P % CHAIN_SUB ? 1 : 0));
+    if (__hip_atomic_fetch_add(stage + g * CHAIN_LINE, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == size - 1)
+      __hip_atomic_fetch_add(stage + CHAIN_SUB * CHAIN_LINE, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// The item's input into LDS (xl, K values): x, or silu(gate) * x rounded to
+// f16 (as qgemv_affine_silu_gate), read from memory at device scope; every
+// load of a thread issued before any is used.
+template <bool ACT_F16>
+__device__ __forceinline__ void chain_stage_x(const ChainLin& D, uint16_t* xl) {
+  constexpr int U = 4;  // 16-byte loads per thread per pass: 256 * 8 * U values
+  const int K = D.K;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(D.x, (uint32_t)(K * 2));
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(D.gate, D.gate ? (uint32_t)(K * 2) : 0u);
+  __syncthreads();  // every wave done with the previous input
+  for (int i0 = 0; i0 < K; i0 += 256 * 8 * U) {
+    u32x4_t v[U], g[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t o = (uint32_t)(i0 + (u * 256 + (int)threadIdx.x) * 8) * 2u;  // past K: zeros
+      v[u] = ld128<CP_DEV>(rx, o);
+      if (D.gate) g[u] = ld128<CP_DEV>(rg, o);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + (u * 256 + (int)threadIdx.x) * 8;
+      if (i < K)
+        *reinterpret_cast<u32x4_t*>(xl + i) = D.gate ? silu_gate_f16(g[u], v[u], ACT_F16) : v[u];
+    }
+  }
+  __syncthreads();
+}
+
+// One item: rows row0base.. of D (4 per row group of waves), the first K
+// chunk's operands in g, the input in LDS (xl).  F16C: the f16 code path
+// (f16 activations, or a gated input).
+template <bool F16C, int SBM>
+__device__ __forceinline__ void chain_compute(const ChainLin& D, int row0base, int gsh, bool out_f16, const ChainRegs& g,
+                                              const uint16_t* xl, float (&red)[4][4]) {
+  using C = Codec<4, F16C>;
+  constexpr int R = 4;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ksh = D.ks, KS = 1 << ksh, N = D.N, K = D.K;
+  const int rg = wave >> ksh, kpart = wave & (KS - 1);
+  const int row0 = row0base + rg * R;
+  const int L = K / 32, nch = (L + 63) >> 6, ng = K >> gsh;
+  const int nrows = __builtin_amdgcn_readfirstlane(min(max(N - row0, 0), R));
+  const int rlast = max(nrows - 1, 0);
+  uint32_t magic = C::MAGIC;
+  asm volatile("" : "+v"(magic));
+  float acc[R] = {0.f, 0.f, 0.f, 0.f};
+  auto chunk = [&](int c, const u32x4_t (&wv)[R], const float (&sv)[R], const float (&bv)[R]) {
+    const int j = c * 64 + lane;
+    const bool jok = j < L;  // (lanes past the row read x as 0: their codes decode to the offset, not 0)
+    const u32x4_t* xq = reinterpret_cast<const u32x4_t*>(xl + (jok ? j : 0) * 32);  // 32 codes = 64 bytes of x
+    u32x4_t raw[C::XR];
+#pragma unroll
+    for (int q = 0; q < C::XR; ++q) {
+      const u32x4_t v = xq[q];
+      raw[q] = jok ? v : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    uint32_t xp[C::XP];
+    float xs[C::NSEG];
+    C::build(raw, xp, xs);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float d = 0.f;
+#pragma unroll
+      for (int p = 0; p < C::PPS; ++p) d = C::xdot(C::pair(wv[r], p, magic), xp, p, d);
+      const float s = sv[r], b = fmaf(-C::OFF, s, bv[r]);
+      acc[r] = fmaf(s, d, fmaf(b, xs[0], acc[r]));
+    }
+  };
+  if (kpart < nch) chunk(kpart, g.wv, g.sv, g.bv);
+  for (int c = kpart + KS; c < nch; c += KS) {  // rows longer than KS chunks
+    ChainRegs h;
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(static_cast<const uint32_t*>(D.w) + (long)row0 * L * 4, (uint32_t)(nrows * L * 16));
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(static_cast<const char*>(D.s) + (long)row0 * ng * 2, (uint32_t)(nrows * ng * 2));
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(static_cast<const char*>(D.b) + (long)row0 * ng * 2, (uint32_t)(nrows * ng * 2));
+    const int j = c * 64 + lane;
+    const bool jok = j < L;
+    const uint32_t wo = jok ? (uint32_t)j * 16u : OOB, po = jok ? (((uint32_t)j * 32u) >> gsh) * 2u : OOB;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t rr = (uint32_t)min(r, rlast);
+      h.wv[r] = ld128<NT>(rw, wo, rr * (uint32_t)L * 16u);
+      h.sv[r] = load_param<SBM>(rs, po, rr * (uint32_t)ng * 2u, 0);
+      h.bv[r] = load_param<SBM>(rb, po, rr * (uint32_t)ng * 2u, 0);
+    }
+    chunk(c, h.wv, h.sv, h.bv);
+  }
+  // row q of tot holds the sum of acc[q]
+  const float tot = wave_sum4(acc);
+  const int q = lane >> 4;
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(D.y, (uint32_t)(N * 2));
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(D.resid, D.resid ? (uint32_t)(N * 2) : 0u);
+  auto store = [&](int row, float v) {
+    if (D.resid) {
+      const uint32_t rb = __builtin_amdgcn_raw_buffer_load_b16(rr, (uint32_t)row * 2u, 0, CP_DEV);
+      v += out_f16 ? f16_bits_to_f32(rb) : bf16_bits_to_f32(rb);
+    }
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_act_bits(v, out_f16), ry, (uint32_t)row * 2u, 0, CP_DEV);
+  };
+  if (KS == 1) {
+    if ((lane & 15) == 0 && q < nrows) store(row0 + q, tot);
+  } else {
+    if ((lane & 15) == 0) red[wave][q] = tot;
+    __syncthreads();
+    if (kpart == 0 && lane < nrows) {
+      float v = 0.f;
+      for (int p = 0; p < KS; ++p) v += red[rg * KS + p][lane];
+      store(row0 + lane, v);
+    }
+    __syncthreads();  // red is written again by the next item
+  }
+}
+
+// The item after `it` of stage st for workgroup bid, in this stage or the
+// first later stage that has one: (stage, item), or (nst, -1).
+__device__ __forceinline__ int2 chain_next(const int* __restrict__ sb, int nst, int st, int it, int P, int bid) {
+  if (it + P < sb[st + 1]) return make_int2(st, it + P);
+  for (int s = st + 1; s < nst; ++s)
+    if (sb[s] + bid < sb[s + 1]) return make_int2(s, sb[s] + bid);
+  return make_int2(nst, -1);
+}
+
+// bar: the stages' counts (CHAIN_STAGE uint32 each, stages 0 .. nst-2),
+// then the finished count and the error word (set by a wait that gave up)
+template <bool ACT_F16>
+__global__ __launch_bounds__(256) void gemv_chain_kernel(const ChainLin* __restrict__ lins, const int2* __restrict__ items,
+                                                          const int* __restrict__ sb, int nst, int gsh,
+                                                          uint32_t* __restrict__ bar) {
+  constexpr int SBM = ACT_F16 ? 1 : 0;
+  __shared__ float red[4][4];
+  extern __shared__ __attribute__((aligned(16))) uint16_t xl[];  // the current input: K values
+  const int P = gridDim.x, bid = blockIdx.x;
+  uint32_t* done = bar + (long)nst * CHAIN_STAGE;
+  uint32_t* err = done + CHAIN_LINE;
+  auto load = [&](int it, ChainRegs& g) {
+    const int2 w = items[it];
+    chain_load<SBM>(lins[w.x], w.y, gsh, g);
+  };
+  ChainRegs cur, nxt;
+  // first item of the workgroup: the first stage that has one
+  int2 at = make_int2(nst, -1);
+  for (int s = 0; s < nst; ++s)
+    if (sb[s] + bid < sb[s + 1]) {
+      at = make_int2(s, sb[s] + bid);
+      break;
+    }
+  if (at.y >= 0) load(at.y, cur);
+  int arrived = 0;  // stages 0 .. arrived-1 counted
+  int staged_st = -1;  // the stage and input whose values xl holds
+  const uint16_t* staged_x = nullptr;
+  const uint16_t* staged_g = nullptr;
+  while (at.y >= 0) {
+    const int st = at.x;
+    // stages done before this one: count them, then wait for the last
+    for (; arrived < st; ++arrived) chain_arrive(bar + (long)arrived * CHAIN_STAGE, P, bid);
+    const int2 nx = chain_next(sb, nst, st, at.y, P, bid);
+    if (nx.y >= 0) load(nx.y, nxt);  // the next item's operands, before the wait and the work
+    if (st > 0 && at.y == sb[st] + bid) chain_wait(bar + (long)(st - 1) * CHAIN_STAGE, P, err);
+    const int2 w = items[at.y];
+    const ChainLin& D = lins[w.x];
+    // the input into LDS once per stage and (x, gate) pair: a later stage may
+    // have rewritten a buffer of the same address, so a stage starts afresh
+    if (st != staged_st || D.x != staged_x || D.gate != staged_g) {
+      chain_stage_x<ACT_F16>(D, xl);
+      staged_st = st;
+      staged_x = D.x;
+      staged_g = D.gate;
+    }
+    if (D.gate)
+      chain_compute<true, SBM>(D, w.y, gsh, ACT_F16, cur, xl, red);
+    else
+      chain_compute<ACT_F16, SBM>(D, w.y, gsh, ACT_F16, cur, xl, red);
+    cur = nxt;
+    at = nx;
+  }
+  for (; arrived < nst - 1; ++arrived) chain_arrive(bar + (long)arrived * CHAIN_STAGE, P, bid);
+  // the last workgroup to finish sets the counts back to zero
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0 &&
+      __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(P - 1)) {
+    for (int st = 0; st + 1 < nst; ++st)
+      for (int g = 0; g <= CHAIN_SUB; ++g)
+        __hip_atomic_store(bar + (long)st * CHAIN_STAGE + g * CHAIN_LINE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+}  // namespace
+
+// Host side of a chain: the descriptors and the stage items in one device
+// allocation, built once; each run is one cooperative launch.
+struct ChainPlan {
+  int dev, act_f16, gsh, nst, P, lds;
+  void* mem;
+  ChainLin* lins;
+  int2* items;
+  int* sb;
+  uint32_t* bar;
+};
+
+hipError_t chain_plan_create(const ChainSpec* spec, int count, int G, int act_f16, void** out) {
+  *out = nullptr;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  int gsh = 0;
+  while ((1 << gsh) < G) ++gsh;
+  const int nst = spec[count - 1].stage + 1;
+  std::vector<ChainLin> lins(count);
+  std::vector<int2> items;
+  std::vector<int> sb(nst + 1, 0);
+  int next = 0;
+  for (int st = 0; st < nst; ++st) {
+    sb[st] = (int)items.size();
+    for (; next < count && spec[next].stage == st; ++next) {
+      const ChainSpec& c = spec[next];
+      const int64_t L = c.K / 32, nch = (L + 63) / 64;
+      const int ksh = nch >= 4 ? 2 : (nch >= 2 ? 1 : 0);
+      ChainLin& d = lins[next];
+      d.x = static_cast<const uint16_t*>(c.x);
+      d.gate = static_cast<const uint16_t*>(c.gate);
+      d.resid = static_cast<const uint16_t*>(c.resid);
+      d.w = c.w;
+      d.s = c.scales;
+      d.b = c.biases;
+      d.y = static_cast<uint16_t*>(c.y);
+      d.N = (int)c.N;
+      d.K = (int)c.K;
+      d.ks = ksh;
+      const int rows = (4 >> ksh) * 4;
+      for (int64_t r = 0; r < c.N; r += rows) items.push_back(make_int2(next, (int)r));
+    }
+  }
+  sb[nst] = (int)items.size();
+  int64_t kmax = 0;
+  for (int i = 0; i < count; ++i) kmax = std::max<int64_t>(kmax, spec[i].K);
+  const int lds = (int)(kmax * 2);  // the input of the longest row
+  if (items.size() >= (size_t(1) << 30)) return hipErrorNotSupported;
+  // workgroups all resident at once (cooperative launch)
+  const void* k = act_f16 ? reinterpret_cast<const void*>(gemv_chain_kernel<true>)
+                          : reinterpret_cast<const void*>(gemv_chain_kernel<false>);
+  e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024);
+  if (e != hipSuccess) return e;
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 256, (size_t)lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorNotSupported;
+  const size_t lb = ((size_t)count * sizeof(ChainLin) + 255) & ~size_t(255);
+  const size_t ib = (items.size() * sizeof(int2) + 255) & ~size_t(255);
+  const size_t sbb = ((size_t)(nst + 1) * sizeof(int) + 255) & ~size_t(255);
+  const size_t bb = ((size_t)nst * CHAIN_STAGE + 2 * CHAIN_LINE) * sizeof(uint32_t);
+  ChainPlan* p = new (std::nothrow) ChainPlan{};
+  if (!p) return hipErrorOutOfMemory;
+  p->dev = dev;
+  p->act_f16 = act_f16;
+  p->gsh = gsh;
+  p->nst = nst;
+  p->P = cus * std::min(per_cu, 2);  // two per CU: more loads in flight (one measured 5% slower)
+  p->lds = lds;
+  e = hipMalloc(&p->mem, lb + ib + sbb + bb);
+  if (e != hipSuccess) {
+    delete p;
+    return e;
+  }
+  char* m = static_cast<char*>(p->mem);
+  p->lins = reinterpret_cast<ChainLin*>(m);
+  p->items = reinterpret_cast<int2*>(m + lb);
+  p->sb = reinterpret_cast<int*>(m + lb + ib);
+  p->bar = reinterpret_cast<uint32_t*>(m + lb + ib + sbb);
+  e = hipMemcpy(p->lins, lins.data(), (size_t)count * sizeof(ChainLin), hipMemcpyHostToDevice);
+  if (e == hipSuccess && !items.empty())
+    e = hipMemcpy(p->items, items.data(), items.size() * sizeof(int2), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(p->sb, sb.data(), (size_t)(nst + 1) * sizeof(int), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemset(p->bar, 0, bb);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    (void)hipFree(p->mem);
+    delete p;
+    return e;
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+hipError_t chain_plan_run(void* plan, hipStream_t s) {
+  ChainPlan* p = static_cast<ChainPlan*>(plan);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev != p->dev) return hipErrorInvalidDevice;
+  const ChainLin* lins = p->lins;
+  const int2* items = p->items;
+  const int* sb = p->sb;
+  int nst = p->nst, gsh = p->gsh;
+  uint32_t* bar = p->bar;
+  void* args[] = {&lins, &items, &sb, &nst, &gsh, &bar};
+  const void* k = p->act_f16 ? reinterpret_cast<const void*>(gemv_chain_kernel<true>)
+                             : reinterpret_cast<const void*>(gemv_chain_kernel<false>);
+  return hipLaunchCooperativeKernel(k, dim3((unsigned)p->P), dim3(256), args, (unsigned)p->lds, s);
+}
+
+hipError_t chain_plan_status(void* plan, int* timed_out) {
+  ChainPlan* p = static_cast<ChainPlan*>(plan);
+  uint32_t v = 0;
+  const hipError_t e = hipMemcpy(&v, p->bar + (long)p->nst * CHAIN_STAGE + CHAIN_LINE, sizeof(v), hipMemcpyDeviceToHost);
+  *timed_out = v != 0;
+  return e;
+}
+
+hipError_t chain_plan_free(void* plan) {
+  ChainPlan* p = static_cast<ChainPlan*>(plan);
+  if (!p) return hipSuccess;
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e == hipSuccess) e = hipSetDevice(p->dev);
+  if (e == hipSuccess) e = hipFree(p->mem);
+  (void)hipSetDevice(cur);
+  delete p;
+  return e;
 }
 
 }  // namespace qaff

@@ -139,6 +139,66 @@ int qgemv_affine_silu_gate(const void* gate, const void* up, const void* resid, 
   return ok();
 }
 
+int qgemv_affine_chain_plan(const qaff_chain_linear* linears, int32_t count, int32_t group_size, int32_t bits,
+                            int32_t act_dtype, void** plan_out) {
+  if (!plan_out) return fail(QAFF_E_INVAL, "null plan_out");
+  *plan_out = nullptr;
+  if (count < 1 || count > (1 << 20)) return fail(QAFF_E_INVAL, "count must be in [1, 2^20] (got %d)", count);
+  if (!linears) return fail(QAFF_E_INVAL, "null linear array");
+  if (bits != 4) return fail(QAFF_E_UNSUPPORTED, "the chain takes 4-bit codes (got %d)", bits);
+  if (!(act_dtype == QAFF_BF16 || act_dtype == QAFF_F16))
+    return fail(QAFF_E_INVAL, "act_dtype must be QAFF_BF16 or QAFF_F16 (got %d)", act_dtype);
+  std::vector<qaff::ChainSpec> spec(count);
+  for (int32_t i = 0; i < count; ++i) {
+    const qaff_chain_linear& l = linears[i];
+    int rc = check_affine(l.x, l.w_packed, l.scales, l.biases, l.y, 1, l.N, l.K, group_size, bits, act_dtype,
+                          act_dtype, act_dtype);
+    if (rc != QAFF_OK) {
+      const std::string msg = g_last_error;
+      return fail(rc, "linear %d: %s", i, msg.c_str());
+    }
+    if (l.N < 1) return fail(QAFF_E_INVAL, "linear %d: N must be >= 1", i);
+    if (l.K % 32 != 0) return fail(QAFF_E_UNSUPPORTED, "linear %d: K must be a multiple of 32 (got %lld)", i, (long long)l.K);
+    if (l.K > 32768) return fail(QAFF_E_UNSUPPORTED, "linear %d: K above 32768 (the input is staged in LDS)", i);
+    if (l.gate && !aligned16(l.gate)) return fail(QAFF_E_ALIGN, "linear %d: gate must be 16-byte aligned", i);
+    if (l.stage < 0 || (i > 0 && l.stage < linears[i - 1].stage))
+      return fail(QAFF_E_INVAL, "linear %d: stages must be >= 0 and nondecreasing", i);
+    if (l.N * l.K / 2 >= (int64_t(1) << 31)) return fail(QAFF_E_UNSUPPORTED, "linear %d too large for 32-bit offsets", i);
+    spec[i] = qaff::ChainSpec{l.x, l.gate, l.resid, l.w_packed, l.scales, l.biases, l.y, l.N, l.K, l.stage};
+  }
+  if (linears[count - 1].stage >= (1 << 20)) return fail(QAFF_E_INVAL, "more than 2^20 stages");
+  (void)hipGetLastError();
+  hipError_t e = qaff::chain_plan_create(spec.data(), count, group_size, act_dtype == QAFF_F16, plan_out);
+  if (e == hipErrorNotSupported) return fail(QAFF_E_UNSUPPORTED, "chain too large or kernel not resident");
+  if (e != hipSuccess) return hip_fail(e, "chain plan");
+  return ok();
+}
+
+int qgemv_affine_chain_run(void* plan, void* stream) {
+  if (!plan) return fail(QAFF_E_INVAL, "null plan");
+  (void)hipGetLastError();
+  hipError_t e = qaff::chain_plan_run(plan, static_cast<hipStream_t>(stream));
+  if (e == hipErrorInvalidDevice) return fail(QAFF_E_INVAL, "the plan belongs to another device");
+  if (e != hipSuccess) return hip_fail(e, "chain launch");
+  return ok();
+}
+
+int qgemv_affine_chain_status(void* plan, int32_t* timed_out) {
+  if (!plan || !timed_out) return fail(QAFF_E_INVAL, "null plan or timed_out");
+  int t = 0;
+  hipError_t e = qaff::chain_plan_status(plan, &t);
+  if (e != hipSuccess) return hip_fail(e, "chain status");
+  *timed_out = t;
+  return ok();
+}
+
+int qgemv_affine_chain_free(void* plan) {
+  if (!plan) return ok();
+  hipError_t e = qaff::chain_plan_free(plan);
+  if (e != hipSuccess) return hip_fail(e, "chain free");
+  return ok();
+}
+
 int qgemv_affine_grouped(const qaff_gemv_problem* problems, int32_t count, int64_t M, int32_t group_size,
                          int32_t bits, int32_t act_dtype, int32_t scale_dtype, int32_t bias_dtype, void* stream) {
   if (count < 0 || count > 65536) return fail(QAFF_E_INVAL, "count must be in [0, 65536] (got %d)", count);

@@ -198,6 +198,61 @@ int qgemv_affine_grouped(const qaff_gemv_problem *problems, int32_t count, int64
                          int32_t bias_dtype, void *stream);
 
 /*
+ * qgemv_affine_chain_* - the linears of a decode step (one x row) in
+ * dependency order, in one launch.  A decoder layer reads its hidden state
+ * in q/k/v, their result in o, o's in gate/up, and silu(gate) * up in
+ * down; the fused inputs are those of the mlx_int8.rs API page
+ * (`gemv_gate_up`: linears sharing one x; `gemv_silu_gate`,
+ * `gemv_silu_gate_resid`: the gated input and the residual).  Each linear
+ * is y = W h (+ resid) with W as in qmm_affine and
+ *     h = x                        (gate == NULL)
+ *     h = silu(gate) * x           (as qgemv_affine_silu_gate, x = up)
+ * and its `stage`: linears of one stage run together, a stage starts when
+ * every linear of every earlier stage has written y, so a linear may read
+ * (as x, gate or resid) the y of any linear of an earlier stage, or any
+ * buffer the caller filled.  No linear may write a buffer that a linear of
+ * its own or a later stage reads, other than its own resid (y == resid is
+ * the in-place residual update).
+ *   x, gate  [K] act_dtype, 16-byte aligned; resid, y [N] act_dtype
+ *   w_packed [N, K/8] (bits = 4 only), 16-byte aligned; scales, biases
+ *            [N, K/G] in act_dtype (BF16 or F16; other combinations:
+ *            QAFF_E_UNSUPPORTED); K % 32 == 0, K <= 32768, G in
+ *            {32, 64, 128}
+ *   stage    >= 0, nondecreasing along the array
+ * qgemv_affine_chain_plan copies the descriptors to the device (it
+ * synchronizes the device; the pointers are kept, not the data) and returns
+ * a plan for the current device.  qgemv_affine_chain_run launches it on
+ * stream (one cooperative launch, two workgroups per CU; runs of one plan
+ * must not overlap).  qgemv_affine_chain_status synchronizes and sets
+ * *timed_out when a run's wait between stages gave up (after about a
+ * second; it cannot happen while every workgroup is resident, which the
+ * cooperative launch guarantees).  qgemv_affine_chain_free releases the
+ * plan (the caller's buffers are untouched).  Accuracy per linear as for
+ * qmm_affine and qgemv_affine_silu_gate, each y rounded once to act_dtype.
+ * On MI355X the same stages as one qgemv_affine_grouped call each, replayed
+ * from a HIP graph, are faster: meeting between stages across the XCDs
+ * inside a launch costs more than a launch boundary there.
+ */
+typedef struct qaff_chain_linear {
+    const void *x;            /* [K] act_dtype; with a gate: the up projection */
+    const void *gate;         /* [K] act_dtype or NULL */
+    const void *resid;        /* [N] act_dtype or NULL */
+    const uint32_t *w_packed; /* [N, K/8] */
+    const void *scales;       /* [N, K/G] act_dtype */
+    const void *biases;       /* [N, K/G] act_dtype */
+    void *y;                  /* [N] act_dtype */
+    int64_t N;
+    int64_t K;
+    int32_t stage;
+} qaff_chain_linear;
+
+int qgemv_affine_chain_plan(const qaff_chain_linear *linears, int32_t count, int32_t group_size, int32_t bits,
+                            int32_t act_dtype, void **plan_out);
+int qgemv_affine_chain_run(void *plan, void *stream);
+int qgemv_affine_chain_status(void *plan, int32_t *timed_out);
+int qgemv_affine_chain_free(void *plan);
+
+/*
  * qmm_gptq - y[M,N] = x[M,K] . W^T for a GPTQ layer in its own layout
  * (TinyGPT "Quantization Expansion", "GPTQReader" / "Format"):
  *     W[n,i] = scales[g, n] * (q - ((qzeros[g, n/8] >> 4*(n%8)) & 15) - 1),

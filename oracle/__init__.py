@@ -274,6 +274,39 @@ def qmm_affine_silu_gate(gate, up, resid, act_dtype: str, packed, scales, biases
     return y
 
 
+# ------------------------------------------------------------- decode chain
+
+def qgemv_affine_chain(linears, buffers, act_dtype: str, G: int, bits: int = 4) -> dict:
+    """A decode step's linears (one x row) in the order of their stages, each
+    y = W h (+ resid) with h = x, or silu(gate) * x when a gate is given (the
+    fused inputs of the mlx_int8.rs API page: gemv_gate_up, gemv_silu_gate,
+    gemv_silu_gate_resid).  Every y is computed in fp64 from the stored
+    values of its inputs (qmm_affine and qmm_affine_silu_gate above), then
+    stored: rounded once to act_dtype, the value later linears read.
+
+    buffers: {name: stored [K] or [N] patterns (np.uint16)}, the inputs; each
+    linear: dict(name, x, gate, resid (names of buffers or of earlier
+    linears, gate/resid may be None), packed, scales, biases (scales and
+    biases in act_dtype), N, K).  Returns {name: fp64 y} and leaves the stored
+    outputs in `buffers`."""
+    rnd = f64_to_f16 if act_dtype == "f16" else f64_to_bf16
+    out = {}
+    for l in linears:
+        N, K = l["N"], l["K"]
+        x = buffers[l["x"]].reshape(1, K)
+        if l.get("gate") is not None:
+            r = None if l.get("resid") is None else buffers[l["resid"]].reshape(1, N)
+            y = qmm_affine_silu_gate(buffers[l["gate"]].reshape(1, K), x, r, act_dtype, l["packed"], l["scales"],
+                                     l["biases"], act_dtype, 1, N, K, G, bits)
+        else:
+            y = qmm_affine(x, act_dtype, l["packed"], l["scales"], l["biases"], act_dtype, 1, N, K, G, bits)
+            if l.get("resid") is not None:
+                y = y + to_f64(buffers[l["resid"]], act_dtype).reshape(1, N)
+        out[l["name"]] = y.reshape(N)
+        buffers[l["name"]] = rnd(y.reshape(N))
+    return out
+
+
 # ------------------------------------------------------------- SmoothQuant + W4A8
 
 def smooth_factors(act_absmax, w, w_dtype: str, N: int, K: int, alpha: float) -> np.ndarray:

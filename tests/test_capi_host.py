@@ -141,3 +141,45 @@ def test_release_with_nothing_held_makes_no_hip_call():
     assert qa.lib().qaff_release_workspaces(C.byref(freed)) == OK
     assert freed.value == 0
     assert qa.lib().qaff_release_workspaces(None) == OK
+
+
+class _ChainLin(C.Structure):
+    _fields_ = [("x", C.c_void_p), ("gate", C.c_void_p), ("resid", C.c_void_p), ("w_packed", C.c_void_p),
+                ("scales", C.c_void_p), ("biases", C.c_void_p), ("y", C.c_void_p), ("N", C.c_int64),
+                ("K", C.c_int64), ("stage", C.c_int32)]
+
+
+def _chain(lins, G=64, bits=4, adt=0, out=True):
+    arr = (_ChainLin * max(len(lins), 1))(*[_ChainLin(**{**dict(x=A, w_packed=A, scales=A, biases=A, y=A, N=64,
+                                                                  K=256, stage=0), **l}) for l in lins])
+    h = C.c_void_p()
+    return qa.lib().qgemv_affine_chain_plan(C.cast(arr, C.c_void_p), len(lins), G, bits, adt,
+                                            C.byref(h) if out else None)
+
+
+@pytest.mark.parametrize("lins,kw,code", [
+    ([{}], dict(bits=8), UNSUP),                       # 4-bit codes only
+    ([{}], dict(adt=2), INVAL),                        # act dtype BF16 or F16
+    ([{}], dict(G=48), INVAL),
+    ([{"K": 96}], {}, INVAL),                          # K not a multiple of G
+    ([{"K": 80}], dict(G=16 * 2), INVAL),              # K % 32 != 0 is also not a multiple of G=32
+    ([{"x": None}], {}, INVAL),
+    ([{"gate": A + 2}], {}, ALIGN),
+    ([{"x": A + 2}], {}, ALIGN),
+    ([{"N": 0}], {}, INVAL),
+    ([{"stage": 1}, {"stage": 0}], {}, INVAL),        # stages nondecreasing
+    ([{"stage": -1}], {}, INVAL),
+    ([], {}, INVAL),                                   # at least one linear
+    ([{}], dict(out=False), INVAL),                    # null plan_out
+])
+def test_chain_plan_argument_errors(lins, kw, code):
+    assert _chain(lins, **kw) == code
+    assert _msg() != ""
+
+
+def test_chain_null_plan_calls():
+    lib = qa.lib()
+    assert lib.qgemv_affine_chain_run(None, None) == INVAL
+    v = C.c_int32(7)
+    assert lib.qgemv_affine_chain_status(None, C.byref(v)) == INVAL
+    assert lib.qgemv_affine_chain_free(None) == OK

@@ -614,3 +614,49 @@ def test_w4a8_smooth_reduces_to_plain_w4a8():
     np.testing.assert_array_equal(q2, q3)
     np.testing.assert_array_equal(s2, s3)
     np.testing.assert_array_equal(a2, a3)
+
+
+# ---------------------------------------------------------------- decode chain
+
+def _np_dequant4(packed, scales, biases, N, K, G, dt):
+    # numpy only: codes by shifts of the words, low nibble = lowest column
+    words = packed.astype(np.uint64)
+    q = np.stack([(words >> (4 * i)) & 15 for i in range(8)], axis=-1).reshape(N, K).astype(np.float64)
+    s = si.bits_to_f32(scales, dt).astype(np.float64)
+    b = si.bits_to_f32(biases, dt).astype(np.float64)
+    return q * np.repeat(s, G, axis=1) + np.repeat(b, G, axis=1)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_chain_matches_numpy_composition(dt):
+    # three stages: a, b from x0; c = W (silu(a) * b) + x0; d = W c.  The
+    # reference dequantizes and multiplies with numpy, stores every output
+    # with the pinned rounding, and feeds the stored values on: wrong
+    # routing, a missing residual, or unrounded values passed on all show.
+    G = 32
+    x0 = si.activations(1, 64, seed=(70, 1), dtype=dt).reshape(64)
+    shapes = {"a": (96, 64), "b": (96, 64), "c": (64, 96), "d": (32, 64)}
+    W = {}
+    lins = []
+    for i, (name, (N, K)) in enumerate(shapes.items()):
+        p, s, b = si.affine_weights(N, K, G, 4, seed=(70, 2, i), scale_range=(0.01, 0.05), bias_mode="noise",
+                                    sb_dtype=dt)
+        W[name] = _np_dequant4(p, s, b, N, K, G, dt)
+        lins.append(dict(name=name, packed=p, scales=s, biases=b, N=N, K=K, x=None, gate=None, resid=None))
+    lins[0]["x"] = lins[1]["x"] = "x0"
+    lins[2].update(x="b", gate="a", resid="x0")
+    lins[3]["x"] = "c"
+    buffers = {"x0": x0}
+    got = oracle.qgemv_affine_chain(lins, buffers, dt, G)
+    rnd = oracle.f64_to_f16 if dt == "f16" else oracle.f64_to_bf16
+    f = lambda bits: oracle.to_f64(bits, dt)
+    ra = W["a"] @ f(x0)
+    rb = W["b"] @ f(x0)
+    a_s, b_s = rnd(ra), rnd(rb)
+    h = f(a_s) / (1.0 + np.exp(-f(a_s))) * f(b_s)
+    rc = W["c"] @ h + f(x0)
+    c_s = rnd(rc)
+    rd = W["d"] @ f(c_s)
+    for name, ref in (("a", ra), ("b", rb), ("c", rc), ("d", rd)):
+        np.testing.assert_allclose(got[name], ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(buffers["d"], rnd(rd))
