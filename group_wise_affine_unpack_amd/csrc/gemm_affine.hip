@@ -620,6 +620,53 @@ struct Gemm {
 };
 // ---------------------------------------------------------------------------
 
+// Epilogue of a tile whose rows all exist: y = 2^(e_m + e_n) * acc, rounded
+// to the activation dtype.  32x32 accumulator layout: lane -> column l32;
+// register r -> row 8*(r/4) + 4*half + r%4, so registers 2i and 2i+1 are
+// consecutive rows of one column: one packed conversion, two 2-byte stores
+// (the second from the high half).
+template <bool OUT_F16, int MB>
+__device__ __forceinline__ void epilogue_full(const f32x16_t (&acc)[MB][2], const int* em_s, const GemmParams& p,
+                                              int m0, int n0, int row0, int half, int l32, int wn) {
+  const long N = p.N;
+  // uniform part: the wave's first row and column block
+  const uint64_t yw = reinterpret_cast<uint64_t>(p.y + (long)(m0 + row0) * N + n0 + wn * 64);
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int n = n0 + wn * 64 + nb * 32 + l32;
+    if (n < p.N) {
+      const int e_n = p.en[n];
+      const uint32_t lo = (uint32_t)(4 * half * N + nb * 32 + l32) * 2u;  // lane part, bytes
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const i32x4_t e4 = *reinterpret_cast<const i32x4_t*>(&em_s[row0 + mb * 32 + 8 * rq + 4 * half]);
+#pragma unroll
+          for (int j = 0; j < 4; j += 2) {
+            const float v0 = ldexpf(acc[mb][nb][4 * rq + j], e4[j] + e_n);
+            const float v1 = ldexpf(acc[mb][nb][4 * rq + j + 1], e4[j + 1] + e_n);
+            uint32_t pk;
+            if constexpr (OUT_F16)
+              pk = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){v0, v1}, f16x2_t));
+            else
+              pk = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){v0, v1}, bf16x2_t));
+            // the rows' addresses as scalar values (kept out of the lane
+            // offset, so each store is scalar base + the lane's offset)
+            uint64_t r0 = yw + (uint64_t)((mb * 32 + 8 * rq + j) * N * 2);
+            uint64_t r1 = r0 + (uint64_t)(N * 2);
+            asm volatile("" : "+s"(r0), "+s"(r1));
+            typedef __attribute__((address_space(1))) unsigned char gbyte;
+            *reinterpret_cast<__attribute__((address_space(1))) uint16_t*>(reinterpret_cast<gbyte*>(r0) + lo) =
+                (uint16_t)pk;
+            *reinterpret_cast<__attribute__((address_space(1))) uint16_t*>(reinterpret_cast<gbyte*>(r1) + lo) =
+                (uint16_t)(pk >> 16);
+          }
+        }
+    }
+  }
+}
+
 template <int BITS, int PS, int MB>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_affine_kernel(GemmParams p) {
   using GK = Gemm<BITS, PS, MB>;
@@ -809,6 +856,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                                   vb + (uint32_t)((mb * 32 + 8 * rq + j) * p.N) * 4u, 0, 0);
         }
     }
+    return;
+  }
+  if (m0 + BM <= p.M) {
+    // Every row of the tile exists (all but a ragged last row tile): the
+    // row offset is uniform and goes into the scalar base address, the lane
+    // keeps one offset for all its stores, two rows share one packed
+    // conversion, and a column past N is masked off.
+    if (p.out_f16) epilogue_full<true, MB>(acc, em_s, p, m0, n0, row0, half, l32, wave & 3);
+    else epilogue_full<false, MB>(acc, em_s, p, m0, n0, row0, half, l32, wave & 3);
     return;
   }
   const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.y, (uint32_t)p.M * p.N * 2);
