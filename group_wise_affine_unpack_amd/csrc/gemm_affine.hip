@@ -97,12 +97,19 @@ __device__ __forceinline__ long tail_idx(int r, int k, int Kt) {
   return ((long)(r >> 5) * (Kt >> 4) + (k >> 4)) * 512 + ((k >> 3) & 1) * 256 + (r & 31) * 8 + (k & 7);
 }
 
-template <int BITS>
+// RC > 0: the row is read once, into registers (RC 16-byte chunks a
+// thread: blocks t + 256 i of BLK columns, i < RC / CPB, all loads in flight
+// at once), and both passes work from there.  The host takes it when the row
+// fits and no k_perm is given; RC = 0 reads the row twice, one loop trip at
+// a time.
+template <int BITS, int RC>
 __device__ __forceinline__ void prep_x_row(int m, const void* __restrict__ x, int act_dt,
                                            const int32_t* __restrict__ k_perm, int M, int K, int G, int Kt, int BM,
                                            _Float16* __restrict__ xh, uint16_t* __restrict__ tA,
                                            int* __restrict__ em) {
   constexpr int BLK = Perm<BITS>::BLK;
+  constexpr int CPB = BLK / 8;                              // 16-byte chunks per block
+  constexpr int RB = RC > 0 ? (RC + CPB - 1) / CPB : 1;    // blocks a thread holds
   const int t = threadIdx.x;
   const int ng = K / G;
   const int nkt = K / 64;
@@ -118,16 +125,44 @@ __device__ __forceinline__ void prep_x_row(int m, const void* __restrict__ x, in
   }
   const bool f16 = act_dt == F16;
   const uint16_t* xr = static_cast<const uint16_t*>(x) + (long)m * K;
+  const int nblk = K / BLK;
+  auto to_f32 = [&](uint32_t h) { return f16 ? f16_bits_to_f32(h) : bf16_bits_to_f32(h); };
+  auto chunk_max = [&](const u32x4_t& v, float a) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a = fmaxf(a, fmaxf(fabsf(to_f32(v[i] & 0xffffu)), fabsf(to_f32(v[i] >> 16))));
+    return a;
+  };
   __shared__ float red[4];
   float amax = 0.f;
-  for (int c = t; c < K / 8; c += 256) {
-    const u32x4_t v = reinterpret_cast<const u32x4_t*>(xr)[c];
+  u32x4_t xc[RB][CPB];
+  if constexpr (RC > 0) {
+    // a block past the row reads zeros (offset past the buffer's range)
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(xr, (uint32_t)K * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float lo = f16 ? f16_bits_to_f32(v[i] & 0xffffu) : bf16_bits_to_f32(v[i] & 0xffffu);
-      const float hi = f16 ? f16_bits_to_f32(v[i] >> 16) : bf16_bits_to_f32(v[i] >> 16);
-      amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
-    }
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int q = 0; q < CPB; ++q) {
+        const int bi = t + 256 * i;
+        const uint32_t off = bi < nblk ? (uint32_t)(bi * BLK + 8 * q) * 2u : 0x80000000u;
+        xc[i][q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, 0));
+      }
+    // max |x| on the raw bits: for bf16 and f16 alike, |x| orders as
+    // (bits & 0x7fff); NaN patterns (above infinity's) are taken as zero,
+    // as the float maximum above ignores a NaN
+    const uint32_t inf = f16 ? 0x7c00u : 0x7f80u;
+    uint32_t mb = 0;
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int q = 0; q < CPB; ++q)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t lo = xc[i][q][u] & 0x7fffu, hi = (xc[i][q][u] >> 16) & 0x7fffu;
+          mb = max(mb, max(lo > inf ? 0u : lo, hi > inf ? 0u : hi));
+        }
+    amax = to_f32(mb);
+  } else {
+    for (int c = t; c < K / 8; c += 256) amax = chunk_max(reinterpret_cast<const u32x4_t*>(xr)[c], amax);
   }
   amax = wave_max(amax);
   if ((t & 63) == 0) red[t >> 6] = amax;
@@ -139,30 +174,10 @@ __device__ __forceinline__ void prep_x_row(int m, const void* __restrict__ x, in
 
   // blocks of BLK permuted columns; the lanes that share a group are
   // consecutive and aligned, so the group sum is a butterfly over them
-  const int nblk = K / BLK;
   const int bpg = G / BLK;  // blocks per group: 2..16, a power of two
-  for (int b0 = 0; b0 < nblk; b0 += 256) {
-    const int bi = b0 + t;
+  auto emit = [&](int bi, const float (&src)[BLK]) {
     float part = 0.f;
     if (bi < nblk) {
-      float src[BLK];
-      if (k_perm == nullptr) {
-#pragma unroll
-        for (int q = 0; q < BLK / 8; ++q) {
-          const u32x4_t v = reinterpret_cast<const u32x4_t*>(xr + bi * BLK)[q];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            src[8 * q + 2 * i] = f16 ? f16_bits_to_f32(v[i] & 0xffffu) : bf16_bits_to_f32(v[i] & 0xffffu);
-            src[8 * q + 2 * i + 1] = f16 ? f16_bits_to_f32(v[i] >> 16) : bf16_bits_to_f32(v[i] >> 16);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < BLK; ++j) {
-          const uint32_t h = xr[k_perm[bi * BLK + j]];
-          src[j] = f16 ? f16_bits_to_f32(h) : bf16_bits_to_f32(h);
-        }
-      }
       _Float16 out[BLK];
 #pragma unroll
       for (int j = 0; j < BLK; ++j) {
@@ -185,6 +200,47 @@ __device__ __forceinline__ void prep_x_row(int m, const void* __restrict__ x, in
       tA[tail_idx(m, 3 * g, Kt)] = hi;
       tA[tail_idx(m, 3 * g + 1, Kt)] = hi;
       tA[tail_idx(m, 3 * g + 2, Kt)] = lo;
+    }
+  };
+  if constexpr (RC > 0) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      float src[BLK];
+#pragma unroll
+      for (int q = 0; q < CPB; ++q)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          src[8 * q + 2 * u] = to_f32(xc[i][q][u] & 0xffffu);
+          src[8 * q + 2 * u + 1] = to_f32(xc[i][q][u] >> 16);
+        }
+      emit(t + 256 * i, src);
+      // one block at a time: its values die before the next one's are made
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    for (int b0 = 0; b0 < nblk; b0 += 256) {
+      const int bi = b0 + t;
+      float src[BLK];
+      if (bi < nblk) {
+        if (k_perm == nullptr) {
+#pragma unroll
+          for (int q = 0; q < CPB; ++q) {
+            const u32x4_t v = reinterpret_cast<const u32x4_t*>(xr + bi * BLK)[q];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              src[8 * q + 2 * u] = to_f32(v[u] & 0xffffu);
+              src[8 * q + 2 * u + 1] = to_f32(v[u] >> 16);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < BLK; ++j) src[j] = to_f32(xr[k_perm[bi * BLK + j]]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < BLK; ++j) src[j] = 0.f;
+      }
+      emit(bi, src);
     }
   }
   for (int k = 3 * ng + t; k < Kt; k += 256) tA[tail_idx(m, k, Kt)] = 0;
@@ -278,6 +334,96 @@ __device__ __forceinline__ void prep_w_rows(int blk, const void* __restrict__ sc
   for (int i = t; i < PW * pad; i += 256) tB[tail_idx(n0 + i / pad, 3 * ng + i % pad, Kt)] = 0;
 }
 
+// The same W-side pass with every load issued at once: thread t takes row
+// t % PW and groups t / PW + 32 i (i < WI), so PW * ng <= 256 * WI.  The
+// loop above waits out one memory latency per trip (ng/64 + ng/32 trips: 11
+// at K = 14336, G = 64), and its blocks start after the rows of x; here a
+// block waits once.  The row maximum is reduced over the 32 threads of a
+// row (three butterfly steps in a wave, then the four waves through LDS).
+// Rows past N load zeros (offsets out of range) and so write zeros, as
+// above.
+constexpr int WI = 8;
+template <int PS>
+__device__ __forceinline__ void prep_w_rows_once(int blk, const void* __restrict__ scales, int s_dt,
+                                                 const void* __restrict__ biases, int b_dt, float off, int eshift,
+                                                 int mshift, int N, int Np, int ng, int G, int Kt,
+                                                 uint32_t* __restrict__ sh, uint16_t* __restrict__ tB,
+                                                 int* __restrict__ en) {
+  __shared__ float wmax[4][PW];
+  const int n0 = blk * PW, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int r = t % PW, n = n0 + r, gq = t / PW;
+  const uint32_t cnt = (uint32_t)N * (uint32_t)ng;
+  // Every parameter is read as the aligned 32-bit word that holds it (16-bit
+  // types: the pair, its half picked by the index), so both dtypes take the
+  // same load, with no branch between the loads: all 2 WI of them are in
+  // flight before the first use.  (The range is rounded up to whole words;
+  // the last word of a 16-bit array may hold two bytes past it, never used.)
+  auto raw = [&](const void* base, int dt, uint32_t (&w)[WI]) {
+    const bool wide = dt == F32;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, wide ? cnt * 4u : (cnt * 2u + 3u) & ~3u);
+#pragma unroll
+    for (int i = 0; i < WI; ++i) {
+      const int g = gq + 32 * i;
+      const uint32_t e = (uint32_t)n * ng + g;
+      const uint32_t o = (n < N && g < ng) ? (wide ? e * 4u : (e * 2u) & ~3u) : 0x80000000u;
+      w[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, o, 0, 0);
+    }
+  };
+  auto val = [&](uint32_t w, int i, int dt) {
+    if (dt == F32) return __uint_as_float(w);
+    const uint32_t h = (((uint32_t)n * ng + gq + 32 * i) & 1u) ? (w >> 16) : (w & 0xffffu);
+    return dt == F16 ? f16_bits_to_f32(h) : bf16_bits_to_f32(h);
+  };
+  uint32_t rsw[WI], rbw[WI];
+  raw(scales, s_dt, rsw);
+  raw(biases, b_dt, rbw);
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < WI; ++i) mx = fmaxf(mx, fabsf(val(rsw[i], i, s_dt)));
+  mx = fmaxf(mx, __shfl_xor(mx, 8));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  if (lane < PW) wmax[wave][lane] = mx;
+  __syncthreads();
+  const int e = exp_of(fmaxf(fmaxf(wmax[0][r], wmax[1][r]), fmaxf(wmax[2][r], wmax[3][r]))) - eshift;
+  if (t < PW) en[n0 + t] = e - mshift;  // the output's: B values carry 2^mshift
+  const float p2 = ldexpf(1.f, -e);
+  const int tpg = G == 128 ? 2 : 1;  // K tiles per group
+#pragma unroll
+  for (int i = 0; i < WI; ++i) {
+    const int g = gq + 32 * i;
+    if (g < ng) {
+      const float sv = val(rsw[i], i, s_dt), bv = val(rbw[i], i, b_dt);
+      const float cb = fmaf(off, sv, bv) * ldexpf(p2, mshift);  // with the B values' factor 2^mshift
+      const uint16_t th = f32_to_bf16_bits(cb);
+      const uint16_t tl = f32_to_bf16_bits(cb - bf16_bits_to_f32(th));
+      float rr = sv * p2;  // exact: a power of two
+      uint32_t pc[PS];
+#pragma unroll
+      for (int j = 0; j < PS; ++j) {
+        const float q = (j == PS - 1) ? rr : trunc_bf16(rr);
+        const uint32_t h = f32_to_f16_bits(q);
+        pc[j] = h | (h << 16);
+        rr -= q;
+      }
+      tB[tail_idx(n, 3 * g, Kt)] = th;
+      tB[tail_idx(n, 3 * g + 1, Kt)] = tl;
+      tB[tail_idx(n, 3 * g + 2, Kt)] = th;
+#pragma unroll
+      for (int j = 0; j < PS; ++j) {
+        if (G == 32) {
+          sh[(((long)(g >> 1) * Np + n) * 2 + (g & 1)) * PS + j] = pc[j];
+        } else {
+          for (int u = 0; u < tpg; ++u) sh[((long)(g * tpg + u) * Np + n) * PS + j] = pc[j];
+        }
+      }
+    }
+  }
+  // the tail's zero padding columns
+  const int pad = Kt - 3 * ng;
+  for (int i = t; i < PW * pad; i += 256) tB[tail_idx(n0 + i / pad, 3 * ng + i % pad, Kt)] = 0;
+}
+
 // prep_x and prep_w in one launch: blocks [0, Mp) take the rows of x, the
 // rest take PW rows of W each; the two halves run side by side.
 struct PrepArgs {
@@ -297,14 +443,20 @@ struct PrepArgs {
   int M, N, K, G, Kt, BM, Mp, Np, ng;
 };
 
-template <int BITS, int PS>
+template <int BITS, int PS, int RC>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
+  // the W rows first: their blocks are short and latency-bound, and run
+  // beside the rows of x instead of after them
+  const int nw = a.Np / PW;
   const int b = blockIdx.x;
-  if (b < a.Mp)
-    prep_x_row<BITS>(b, a.x, a.act_dt, a.k_perm, a.M, a.K, a.G, a.Kt, a.BM, a.xh, a.tA, a.em);
+  if (b >= nw)
+    prep_x_row<BITS, RC>(b - nw, a.x, a.act_dt, a.k_perm, a.M, a.K, a.G, a.Kt, a.BM, a.xh, a.tA, a.em);
+  else if (PW * a.ng <= 256 * WI)
+    prep_w_rows_once<PS>(b, a.scales, a.s_dt, a.biases, a.b_dt, a.off, a.eshift, a.mshift, a.N, a.Np, a.ng, a.G, a.Kt,
+                         a.sh, a.tB, a.en);
   else
-    prep_w_rows<PS>(b - a.Mp, a.scales, a.s_dt, a.biases, a.b_dt, a.off, a.eshift, a.mshift, a.N, a.Np, a.ng, a.G, a.Kt, a.sh, a.tB,
-                    a.en);
+    prep_w_rows<PS>(b, a.scales, a.s_dt, a.biases, a.b_dt, a.off, a.eshift, a.mshift, a.N, a.Np, a.ng, a.G, a.Kt, a.sh,
+                    a.tB, a.en);
 }
 
 // ---------------------------------------------------------------------------
@@ -763,12 +915,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   P.last_kt = nkt - 1;
 
   // ---- the bias tail first: acc = sum_g xs * cb on bf16 MFMA over the Kt
-  // tail columns (a multiple of 16 TD), first split only.  Operands come
+  // tail columns (a multiple of 16), first split only.  Operands come
   // straight from global memory (L2-resident), TD 16-column steps in flight;
   // the first ones are issued ahead of the first two tiles' copies, so their
-  // latency and the copies' overlap.
+  // latency and the copies' overlap.  A load for a step past the end re-reads
+  // the last step (in range, never used).  (Four or six steps in flight,
+  // where the registers allow, measured no faster.)
   constexpr int TD = 3;
   const bool tail = sp == 0;
+  const int nk = p.Kt / 16;
   // (fragment-ordered operands: a 32 x 16 block is 1 KiB, lane l's 16
   // bytes at 16 l; 32-row blocks are Kt/16 blocks apart)
   const long tblk = (long)(p.Kt >> 4) * 512;
@@ -790,24 +945,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   if (tail) {
 #pragma unroll
-    for (int i = 0; i < TD; ++i) tail_load(i, ta_r[i], tb_r[i]);
+    for (int i = 0; i < TD; ++i) tail_load(min(i, nk - 1), ta_r[i], tb_r[i]);
   }
 
   P.issue(0, xs[0], ws[0], ss[0]);
   P.issue(1, xs[1], ws[1], ss[1]);
 
   if (tail) {
-    const int nk = p.Kt / 16;
     int k = 0;
     for (; k + TD < nk; k += TD) {
 #pragma unroll
       for (int i = 0; i < TD; ++i) {
         tail_mfma(ta_r[i], tb_r[i]);
-        tail_load(k + TD + i, ta_r[i], tb_r[i]);
+        tail_load(min(k + TD + i, nk - 1), ta_r[i], tb_r[i]);
       }
     }
 #pragma unroll
-    for (int i = 0; i < TD; ++i) tail_mfma(ta_r[i], tb_r[i]);
+    for (int i = 0; i < TD; ++i)
+      if (k + i < nk) tail_mfma(ta_r[i], tb_r[i]);
   }
 
   uint32_t magic = 0x64006400u;
@@ -909,9 +1064,8 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
     return hipErrorNotSupported;
   const int M = (int)a.M, N = (int)a.N, K = (int)a.K, G = a.G;
   const int ng = K / G;
-  // tail columns: 3 per group, padded with zeros to whole rounds of the
-  // kernel's three 16-column steps in flight
-  const int Kt = (3 * ng + 47) / 48 * 48;
+  // tail columns: 3 per group, padded with zeros to whole 16-column MFMA steps
+  const int Kt = (3 * ng + 15) / 16 * 16;
   // the largest row tile whose grid still fills three quarters of the CUs
   // in one round: a bigger tile's efficiency is worth a few idle CUs, and a
   // grid just past one round runs its last tiles as a second round alone
@@ -989,7 +1143,16 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
   pa.Mp = Mp;
   pa.Np = Np;
   pa.ng = ng;
-  hipLaunchKernelGGL((prep_kernel<BITS, PS>), dim3(Mp + Np / PW), dim3(256), 0, s, pa);
+  // x rows held in registers between the two passes when they fit (RC
+  // 16-byte chunks a thread)
+  const int nch = K / 8;
+  const dim3 pg(Mp + Np / PW);
+  if (a.k_perm == nullptr && nch <= 256 * 2)
+    hipLaunchKernelGGL((prep_kernel<BITS, PS, 2>), pg, dim3(256), 0, s, pa);
+  else if (a.k_perm == nullptr && nch <= 256 * 8)
+    hipLaunchKernelGGL((prep_kernel<BITS, PS, 8>), pg, dim3(256), 0, s, pa);
+  else
+    hipLaunchKernelGGL((prep_kernel<BITS, PS, 0>), pg, dim3(256), 0, s, pa);
 
   GemmParams p;
   p.xh = xh;
