@@ -170,7 +170,8 @@ __device__ __forceinline__ void prep_x_row(int m, const void* __restrict__ x, in
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const int e = exp_of(amax);
   if (t == 0) em[m] = e;
-  const float sc = ldexpf(1.f, -e);
+  // (the exponent applied with ldexp: 2^-e itself overflows fp32 for rows
+  // whose largest |x| is below 2^-127, bf16 subnormals)
 
   // blocks of BLK permuted columns; the lanes that share a group are
   // consecutive and aligned, so the group sum is a butterfly over them
@@ -181,7 +182,7 @@ __device__ __forceinline__ void prep_x_row(int m, const void* __restrict__ x, in
       _Float16 out[BLK];
 #pragma unroll
       for (int j = 0; j < BLK; ++j) {
-        const float v = src[Perm<BITS>::src(j)] * sc;
+        const float v = ldexpf(src[Perm<BITS>::src(j)], -e);
         out[j] = (_Float16)v;
         part += v;
       }
@@ -301,11 +302,12 @@ __device__ __forceinline__ void prep_w_rows(int blk, const void* __restrict__ sc
     if (n < N) {
       const float sv = load_as_f32(scales, (long)n * ng + g, s_dt);
       const float bv = load_as_f32(biases, (long)n * ng + g, b_dt);
-      const float p2 = ldexpf(1.f, -e_s[r]);
-      const float cb = fmaf(off, sv, bv) * ldexpf(p2, mshift);  // with the B values' factor 2^mshift
+      // with the B values' factor 2^mshift; ldexp, as 2^-e overflows fp32 for
+      // scales below about 2^-121
+      const float cb = ldexpf(fmaf(off, sv, bv), mshift - e_s[r]);
       th = f32_to_bf16_bits(cb);
       tl = f32_to_bf16_bits(cb - bf16_bits_to_f32(th));
-      float rr = sv * p2;  // exact: a power of two
+      float rr = ldexpf(sv, -e_s[r]);  // exact
 #pragma unroll
       for (int j = 0; j < PS; ++j) {
         const float q = (j == PS - 1) ? rr : trunc_bf16(rr);
@@ -387,17 +389,16 @@ __device__ __forceinline__ void prep_w_rows_once(int blk, const void* __restrict
   __syncthreads();
   const int e = exp_of(fmaxf(fmaxf(wmax[0][r], wmax[1][r]), fmaxf(wmax[2][r], wmax[3][r]))) - eshift;
   if (t < PW) en[n0 + t] = e - mshift;  // the output's: B values carry 2^mshift
-  const float p2 = ldexpf(1.f, -e);
   const int tpg = G == 128 ? 2 : 1;  // K tiles per group
 #pragma unroll
   for (int i = 0; i < WI; ++i) {
     const int g = gq + 32 * i;
     if (g < ng) {
       const float sv = val(rsw[i], i, s_dt), bv = val(rbw[i], i, b_dt);
-      const float cb = fmaf(off, sv, bv) * ldexpf(p2, mshift);  // with the B values' factor 2^mshift
+      const float cb = ldexpf(fmaf(off, sv, bv), mshift - e);  // with the B values' factor 2^mshift
       const uint16_t th = f32_to_bf16_bits(cb);
       const uint16_t tl = f32_to_bf16_bits(cb - bf16_bits_to_f32(th));
-      float rr = sv * p2;  // exact: a power of two
+      float rr = ldexpf(sv, -e);  // exact
       uint32_t pc[PS];
 #pragma unroll
       for (int j = 0; j < PS; ++j) {

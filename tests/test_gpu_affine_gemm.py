@@ -187,3 +187,41 @@ def test_padded_rows_offset_guard():
         qa.qmm_affine(x, w, s, s, G, bits, out=y)
     torch.cuda.synchronize()
     assert ei.value.status == 2, str(ei.value)   # QAFF_E_UNSUPPORTED
+
+
+@pytest.mark.parametrize("K,G,bits", [(17408, 32, 4), (8704, 32, 8), (8192, 64, 2), (16384, 128, 4)])
+def test_prepass_row_lengths(K, G, bits):
+    # the pre-pass holds a row of x in registers up to K = 16384 and reads it
+    # twice past that (17408); W rows take every scale and bias load at once
+    # up to 256 groups and a loop past that (G = 32 at K = 8704, 17408)
+    case = si.affine_case(70, 264, K, G, bits, seed=(23, K, G, bits), scale_range=(0.002, 0.01),
+                          name=f"gemm_prepass_K{K}_G{G}_b{bits}")
+    y = _run(case)
+    assert_float_bar(host_f64(y), oracle.qmm_affine_case(case), case.name)
+
+
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+def test_prepass_row_maximum_special_rows(act):
+    # rows whose maximum |x| the pre-pass takes on the raw bits: a NaN (left
+    # out of the maximum; the row's outputs are all NaN on both sides), a
+    # maximum near the dtype's top, subnormals only (their scale 2^-e is
+    # past fp32's range for bf16), all zeros, and negative zeros
+    M, N, K, G = 70, 130, 1024, 64
+    case = si.affine_case(M, N, K, G, 4, seed=(24, act == "f16"), act_dtype=act, scale_range=(0.002, 0.004),
+                          name=f"gemm_rowmax_{act}")
+    xf = si.bits_to_f32(case.x, act).astype(np.float64).reshape(M, K)
+    big = 65504.0 / 64 if act == "f16" else 3.0e36
+    tiny = 2.0 ** -20 if act == "f16" else 2.0 ** -130
+    xf[3, 5] = np.nan
+    xf[10, :] *= big / np.abs(xf[10]).max()       # the row's maximum at the dtype's top
+    xf[20, :] = tiny * np.sign(xf[20])             # subnormal values only
+    xf[30, :] = 0.0
+    xf[40, :] = -0.0
+    case.x = si.store(xf.astype(np.float32), act).reshape(case.x.shape)
+    y = host_f64(_run(case))
+    ref = oracle.qmm_affine_case(case)
+    assert np.isnan(y[3]).all() and np.isnan(ref[3]).all()
+    keep = np.ones(M, bool)
+    keep[3] = False
+    assert_float_bar(y[keep], ref[keep], case.name)
+    assert (y[30] == 0).all() and (y[40] == 0).all()
