@@ -261,11 +261,12 @@ int qgemv_affine_chain_free(void *plan);
  *   qweight [K/8, N]  int32 (read as uint32),   qzeros [K/G, N/8] int32
  *   scales  [K/G, N]  f16;                       g_idx [K] int32 or NULL,
  *           values in [0, K/G) (not checked on the device)
- *   K % 8 == 0, K % G == 0, N % 8 == 0, G in {32, 64, 128}; with g_idx, at
- *   most 192 groups (K/G), else QAFF_E_UNSUPPORTED (the per-workgroup table
- *   of scales and zeros for every group must fit in LDS).  A layer without
- *   act-order (g_idx[i] = i/G) should pass g_idx = NULL: then a workgroup's
- *   table holds only the groups of its K slice, and any K/G is taken.
+ *   K % 8 == 0, K % G == 0, N % 8 == 0, G in {32, 64, 128}.  With g_idx,
+ *   each workgroup keeps a table of (scale, bias) for every group in LDS
+ *   when it fits; with more groups than that, a pre-pass writes the table to
+ *   library scratch and the kernel reads it through L2 (slower).  A layer
+ *   without act-order (g_idx[i] = i/G) should pass g_idx = NULL: then a
+ *   workgroup's table holds only the groups of its K slice.
  * Kernels: M < 8 on the VALU (w exact in fp32); M >= 8 on the matrix cores
  * (w as two exact fp16 pieces relative to each column's largest scale in
  * the table) when g_idx is NULL or there are at most 96 groups, else on
