@@ -1069,12 +1069,17 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
   const int Kt = (3 * ng + 15) / 16 * 16;
   // the largest row tile whose grid still fills three quarters of the CUs
   // in one round: a bigger tile's efficiency is worth a few idle CUs, and a
-  // grid just past one round runs its last tiles as a second round alone
+  // grid just past one round runs its last tiles as a second round alone.
+  // When no tile does (few columns: K is split below), 128-row tiles from
+  // M = 1024 on: each decoded code serves twice the rows of a 64-row tile,
+  // against twice the splits (M = 2048, N = 1024, K = 4096: 8-bit 70-76 ->
+  // 62 us, 4-bit 49-50 -> 48.5 us; 256-row tiles with 8 splits were slower)
   int MB = 2;
   if (M > 64) {
     const int64_t tn = (N + BN - 1) / BN;
     if ((int64_t)((M + 255) / 256) * tn >= 192) MB = 8;
     else if ((int64_t)((M + 127) / 128) * tn >= 192) MB = 4;
+    else if (M >= 1024) MB = 4;
   }
   // 8-bit codes with three scale pieces do not fit the registers of the
   // 256-row tile
