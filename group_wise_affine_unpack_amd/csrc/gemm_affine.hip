@@ -1070,6 +1070,11 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
   // the largest row tile whose grid still fills three quarters of the CUs
   // in one round: a bigger tile's efficiency is worth a few idle CUs, and a
   // grid just past one round runs its last tiles as a second round alone.
+  // With a long K, 256-row tiles that fill half the CUs take K in two
+  // splits instead of 128-row tiles (the bigger tile decodes each code for
+  // twice the rows; the fp32 partials cost less than that saves from K =
+  // 8192 on: M = 2048, N = 4096, K = 14336: 4-bit 292-295 -> 265-268 us,
+  // 8-bit 451-454 -> 430-432 us; at K = 4096 it was 4-10% slower).
   // When no tile does (few columns: K is split below), 128-row tiles from
   // M = 1024 on: each decoded code serves twice the rows of a 64-row tile,
   // against twice the splits (M = 2048, N = 1024, K = 4096: 8-bit 70-76 ->
@@ -1078,6 +1083,7 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
   if (M > 64) {
     const int64_t tn = (N + BN - 1) / BN;
     if ((int64_t)((M + 255) / 256) * tn >= 192) MB = 8;
+    else if ((int64_t)((M + 255) / 256) * tn >= 96 && K >= 8192) MB = 8;
     else if ((int64_t)((M + 127) / 128) * tn >= 192) MB = 4;
     else if (M >= 1024) MB = 4;
   }
