@@ -225,3 +225,37 @@ def test_prepass_row_maximum_special_rows(act):
     keep[3] = False
     assert_float_bar(y[keep], ref[keep], case.name)
     assert (y[30] == 0).all() and (y[40] == 0).all()
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_long_k_split_of_256_row_tiles(bits):
+    # From K = 8192, 256-row tiles that fill half the CUs take K in two
+    # splits (fp32 partials, then the summing pass): M = 2048, N = 3072 gives
+    # 8 x 12 = 96 tiles.  Every column of 40 rows (tile edges included).
+    M, N, K = 2048, 3072, 8192
+    case = si.affine_case(M, N, K, 64, bits, seed=(25, bits), scale_range=(0.002, 0.01),
+                          name=f"gemm_longk_split_b{bits}")
+    y = _run(case)
+    rows = np.unique(np.concatenate([si.sample_indices(M, 32, seed=(25, 1, bits)),
+                                     np.array([0, 255, 256, 1023, 1024, 1791, 1792, 2047])])).astype(np.int64)
+    cols = np.arange(N, dtype=np.int64)
+    ysub = host_f64(y[torch.from_numpy(rows).to(y.device)])
+    assert_float_bar(ysub, oracle.qmm_affine_case(case, rows=rows, cols=cols), case.name)
+    assert torch.isfinite(y.float()).all()
+
+
+@pytest.mark.parametrize("M", [512, 500])
+@pytest.mark.parametrize("bits", [2, 4])
+def test_256_row_tiles_wide_n(M, bits):
+    # 256-row tiles without a K split: M = 512 (500: a ragged last row tile)
+    # x N = 24576 is 192 of them.  Every column of 40 rows, edges of the
+    # 128- and 256-row blocks included.
+    N, K = 24576, 1024
+    case = si.affine_case(M, N, K, 64, bits, seed=(26, M, bits), scale_range=(0.002, 0.01),
+                          name=f"gemm_wide_M{M}_b{bits}")
+    y = _run(case)
+    rows = np.unique(np.concatenate([si.sample_indices(M, 32, seed=(26, 1, M)),
+                                     np.array([0, 127, 128, 255, 256, 383, 384, M - 1])])).astype(np.int64)
+    ysub = host_f64(y[torch.from_numpy(rows).to(y.device)])
+    assert_float_bar(ysub, oracle.qmm_affine_case(case, rows=rows, cols=np.arange(N, dtype=np.int64)), case.name)
+    assert torch.isfinite(y.float()).all()
