@@ -549,7 +549,6 @@ __global__ __launch_bounds__(256, 2) void gemv_mfma4_kernel(MfmaBatch B) {
   constexpr int NB = 4, GPS = Geo::GPS, WPG = Geo::WPG;
   using frag_t = typename std::conditional<F16, f16x8_t, bf16x8_t>::type;
   using X = u32x4_t[4];
-  using W = u32x4_t[4];
   constexpr int CS = Geo::CS;
   constexpr float OFF = F16 ? 1024.f : 128.f;
   __shared__ __attribute__((aligned(1024))) unsigned char st0[Geo::STAGE];
