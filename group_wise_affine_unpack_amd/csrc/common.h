@@ -42,6 +42,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
   return __builtin_bit_cast(uint16_t, (_Float16)v);
 }
+// Two floats rounded to f16 (nearest even) in one word, the first in the low
+// half, each exactly as f32_to_f16_bits rounds it on its own: where the value
+// is a product, the compiler folds that multiply into the rounding (one
+// v_fma_mix, a single rounding of the exact product), and a packed
+// conversion of the two fp32 products would round twice (measured to differ
+// on about 0.007% of W4A8 outputs).  The barrier keeps the pair from being
+// merged into the packed conversion.
+__device__ __forceinline__ uint32_t f32x2_to_f16x2_bits(float lo, float hi) {
+  uint32_t a = f32_to_f16_bits(lo), b = f32_to_f16_bits(hi);
+  asm volatile("" : "+v"(a), "+v"(b));
+  return a | (b << 16);
+}
 __device__ __forceinline__ uint16_t f32_to_act_bits(float v, bool f16) {
   return f16 ? f32_to_f16_bits(v) : f32_to_bf16_bits(v);
 }

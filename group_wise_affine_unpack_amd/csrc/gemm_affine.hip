@@ -776,8 +776,9 @@ struct Gemm {
 // Epilogue of a tile whose rows all exist: y = 2^(e_m + e_n) * acc, rounded
 // to the activation dtype.  32x32 accumulator layout: lane -> column l32;
 // register r -> row 8*(r/4) + 4*half + r%4, so registers 2i and 2i+1 are
-// consecutive rows of one column: one packed conversion, two 2-byte stores
-// (the second from the high half).
+// consecutive rows of one column: one packed pair (bf16: one packed
+// conversion, the instruction a single value takes too; f16: two scalar
+// conversions), two 2-byte stores (the second from the high half).
 template <bool OUT_F16, int MB>
 __device__ __forceinline__ void epilogue_full(const f32x16_t (&acc)[MB][2], const int* em_s, const GemmParams& p,
                                               int m0, int n0, int row0, int half, int l32, int wn) {
@@ -801,7 +802,7 @@ __device__ __forceinline__ void epilogue_full(const f32x16_t (&acc)[MB][2], cons
             const float v1 = ldexpf(acc[mb][nb][4 * rq + j + 1], e4[j + 1] + e_n);
             uint32_t pk;
             if constexpr (OUT_F16)
-              pk = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){v0, v1}, f16x2_t));
+              pk = f32x2_to_f16x2_bits(v0, v1);
             else
               pk = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){v0, v1}, bf16x2_t));
             // the rows' addresses as scalar values (kept out of the lane
@@ -1073,8 +1074,7 @@ __global__ __launch_bounds__(256) void gemm_split_sum8_kernel(const float* __res
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const f32x2_t v = j < 2 ? f32x2_t{a[2 * j], a[2 * j + 1]} : f32x2_t{b[2 * j - 4], b[2 * j - 3]};
-    o[j] = out_f16 ? __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t))
-                   : __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+    o[j] = out_f16 ? f32x2_to_f16x2_bits(v[0], v[1]) : __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
   }
   *reinterpret_cast<u32x4_t*>(y + i) = o;
 }

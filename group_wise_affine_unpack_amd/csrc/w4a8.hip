@@ -504,6 +504,40 @@ __global__ __launch_bounds__(256) void w4a8_gemm_kernel(Params p) {
       else
         sxv[mb][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsx, (uint32_t)(m0 + rr) * 4u, 0, 0));
     }
+  if (m0 + BM <= p.M && p.acc_out == nullptr) {
+    // Every row of the tile exists and no accumulators are asked for: the
+    // row offset is uniform and goes into the scalar base address, the lane
+    // keeps one offset for all its stores, and registers r and r+1 (r even:
+    // consecutive rows of one column) are rounded as below and stored as the
+    // low and the high half of one word.
+    const long N = p.N;
+    const int wu = __builtin_amdgcn_readfirstlane(wave);  // (uniform: the base goes in scalar registers)
+    const uint64_t yw = reinterpret_cast<uint64_t>(p.y + (long)m0 * N + n0 + wu * NB * 32);
+    typedef __attribute__((address_space(1))) unsigned char gbyte;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int n = n0 + wave * NB * 32 + nb * 32 + l32;
+      if (n >= p.N) continue;
+      const float swn = f16_bits_to_f32(p.sw[n]);
+      const uint32_t lo = (uint32_t)(4 * h * N + nb * 32 + l32) * 2u;  // lane part, bytes
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float v0 = ((float)(acc[mb][nb][r] >> 4) * sxv[mb][r]) * swn;
+          const float v1 = ((float)(acc[mb][nb][r + 1] >> 4) * sxv[mb][r + 1]) * swn;
+          const uint32_t pk = f32x2_to_f16x2_bits(v0, v1);
+          uint64_t r0 = yw + (uint64_t)((mb * 32 + 8 * (r >> 2) + (r & 3)) * N * 2);
+          uint64_t r1 = r0 + (uint64_t)(N * 2);
+          asm volatile("" : "+s"(r0), "+s"(r1));
+          *reinterpret_cast<__attribute__((address_space(1))) uint16_t*>(reinterpret_cast<gbyte*>(r0) + lo) =
+              (uint16_t)pk;
+          *reinterpret_cast<__attribute__((address_space(1))) uint16_t*>(reinterpret_cast<gbyte*>(r1) + lo) =
+              (uint16_t)(pk >> 16);
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int n = n0 + wave * NB * 32 + nb * 32 + l32;

@@ -226,3 +226,28 @@ def test_tiled_rejects_small_m_and_unbuilt_tiles():
     with pytest.raises(qa.QaffError) as e2:
         qa.qgemm_w4a8_tiled(x2, w, sw, True, 96, 128)
     assert e2.value.status == 2
+
+
+@pytest.mark.parametrize("M,N,K,bm,bn,staged", [
+    (2048, 4096, 1024, 128, 256, False), (256, 1000, 2048, 64, 256, False), (300, 1024, 1024, 64, 128, False),
+    (128, 520, 4096, 32, 128, True), (2048, 1024, 1024, 128, 256, True)])
+def test_epilogue_paths_same_bits(M, N, K, bm, bn, staged):
+    # Without accumulators asked for, tiles whose rows all exist store y from
+    # scalar row bases and packed conversions; with them (or in a ragged last
+    # row tile) the per-value path runs.  Both round the same product, so y
+    # must be the same bits (M = 300 and N = 1000 / 520: ragged tiles).
+    from gpu_util import dev16
+    case = si.w4a8_case(M, N, K, seed=(65, M, N), name=f"w4a8_epi_M{M}_N{N}_K{K}_{bm}x{bn}_{staged}")
+    dev = require_gpu()
+    x = dev16(case.x, "f16", dev)
+    w = torch.from_numpy(np.ascontiguousarray(case.w_q4).view(np.int32)).to(dev)
+    sw = dev16(case.s_w, "f16", dev)
+    print(f"[case] {case.name}", flush=True)
+    y0, _, _, _ = qa.qgemm_w4a8_tiled(x, w, sw, staged, bm, bn, want_acc=False)
+    y1, _, _, acc = qa.qgemm_w4a8_tiled(x, w, sw, staged, bm, bn, want_acc=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y0.cpu().numpy().view(np.uint16), y1.cpu().numpy().view(np.uint16))
+    if M == 2048 and not staged:
+        y2, _, _, _ = qa.qgemm_w4a8(x, w, sw)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(y2.cpu().numpy().view(np.uint16), y1.cpu().numpy().view(np.uint16))
