@@ -259,3 +259,20 @@ def test_256_row_tiles_wide_n(M, bits):
     ysub = host_f64(y[torch.from_numpy(rows).to(y.device)])
     assert_float_bar(ysub, oracle.qmm_affine_case(case, rows=rows, cols=np.arange(N, dtype=np.int64)), case.name)
     assert torch.isfinite(y.float()).all()
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_xcd_tile_rectangles_ragged(bits):
+    # Without a K split, a tile grid divisible 4 x 2 is dealt to the XCDs as
+    # rectangles: M = 1000, N = 12200 is 4 x 48 tiles of 256 x 256, with a
+    # ragged last row tile (768..999) and a ragged last column tile.  Every
+    # column of 40 rows, tile edges included.
+    M, N, K = 1000, 12200, 1024
+    case = si.affine_case(M, N, K, 64, bits, seed=(27, bits), scale_range=(0.002, 0.01),
+                          name=f"gemm_rect_b{bits}")
+    y = _run(case)
+    rows = np.unique(np.concatenate([si.sample_indices(M, 32, seed=(27, 1, bits)),
+                                     np.array([0, 255, 256, 511, 512, 767, 768, 999])])).astype(np.int64)
+    ysub = host_f64(y[torch.from_numpy(rows).to(y.device)])
+    assert_float_bar(ysub, oracle.qmm_affine_case(case, rows=rows, cols=np.arange(N, dtype=np.int64)), case.name)
+    assert torch.isfinite(y.float()).all()
