@@ -475,7 +475,7 @@ struct GemmParams {
   int M, N, K, ng, Kt, G;
   int Np, gsh;  // padded row count of the W-side scratch; log2(G) - 5
   int Tm, Tn, per_xcd;
-  int rect;     // XCD tile rectangles (see the kernel)
+  int rect;     // XCD tile rectangles: 0, or the row-block split a (4 or 2; see the kernel)
   int out_f16;
   int S;        // K splits; S > 1 writes fp32 partials [S][M][N] to `part`
   float* part;
@@ -833,11 +833,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int v = vs / p.S, sp = vs % p.S;
   int tm = v / p.Tn, tn = v % p.Tn;
   if (p.rect) {
-    // XCD x takes the tile rectangle (x / 2, x % 2) of a 4 x 2 split of the
-    // grid, row blocks fastest (p.S == 1, Tm % 4 == 0, Tn % 2 == 0)
-    const int x = b & 7, j = b >> 3, rm = p.Tm / 4, rn = p.Tn / 2;
-    tm = (x >> 1) * rm + j % rm;
-    tn = (x & 1) * rn + j / rm;
+    // XCD x takes the tile rectangle (x / nb, x % nb) of an a x nb split of
+    // the grid (a = p.rect, a * nb = 8), row blocks fastest (p.S == 1,
+    // Tm % a == 0, Tn % nb == 0)
+    const int a = p.rect, nb = 8 / a;
+    const int x = b & 7, j = b >> 3, rm = p.Tm / a, rn = p.Tn / nb;
+    tm = (x / nb) * rm + j % rm;
+    tn = (x % nb) * rn + j / rm;
   }
   const int m0 = tm * BM, n0 = tn * BN;
   const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, half = lane >> 5;
@@ -1221,12 +1223,20 @@ hipError_t run(const AffineArgs& a, hipStream_t s) {
   p.S = S;
   p.part = S > 1 ? (float*)(scratch + o_pt) : nullptr;
   p.per_xcd = (p.Tm * p.Tn * S + 7) / 8;
-  // Without a K split, each XCD takes a rectangle of the tile grid (a 4 x 2
-  // split) instead of whole rows of tiles: the tiles resident on one XCD then
-  // share a quarter of x's row blocks and half of W's columns through its L2
-  // (M = 2048, N = 14336, 4-bit: 251-255 -> 244-246 us; 8-bit N = K = 4096:
-  // 150-154 -> 145-146 us).
-  p.rect = S == 1 && p.Tm % 4 == 0 && p.Tn % 2 == 0;
+  // Without a K split, each XCD takes a rectangle of the tile grid instead of
+  // whole rows of tiles: the tiles resident on one XCD then share some of
+  // x's row blocks and of W's columns through its L2 (with a 4 x 2 split,
+  // M = 2048, N = 14336, 4-bit: 251-255 -> 244-246 us; 8-bit N = K = 4096:
+  // 150-154 -> 145-146 us).  Of the 4 x 2 and 2 x 4 splits, the one whose
+  // rectangle holds fewer bytes of x and W.
+  p.rect = 0;
+  if (S == 1) {
+    const double xb = (double)BM * K * 2, wb = (double)BN * K * BITS / 8;
+    auto bytes = [&](int a) { return (p.Tm / a) * xb + (p.Tn / (8 / a)) * wb; };
+    const bool ok4 = p.Tm % 4 == 0 && p.Tn % 2 == 0, ok2 = p.Tm % 2 == 0 && p.Tn % 4 == 0;
+    if (ok4 && (!ok2 || bytes(4) <= bytes(2))) p.rect = 4;
+    else if (ok2) p.rect = 2;
+  }
   const dim3 grid(8 * p.per_xcd);
   // row tile BM = 32 MB: each wave takes MB/2 32-row blocks
   if (MB == 2)
