@@ -225,20 +225,23 @@ def graph_replay_times(torch, fn, replays, warmup=2):
 
 def time_stream_read(torch, qa, device, nbytes=1 << 30, iters=20):
     """The achievable streaming-read rate: qaff_stream_read over 1 GiB, the
-    best of three grid sizes, median of `iters` launches each."""
+    best of five grid sizes (2 to 32 workgroups per CU), median of `iters`
+    launches each.  The rate depends on the grid: 4 workgroups per CU read
+    faster than 8 or more."""
     buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
     buf.fill_(3)
-    best = None
-    for blocks in (2048, 4096, 8192):
+    best, by_grid = None, {}
+    for blocks in (512, 1024, 2048, 4096, 8192):
         sink = torch.empty(blocks * 256, dtype=torch.int32, device=device)
         t = pct(event_times(torch, lambda: qa.stream_read(buf, sink, blocks), iters, 3))
         gbs = nbytes / (t["median_us"] * 1e-6) / 1e9
+        by_grid[str(blocks)] = round(gbs, 1)
         if best is None or gbs > best["gbs"]:
             best = {"bytes": nbytes, "blocks": blocks, **t, "gbs": round(gbs, 1),
                     "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
     del buf
     torch.cuda.empty_cache()
-    return best
+    return {**best, "gbs_by_grid": by_grid}
 
 
 def time_cold_gemv(torch, qa, si, device, N, K, Ms=(1, 4, 16), min_bytes=1 << 30, replays=5):
